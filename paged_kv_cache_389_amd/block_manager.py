@@ -1,0 +1,193 @@
+"""Host-side block manager: physical block pool, block tables, reference counts,
+fork and copy-on-write.
+
+This is the host logic that produces the integer inputs of the three device
+calls (block tables, context lengths, slot mappings, copy pairs).  It does no
+device work.
+
+Behaviour, from the pages:
+
+* The KV memory is a pool of equal-sized physical blocks; a sequence is a run
+  of logical blocks that map to arbitrary physical blocks through a per-
+  sequence block table ("Memory Optimization in LLM Serving with
+  PagedAttention", section "How PagedAttention Works", items 1-3).
+* A block is taken from the pool only when the sequence needs it; nothing is
+  reserved up front, so only the last block of a sequence is partly filled
+  (same section, the two bullets after the list; "vLLM and PagedAttention:
+  How Ideas from Operating Systems Accelerated LLM Inference", paragraph on the
+  solution).
+* Sequences may share physical blocks (parallel sampling, beam search,
+  common prefixes).  Each block carries a reference count.  Before appending
+  into a shared block (count above one) the sequence gets a fresh block, the
+  content is copied into it, the table entry is redirected to the copy, and
+  only then is the token written ("Memory Optimization ...", section
+  "Advanced Capabilities: Memory Sharing with Copy-on-Write"; "vLLM and
+  PagedAttention ...", paragraph on sharing).
+
+Readings where the pages are silent:
+
+* The count of the old block drops by one when a holder moves to its copy.
+* A holder that finds the count at one writes in place (no copy).
+* Slot numbering: slot ``b * block_size + o`` is offset ``o`` of block ``b``.
+* Free blocks are handed out from the end of a free list; its initial order
+  may be given (a seeded permutation gives random placement).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+class OutOfBlocks(RuntimeError):
+    """The pool has no free block; the manager's state is left unchanged."""
+
+
+class Sequence:
+    """One sequence's logical view: its block table and its token count."""
+
+    __slots__ = ("seq_id", "table", "length")
+
+    def __init__(self, seq_id: int):
+        self.seq_id = seq_id
+        self.table: list[int] = []
+        self.length = 0
+
+    def __repr__(self):
+        return f"Sequence(id={self.seq_id}, len={self.length}, table={self.table})"
+
+
+class BlockManager:
+    """A pool of ``num_blocks`` physical blocks of ``block_size`` token slots."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        if free_order is None:
+            # pop() takes from the end, so block 0 is handed out first
+            self._free = list(range(self.num_blocks - 1, -1, -1))
+        else:
+            order = [int(b) for b in free_order]
+            if sorted(order) != list(range(self.num_blocks)):
+                raise ValueError("free_order must be a permutation of the pool")
+            self._free = order
+        self.refcount = np.zeros(self.num_blocks, dtype=np.int64)
+        self._next_id = 0
+        # copy-on-write pairs (src, dst) emitted since the last take_copy_pairs()
+        self._pending_copies: list[tuple[int, int]] = []
+
+    # ------------------------------------------------------------------ pool
+    @property
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def free_blocks(self) -> list[int]:
+        return list(self._free)
+
+    def _take(self) -> int:
+        if not self._free:
+            raise OutOfBlocks(f"pool of {self.num_blocks} blocks is exhausted")
+        b = self._free.pop()
+        self.refcount[b] = 1
+        return b
+
+    def _release(self, b: int) -> None:
+        self.refcount[b] -= 1
+        if self.refcount[b] < 0:
+            raise AssertionError(f"block {b} released more often than held")
+        if self.refcount[b] == 0:
+            self._free.append(b)
+
+    # ------------------------------------------------------------- sequences
+    def new_sequence(self) -> Sequence:
+        seq = Sequence(self._next_id)
+        self._next_id += 1
+        return seq
+
+    def append_slot(self, seq: Sequence) -> int:
+        """Reserve the slot of the sequence's next token and return it.
+
+        Takes a new block when the last one is full (or there is none);
+        performs copy-on-write when the last block is partly filled and shared.
+        Raises :class:`OutOfBlocks` without changing any state if the pool
+        cannot supply the block.
+        """
+        bs = self.block_size
+        offset = seq.length % bs
+        if offset == 0:
+            seq.table.append(self._take())
+        else:
+            last = seq.table[-1]
+            if self.refcount[last] > 1:
+                fresh = self._take()
+                self.refcount[last] -= 1
+                seq.table[-1] = fresh
+                self._pending_copies.append((last, fresh))
+        slot = seq.table[seq.length // bs] * bs + offset
+        seq.length += 1
+        return slot
+
+    def extend(self, seq: Sequence, num_tokens: int) -> np.ndarray:
+        """Append ``num_tokens`` tokens; returns their slots (int64)."""
+        if num_tokens < 0:
+            raise ValueError("num_tokens must be >= 0")
+        bs = self.block_size
+        need = -(-(seq.length + num_tokens) // bs) - len(seq.table)
+        shared_tail = (seq.length % bs != 0 and num_tokens > 0
+                       and self.refcount[seq.table[-1]] > 1)
+        if need + int(shared_tail) > self.num_free:
+            raise OutOfBlocks(
+                f"need {need + int(shared_tail)} blocks, {self.num_free} free")
+        return np.array([self.append_slot(seq) for _ in range(num_tokens)],
+                        dtype=np.int64)
+
+    def fork(self, parent: Sequence) -> Sequence:
+        """A child that shares every block of ``parent`` (counts go up by one)."""
+        child = self.new_sequence()
+        child.table = list(parent.table)
+        child.length = parent.length
+        for b in child.table:
+            self.refcount[b] += 1
+        return child
+
+    def free(self, seq: Sequence) -> None:
+        """Drop the sequence's hold on its blocks; unreferenced blocks return."""
+        for b in reversed(seq.table):
+            self._release(b)
+        seq.table = []
+        seq.length = 0
+
+    def take_copy_pairs(self) -> np.ndarray:
+        """Copy-on-write pairs emitted since the last call, as int64 [n, 2]."""
+        pairs = np.array(self._pending_copies, dtype=np.int64).reshape(-1, 2)
+        self._pending_copies = []
+        return pairs
+
+    # ------------------------------------------------------------ exports
+    def block_table_array(self, seqs, width: int | None = None, pad: int = 0):
+        """int32 ``[len(seqs), width]`` block tables, padded with ``pad``."""
+        need = max((len(s.table) for s in seqs), default=0)
+        width = need if width is None else int(width)
+        if width < need:
+            raise ValueError("width is smaller than the longest block table")
+        arr = np.full((len(seqs), max(width, 1)), pad, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            arr[i, :len(s.table)] = s.table
+        return arr
+
+    def context_lens(self, seqs) -> np.ndarray:
+        return np.array([s.length for s in seqs], dtype=np.int32)
+
+    def utilisation(self, seqs) -> float:
+        """Filled token slots over allocated slots, each shared block counted
+        once (the page-level memory figure the pages quote)."""
+        allocated = int(np.count_nonzero(self.refcount)) * self.block_size
+        if allocated == 0:
+            return 1.0
+        filled = {}
+        for s in seqs:
+            for j, b in enumerate(s.table):
+                used = min(self.block_size, s.length - j * self.block_size)
+                filled[b] = max(filled.get(b, 0), used)
+        return sum(filled.values()) / allocated

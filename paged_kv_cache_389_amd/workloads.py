@@ -1,0 +1,325 @@
+"""Seeded synthetic workloads for the paged decode path.
+
+This module only draws random numbers and asks the host block manager for
+block tables and slots.  It holds none of the attention or cache arithmetic,
+so both the device path and the CPU oracle can be fed from it.
+
+Five workload shapes (names used throughout the tests and the benchmark):
+
+``tiny_fp32``
+    4 sequences, 4 query heads = 4 KV heads, head_dim 64, block_size 16,
+    context lengths uniform in [1, 64], a pool of 32 blocks handed out in a
+    random order; scale 1/sqrt(64).
+``opt13b_fp16``
+    OPT-13B-shaped decode layer: 40 heads (MHA), head_dim 128, block_size 16,
+    64 sequences, context lengths uniform in [128, 2048], blocks drawn at
+    random from a pool of 8192.
+``llama3_8b_gqa_bf16``
+    Llama-3-8B-shaped GQA decode: 32 query / 8 KV heads, head_dim 128,
+    block_size 16, 256 sequences, context lengths log-uniform in [16, 4096],
+    random placement in a pool of 32768 blocks; each step first writes one new
+    token per sequence through the slot mapping (the new token is the last
+    of the ``L`` positions it then attends over).
+``long_context_gqa_bf16``
+    64 query / 8 KV heads, head_dim 128, block_size 32, 8 sequences, context
+    lengths uniform in [16384, 32768], random placement in a pool of 12288
+    blocks; 1% of key rows are multiplied by 8 after the cast.
+``sharing_fp16``
+    32 prompts, each forked into 8 sequences that share the prompt's blocks
+    through reference counts, then diverge by 0-256 generated tokens; the
+    first append into the shared partly filled last block triggers
+    copy-on-write.  32 heads (MHA), head_dim 128, block_size 16, pool of 8192.
+
+Values are N(0, 1) float32 draws cast (round to nearest even) to the
+workload dtype.  Integer draws use numpy's PCG64 seeded with the workload
+seed; tensor draws use a torch generator on the target device seeded with
+the same seed, in the order q, K pool, V pool, key-outlier mask, new K, new V.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from .block_manager import BlockManager
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class DecodeStepInputs:
+    """The integer and tensor inputs of one decode step's cache writes."""
+    copy_pairs: np.ndarray          # int64 [n_pairs, 2]
+    slot_mapping: np.ndarray        # int64 [n_tokens]
+    seq_index: np.ndarray           # int64 [n_tokens], sequence of each token
+    new_k: torch.Tensor | None = None   # [n_tokens, Hkv, hd]
+    new_v: torch.Tensor | None = None
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: torch.dtype
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    seed: int
+    context_lens: np.ndarray        # int32 [B]
+    block_tables: np.ndarray        # int32 [B, W]
+    q: torch.Tensor                 # [B, Hq, hd]
+    k_cache: torch.Tensor           # [num_blocks, Hkv, bs, hd]
+    v_cache: torch.Tensor
+    # the cache writes of the (last) step, applied before the attention
+    step: DecodeStepInputs | None = None
+    # multi-step history (sharing workload): every step's writes, in order
+    history: list = field(default_factory=list)
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max(initial=0))
+
+    @property
+    def esize(self) -> int:
+        return torch.tensor([], dtype=self.dtype).element_size()
+
+    def kv_bytes(self) -> int:
+        """K+V bytes the attention must read: each sequence's own context."""
+        return int(self.context_lens.astype(np.int64).sum()) * 2 * \
+            self.num_kv_heads * self.head_dim * self.esize
+
+    def unique_kv_bytes(self) -> int:
+        """K+V bytes of the distinct physical token slots referenced."""
+        bs = self.block_size
+        filled = {}
+        for s in range(self.num_seqs):
+            L = int(self.context_lens[s])
+            for j in range((L + bs - 1) // bs):
+                b = int(self.block_tables[s, j])
+                filled[b] = max(filled.get(b, 0), min(bs, L - j * bs))
+        return sum(filled.values()) * 2 * self.num_kv_heads * self.head_dim * self.esize
+
+    def decode_bytes(self) -> int:
+        """Algorithmic bytes of one decode call: K/V, q in, out, tables, lens."""
+        bs = self.block_size
+        nblk = int(((self.context_lens.astype(np.int64) + bs - 1) // bs).sum())
+        qo = 2 * self.num_seqs * self.num_q_heads * self.head_dim * self.esize
+        return self.kv_bytes() + qo + 4 * nblk + 4 * self.num_seqs
+
+    def write_bytes(self) -> int:
+        """Algorithmic bytes of the step's cache writes (read + write, K and V)."""
+        if self.step is None:
+            return 0
+        row = self.num_kv_heads * self.head_dim * self.esize
+        n_tok = len(self.step.slot_mapping)
+        n_pair = len(self.step.copy_pairs)
+        blk = row * self.block_size
+        return 2 * (2 * n_tok * row) + 8 * n_tok + 2 * (2 * n_pair * blk) + 16 * n_pair
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, dtype, g, device):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def _uniform_lens(lo, hi):
+    def draw(rng, n):
+        return rng.integers(lo, hi + 1, size=n)
+    return draw
+
+
+def _log_uniform_lens(lo, hi):
+    def draw(rng, n):
+        x = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))
+        return np.clip(np.rint(x), lo, hi).astype(np.int64)
+    return draw
+
+
+def build_decode(name, *, dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                 block_size, num_blocks, lens, seed, device="cpu", scale=None,
+                 key_outlier_frac=0.0, key_outlier_scale=8.0, new_token=False,
+                 placement="random"):
+    """A one-step decode workload (no sharing).
+
+    ``lens`` is ``(lo, hi, "uniform"|"loguniform")`` or an explicit array.
+    ``placement`` is ``"random"`` (a seeded permutation of the pool) or
+    ``"sequential"`` (blocks handed out in increasing order; a control).
+    """
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    rng = np.random.default_rng(seed)
+    if isinstance(lens, tuple):
+        lo, hi, kind = lens
+        draw = _uniform_lens(lo, hi) if kind == "uniform" else _log_uniform_lens(lo, hi)
+        context_lens = draw(rng, num_seqs).astype(np.int64)
+    else:
+        context_lens = np.asarray(lens, dtype=np.int64)
+        assert len(context_lens) == num_seqs
+    order = rng.permutation(num_blocks)
+    if placement == "sequential":
+        order = np.arange(num_blocks)[::-1]
+    bm = BlockManager(num_blocks, block_size, free_order=order)
+    seqs, slots = [], []
+    for L in context_lens.tolist():
+        s = bm.new_sequence()
+        if new_token and L > 0:
+            bm.extend(s, L - 1)
+            slots.append(bm.append_slot(s))
+        else:
+            bm.extend(s, L)
+        seqs.append(s)
+    tables = bm.block_table_array(seqs, pad=0)
+    g = _gen(device, seed)
+    q = _randn((num_seqs, num_q_heads, head_dim), dt, g, device)
+    pool_shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    k_cache = _randn(pool_shape, dt, g, device)
+    v_cache = _randn(pool_shape, dt, g, device)
+    if key_outlier_frac > 0:
+        mask = torch.rand(pool_shape[:3], generator=g, device=device) < key_outlier_frac
+        k_cache[mask] *= key_outlier_scale
+    step = None
+    if new_token:
+        n = len(slots)
+        step = DecodeStepInputs(
+            copy_pairs=np.zeros((0, 2), np.int64),
+            slot_mapping=np.asarray(slots, np.int64),
+            seq_index=np.arange(num_seqs, dtype=np.int64)[context_lens > 0],
+            new_k=_randn((n, num_kv_heads, head_dim), dt, g, device),
+            new_v=_randn((n, num_kv_heads, head_dim), dt, g, device))
+    return Workload(
+        name=name, dtype=dt, num_seqs=num_seqs, num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+        num_blocks=num_blocks,
+        scale=(1.0 / math.sqrt(head_dim)) if scale is None else float(scale),
+        seed=seed, context_lens=context_lens.astype(np.int32), block_tables=tables,
+        q=q, k_cache=k_cache, v_cache=v_cache, step=step,
+        meta={"placement": placement, "utilisation": bm.utilisation(seqs)})
+
+
+def build_sharing(name="sharing_fp16", *, dtype="fp16", num_prompts=32, fanout=8,
+                  prompt_len=1024, prompt_extra=(1, 15), max_gen=256,
+                  num_heads=32, head_dim=128, block_size=16, num_blocks=8192,
+                  seed=5, device="cpu", tensors=True):
+    """Parallel-sampling workload with copy-on-write.
+
+    Each prompt has ``prompt_len + r`` tokens already in the cache (``r``
+    uniform in ``prompt_extra``: tokens the parent decoded before forking, so
+    that the last shared block is partly filled).  The prompt is forked into
+    ``fanout`` children holding every prompt block (count ``fanout``), and the
+    parent's own hold is dropped.  Child ``c`` then appends ``d_c`` tokens,
+    ``d_c`` uniform in [0, max_gen]; step ``t`` appends one token to every
+    child with ``d_c >= t``, in sequence order.  ``history`` holds every step's
+    copy pairs, slots and new rows; the decode runs over the final state.
+    With ``prompt_extra=(0, 0)`` every shared block is full and no step copies.
+    ``tensors=False`` skips every tensor draw (integer structure only).
+    """
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    rng = np.random.default_rng(seed)
+    lo, hi = prompt_extra
+    extra = rng.integers(lo, hi + 1, size=num_prompts)
+    gen = rng.integers(0, max_gen + 1, size=(num_prompts, fanout))
+    bm = BlockManager(num_blocks, block_size, free_order=rng.permutation(num_blocks))
+    children = []
+    for p in range(num_prompts):
+        parent = bm.new_sequence()
+        bm.extend(parent, prompt_len + int(extra[p]))
+        kids = [bm.fork(parent) for _ in range(fanout)]
+        bm.free(parent)
+        children.extend(kids)
+    d = gen.reshape(-1)
+    g = _gen(device, seed)
+    num_seqs = num_prompts * fanout
+    pool_shape = (num_blocks, num_heads, block_size, head_dim)
+    q = k_cache = v_cache = None
+    if tensors:
+        q = _randn((num_seqs, num_heads, head_dim), dt, g, device)
+        k_cache = _randn(pool_shape, dt, g, device)
+        v_cache = _randn(pool_shape, dt, g, device)
+    history = []
+    for t in range(1, int(d.max(initial=0)) + 1):
+        active = np.nonzero(d >= t)[0]
+        slots = np.array([bm.append_slot(children[i]) for i in active], np.int64)
+        pairs = bm.take_copy_pairs()
+        st = DecodeStepInputs(copy_pairs=pairs, slot_mapping=slots,
+                              seq_index=active.astype(np.int64))
+        if tensors:
+            st.new_k = _randn((len(slots), num_heads, head_dim), dt, g, device)
+            st.new_v = _randn((len(slots), num_heads, head_dim), dt, g, device)
+        history.append(st)
+    tables = bm.block_table_array(children, pad=0)
+    wl = Workload(
+        name=name, dtype=dt, num_seqs=num_seqs, num_q_heads=num_heads,
+        num_kv_heads=num_heads, head_dim=head_dim, block_size=block_size,
+        num_blocks=num_blocks, scale=1.0 / math.sqrt(head_dim), seed=seed,
+        context_lens=bm.context_lens(children), block_tables=tables, q=q,
+        k_cache=k_cache, v_cache=v_cache,
+        step=history[-1] if history else None, history=history,
+        meta={"prompt_extra": extra, "gen": gen, "fanout": fanout,
+              "prompt_len": prompt_len, "utilisation": bm.utilisation(children)})
+    # copy-on-write pairs of the first step (the only step that copies)
+    wl.meta["first_step_pairs"] = history[0].copy_pairs if history else np.zeros((0, 2), np.int64)
+    return wl
+
+
+# Full-size presets -------------------------------------------------------
+
+def tiny_fp32(seed=1, device="cpu", **kw):
+    args = dict(dtype="fp32", num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                block_size=16, num_blocks=32, lens=(1, 64, "uniform"), scale=1.0 / 8.0)
+    args.update(kw)
+    return build_decode("tiny_fp32", seed=seed, device=device, **args)
+
+
+def opt13b_fp16(seed=2, device="cpu", **kw):
+    args = dict(dtype="fp16", num_seqs=64, num_q_heads=40, num_kv_heads=40, head_dim=128,
+                block_size=16, num_blocks=8192, lens=(128, 2048, "uniform"))
+    args.update(kw)
+    return build_decode("opt13b_fp16", seed=seed, device=device, **args)
+
+
+def llama3_8b_gqa_bf16(seed=3, device="cpu", **kw):
+    args = dict(dtype="bf16", num_seqs=256, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, num_blocks=32768, lens=(16, 4096, "loguniform"),
+                new_token=True)
+    args.update(kw)
+    return build_decode("llama3_8b_gqa_bf16", seed=seed, device=device, **args)
+
+
+def long_context_gqa_bf16(seed=4, device="cpu", **kw):
+    args = dict(dtype="bf16", num_seqs=8, num_q_heads=64, num_kv_heads=8, head_dim=128,
+                block_size=32, num_blocks=12288, lens=(16384, 32768, "uniform"),
+                key_outlier_frac=0.01)
+    args.update(kw)
+    return build_decode("long_context_gqa_bf16", seed=seed, device=device, **args)
+
+
+def sharing_fp16(seed=5, device="cpu", **kw):
+    return build_sharing("sharing_fp16", seed=seed, device=device, **kw)
+
+
+WORKLOADS = {
+    "tiny_fp32": tiny_fp32,
+    "opt13b_fp16": opt13b_fp16,
+    "llama3_8b_gqa_bf16": llama3_8b_gqa_bf16,
+    "long_context_gqa_bf16": long_context_gqa_bf16,
+    "sharing_fp16": sharing_fp16,
+}
+
+
+def make(name, **kw) -> Workload:
+    return WORKLOADS[name](**kw)
