@@ -1,0 +1,219 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = the whole path over one batch: copy_blocks (the step's
+copy-on-write pairs, if any) -> reshape_and_cache (the step's new tokens, if
+any) -> paged_attention_decode over every sequence.  Inputs are synthetic,
+seeded, and resident in HBM before the timed region.
+
+Prints ONE JSON line.  ``value`` is whole-step throughput in algorithmic
+bytes per second (GB/s): the K/V bytes the attention must read plus q, out,
+tables, lengths and the cache writes.  ``roofline`` reports the decode
+call's own achieved HBM bandwidth (its algorithmic bytes over its average
+duration, timed with HIP events on the launch stream) against the MI355X
+HBM3E peak of 8 TB/s.  ``cpu_baseline`` times the float64 CPU oracle on a
+bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "opt13b_fp16"
+DTYPE_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+WORKLOAD_DESC = {
+    "tiny_fp32": dict(num_seqs=4, heads="4/4", head_dim=64, block_size=16,
+                      context_lens="U[1,64]", pool_blocks=32),
+    "opt13b_fp16": dict(num_seqs=64, heads="40/40", head_dim=128, block_size=16,
+                        context_lens="U[128,2048]", pool_blocks=8192),
+    "llama3_8b_gqa_bf16": dict(num_seqs=256, heads="32/8", head_dim=128, block_size=16,
+                               context_lens="logU[16,4096]", pool_blocks=32768,
+                               new_token_per_seq=True),
+    "long_context_gqa_bf16": dict(num_seqs=8, heads="64/8", head_dim=128, block_size=32,
+                                  context_lens="U[16384,32768]", pool_blocks=12288,
+                                  key_outliers="1% x8"),
+    "sharing_fp16": dict(num_seqs=256, prompts=32, fanout=8, heads="32/32", head_dim=128,
+                         block_size=16, context_lens="1024+U[1,15]+U[0,256]",
+                         pool_blocks=8192),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOAD_DESC))
+    p.add_argument("--sweep", action="store_true", help="one line per workload")
+    p.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = auto)")
+    p.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA, 3 contiguous")
+    p.add_argument("--placement", default="random", choices=["random", "sequential"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return p.parse_args()
+
+
+def build_inputs(name, placement):
+    from paged_kv_cache_389_amd import workloads
+    kw = {"device": "cuda"}
+    if placement != "random":
+        kw["placement"] = placement
+    wl = workloads.make(name, **kw)
+    dev = dict(q=wl.q, k=wl.k_cache, v=wl.v_cache,
+               tables=torch.from_numpy(wl.block_tables).cuda(),
+               lens=torch.from_numpy(wl.context_lens).cuda(),
+               out=torch.empty_like(wl.q))
+    step = wl.step
+    pairs = wl.meta.get("first_step_pairs") if wl.history else None
+    if pairs is None and step is not None:
+        pairs = step.copy_pairs
+    dev["pairs"] = torch.from_numpy(np.ascontiguousarray(pairs)).cuda() \
+        if pairs is not None and len(pairs) else None
+    if step is not None and len(step.slot_mapping):
+        dev["slots"] = torch.from_numpy(step.slot_mapping).cuda()
+        dev["new_k"], dev["new_v"] = step.new_k, step.new_v
+    else:
+        dev["slots"] = None
+    return wl, dev
+
+
+def step_bytes(wl, dev):
+    row = wl.num_kv_heads * wl.head_dim * wl.esize
+    n_tok = 0 if dev["slots"] is None else int(dev["slots"].numel())
+    n_pair = 0 if dev["pairs"] is None else int(dev["pairs"].shape[0])
+    writes = 2 * (2 * n_tok * row) + 8 * n_tok
+    copies = 2 * (2 * n_pair * row * wl.block_size) + 16 * n_pair
+    return wl.decode_bytes(), writes + copies
+
+
+def run_gpu(wl, dev, steps, warmup, partition, path):
+    from paged_kv_cache_389_amd import _native as pk
+    ws_len = pk.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                wl.block_size, wl.max_context_len, partition)
+    ws = torch.empty(max(ws_len, 1), dtype=torch.uint8, device="cuda")
+    tables = None if path == 3 else dev["tables"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    def one_step(i=None):
+        if dev["pairs"] is not None:
+            pk.copy_blocks(dev["k"], dev["v"], dev["pairs"])
+        if dev["slots"] is not None:
+            pk.reshape_and_cache(dev["new_k"], dev["new_v"], dev["k"], dev["v"], dev["slots"])
+        if i is not None:
+            ev[i][0].record()
+        pk.paged_attention_decode(dev["out"], dev["q"], dev["k"], dev["v"], tables, dev["lens"],
+                                  wl.scale, wl.max_context_len, workspace=ws,
+                                  partition_tokens=partition, path=path)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, decode_ms
+
+
+def cpu_baseline(wl, budget_s):
+    """The float64 oracle, single-threaded, over whole sequences (all heads)
+    in index order until the time budget is used; throughput in the same
+    unit as the metric (algorithmic KV GB/s of the sample)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import compact_pool
+    done, secs, kv = [], 0.0, 0
+    row = 2 * wl.num_kv_heads * wl.head_dim * wl.esize
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        q_cpu = wl.q.cpu()
+        for s in range(wl.num_seqs):
+            kc, vc, tables = compact_pool(wl, [s])
+            t = time.perf_counter()
+            oracle.decode(q_cpu, kc, vc, tables, wl.context_lens, wl.scale, wl.num_kv_heads,
+                          seqs=[s])
+            secs += time.perf_counter() - t
+            done.append(s)
+            kv += int(wl.context_lens[s]) * row
+            if secs >= budget_s:
+                break
+    return {"value": round(kv / secs / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(secs, 3), "queries_per_s": round(len(done) * wl.num_q_heads / secs, 3),
+            "sample": f"{len(done)} of {wl.num_seqs} sequences x all {wl.num_q_heads} query heads "
+                      f"(decode only, float64 numpy, one thread)"}
+
+
+def bench_one(name, args, with_cpu):
+    wl, dev = build_inputs(name, args.placement)
+    alg_decode, alg_writes = step_bytes(wl, dev)
+    wall, decode_ms = run_gpu(wl, dev, args.steps, args.warmup, args.partition, args.path)
+    ms_per_step = wall / args.steps * 1e3
+    dec_ms = float(np.mean(decode_ms))
+    achieved = alg_decode / (dec_ms / 1e3) / 1e9
+    line = {
+        "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + queries/s",
+        "value": round((alg_decode + alg_writes) / (ms_per_step / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[wl.dtype],
+        "data": "synthetic (seeded N(0,1) values, random block placement)",
+        "config": {"workload": name, **WORKLOAD_DESC[name], "seed": wl.seed,
+                   "placement": args.placement,
+                   "partition_tokens": args.partition or "auto",
+                   "path": ["auto", "valu", "mfma", "contiguous"][args.path]},
+        "queries_per_s": round(wl.num_seqs / (ms_per_step / 1e3), 1),
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "decode_ms": round(dec_ms, 5),
+        "decode_ms_min": round(float(np.min(decode_ms)), 5),
+        "bytes": {"decode_alg": alg_decode, "writes_alg": alg_writes,
+                  "kv_logical": wl.kv_bytes()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_decode call (main kernel + partition reduce)"},
+    }
+    if name == "sharing_fp16":
+        line["bytes"]["kv_unique"] = wl.unique_kv_bytes()
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path needs no communication; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    names = sorted(WORKLOAD_DESC) if args.sweep else [args.workload]
+    for name in names:
+        line = bench_one(name, args, with_cpu=not args.no_cpu_baseline and not args.sweep)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv.so: the paged KV-cache decode path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, each one or two hand-written HIP kernels:
+ *
+ *   pkv_paged_attention_decode  single-query attention of every sequence in
+ *                               a batch over its KV cache, which lives in
+ *                               fixed-size physical blocks reached through a
+ *                               per-sequence block table;
+ *   pkv_reshape_and_cache       write new tokens' key/value rows into the
+ *                               cache slots the block manager assigned;
+ *   pkv_copy_blocks             copy whole physical blocks (the copy step of
+ *                               copy-on-write).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array argument is a DEVICE pointer (memory the caller allocated
+ *   on the current HIP device, e.g. a torch tensor's data_ptr()).  The
+ *   library never allocates device memory, never frees caller memory and
+ *   keeps no pointer after the call's work has been enqueued.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *   asynchronous on that stream; calls on one stream run in order, so
+ *   copy_blocks -> reshape_and_cache -> paged_attention_decode performs
+ *   "copy, redirect, then write, then attend".
+ * - All arrays are dense, row-major (C order), with no padding.
+ * - KV cache layout, for both k_cache and v_cache:
+ *       [num_blocks][num_kv_heads][block_size][head_dim]
+ *   so one (block, kv head) tile is block_size*head_dim contiguous elements
+ *   and one physical block is num_kv_heads*block_size*head_dim contiguous
+ *   elements.
+ * - Slot numbering: slot = physical_block * block_size + offset.
+ * - Element type is given by `dtype`; q, out, k, v and both caches share it.
+ *   Attention accumulates in fp32 and rounds the result to nearest even.
+ * - Return value: PKV_OK (0) or a negative pkv_status.  Argument errors are
+ *   detected on the host before anything is enqueued.  PKV_EHIP reports a
+ *   failed launch; pkv_last_error() gives the HIP error text.
+ * - Calls are thread-safe for distinct streams and buffers.
+ *
+ * Sources: the three web pages on PagedAttention ("Memory Optimization in
+ * LLM Serving with PagedAttention"; "vLLM and PagedAttention: How Ideas
+ * from Operating Systems Accelerated LLM Inference"; "Scaling LLM
+ * Inference: Memory Management with PagedAttention and vLLM").
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_F32 = 0,  /* IEEE binary32 */
+  PKV_F16 = 1,  /* IEEE binary16 */
+  PKV_BF16 = 2  /* bfloat16 */
+} pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* null pointer, negative size, Hq % Hkv != 0, ... */
+  PKV_EUNSUPPORTED = -2,  /* head_dim / block_size / dtype not compiled in */
+  PKV_EWORKSPACE = -3,    /* workspace missing or smaller than required */
+  PKV_EHIP = -4           /* a HIP launch failed; see pkv_last_error() */
+} pkv_status;
+
+/* Decode kernel variants for pkv_paged_attention_decode_ex. */
+typedef enum {
+  PKV_PATH_AUTO = 0,       /* MFMA when 2 <= Hq/Hkv <= 16 and 16-bit, else VALU */
+  PKV_PATH_VALU = 1,       /* one query head per workgroup, vector ALU dot products */
+  PKV_PATH_MFMA = 2,       /* one KV head per workgroup, all its query heads on MFMA */
+  PKV_PATH_CONTIGUOUS = 3  /* control: ignore block_tables; sequence s's logical
+                              block j is physical block s*max_blocks_per_seq + j */
+} pkv_decode_path;
+
+/* Library version, e.g. "pagedkv 0.1.0 gfx950". Static string. */
+const char* pkv_version(void);
+
+/* Static text of a status code. */
+const char* pkv_status_string(int status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Supported shapes: nonzero if (dtype, head_dim, block_size) is compiled in.
+ * head_dim in {64, 128, 256}; block_size in {8, 16, 32}. */
+int pkv_supported(pkv_dtype dtype, int head_dim, int block_size);
+
+/*
+ * Workspace bytes pkv_paged_attention_decode needs for these sizes.
+ *
+ * Long contexts are split into partitions of `partition_tokens` tokens
+ * (0 = the library's choice, the same one the decode call makes) whose
+ * partial softmax states (running max, running sum, unnormalised output,
+ * all fp32) are merged by a second reduce kernel.  Returns 0 when no split
+ * is needed, and (size_t)-1 for invalid sizes.
+ */
+size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                           int head_dim, int block_size, int max_context_len,
+                                           int partition_tokens);
+
+/*
+ * paged_attention_decode: out[s][h][:] = softmax(scale * K_s q[s][h]) V_s
+ *
+ * For each sequence s and query head h, with L = context_lens[s] and
+ * kv head g = h / (num_q_heads / num_kv_heads), token t < L of the sequence
+ * is read from physical block block_tables[s][t / block_size] at offset
+ * t % block_size.  The keys of its L tokens are scored against q[s][h],
+ * scaled by `scale`, passed through a softmax over the L scores, and the
+ * value rows are summed with those weights.
+ *
+ * Passages: the kernel gathers a sequence's scattered KV blocks through its
+ * block table to compute the attention ("Memory Optimization in LLM Serving
+ * with PagedAttention", section "How PagedAttention Works"; "vLLM and
+ * PagedAttention ...", paragraph on the engine's custom kernels).  Only the
+ * last block of a sequence is partly filled (same section, bullet on
+ * fragmentation), so the kernel reads ceil(L / block_size) table entries and
+ * masks the tail by index.  The attention formula and the grouping of query
+ * heads onto KV heads are standard readings; the pages do not print them.
+ *
+ * Arguments (sizes are element counts unless noted):
+ *   out           [num_seqs][num_q_heads][head_dim]       written
+ *   q             [num_seqs][num_q_heads][head_dim]       read
+ *   k_cache,
+ *   v_cache       [num_blocks][num_kv_heads][block_size][head_dim]   read
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]    read; entries at
+ *                 index >= ceil(L / block_size) are never read
+ *   context_lens  int32 [num_seqs]                        read
+ *   scale         softmax scale (usually 1/sqrt(head_dim))
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid;
+ *                 no device-to-host read happens)
+ *   workspace     device scratch of at least
+ *                 pkv_paged_attention_workspace_bytes(...) bytes (may be NULL
+ *                 when that is 0); contents need not be initialised.
+ *
+ * Result for L == 0: a zero row.  Preconditions that are not checked on the
+ * device: 0 <= context_lens[s] <= min(max_context_len,
+ * max_blocks_per_seq*block_size) and table entries in [0, num_blocks).
+ * Violations never cause out-of-bounds accesses: a length is clamped to
+ * those bounds, and a table entry outside [0, num_blocks) makes that
+ * (sequence, head) output NaN.  `out` must not alias any input.
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, int max_context_len, pkv_dtype dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as pkv_paged_attention_decode with an explicit partition size
+ * (0 = library choice; otherwise a multiple of block_size, >= 64) and kernel
+ * variant (pkv_decode_path).  Used for tuning sweeps and for the
+ * contiguous-layout control. */
+int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, float scale, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_context_len, pkv_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, int partition_tokens, int path,
+                                  void* stream);
+
+/*
+ * reshape_and_cache: for every token j with slot = slot_mapping[j] >= 0,
+ *   k_cache[slot / block_size][g][slot % block_size][:] = k[j][g][:]
+ *   v_cache[slot / block_size][g][slot % block_size][:] = v[j][g][:]
+ * for every kv head g.  A byte-exact copy; no arithmetic on the values.
+ *
+ * Passage: blocks are filled as generation proceeds, each new token going
+ * into the slot its sequence's block table provides ("Memory Optimization
+ * in LLM Serving with PagedAttention", section "How PagedAttention Works",
+ * on-demand allocation; "vLLM and PagedAttention ...", paragraph on the
+ * solution); after a copy-on-write the write goes to the new copy (section
+ * "Advanced Capabilities: Memory Sharing with Copy-on-Write").
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim]    read
+ *   slot_mapping  int64 [num_tokens]; negative = skip     read
+ *   k_cache, v_cache  as above                            written at the slots
+ *
+ * Slots must be distinct (else which write wins is unspecified).  A slot
+ * >= num_blocks*block_size is skipped (never written out of bounds).
+ * num_tokens == 0 is a no-op.
+ */
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                          int head_dim, int block_size, int num_blocks, pkv_dtype dtype,
+                          void* stream);
+
+/*
+ * copy_blocks: for every pair i, k_cache[dst_i] = k_cache[src_i] and
+ * v_cache[dst_i] = v_cache[src_i], whole physical blocks
+ * (num_kv_heads*block_size*head_dim elements each), byte for byte.
+ *
+ * Passage: copy-on-write allocates a new block and copies the content of
+ * the shared block into it before the table is redirected and the token is
+ * written ("Memory Optimization in LLM Serving with PagedAttention", section
+ * "Advanced Capabilities: Memory Sharing with Copy-on-Write"); one block is
+ * copied, not the whole cache ("vLLM and PagedAttention ...", paragraph on
+ * sharing).
+ *
+ *   src_dst_pairs  int64 [num_pairs][2] = {src, dst}      read
+ *
+ * Destinations must be distinct and must not be the source of any pair in
+ * the same call (copy-on-write always copies into a fresh block).  A pair
+ * with an index outside [0, num_blocks) is skipped.  num_pairs == 0 is a
+ * no-op.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int num_pairs,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    pkv_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

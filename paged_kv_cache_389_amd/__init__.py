@@ -1,0 +1,30 @@
+"""MI355X-native paged KV-cache decode path.
+
+Device calls (hand-written gfx950 HIP kernels behind the C ABI in
+``include/pagedkv.h``; the Python names are the C names without ``pkv_``):
+
+* :func:`paged_attention_decode` - single-query attention over a KV cache kept
+  in fixed-size physical blocks reached through per-sequence block tables;
+* :func:`reshape_and_cache` - write new tokens' K/V rows into their slots;
+* :func:`copy_blocks` - copy whole blocks (the copy of copy-on-write).
+
+Host side: :mod:`.block_manager` (block pool, tables, reference counts, fork,
+copy-on-write) and :mod:`.workloads` (seeded synthetic inputs).
+
+The device calls load ``libpagedkv.so`` on first use and raise
+:class:`NativeLibraryMissing` if it is not built; nothing falls back to a
+CPU implementation.
+"""
+
+_NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_bytes",
+           "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
+           "PATH_MFMA", "PATH_CONTIGUOUS")
+
+__all__ = list(_NATIVE) + ["block_manager", "workloads"]
+
+
+def __getattr__(name):
+    if name in _NATIVE:
+        from . import _native
+        return getattr(_native, name)
+    raise AttributeError(name)

@@ -1,0 +1,205 @@
+"""ctypes binding of libpagedkv.so (argument marshalling only).
+
+Every function takes torch tensors that live on a HIP device, checks their
+shapes and dtypes against the C contract (``include/pagedkv.h``), and passes
+raw device pointers plus the current HIP stream to the C ABI.  All compute
+runs in the library's kernels.  If the library is not built, importing this
+module raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so the library shares it
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_CONTIGUOUS = 0, 1, 2, 3
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+_SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+class NativeLibraryMissing(ImportError):
+    pass
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, call, status, lib):
+        msg = lib.pkv_status_string(status).decode()
+        detail = lib.pkv_last_error().decode()
+        super().__init__(f"{call} failed: {msg} ({status})" + (f": {detail}" if detail else ""))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise NativeLibraryMissing(
+            f"{LIB_PATH} is missing; build it with `python -m paged_kv_cache_389_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, i32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    f32, sz = ctypes.c_float, ctypes.c_size_t
+    lib.pkv_version.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [i32]
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    lib.pkv_supported.restype = i32
+    lib.pkv_supported.argtypes = [i32, i32, i32]
+    lib.pkv_paged_attention_workspace_bytes.restype = sz
+    lib.pkv_paged_attention_workspace_bytes.argtypes = [i32] * 7
+    lib.pkv_paged_attention_decode.restype = i32
+    lib.pkv_paged_attention_decode.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.pkv_paged_attention_decode_ex.restype = i32
+    lib.pkv_paged_attention_decode_ex.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+        i32, i32, vp]
+    lib.pkv_reshape_and_cache.restype = i32
+    lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
+    lib.pkv_copy_blocks.restype = i32
+    lib.pkv_copy_blocks.argtypes = [vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
+    return lib
+
+
+lib = _load()
+
+EXPORTED = (
+    "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_supported",
+    "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_decode",
+    "pkv_paged_attention_decode_ex", "pkv_reshape_and_cache", "pkv_copy_blocks",
+)
+
+
+def version() -> str:
+    return lib.pkv_version().decode()
+
+
+def _check(call, status):
+    if status != 0:
+        raise PagedKVError(call, status, lib)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                    max_context_len, partition_tokens=0) -> int:
+    n = lib.pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                block_size, max_context_len, partition_tokens)
+    if n == _SIZE_MAX:
+        raise ValueError("invalid sizes for the decode workspace")
+    return int(n)
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           max_context_len, workspace=None, partition_tokens=0,
+                           path=PATH_AUTO, stream=None):
+    """``out[s, h] = softmax(scale * K_s q[s, h]) V_s`` over each sequence's
+    paged KV (see ``pkv_paged_attention_decode``).  ``max_context_len`` is a
+    host-side bound of ``context_lens``.  ``workspace`` is a uint8 device
+    tensor; when None one of the required size is allocated."""
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (context_lens, "context_lens")):
+        _dev(t, n)
+    if path != PATH_CONTIGUOUS or block_tables is not None:
+        _dev(block_tables, "block_tables")
+        if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+            raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t, n in ((out, "out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} dtype {t.dtype} != q dtype {q.dtype}")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    num_seqs, hq, hd = q.shape
+    nb, hkv, bs, hd2 = k_cache.shape
+    if hd2 != hd:
+        raise ValueError("head_dim of q and caches differ")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (num_seqs,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    max_blocks = block_tables.shape[1] if block_tables is not None else \
+        -(-int(max_context_len) // bs)
+    if block_tables is not None and block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must have num_seqs rows")
+    need = workspace_bytes(num_seqs, hq, hkv, hd, bs, int(max_context_len), partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    tables_ptr = _ptr(block_tables) if block_tables is not None else None
+    with torch.cuda.device(q.device):
+        st = lib.pkv_paged_attention_decode_ex(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), tables_ptr, _ptr(context_lens),
+            ctypes.c_float(scale), num_seqs, hq, hkv, hd, bs, nb, max_blocks,
+            int(max_context_len), _DTYPE_CODE[q.dtype], ws_ptr, ws_len, int(partition_tokens),
+            int(path), _stream(q, stream))
+    _check("paged_attention_decode", st)
+    return out
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """Write new tokens' K/V rows ([num_tokens, Hkv, hd]) into the cache slots
+    ``slot_mapping`` (int64, negative = skip)."""
+    for t, n in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (slot_mapping, "slot_mapping")):
+        _dev(t, n)
+    if k.dtype not in _DTYPE_CODE or any(t.dtype != k.dtype for t in (v, k_cache, v_cache)):
+        raise ValueError("k, v and both caches must share one supported dtype")
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must both be [num_tokens, num_kv_heads, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, hkv, bs, hd = k_cache.shape
+    if k.shape[1:] != (hkv, hd):
+        raise ValueError("k/v rows do not match the cache's [num_kv_heads, head_dim]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k.shape[0],):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    with torch.cuda.device(k.device):
+        st = lib.pkv_reshape_and_cache(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(slot_mapping), k.shape[0], hkv, hd, bs, nb,
+                                       _DTYPE_CODE[k.dtype], _stream(k, stream))
+    _check("reshape_and_cache", st)
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
+    """Copy whole blocks ``cache[dst] = cache[src]`` for each int64 pair row."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (src_dst_pairs, "src_dst_pairs")):
+        _dev(t, n)
+    if k_cache.dtype not in _DTYPE_CODE or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must share one supported dtype")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or \
+            src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    nb, hkv, bs, hd = k_cache.shape
+    with torch.cuda.device(k_cache.device):
+        st = lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src_dst_pairs),
+                                 src_dst_pairs.shape[0], hkv, hd, bs, nb,
+                                 _DTYPE_CODE[k_cache.dtype], _stream(k_cache, stream))
+    _check("copy_blocks", st)

@@ -1,0 +1,315 @@
+// Paged decode attention for grouped query heads, on the matrix cores.
+//
+// One workgroup (4 waves) computes all G query heads that share one KV head
+// of one sequence, over one partition of the context.  Against a tile of 16
+// tokens the G query rows form a small dense contraction, so both products
+// run as gfx950 MFMA instructions with fp32 accumulation:
+//
+//   S^T[16 tok][16 head] = K[16 tok][HD] * Q^T[HD][16 head]   (16x16x32, HD/32 steps)
+//   O^T[HD][16 head]    += V^T[HD][16 tok] * P^T[16 tok][16 head]   (16x16x16, HD/16 tiles)
+//
+// Lane l of a wave owns head column n = l % 16 and token/dim group
+// g4 = l / 16.  Operand layouts line up without any data exchange:
+// * K is read in the matrix-core A layout: lane l loads 16 bytes of token
+//   row n at dims 32*kk + 8*g4 .. +8 (each load instruction covers 64
+//   contiguous bytes of all 16 rows).  Q^T is held in the matching B layout.
+// * The S result gives lane l the scores of tokens 4*g4 + i (i < 4) for its
+//   head n, which is exactly the B layout P^T needs for the second product.
+// * V is read row-wise: lane l loads tokens 4*g4 + i, dims n*HD/16 .. +HD/16.
+//   Regrouping those registers gives, for each e < HD/16, the A operand of
+//   V^T restricted to the dims n*HD/16 + e (a byte permute per register
+//   pair, no LDS); output tile e then holds dims (4*g4 + i)*HD/16 + e.
+// The softmax state (running max in log2 units, running sum) is per head,
+// so it lives in lane column n; the max over a tile's 16 tokens needs two
+// cross-group shuffles.  With bf16 the probabilities are split into a bf16
+// high part and a bf16 remainder and both are multiplied in, which keeps
+// them at about 16 significant bits.
+//
+// Passages: a sequence's KV blocks are gathered through its block table
+// ("Memory Optimization in LLM Serving with PagedAttention", section "How
+// PagedAttention Works"); only the last block is partly filled (same
+// section).  Grouped query heads are not on the pages: query head h reads
+// KV head h / G.
+#include "common.h"
+#include "decode.h"
+
+namespace pkv {
+
+template <typename E>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<F16> {
+  static constexpr bool kSplit = false;
+  __device__ static inline f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    f16x2 h = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ static inline float widen_lo(uint32_t v) {
+    return (float)__builtin_bit_cast(f16x2, v)[0];
+  }
+  __device__ static inline float widen_hi(uint32_t v) {
+    return (float)__builtin_bit_cast(f16x2, v)[1];
+  }
+};
+
+template <>
+struct MfmaOps<BF16> {
+  static constexpr bool kSplit = true;
+  __device__ static inline f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                     __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    bf16x2 h = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ static inline float widen_lo(uint32_t v) { return __uint_as_float(v << 16); }
+  __device__ static inline float widen_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+};
+
+// {lo16 = element E of x, hi16 = element E of y}
+template <int E>
+__device__ inline uint32_t pair_of(const uint32_t* x, const uint32_t* y) {
+  // v_perm_b32 selector: bytes 0-3 come from the second source, 4-7 from the first
+  constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+  return __builtin_amdgcn_perm(y[E >> 1], x[E >> 1], sel);
+}
+
+template <typename E, int HD, int BS>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+  using T = typename E::storage;
+  using Ops = MfmaOps<E>;
+  constexpr int NWAVES = 4;
+  constexpr int KSTEPS = HD / 32;      // QK MFMAs per tile
+  constexpr int DPL = HD / 16;         // V dims per lane per token == PV MFMAs per tile
+  constexpr int VW = DPL / 2;          // dwords of V per lane per token
+  constexpr int TILES_PER_BLOCK = BS / 16;
+  static_assert(HD % 32 == 0 && BS % 16 == 0 && VW >= 1, "unsupported shape");
+
+  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int G = a.group;
+
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int P = a.part_tokens;
+  const int tok_begin = part * P;
+  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G) * HD;
+  if (L == 0) {
+    if (part == 0)
+      for (int i = tid; i < G * HD; i += 256) out[i] = E::round(0.f);
+    return;
+  }
+  if (tok_begin >= L) return;
+  const int tok_end = min(L, tok_begin + P);
+  const int nparts = (L + P - 1) / P;
+
+  // Q^T in the B layout: head n, dims 32*kk + 8*g4 .. +8 (zero for padding heads)
+  u32x4 qb[KSTEPS];
+  {
+    const int hn = n < G ? n : G - 1;   // padding heads load nothing
+    const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qb[kk] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+  }
+  const size_t block_stride = (size_t)a.num_kv_heads * BS * HD;
+  const T* kbase = static_cast<const T*>(a.k_cache) + (size_t)g * BS * HD + n * HD + g4 * 8;
+  const T* vbase = static_cast<const T*>(a.v_cache) + (size_t)g * BS * HD + (4 * g4) * HD + n * DPL;
+  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
+
+  f32x4 acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  int bad = 0;
+
+  const int tile_end = (tok_end + 15) / 16;
+  for (int ti = tok_begin / 16 + wave; ti < tile_end; ti += NWAVES) {
+    const int jb = ti / TILES_PER_BLOCK;
+    const int phys = uniform(a.contiguous ? s * a.max_blocks + jb : table[jb]);
+    if (phys < 0 || phys >= a.num_blocks) {
+      bad = 1;
+      continue;
+    }
+    const size_t toff = (size_t)phys * block_stride + (size_t)(ti % TILES_PER_BLOCK) * 16 * HD;
+    u32x4 ka[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = ld16(kbase + toff + kk * 32);
+    uint32_t vv[4][VW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const T* vp = vbase + toff + i * HD;
+      if constexpr (VW == 2) {
+        u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+        vv[i][0] = x[0];
+        vv[i][1] = x[1];
+      } else {
+#pragma unroll
+        for (int w = 0; w < VW; w += 4) {
+          u32x4 x = ld16(vp + 2 * w);
+          vv[i][w] = x[0];
+          vv[i][w + 1] = x[1];
+          vv[i][w + 2] = x[2];
+          vv[i][w + 3] = x[3];
+        }
+      }
+    }
+
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
+
+    const int t0 = ti * 16 + 4 * g4;   // token of sacc[0] for this lane
+    const bool whole = ti * 16 + 16 <= tok_end;
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * a.scale_log2e;
+    if (!whole) {
+      // tail tile: mask by index; zero the value rows past the context so a
+      // non-finite value there cannot reach the product
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (t0 + i >= tok_end) {
+          sc[i] = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < VW; ++w) vv[i][w] = 0u;
+        }
+      }
+    }
+    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float corr = fast_exp2(m - mu);
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mu);   // exp2(-inf) == 0
+    l = __builtin_fmaf(l, corr, (p[0] + p[1]) + (p[2] + p[3]));
+    if (__any(corr != 1.f)) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] *= corr;
+    }
+
+    // P^T in the B layout: tokens 4*g4 + j of head n
+    u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
+    u32x2 pr = {0u, 0u};
+    if constexpr (Ops::kSplit) {
+      pr[0] = Ops::pack2(p[0] - Ops::widen_lo(pb[0]), p[1] - Ops::widen_hi(pb[0]));
+      pr[1] = Ops::pack2(p[2] - Ops::widen_lo(pb[1]), p[3] - Ops::widen_hi(pb[1]));
+    }
+    // V^T in the A layout, one MFMA per lane-dim e
+#define PKV_PV_STEP(EE)                                                          \
+  if constexpr ((EE) < DPL) {                                                    \
+    const u32x2 va = {pair_of<(EE)>(vv[0], vv[1]), pair_of<(EE)>(vv[2], vv[3])}; \
+    acc[EE] = Ops::pv(va, pb, acc[EE]);                                          \
+    if constexpr (Ops::kSplit) acc[EE] = Ops::pv(va, pr, acc[EE]);               \
+  }
+    PKV_PV_STEP(0) PKV_PV_STEP(1) PKV_PV_STEP(2) PKV_PV_STEP(3)
+    PKV_PV_STEP(4) PKV_PV_STEP(5) PKV_PV_STEP(6) PKV_PV_STEP(7)
+    PKV_PV_STEP(8) PKV_PV_STEP(9) PKV_PV_STEP(10) PKV_PV_STEP(11)
+    PKV_PV_STEP(12) PKV_PV_STEP(13) PKV_PV_STEP(14) PKV_PV_STEP(15)
+#undef PKV_PV_STEP
+  }
+
+  // the four token groups of a head column hold partial sums of l
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  constexpr int OS = HD + 4;   // padded row stride of the LDS output tiles
+  __shared__ float sm_m[NWAVES][16], sm_l[NWAVES][16];
+  __shared__ float sm_o[NWAVES][16 * OS];
+  __shared__ int sm_bad[NWAVES];
+  if (g4 == 0) {
+    sm_m[wave][n] = m;
+    sm_l[wave][n] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[wave][n * OS + (4 * g4 + i) * DPL + e] = acc[e][i];
+  if (lane == 0) sm_bad[wave] = bad;
+  __syncthreads();
+
+  const int any_bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
+  for (int idx = tid; idx < G * HD; idx += 256) {
+    const int hh = idx / HD, d = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) {
+      const float wt = fast_exp2(sm_m[w][hh] - M);
+      Ls = __builtin_fmaf(wt, sm_l[w][hh], Ls);
+      O = __builtin_fmaf(wt, sm_o[w][hh * OS + d], O);
+    }
+    if (any_bad) O = __builtin_nanf("");
+    if (nparts == 1) {
+      out[idx] = E::round(O / Ls);
+    } else {
+      const size_t pidx = ((size_t)s * a.num_q_heads + (size_t)g * G + hh) * a.max_parts + part;
+      a.part_o[pidx * HD + d] = O;
+      if (d == 0) {
+        a.part_ml[2 * pidx] = M;
+        a.part_ml[2 * pidx + 1] = Ls;
+      }
+    }
+  }
+}
+
+template <typename E, int HD, int BS>
+static hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t st) {
+  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename E, int HD>
+static hipError_t launch_mfma_hd(int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (bs) {
+    case 16: return launch_mfma_t<E, HD, 16>(a, st);
+    case 32: return launch_mfma_t<E, HD, 32>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t launch_mfma_e(int hd, int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (hd) {
+    case 64: return launch_mfma_hd<E, 64>(bs, a, st);
+    case 128: return launch_mfma_hd<E, 128>(bs, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool decode_mfma_supported(Elem e, int hd, int bs) {
+  return (e == Elem::F16 || e == Elem::BF16) && (hd == 64 || hd == 128) && (bs == 16 || bs == 32);
+}
+
+hipError_t launch_decode_mfma(Elem e, int hd, int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (e) {
+    case Elem::F16: return launch_mfma_e<F16>(hd, bs, a, st);
+    case Elem::BF16: return launch_mfma_e<BF16>(hd, bs, a, st);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

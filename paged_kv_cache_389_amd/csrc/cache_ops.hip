@@ -1,0 +1,90 @@
+// Cache writers: the slot scatter of new tokens and the whole-block copy of
+// copy-on-write.  Both move bytes only, with 16-byte vector loads/stores.
+#include "common.h"
+#include "decode.h"
+
+namespace pkv {
+
+// One workgroup per new token.  Its K and V rows ([Hkv][HD] each) go to
+// offset slot % BS of physical block slot / BS, for every KV head.  A
+// negative slot is skipped (padding); a slot past the pool is skipped so a
+// bad slot can never write out of bounds.
+//
+// Passage: new tokens fill the slots their blocks provide as generation
+// proceeds ("Memory Optimization in LLM Serving with PagedAttention", section
+// "How PagedAttention Works"); after copy-on-write they land in the copy
+// (section "Advanced Capabilities: Memory Sharing with Copy-on-Write").
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, u32x4* __restrict__ k_cache,
+    u32x4* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_kv_heads,
+    int row_vecs, int block_size, int64_t num_slots) {
+  const int token = blockIdx.x;
+  const int64_t slot = slot_mapping[token];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot % block_size);
+  const int per_token = num_kv_heads * row_vecs;
+  const u32x4* ks = k + (size_t)token * per_token;
+  const u32x4* vs = v + (size_t)token * per_token;
+  for (int i = threadIdx.x; i < per_token; i += blockDim.x) {
+    const int g = i / row_vecs, c = i % row_vecs;
+    const size_t dst = (((size_t)blk * num_kv_heads + g) * block_size + off) * row_vecs + c;
+    k_cache[dst] = ks[i];
+    v_cache[dst] = vs[i];
+  }
+}
+
+// Grid (chunks, 2, pairs): y selects the K or the V cache; each workgroup
+// copies one chunk of 256 threads x 4 vectors (16 KiB) of one block.
+//
+// Passage: copy-on-write copies the shared block's content into a new block
+// ("Memory Optimization ...", section "Advanced Capabilities: Memory Sharing
+// with Copy-on-Write"); one block is copied, not the whole cache ("vLLM and
+// PagedAttention ...", paragraph on sharing).
+constexpr int kCopyUnroll = 4;
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* k_cache, u32x4* v_cache,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t block_vecs, int num_blocks) {
+  const int64_t src = pairs[2 * (size_t)blockIdx.z];
+  const int64_t dst = pairs[2 * (size_t)blockIdx.z + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  u32x4* cache = blockIdx.y == 0 ? k_cache : v_cache;
+  const u32x4* from = cache + src * block_vecs;
+  u32x4* to = cache + dst * block_vecs;
+  const int64_t base = (int64_t)blockIdx.x * 256 * kCopyUnroll + threadIdx.x;
+  u32x4 buf[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < block_vecs) buf[u] = from[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < block_vecs) to[i] = buf[u];
+  }
+}
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                    int row_bytes, int block_size, int num_blocks,
+                                    hipStream_t st) {
+  const int row_vecs = row_bytes / 16;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(num_tokens), dim3(256), 0, st,
+                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slot_mapping,
+                     num_kv_heads, row_vecs, block_size, (int64_t)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
+                              size_t block_bytes, int num_blocks, hipStream_t st) {
+  const int64_t block_vecs = (int64_t)(block_bytes / 16);
+  const int64_t per_wg = 256 * kCopyUnroll;
+  dim3 grid((unsigned)((block_vecs + per_wg - 1) / per_wg), 2, (unsigned)num_pairs);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, st, static_cast<u32x4*>(k_cache),
+                     static_cast<u32x4*>(v_cache), pairs, block_vecs, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

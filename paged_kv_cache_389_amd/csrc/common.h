@@ -1,0 +1,119 @@
+// Device-side building blocks shared by the paged decode kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Reinterpret one 32-bit lane of a vector.  The element is copied into a
+// scalar first: bit-casting a vector element expression directly picks the
+// wrong element with this compiler.
+template <typename To>
+__device__ inline To lane_as(uint32_t x) {
+  return __builtin_bit_cast(To, x);
+}
+
+// Element types.  Each describes how a 16-byte vector of the type is read
+// into fp32 and how an fp32 result is rounded back (nearest even).
+struct F32 {
+  using storage = float;
+  static constexpr int kVec = 4;  // elements per 16 bytes
+  __device__ static inline float dot16(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), acc);
+    return acc;
+  }
+  __device__ static inline void unpack16(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(a[i]);
+  }
+  __device__ static inline storage round(float x) { return x; }
+};
+
+struct F16 {
+  using storage = _Float16;
+  static constexpr int kVec = 8;
+  __device__ static inline float dot16(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(lane_as<f16x2>(a[i]), lane_as<f16x2>(b[i]), acc, false);
+    return acc;
+  }
+  __device__ static inline void unpack16(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 h = lane_as<f16x2>(a[i]);
+      out[2 * i] = (float)h[0];
+      out[2 * i + 1] = (float)h[1];
+    }
+  }
+  __device__ static inline storage round(float x) { return (_Float16)x; }
+};
+
+struct BF16 {
+  using storage = __bf16;
+  static constexpr int kVec = 8;
+  __device__ static inline float dot16(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(lane_as<bf16x2>(a[i]), lane_as<bf16x2>(b[i]), acc,
+                                            false);
+    return acc;
+  }
+  __device__ static inline void unpack16(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(a[i] << 16);
+      out[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline storage round(float x) { return (__bf16)x; }
+};
+
+// 16-byte global load / store.
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Cross-lane moves inside a 16-lane DPP row.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N a power of two, 1..64); every lane
+// of a group receives the group's sum.  Steps inside a 16-lane row use DPP;
+// the 32- and 64-lane steps use cross-row shuffles.
+template <int N>
+__device__ inline float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp<kDppRowHalfMirror>(v);   // quads uniform: mirror == xor 4
+  if constexpr (N >= 16) v += dpp<kDppRowMirror>(v);      // halves uniform: mirror == xor 8
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scalar (wave-uniform) copy of a value.
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace pkv

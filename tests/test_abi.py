@@ -1,0 +1,123 @@
+"""The C ABI library: it loads, exports every symbol the header declares, and
+rejects bad arguments on the host before touching a device (no GPU needed;
+no call here launches anything)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def native():
+    from paged_kv_cache_389_amd import _native
+    return _native
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for call in ("pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks"):
+        assert call in names
+
+
+def test_library_exports_every_declared_symbol(native):
+    raw = ctypes.CDLL(native.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, f"not exported: {missing}"
+    assert set(declared_functions()) == set(native.EXPORTED)
+
+
+def test_version_and_status_strings(native):
+    assert "gfx950" in native.version()
+    lib = native.lib
+    assert lib.pkv_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4):
+        assert lib.pkv_status_string(code) != b"unknown status"
+
+
+def test_supported_shapes(native):
+    lib = native.lib
+    for dt in (0, 1, 2):
+        for hd in (64, 128, 256):
+            for bs in (8, 16, 32):
+                assert lib.pkv_supported(dt, hd, bs) == 1
+    assert lib.pkv_supported(1, 96, 16) == 0
+    assert lib.pkv_supported(1, 128, 12) == 0
+    assert lib.pkv_supported(7, 128, 16) == 0
+
+
+def test_workspace_bytes(native):
+    # one partition (short contexts): no workspace
+    assert native.workspace_bytes(4, 4, 4, 64, 16, 64) == 0
+    # long contexts: fp32 (m, l) + [head_dim] per (seq, q head, partition)
+    parts = -(-32768 // 512)
+    assert native.workspace_bytes(8, 64, 8, 128, 32, 32768) == 8 * 64 * parts * 130 * 4
+    assert native.workspace_bytes(8, 64, 8, 128, 32, 32768, 1024) == 8 * 64 * 32 * 130 * 4
+    with pytest.raises(ValueError):
+        native.workspace_bytes(8, 64, 8, 128, 32, 32768, 100)   # not a multiple of 32
+
+
+def _decode(lib, **over):
+    args = dict(out=1, q=1, k=1, v=1, tables=1, lens=1, scale=1.0, B=2, Hq=4, Hkv=2, hd=128,
+                bs=16, nb=64, maxb=8, maxL=100, dtype=1, ws=None, wsb=0, part=0, path=0)
+    args.update(over)
+    a = args
+    return lib.pkv_paged_attention_decode_ex(
+        a["out"], a["q"], a["k"], a["v"], a["tables"], a["lens"], ctypes.c_float(a["scale"]),
+        a["B"], a["Hq"], a["Hkv"], a["hd"], a["bs"], a["nb"], a["maxb"], a["maxL"], a["dtype"],
+        a["ws"], a["wsb"], a["part"], a["path"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Hq=5), -1),            # not a multiple of Hkv
+    (dict(Hkv=0), -1),
+    (dict(dtype=9), -1),
+    (dict(out=None), -1),
+    (dict(tables=None), -1),
+    (dict(hd=96), -2),
+    (dict(bs=12), -2),
+    (dict(part=48), -1),         # not a multiple of 32
+    (dict(path=2, Hq=2, Hkv=2), -2),   # MFMA needs grouped heads
+    (dict(path=2, dtype=0), -2),       # MFMA needs 16-bit types
+    (dict(maxL=4096, maxb=256), -3),   # several partitions and no workspace
+    (dict(path=7), -1),
+])
+def test_decode_rejects_bad_arguments_before_launch(native, over, status):
+    assert _decode(native.lib, **over) == status
+
+
+def test_empty_batch_is_a_no_op(native):
+    assert _decode(native.lib, B=0, out=None, q=None) == 0
+
+
+def test_cache_ops_reject_bad_arguments(native):
+    lib = native.lib
+    # num_tokens == 0 and num_pairs == 0 are no-ops (nothing is launched)
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 64, 1, None) == 0
+    assert lib.pkv_copy_blocks(None, None, None, 0, 8, 128, 16, 64, 1, None) == 0
+    assert lib.pkv_reshape_and_cache(1, 1, 1, 1, None, 4, 8, 128, 16, 64, 1, None) == -1
+    assert lib.pkv_reshape_and_cache(1, 1, 1, 1, 1, 4, 8, 4, 16, 64, 1, None) == -2
+    assert lib.pkv_copy_blocks(1, 1, None, 3, 8, 128, 16, 64, 1, None) == -1
+    assert lib.pkv_copy_blocks(1, 1, 1, -1, 8, 128, 16, 64, 1, None) == -1
+    assert lib.pkv_copy_blocks(1, 1, 1, 3, 8, 128, 16, 64, 5, None) == -1
+
+
+def test_binding_rejects_cpu_tensors(native):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(2, 2, 8)
+    with pytest.raises(ValueError):
+        native.copy_blocks(torch.zeros(4, 1, 2, 8), torch.zeros(4, 1, 2, 8),
+                           torch.zeros(1, 2, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        native.reshape_and_cache(x, x, torch.zeros(4, 2, 2, 8), torch.zeros(4, 2, 2, 8),
+                                 torch.zeros(2, dtype=torch.int64))
