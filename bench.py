@@ -60,7 +60,23 @@ def parse():
     p.add_argument("--placement", default="random", choices=["random", "sequential"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (counter calibration)")
     return p.parse_args()
+
+
+def copy_calibration(mib, reps=5):
+    """A plain device-to-device copy of a known size, run under rocprofv3
+    --pmc to learn how FETCH_SIZE / WRITE_SIZE count bytes on this part."""
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "reps": reps}),
+          flush=True)
 
 
 def build_inputs(name, placement):
@@ -209,6 +225,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     names = sorted(WORKLOAD_DESC) if args.sweep else [args.workload]
     for name in names:
         line = bench_one(name, args, with_cpu=not args.no_cpu_baseline and not args.sweep)
