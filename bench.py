@@ -114,10 +114,14 @@ def step_bytes(wl, dev):
 
 def run_gpu(wl, dev, steps, warmup, partition, path):
     from paged_kv_cache_389_amd import _native as pk
-    ws_len = pk.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                wl.block_size, wl.max_context_len, partition)
-    ws = torch.empty(max(ws_len, 1), dtype=torch.uint8, device="cuda")
     tables = None if path == 3 else dev["tables"]
+    max_blocks = -(-wl.max_context_len // wl.block_size) if tables is None else tables.shape[1]
+    ws_len = pk.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                wl.block_size, max_blocks, wl.max_context_len, wl.dtype,
+                                partition, path)
+    ws = torch.empty(max(ws_len, 1), dtype=torch.uint8, device="cuda")
+    plan = pk.plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                   max_blocks, wl.max_context_len, wl.dtype, partition, path)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
 
@@ -143,7 +147,7 @@ def run_gpu(wl, dev, steps, warmup, partition, path):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     decode_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, decode_ms
+    return wall, decode_ms, plan
 
 
 def cpu_baseline(wl, budget_s):
@@ -178,7 +182,7 @@ def cpu_baseline(wl, budget_s):
 def bench_one(name, args, with_cpu):
     wl, dev = build_inputs(name, args.placement)
     alg_decode, alg_writes = step_bytes(wl, dev)
-    wall, decode_ms = run_gpu(wl, dev, args.steps, args.warmup, args.partition, args.path)
+    wall, decode_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition, args.path)
     ms_per_step = wall / args.steps * 1e3
     dec_ms = float(np.mean(decode_ms))
     achieved = alg_decode / (dec_ms / 1e3) / 1e9
@@ -197,8 +201,9 @@ def bench_one(name, args, with_cpu):
         "data": "synthetic (seeded N(0,1) values, random block placement)",
         "config": {"workload": name, **WORKLOAD_DESC[name], "seed": wl.seed,
                    "placement": args.placement,
-                   "partition_tokens": args.partition or "auto",
-                   "path": ["auto", "valu", "mfma", "contiguous"][args.path]},
+                   "partition_tokens": plan[0], "max_parts": plan[1],
+                   "path": ["auto", "valu", "mfma", "contiguous"][args.path],
+                   "kernel": ["auto", "valu", "mfma"][plan[2]], "longest_first": plan[3]},
         "queries_per_s": round(wl.num_seqs / (ms_per_step / 1e3), 1),
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 5),

@@ -89,17 +89,47 @@ const char* pkv_last_error(void);
 int pkv_supported(pkv_dtype dtype, int head_dim, int block_size);
 
 /*
- * Workspace bytes pkv_paged_attention_decode needs for these sizes.
+ * How a decode call with these sizes would run: the kernel variant and the
+ * partition size.  Long contexts are cut into partitions of
+ * `partition_tokens` tokens; each partition's partial softmax state (running
+ * max, running sum and unnormalised output, all fp32) goes to the workspace
+ * and a second kernel merges them.  With partition_tokens == 0 the library
+ * chooses: one partition per sequence unless the (sequence, head) units of
+ * work are too few to give every compute unit about four workgroups, and
+ * never partitions shorter than 512 tokens.  An explicit partition_tokens
+ * must be a multiple of 32 and of block_size and at most 256 units of the
+ * chosen kernel (4096 tokens for 16-bit types with head_dim 128).
+ * `path` is a pkv_decode_path.
  *
- * Long contexts are split into partitions of `partition_tokens` tokens
- * (0 = the library's choice, the same one the decode call makes) whose
- * partial softmax states (running max, running sum, unnormalised output,
- * all fp32) are merged by a second reduce kernel.  Returns 0 when no split
- * is needed, and (size_t)-1 for invalid sizes.
+ * When the grid holds more than about two rounds of resident workgroups, a
+ * small kernel first orders the sequences longest first (stable within
+ * half-octave length bins) and the decode grid visits them in that order,
+ * so long sequences do not start last and finish alone.  The order only
+ * changes when each sequence is computed, never its result.
+ *
+ * Writes the chosen partition size, the number of partitions the grid
+ * covers per sequence, the kernel variant (PKV_PATH_VALU or PKV_PATH_MFMA)
+ * and whether the longest-first order is used (0/1) to the non-NULL out
+ * pointers.  Returns PKV_OK or the status pkv_paged_attention_decode_ex
+ * would return for these sizes.  Host only.
+ */
+int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int max_context_len,
+                             pkv_dtype dtype, int partition_tokens, int path,
+                             int* out_partition_tokens, int* out_max_parts, int* out_path,
+                             int* out_sorted);
+
+/*
+ * Workspace bytes pkv_paged_attention_decode(_ex) needs for these sizes:
+ * num_seqs * num_q_heads * max_parts * (head_dim + 2) * 4 when the plan has
+ * several partitions, plus num_seqs * 4 when it uses the longest-first
+ * order; 0 when it needs neither.  Returns (size_t)-1 for invalid sizes.
+ * Host only.
  */
 size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
-                                           int head_dim, int block_size, int max_context_len,
-                                           int partition_tokens);
+                                           int head_dim, int block_size, int max_blocks_per_seq,
+                                           int max_context_len, pkv_dtype dtype,
+                                           int partition_tokens, int path);
 
 /*
  * paged_attention_decode: out[s][h][:] = softmax(scale * K_s q[s][h]) V_s
@@ -132,8 +162,10 @@ size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int nu
  *   max_context_len  host-side upper bound of context_lens (sizes the grid;
  *                 no device-to-host read happens)
  *   workspace     device scratch of at least
- *                 pkv_paged_attention_workspace_bytes(...) bytes (may be NULL
- *                 when that is 0); contents need not be initialised.
+ *                 pkv_paged_attention_workspace_bytes(...) bytes, 16-byte
+ *                 aligned (may be NULL when that is 0); contents need not be
+ *                 initialised.  Calls that share a workspace must be ordered
+ *                 (for example, on one stream).
  *
  * Result for L == 0: a zero row.  Preconditions that are not checked on the
  * device: 0 <= context_lens[s] <= min(max_context_len,
@@ -150,8 +182,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Same as pkv_paged_attention_decode with an explicit partition size
- * (0 = library choice; otherwise a multiple of block_size, >= 64) and kernel
- * variant (pkv_decode_path).  Used for tuning sweeps and for the
+ * (0 = library choice; see pkv_paged_attention_plan for the rules) and
+ * kernel variant (pkv_decode_path).  Used for tuning sweeps and for the
  * contiguous-layout control. */
 int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_tables,

@@ -16,7 +16,7 @@ The device calls load ``libpagedkv.so`` on first use and raise
 CPU implementation.
 """
 
-_NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_bytes",
+_NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
            "PATH_MFMA", "PATH_CONTIGUOUS")
 

@@ -51,7 +51,10 @@ def _load():
     lib.pkv_supported.restype = i32
     lib.pkv_supported.argtypes = [i32, i32, i32]
     lib.pkv_paged_attention_workspace_bytes.restype = sz
-    lib.pkv_paged_attention_workspace_bytes.argtypes = [i32] * 7
+    lib.pkv_paged_attention_workspace_bytes.argtypes = [i32] * 10
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.pkv_paged_attention_plan.restype = i32
+    lib.pkv_paged_attention_plan.argtypes = [i32] * 10 + [ip, ip, ip, ip]
     lib.pkv_paged_attention_decode.restype = i32
     lib.pkv_paged_attention_decode.argtypes = [
         vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
@@ -70,7 +73,8 @@ lib = _load()
 
 EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_supported",
-    "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_decode",
+    "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_plan",
+    "pkv_paged_attention_decode",
     "pkv_paged_attention_decode_ex", "pkv_reshape_and_cache", "pkv_copy_blocks",
 )
 
@@ -104,10 +108,33 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dtype_code(dtype):
+    if isinstance(dtype, int):
+        return dtype
+    if dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return _DTYPE_CODE[dtype]
+
+
+def plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+         max_context_len, dtype, partition_tokens=0, path=PATH_AUTO):
+    """(partition_tokens, max_parts, path, sorted) a decode call with these
+    sizes would use (see ``pkv_paged_attention_plan``)."""
+    pt, mp, pa, so = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    st = lib.pkv_paged_attention_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, max_context_len, _dtype_code(dtype),
+                                      partition_tokens, path, ctypes.byref(pt), ctypes.byref(mp),
+                                      ctypes.byref(pa), ctypes.byref(so))
+    _check("paged_attention_plan", st)
+    return pt.value, mp.value, pa.value, bool(so.value)
+
+
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                    max_context_len, partition_tokens=0) -> int:
+                    max_blocks_per_seq, max_context_len, dtype, partition_tokens=0,
+                    path=PATH_AUTO) -> int:
     n = lib.pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                block_size, max_context_len, partition_tokens)
+                                                block_size, max_blocks_per_seq, max_context_len,
+                                                _dtype_code(dtype), partition_tokens, path)
     if n == _SIZE_MAX:
         raise ValueError("invalid sizes for the decode workspace")
     return int(n)
@@ -146,7 +173,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         -(-int(max_context_len) // bs)
     if block_tables is not None and block_tables.shape[0] != num_seqs:
         raise ValueError("block_tables must have num_seqs rows")
-    need = workspace_bytes(num_seqs, hq, hkv, hd, bs, int(max_context_len), partition_tokens)
+    need = workspace_bytes(num_seqs, hq, hkv, hd, bs, max_blocks, int(max_context_len), q.dtype,
+                           partition_tokens, path)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None

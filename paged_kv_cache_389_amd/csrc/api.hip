@@ -1,10 +1,12 @@
 // C ABI of libpagedkv.so: argument validation, the split heuristic and
 // kernel dispatch.  See include/pagedkv.h for the contract of every call.
+#include <stdint.h>
 #include <stdlib.h>
 
 #include <string>
 
 #include "decode.h"
+#include "order.h"
 #include "pagedkv.h"
 
 using namespace pkv;
@@ -13,9 +15,11 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr int kMinPartition = 32;       // tokens; keeps partitions tile aligned
-constexpr int kDefaultPartition = 512;  // tokens per workgroup on long contexts
+constexpr int kPartAlign = 32;          // tokens; partitions are whole 32-token spans
+constexpr int kMinAutoPartition = 512;  // the library never splits finer than this
+constexpr int kWgPerCu = 4;             // split until about this many workgroups per CU
 constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxDevices = 64;
 
 int elem_size(pkv_dtype d) { return d == PKV_F32 ? 4 : 2; }
 bool dtype_ok(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
@@ -30,23 +34,94 @@ int fail_hip(hipError_t e) {
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Tokens per partition.  Short contexts run as one partition (no reduce);
-// longer ones are cut into fixed-size pieces so that very uneven lengths
-// still spread evenly over the 256 compute units.
-int partition_tokens(int max_context_len, int block_size, int requested) {
-  const int unit = block_size > kMinPartition ? block_size : kMinPartition;
-  if (requested > 0) return requested;
-  if (max_context_len <= kDefaultPartition) return round_up(max_context_len > 0 ? max_context_len : 1, unit);
-  return round_up(kDefaultPartition, unit);
+// Compute units of the current device (cached per device; 256 if unknown).
+int compute_units() {
+  static int cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  return n;
 }
 
-bool partition_ok(int p, int block_size) {
-  return p >= kMinPartition && p % kMinPartition == 0 && p % block_size == 0;
+// The kernel a decode call runs and how it cuts contexts into partitions.
+struct Plan {
+  bool mfma = false;
+  int part_tokens = 0;   // tokens per partition
+  int max_parts = 0;     // partitions the grid covers per sequence
+  int len_cap = 0;       // context lengths are clamped to this
+  bool sort = false;     // visit sequences longest first
+  bool sort_kernel = false;  // ... through the order kernel (large batches)
+  int status = PKV_OK;
+};
+
+Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+               int max_blocks_per_seq, int max_context_len, pkv_dtype dtype, int requested,
+               int path) {
+  Plan pl;
+  const Elem e = to_elem(dtype);
+  if (!decode_valu_supported(e, head_dim, block_size)) {
+    pl.status = PKV_EUNSUPPORTED;
+    return pl;
+  }
+  const int group = num_q_heads / num_kv_heads;
+  const bool mfma_ok = group >= 2 && group <= 16 && decode_mfma_supported(e, head_dim, block_size);
+  if (path == PKV_PATH_MFMA && !mfma_ok) {
+    pl.status = PKV_EUNSUPPORTED;
+    return pl;
+  }
+  pl.mfma = path == PKV_PATH_MFMA || ((path == PKV_PATH_AUTO || path == PKV_PATH_CONTIGUOUS) && mfma_ok);
+
+  const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+  pl.len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
+
+  // a wave handles at most 64 units of a partition
+  const int unit = pl.mfma ? 16 : valu_unit_tokens(e, head_dim, block_size);
+  const int p_max = 256 * unit / kPartAlign * kPartAlign;
+  int p;
+  if (requested > 0) {
+    if (requested % kPartAlign || requested % block_size || requested > p_max) {
+      pl.status = PKV_EINVAL;
+      return pl;
+    }
+    p = requested;
+  } else {
+    // one partition per (sequence, head) unit unless those units are too
+    // few to give every compute unit several workgroups
+    const int64_t units = (int64_t)num_seqs * (pl.mfma ? num_kv_heads : num_q_heads);
+    const int64_t target = (int64_t)kWgPerCu * compute_units();
+    const int64_t parts = units >= target ? 1 : (target + units - 1) / units;
+    const int len = pl.len_cap > 0 ? pl.len_cap : 1;
+    p = round_up((int)((len + parts - 1) / parts), kPartAlign);
+    if (p < kMinAutoPartition) p = round_up(len < kMinAutoPartition ? len : kMinAutoPartition, kPartAlign);
+    if (p > p_max) p = p_max;
+  }
+  pl.part_tokens = p;
+  pl.max_parts = pl.len_cap > 0 ? (pl.len_cap + p - 1) / p : 1;
+  // Longest first pays off once the grid is more than about two rounds of
+  // resident workgroups (the VALU kernel keeps 4 per compute unit, the MFMA
+  // kernel 3); with fewer, nearly every workgroup starts at once anyway.
+  const int64_t wgs = (int64_t)pl.max_parts * (pl.mfma ? num_kv_heads : num_q_heads) * num_seqs;
+  const int64_t resident = (int64_t)(pl.mfma ? 3 : 4) * compute_units();
+  pl.sort = num_seqs > 1 && wgs > 2 * resident;
+  pl.sort_kernel = pl.sort && num_seqs > kFusedOrderMax;
+  return pl;
 }
 
-size_t workspace_for(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+// Workspace layout: partial outputs [B][Hq][max_parts][HD] fp32, then
+// partial (max, sum) [B][Hq][max_parts][2] fp32 (both only with several
+// partitions), then the sequence order [B] int32 (only when sorting).
+size_t partials_bytes(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
   if (max_parts <= 1) return 0;
   return (size_t)num_seqs * num_q_heads * max_parts * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+size_t workspace_for(int num_seqs, int num_q_heads, int head_dim, const Plan& pl) {
+  return partials_bytes(num_seqs, num_q_heads, head_dim, pl.max_parts) +
+         (pl.sort_kernel ? (size_t)num_seqs * sizeof(int32_t) : 0);
 }
 
 }  // namespace
@@ -74,15 +149,38 @@ int pkv_supported(pkv_dtype dtype, int head_dim, int block_size) {
 }
 
 size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
-                                           int head_dim, int block_size, int max_context_len,
-                                           int partition) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || max_context_len < 0 || partition < 0)
+                                           int head_dim, int block_size, int max_blocks_per_seq,
+                                           int max_context_len, pkv_dtype dtype,
+                                           int partition_tokens, int path) {
+  if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      num_q_heads % num_kv_heads)
     return (size_t)-1;
-  const int p = partition_tokens(max_context_len, block_size, partition);
-  if (!partition_ok(p, block_size)) return (size_t)-1;
-  const int max_parts = (max_context_len + p - 1) / p;
-  return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+  const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, max_context_len, dtype, partition_tokens, path);
+  if (pl.status != PKV_OK) return (size_t)-1;
+  return workspace_for(num_seqs, num_q_heads, head_dim, pl);
+}
+
+int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int max_context_len,
+                             pkv_dtype dtype, int partition_tokens, int path,
+                             int* out_partition_tokens, int* out_max_parts, int* out_path,
+                             int* out_sorted) {
+  if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      num_q_heads % num_kv_heads)
+    return PKV_EINVAL;
+  const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, max_context_len, dtype, partition_tokens, path);
+  if (pl.status != PKV_OK) return pl.status;
+  if (out_partition_tokens) *out_partition_tokens = pl.part_tokens;
+  if (out_max_parts) *out_max_parts = pl.max_parts;
+  if (out_path) *out_path = pl.mfma ? PKV_PATH_MFMA : PKV_PATH_VALU;
+  if (out_sorted) *out_sorted = pl.sort ? 1 : 0;
+  return PKV_OK;
 }
 
 int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
@@ -103,29 +201,18 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_tables && !contiguous))
     return PKV_EINVAL;
   if (num_seqs > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PKV_EUNSUPPORTED;
+  if (max_blocks_per_seq > (1 << 30) / block_size) return PKV_EUNSUPPORTED;
   if (contiguous && (int64_t)num_seqs * max_blocks_per_seq > num_blocks) return PKV_EINVAL;
 
   const Elem e = to_elem(dtype);
-  const int group = num_q_heads / num_kv_heads;
-  const bool mfma_ok = group >= 2 && group <= 16 && decode_mfma_supported(e, head_dim, block_size);
-  bool use_mfma;
-  if (path == PKV_PATH_MFMA) {
-    if (!mfma_ok) return PKV_EUNSUPPORTED;
-    use_mfma = true;
-  } else if (path == PKV_PATH_VALU) {
-    use_mfma = false;
-  } else {
-    use_mfma = mfma_ok;
-  }
-  if (!decode_valu_supported(e, head_dim, block_size)) return PKV_EUNSUPPORTED;
-
-  const int p = partition_tokens(max_context_len, block_size, partition);
-  if (!partition_ok(p, block_size)) return PKV_EINVAL;
-  const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
-  const int len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
-  const int max_parts = len_cap > 0 ? (len_cap + p - 1) / p : 1;
-  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+  const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, max_context_len, dtype, partition, path);
+  if (pl.status != PKV_OK) return pl.status;
+  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, pl);
+  const size_t partials = partials_bytes(num_seqs, num_q_heads, head_dim, pl.max_parts);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
+  const bool use_mfma = pl.mfma;
 
   DecodeArgs a;
   a.out = out;
@@ -134,26 +221,37 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.part_ml = static_cast<float*>(workspace);
-  a.part_o = need ? static_cast<float*>(workspace) + (size_t)num_seqs * num_q_heads * max_parts * 2
-                  : nullptr;
+  a.part_o = partials ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = partials ? static_cast<float*>(workspace) +
+                             (size_t)num_seqs * num_q_heads * pl.max_parts * head_dim
+                       : nullptr;
+  a.seq_order = pl.sort_kernel
+                    ? reinterpret_cast<const int32_t*>(static_cast<char*>(workspace) + partials)
+                    : nullptr;
+  a.order_mode = pl.sort_kernel ? 1 : (pl.sort ? 2 : 0);
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
-  a.group = group;
+  a.group = num_q_heads / num_kv_heads;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
-  a.len_cap = len_cap;
-  a.part_tokens = p;
-  a.max_parts = max_parts;
+  a.len_cap = pl.len_cap;
+  a.part_tokens = pl.part_tokens;
+  a.max_parts = pl.max_parts;
   a.contiguous = contiguous ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t err = use_mfma ? launch_decode_mfma(e, head_dim, block_size, a, st)
-                            : launch_decode_valu(e, head_dim, block_size, a, st);
+  hipError_t err;
+  if (pl.sort_kernel) {
+    err = launch_seq_order(context_lens, num_seqs, pl.len_cap,
+                           const_cast<int32_t*>(a.seq_order), st);
+    if (err != hipSuccess) return fail_hip(err);
+  }
+  err = use_mfma ? launch_decode_mfma(e, head_dim, block_size, a, st)
+                 : launch_decode_valu(e, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
-  if (max_parts > 1) {
+  if (pl.max_parts > 1) {
     err = launch_decode_reduce(e, head_dim, a, st);
     if (err != hipSuccess) return fail_hip(err);
   }

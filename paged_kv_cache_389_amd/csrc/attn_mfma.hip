@@ -25,6 +25,12 @@
 // high part and a bf16 remainder and both are multiplied in, which keeps
 // them at about 16 significant bits.
 //
+// Latency hiding, as in the vector-ALU kernel: wave w takes tiles w, w+4,
+// ... of the partition; the physical blocks of all its tiles are fetched up
+// front with one vector load (lane i holds the entry of the wave's i-th
+// tile), and the loads of tile i+1 are issued before tile i is computed.
+// The four waves' states are merged in LDS, sized for at most GMAX heads.
+//
 // Passages: a sequence's KV blocks are gathered through its block table
 // ("Memory Optimization in LLM Serving with PagedAttention", section "How
 // PagedAttention Works"); only the last block is partly filled (same
@@ -32,6 +38,7 @@
 // KV head h / G.
 #include "common.h"
 #include "decode.h"
+#include "order.h"
 
 namespace pkv {
 
@@ -80,34 +87,55 @@ struct MfmaOps<BF16> {
   __device__ static inline float widen_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 };
 
-// {lo16 = element E of x, hi16 = element E of y}
-template <int E>
-__device__ inline uint32_t pair_of(const uint32_t* x, const uint32_t* y) {
+// {lo16 = 16-bit element e of x, hi16 = element e of y}; e is a constant
+// after unrolling
+__device__ inline uint32_t pair_of(int e, const uint32_t* x, const uint32_t* y) {
   // v_perm_b32 selector: bytes 0-3 come from the second source, 4-7 from the first
-  constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-  return __builtin_amdgcn_perm(y[E >> 1], x[E >> 1], sel);
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  return __builtin_amdgcn_perm(y[e >> 1], x[e >> 1], sel);
 }
 
-template <typename E, int HD, int BS>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+template <typename E, int HD, int BS, int GMAX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeArgs a) {
   using T = typename E::storage;
   using Ops = MfmaOps<E>;
-  constexpr int NWAVES = 4;
+  constexpr int NW = 4;
   constexpr int KSTEPS = HD / 32;      // QK MFMAs per tile
   constexpr int DPL = HD / 16;         // V dims per lane per token == PV MFMAs per tile
   constexpr int VW = DPL / 2;          // dwords of V per lane per token
-  constexpr int TILES_PER_BLOCK = BS / 16;
-  static_assert(HD % 32 == 0 && BS % 16 == 0 && VW >= 1, "unsupported shape");
+  constexpr int TPB = BS / 16;         // tiles per block
+  constexpr int OS = HD + 4;           // padded row stride of the LDS output tiles
+  static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
 
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int part = blockIdx.x, g = blockIdx.y;
+  __shared__ OrderScratch sm_order;
+  const int s = a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs, a.len_cap,
+                                                    blockIdx.z, sm_order)
+                                  : sequence_of(a, blockIdx.z);
+  const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
   const int n = lane & 15, g4 = lane >> 4;
   const int G = a.group;
-
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   const int P = a.part_tokens;
   const int tok_begin = part * P;
+  const int unit_begin = tok_begin / 16;
+
+  // independent loads first: the length, the query group, this wave's table entries
+  int L = a.context_lens[s];
+  u32x4 qb[KSTEPS];   // Q^T in the B layout: head n, dims 32*kk + 8*g4 .. +8 (zero past G)
+  {
+    const int hn = n < G ? n : G - 1;
+    const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qb[kk] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+  }
+  int tbl;
+  {
+    const int blk = min((unit_begin + wave + NW * lane) / TPB, a.max_blocks - 1);
+    tbl = a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
+  }
+
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G) * HD;
   if (L == 0) {
     if (part == 0)
@@ -117,20 +145,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   if (tok_begin >= L) return;
   const int tok_end = min(L, tok_begin + P);
   const int nparts = (L + P - 1) / P;
+  const int n_units = (tok_end + 15) / 16 - unit_begin;   // <= 4 * 64
+  const int mine = n_units > wave ? (n_units - wave + NW - 1) / NW : 0;
 
-  // Q^T in the B layout: head n, dims 32*kk + 8*g4 .. +8 (zero for padding heads)
-  u32x4 qb[KSTEPS];
-  {
-    const int hn = n < G ? n : G - 1;   // padding heads load nothing
-    const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      qb[kk] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
-  }
   const size_t block_stride = (size_t)a.num_kv_heads * BS * HD;
   const T* kbase = static_cast<const T*>(a.k_cache) + (size_t)g * BS * HD + n * HD + g4 * 8;
   const T* vbase = static_cast<const T*>(a.v_cache) + (size_t)g * BS * HD + (4 * g4) * HD + n * DPL;
-  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
   f32x4 acc[DPL];
 #pragma unroll
@@ -138,56 +158,54 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   float m = -INFINITY, l = 0.f;
   int bad = 0;
 
-  const int tile_end = (tok_end + 15) / 16;
-  for (int ti = tok_begin / 16 + wave; ti < tile_end; ti += NWAVES) {
-    const int jb = ti / TILES_PER_BLOCK;
-    const int phys = uniform(a.contiguous ? s * a.max_blocks + jb : table[jb]);
-    if (phys < 0 || phys >= a.num_blocks) {
+  // issue the loads of the wave's i-th 16-token tile: K in the A layout
+  // (token row n, dims 32*kk + 8*g4 .. +8), V row-wise (tokens 4*g4 + r,
+  // dims n*DPL .. +DPL)
+  auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VW]) {
+    const int u = unit_begin + wave + NW * i;
+    int phys = lane_value(tbl, i);
+    if ((unsigned)phys >= (unsigned)a.num_blocks) {
       bad = 1;
-      continue;
+      phys = 0;
     }
-    const size_t toff = (size_t)phys * block_stride + (size_t)(ti % TILES_PER_BLOCK) * 16 * HD;
-    u32x4 ka[KSTEPS];
+    const size_t toff = (size_t)phys * block_stride + (size_t)(u % TPB) * 16 * HD;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = ld16(kbase + toff + kk * 32);
-    uint32_t vv[4][VW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const T* vp = vbase + toff + i * HD;
+    for (int r = 0; r < 4; ++r) {
+      const T* vp = vbase + toff + r * HD;
       if constexpr (VW == 2) {
-        u32x2 x = *reinterpret_cast<const u32x2*>(vp);
-        vv[i][0] = x[0];
-        vv[i][1] = x[1];
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+        vv[r][0] = x[0];
+        vv[r][1] = x[1];
       } else {
-#pragma unroll
-        for (int w = 0; w < VW; w += 4) {
-          u32x4 x = ld16(vp + 2 * w);
-          vv[i][w] = x[0];
-          vv[i][w + 1] = x[1];
-          vv[i][w + 2] = x[2];
-          vv[i][w + 3] = x[3];
-        }
+        const u32x4 x = ld16(vp);
+        vv[r][0] = x[0];
+        vv[r][1] = x[1];
+        vv[r][2] = x[2];
+        vv[r][3] = x[3];
       }
     }
+  };
 
+  auto compute_tile = [&](int i, const u32x4* ka, uint32_t (*vv)[VW]) {
+    const int u = unit_begin + wave + NW * i;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
-
-    const int t0 = ti * 16 + 4 * g4;   // token of sacc[0] for this lane
-    const bool whole = ti * 16 + 16 <= tok_end;
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * a.scale_log2e;
-    if (!whole) {
-      // tail tile: mask by index; zero the value rows past the context so a
-      // non-finite value there cannot reach the product
+    for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
+    if (u * 16 + 16 > tok_end) {
+      // the partition's last tile: mask by index, and zero the value rows
+      // past the context so a non-finite value there cannot reach the product
+      const int t0 = u * 16 + 4 * g4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (t0 + i >= tok_end) {
-          sc[i] = -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        if (t0 + r >= tok_end) {
+          sc[r] = -INFINITY;
 #pragma unroll
-          for (int w = 0; w < VW; ++w) vv[i][w] = 0u;
+          for (int w = 0; w < VW; ++w) vv[r][w] = 0u;
         }
       }
     }
@@ -200,76 +218,98 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     m = mn;
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mu);   // exp2(-inf) == 0
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);   // exp2(-inf) == 0
     l = __builtin_fmaf(l, corr, (p[0] + p[1]) + (p[2] + p[3]));
     if (__any(corr != 1.f)) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] *= corr;
     }
 
-    // P^T in the B layout: tokens 4*g4 + j of head n
-    u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
+    // P^T in the B layout: tokens 4*g4 + r of head n
+    const u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
     u32x2 pr = {0u, 0u};
     if constexpr (Ops::kSplit) {
       pr[0] = Ops::pack2(p[0] - Ops::widen_lo(pb[0]), p[1] - Ops::widen_hi(pb[0]));
       pr[1] = Ops::pack2(p[2] - Ops::widen_lo(pb[1]), p[3] - Ops::widen_hi(pb[1]));
     }
     // V^T in the A layout, one MFMA per lane-dim e
-#define PKV_PV_STEP(EE)                                                          \
-  if constexpr ((EE) < DPL) {                                                    \
-    const u32x2 va = {pair_of<(EE)>(vv[0], vv[1]), pair_of<(EE)>(vv[2], vv[3])}; \
-    acc[EE] = Ops::pv(va, pb, acc[EE]);                                          \
-    if constexpr (Ops::kSplit) acc[EE] = Ops::pv(va, pr, acc[EE]);               \
-  }
-    PKV_PV_STEP(0) PKV_PV_STEP(1) PKV_PV_STEP(2) PKV_PV_STEP(3)
-    PKV_PV_STEP(4) PKV_PV_STEP(5) PKV_PV_STEP(6) PKV_PV_STEP(7)
-    PKV_PV_STEP(8) PKV_PV_STEP(9) PKV_PV_STEP(10) PKV_PV_STEP(11)
-    PKV_PV_STEP(12) PKV_PV_STEP(13) PKV_PV_STEP(14) PKV_PV_STEP(15)
-#undef PKV_PV_STEP
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const u32x2 va = {pair_of(e, vv[0], vv[1]), pair_of(e, vv[2], vv[3])};
+      acc[e] = Ops::pv(va, pb, acc[e]);
+      if constexpr (Ops::kSplit) acc[e] = Ops::pv(va, pr, acc[e]);
+    }
+  };
+
+  // two register buffers: the loads of tile i+1 are in flight while tile i
+  // is computed
+  u32x4 kA[KSTEPS], kB[KSTEPS];
+  uint32_t vA[4][VW], vB[4][VW];
+  if (mine > 0) {
+    load_tile(0, kA, vA);
+    int i = 0;
+    // steady state: the loads of the next tile are always issued, so the
+    // wait before each tile's math covers only that tile's own loads
+    for (; i + 2 < mine; i += 2) {
+      load_tile(i + 1, kB, vB);
+      compute_tile(i, kA, vA);
+      load_tile(i + 2, kA, vA);
+      compute_tile(i + 1, kB, vB);
+    }
+    if (i + 1 < mine) {
+      load_tile(i + 1, kB, vB);
+      compute_tile(i, kA, vA);
+      compute_tile(i + 1, kB, vB);
+    } else {
+      compute_tile(i, kA, vA);
+    }
   }
 
   // the four token groups of a head column hold partial sums of l
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
 
-  constexpr int OS = HD + 4;   // padded row stride of the LDS output tiles
-  __shared__ float sm_m[NWAVES][16], sm_l[NWAVES][16];
-  __shared__ float sm_o[NWAVES][16 * OS];
-  __shared__ int sm_bad[NWAVES];
-  if (g4 == 0) {
-    sm_m[wave][n] = m;
-    sm_l[wave][n] = l;
+  // merge the 4 waves in LDS
+  __shared__ float sm_m[NW][GMAX], sm_l[NW][GMAX];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][GMAX][OS];
+  __shared__ int sm_bad[NW];
+  if (n < G) {
+    if (g4 == 0) {
+      sm_m[wave][n] = m;
+      sm_l[wave][n] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm_o[wave][n][(4 * g4 + r) * DPL + e] = acc[e][r];
   }
-#pragma unroll
-  for (int e = 0; e < DPL; ++e)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[wave][n * OS + (4 * g4 + i) * DPL + e] = acc[e][i];
-  if (lane == 0) sm_bad[wave] = bad;
+  const int any_bad = __any(bad);
+  if (lane == 0) sm_bad[wave] = any_bad;
   __syncthreads();
 
-  const int any_bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
-  for (int idx = tid; idx < G * HD; idx += 256) {
-    const int hh = idx / HD, d = idx % HD;
+  const int all_bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
+  for (int idx = tid; idx < G * (HD / 4); idx += 256) {
+    const int hh = idx / (HD / 4), d = (idx % (HD / 4)) * 4;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, sm_m[w][hh]);
-    float Ls = 0.f, O = 0.f;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float Ls = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) {
-      const float wt = fast_exp2(sm_m[w][hh] - M);
+    for (int w = 0; w < NW; ++w) {
+      const float wt = fast_exp2(sm_m[w][hh] - M);   // M is finite: the partition has a token
       Ls = __builtin_fmaf(wt, sm_l[w][hh], Ls);
-      O = __builtin_fmaf(wt, sm_o[w][hh * OS + d], O);
+      O += wt * *reinterpret_cast<const f32x4*>(&sm_o[w][hh][d]);
     }
-    if (any_bad) O = __builtin_nanf("");
+    if (all_bad) O = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     if (nparts == 1) {
-      out[idx] = E::round(O / Ls);
+      const float inv = 1.f / Ls;
+      float r[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
+      store_rounded<E, 4>(out + hh * HD + d, r);
     } else {
       const size_t pidx = ((size_t)s * a.num_q_heads + (size_t)g * G + hh) * a.max_parts + part;
-      a.part_o[pidx * HD + d] = O;
-      if (d == 0) {
-        a.part_ml[2 * pidx] = M;
-        a.part_ml[2 * pidx + 1] = Ls;
-      }
+      *reinterpret_cast<f32x4*>(a.part_o + pidx * HD + d) = O;
+      if (d == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * pidx) = f32x2{M, Ls};
     }
   }
 }
@@ -277,7 +317,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 template <typename E, int HD, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
+  if (a.group <= 4)
+    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, 4>), grid, dim3(256), 0, st, a);
+  else if (a.group <= 8)
+    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, 8>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, 16>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,48 +1,86 @@
-// Paged decode attention, vector-ALU variant, and the partition reduce.
+// Paged decode attention, vector-ALU variant (one query head per workgroup).
 //
-// One workgroup (4 waves) computes one query head of one sequence over one
+// A workgroup (4 waves) computes one query head of one sequence over one
 // partition of its context.  The sequence's KV lives in fixed-size physical
 // blocks reached through its block table ("Memory Optimization in LLM
 // Serving with PagedAttention", section "How PagedAttention Works"); only the
 // last block is partly filled, and its tail is masked by token index.
 //
-// Data movement: a (block, kv head) tile is block_size rows of head_dim
-// contiguous elements.  A wave reads it with 16-byte loads, LPR lanes per row
-// and 64/LPR rows per load instruction, so every load instruction covers
-// whole rows and is fully coalesced.  Each lane keeps the 16 bytes of the
-// query that match its columns; a row's dot product is LPR partial dot
-// products (v_dot2 for 16-bit types) summed across the row with DPP.
+// Work unit: UT consecutive tokens of one block (UT = CH * RPI, at most a
+// whole block).  A wave reads a unit's K rows and V rows with CH 16-byte
+// loads each: LPR lanes cover one token row of head_dim elements and one
+// load instruction covers RPI whole rows, so every load is fully coalesced.
+// Each lane keeps the 16 bytes of the query that match its columns; a row's
+// dot product is LPR partial dot products (v_dot2 for 16-bit types) summed
+// across the row with DPP.
+//
+// Latency hiding: wave w takes units w, w+4, w+8, ... of the partition.  The
+// physical block of each of its units is fetched up front with one vector
+// load (lane i holds the entry of the wave's i-th unit), so no unit waits on
+// a table read, and the loads of unit i+1 are issued before unit i is
+// computed (two register buffers), so every wave keeps loads in flight.
 //
 // Softmax: every row group of a wave keeps its own online state (running
 // max m in log2 units, running sum l, unnormalised output o) over the tokens
-// it sees; the 4*RPI states of the workgroup are merged in LDS at the end.
-// When the context is split into several partitions, each partition stores
-// (m, l, o) in fp32 and a second kernel merges them (log-sum-exp rule).
+// it sees; the states are merged across row groups with lane shuffles and
+// across waves in LDS.  When the context is split into several partitions,
+// each partition stores (m, l, o) in fp32 and attn_reduce.hip merges them.
 #include "common.h"
 #include "decode.h"
+#include "order.h"
 
 namespace pkv {
 
 template <typename E, int HD, int BS>
+struct ValuTiling {
+  static constexpr int VEC = E::kVec;            // elements per 16-byte load
+  static constexpr int LPR = HD / VEC;           // lanes per token row
+  static constexpr int RPI = kWave / LPR;        // token rows per load instruction
+  static constexpr int LPB = BS / RPI;           // load instructions per block
+  static constexpr int CH = LPB < 4 ? LPB : 4;   // load instructions per unit
+  static constexpr int UT = CH * RPI;            // tokens per unit
+  static constexpr int UPB = BS / UT;            // units per block
+  static_assert(RPI * LPR == kWave && BS % RPI == 0 && LPB % CH == 0, "unsupported shape");
+};
+
+int valu_unit_tokens(Elem e, int head_dim, int block_size) {
+  const int vec = e == Elem::F32 ? 4 : 8;
+  const int rpi = kWave / (head_dim / vec);
+  const int lpb = block_size / rpi;
+  return (lpb < 4 ? lpb : 4) * rpi;
+}
+
+template <typename E, int HD, int BS>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   using T = typename E::storage;
-  constexpr int VEC = E::kVec;           // elements per 16-byte load
-  constexpr int LPR = HD / VEC;          // lanes per token row
-  constexpr int RPI = kWave / LPR;       // token rows per load instruction
-  constexpr int TPL = BS / RPI;          // loads per block per lane (K, and again V)
-  constexpr int CH = TPL < 8 ? TPL : 8;  // loads issued together (bounds registers)
-  constexpr int NWAVES = 4;
-  constexpr int NROWS = NWAVES * RPI;    // online-softmax states per workgroup
-  static_assert(RPI * LPR == kWave && BS % RPI == 0 && TPL % CH == 0, "unsupported shape");
+  using Tl = ValuTiling<E, HD, BS>;
+  constexpr int VEC = Tl::VEC, LPR = Tl::LPR, RPI = Tl::RPI, CH = Tl::CH, UT = Tl::UT,
+                UPB = Tl::UPB;
+  constexpr int NW = 4;
 
-  const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int part = blockIdx.x, h = blockIdx.y;
+  __shared__ OrderScratch sm_order;
+  const int s = a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs, a.len_cap,
+                                                    blockIdx.z, sm_order)
+                                  : sequence_of(a, blockIdx.z);
+  const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
   const int row = lane / LPR, col = lane % LPR;
-
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   const int P = a.part_tokens;
   const int tok_begin = part * P;
+  const int unit_begin = tok_begin / UT;
+  const int g = h / a.group;
+
+  // independent loads first: the length, the query slice, this wave's table entries
+  int L = a.context_lens[s];
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + h) * HD;
+  const u32x4 qv = ld16(qrow + col * VEC);
+  int tbl;
+  {
+    const int blk = min((unit_begin + wave + NW * lane) / UPB, a.max_blocks - 1);
+    tbl = a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
+  }
+
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
   if (L == 0) {
     if (part == 0)
@@ -52,158 +90,181 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   if (tok_begin >= L) return;
   const int tok_end = min(L, tok_begin + P);
   const int nparts = (L + P - 1) / P;
-  const int g = h / a.group;
+  const int n_units = (tok_end + UT - 1) / UT - unit_begin;   // <= 4 * 64
+  const int mine = n_units > wave ? (n_units - wave + NW - 1) / NW : 0;
 
-  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + h) * HD;
-  const u32x4 qv = ld16(qrow + col * VEC);
   const T* kbase = static_cast<const T*>(a.k_cache) + (size_t)g * BS * HD + row * HD + col * VEC;
   const T* vbase = static_cast<const T*>(a.v_cache) + (size_t)g * BS * HD + row * HD + col * VEC;
   const size_t block_stride = (size_t)a.num_kv_heads * BS * HD;
-  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
   float m = -INFINITY, l = 0.f, o[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.f;
   int bad = 0;
 
-  const int blk_end = (tok_end + BS - 1) / BS;
-  for (int jb = tok_begin / BS + wave; jb < blk_end; jb += NWAVES) {
-    const int phys = uniform(a.contiguous ? s * a.max_blocks + jb : table[jb]);
-    if (phys < 0 || phys >= a.num_blocks) {
+  // issue the loads of the wave's i-th unit
+  auto load_unit = [&](int i, u32x4* kr, u32x4* vr) {
+    const int u = unit_begin + wave + NW * i;
+    int phys = lane_value(tbl, i);
+    if ((unsigned)phys >= (unsigned)a.num_blocks) {
       bad = 1;
-      continue;
+      phys = 0;
     }
-    const T* kt = kbase + (size_t)phys * block_stride;
-    const T* vt = vbase + (size_t)phys * block_stride;
-    const bool whole = (jb + 1) * BS <= tok_end;
+    const size_t off = (size_t)phys * block_stride + (size_t)(u % UPB) * UT * HD;
 #pragma unroll
-    for (int c0 = 0; c0 < TPL; c0 += CH) {
-      u32x4 kr[CH], vr[CH];
+    for (int c = 0; c < CH; ++c) kr[c] = ld16(kbase + off + c * RPI * HD);
 #pragma unroll
-      for (int i = 0; i < CH; ++i) kr[i] = ld16(kt + (c0 + i) * RPI * HD);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) vr[i] = ld16(vt + (c0 + i) * RPI * HD);
-      float sc[CH];
-#pragma unroll
-      for (int i = 0; i < CH; ++i)
-        sc[i] = group_sum<LPR>(E::dot16(kr[i], qv, 0.f)) * a.scale_log2e;
+    for (int c = 0; c < CH; ++c) vr[c] = ld16(vbase + off + c * RPI * HD);
+  };
 
-      if (whole) {
-        // every token of the block is inside the context
-        float mb = sc[0];
+  // fold the wave's i-th unit into the online state
+  auto compute_unit = [&](int i, const u32x4* kr, const u32x4* vr) {
+    const int u = unit_begin + wave + NW * i;
+    float sc[CH];
 #pragma unroll
-        for (int i = 1; i < CH; ++i) mb = fmaxf(mb, sc[i]);
-        const float mn = fmaxf(m, mb);
-        const float corr = fast_exp2(m - mn);
-        m = mn;
-        l *= corr;
+    for (int c = 0; c < CH; ++c) sc[c] = group_sum<LPR>(E::dot16(kr[c], qv, 0.f)) * a.scale_log2e;
+    if ((u + 1) * UT <= tok_end) {
+      // every token of the unit is inside the partition
+      float mb = sc[0];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] *= corr;
+      for (int c = 1; c < CH; ++c) mb = fmaxf(mb, sc[c]);
+      const float mn = fmaxf(m, mb);
+      const float corr = fast_exp2(m - mn);
+      m = mn;
+      l *= corr;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          const float p = fast_exp2(sc[i] - mn);
+      for (int e = 0; e < VEC; ++e) o[e] *= corr;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const float p = fast_exp2(sc[c] - mn);
+        l += p;
+        float vf[VEC];
+        E::unpack16(vr[c], vf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
+      }
+    } else {
+      // the partition's last unit: tokens at or past tok_end are masked by
+      // index, never by arithmetic, so whatever those slots hold cannot
+      // reach the result
+      const int t0 = u * UT + row;
+      float mb = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (t0 + c * RPI < tok_end) mb = fmaxf(mb, sc[c]);
+      const float mn = fmaxf(m, mb);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float corr = fast_exp2(m - mu);
+      m = mn;
+      l *= corr;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] *= corr;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (t0 + c * RPI < tok_end) {
+          const float p = fast_exp2(sc[c] - mu);
           l += p;
           float vf[VEC];
-          E::unpack16(vr[i], vf);
+          E::unpack16(vr[c], vf);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
         }
-      } else {
-        // last block: tokens at or past tok_end are masked by index, never
-        // by arithmetic, so whatever those slots hold cannot reach the result
-        const int t0 = jb * BS + c0 * RPI + row;
-        float mb = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-          if (t0 + i * RPI < tok_end) mb = fmaxf(mb, sc[i]);
-        const float mn = fmaxf(m, mb);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float corr = fast_exp2(m - mu);
-        m = mn;
-        l *= corr;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] *= corr;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          if (t0 + i * RPI < tok_end) {
-            const float p = fast_exp2(sc[i] - mu);
-            l += p;
-            float vf[VEC];
-            E::unpack16(vr[i], vf);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
-          }
-        }
       }
     }
-  }
+  };
 
-  // merge the workgroup's NROWS partial states
-  __shared__ float sm_m[NROWS], sm_l[NROWS];
-  __shared__ float sm_o[NROWS][HD];
-  __shared__ int sm_bad[NWAVES];
-  const int r = wave * RPI + row;
-  if (col == 0) {
-    sm_m[r] = m;
-    sm_l[r] = l;
-  }
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) sm_o[r][col * VEC + e] = o[e];
-  if (lane == 0) sm_bad[wave] = bad;
-  __syncthreads();
-
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NROWS; ++i) M = fmaxf(M, sm_m[i]);
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVES; ++w) any_bad |= sm_bad[w];
-  const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + part;
-  for (int d = tid; d < HD; d += 256) {
-    float Ls = 0.f, O = 0.f;
-#pragma unroll
-    for (int i = 0; i < NROWS; ++i) {
-      const float w = fast_exp2(sm_m[i] - M);
-      Ls = __builtin_fmaf(w, sm_l[i], Ls);
-      O = __builtin_fmaf(w, sm_o[i][d], O);
+  // two register buffers: the loads of unit i+1 are in flight while unit i
+  // is computed
+  u32x4 kA[CH], vA[CH], kB[CH], vB[CH];
+  if (mine > 0) {
+    load_unit(0, kA, vA);
+    int i = 0;
+    // steady state: the loads of the next unit are always issued, so the
+    // wait before each unit's math covers only that unit's own loads
+    for (; i + 2 < mine; i += 2) {
+      load_unit(i + 1, kB, vB);
+      compute_unit(i, kA, vA);
+      load_unit(i + 2, kA, vA);
+      compute_unit(i + 1, kB, vB);
     }
-    if (any_bad) O = __builtin_nanf("");
-    if (nparts == 1) {
-      out[d] = E::round(O / Ls);
+    if (i + 1 < mine) {
+      load_unit(i + 1, kB, vB);
+      compute_unit(i, kA, vA);
+      compute_unit(i + 1, kB, vB);
     } else {
-      a.part_o[pidx * HD + d] = O;
-      if (d == 0) {
-        a.part_ml[2 * pidx] = M;
-        a.part_ml[2 * pidx + 1] = Ls;
-      }
+      compute_unit(i, kA, vA);
     }
   }
-}
 
-// Merge the partitions of one (sequence, query head): with per-partition
-// running max m_p (log2 units), sum l_p and unnormalised output o_p,
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-template <typename E, int HD>
-__global__ __launch_bounds__(HD) void decode_reduce_kernel(DecodeArgs a) {
-  using T = typename E::storage;
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;
-  const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
-  const float* ml = a.part_ml + 2 * base;
-  const float* po = a.part_o + base * HD + d;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  float Ls = 0.f, O = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(ml[2 * p] - M);
-    Ls = __builtin_fmaf(w, ml[2 * p + 1], Ls);
-    O = __builtin_fmaf(w, po[(size_t)p * HD], O);
+  // merge the wave's RPI row groups (lanes that differ in `row`)
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    const float mo = __shfl_xor(m, off, 64);
+    const float lo = __shfl_xor(l, off, 64);
+    const float mn = fmaxf(m, mo);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float wa = fast_exp2(m - mu), wb = fast_exp2(mo - mu);
+    l = l * wa + lo * wb;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = o[e] * wa + __shfl_xor(o[e], off, 64) * wb;
+    m = mn;
   }
-  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
-  out[d] = E::round(O / Ls);
+
+  // merge the 4 waves in LDS
+  __shared__ float sm_m[NW], sm_l[NW];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][HD];
+  __shared__ int sm_bad[NW];
+  if (lane == 0) {
+    sm_m[wave] = m;
+    sm_l[wave] = l;
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<f32x4*>(&sm_o[wave][col * VEC + e]) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+  }
+  const int any_bad = __any(bad);
+  if (lane == 0) sm_bad[wave] = any_bad;
+  __syncthreads();
+  if (wave != 0 || row != 0) return;
+
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w]);
+  float wt[NW], Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wt[w] = fast_exp2(sm_m[w] - M);   // M is finite: this partition has a token
+    Ls = __builtin_fmaf(wt[w], sm_l[w], Ls);
+  }
+  float O[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; e += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&sm_o[w][col * VEC + e]);
+    O[e] = acc[0];
+    O[e + 1] = acc[1];
+    O[e + 2] = acc[2];
+    O[e + 3] = acc[3];
+  }
+  if (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) O[e] = __builtin_nanf("");
+  }
+  if (nparts == 1) {
+    const float inv = 1.f / Ls;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) O[e] *= inv;
+    store_rounded<E, VEC>(out + col * VEC, O);
+  } else {
+    const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + part;
+    float* po = a.part_o + pidx * HD + col * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<f32x4*>(po + e) = f32x4{O[e], O[e + 1], O[e + 2], O[e + 3]};
+    if (col == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * pidx) = f32x2{M, Ls};
+  }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -245,32 +306,6 @@ hipError_t launch_decode_valu(Elem e, int hd, int bs, const DecodeArgs& a, hipSt
     case Elem::F32: return launch_valu_e<F32>(hd, bs, a, st);
     case Elem::F16: return launch_valu_e<F16>(hd, bs, a, st);
     case Elem::BF16: return launch_valu_e<BF16>(hd, bs, a, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename E, int HD>
-static hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.num_q_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_reduce_kernel<E, HD>), grid, dim3(HD), 0, st, a);
-  return hipGetLastError();
-}
-
-template <typename E>
-static hipError_t launch_reduce_e(int hd, const DecodeArgs& a, hipStream_t st) {
-  switch (hd) {
-    case 64: return launch_reduce_t<E, 64>(a, st);
-    case 128: return launch_reduce_t<E, 128>(a, st);
-    case 256: return launch_reduce_t<E, 256>(a, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_reduce(Elem e, int hd, const DecodeArgs& a, hipStream_t st) {
-  switch (e) {
-    case Elem::F32: return launch_reduce_e<F32>(hd, a, st);
-    case Elem::F16: return launch_reduce_e<F16>(hd, a, st);
-    case Elem::BF16: return launch_reduce_e<BF16>(hd, a, st);
   }
   return hipErrorInvalidValue;
 }

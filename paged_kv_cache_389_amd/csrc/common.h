@@ -9,6 +9,7 @@ namespace pkv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -25,6 +26,10 @@ template <typename To>
 __device__ inline To lane_as(uint32_t x) {
   return __builtin_bit_cast(To, x);
 }
+
+// 16-byte global load / store.
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Element types.  Each describes how a 16-byte vector of the type is read
 // into fp32 and how an fp32 result is rounded back (nearest even).
@@ -61,6 +66,11 @@ struct F16 {
     }
   }
   __device__ static inline storage round(float x) { return (_Float16)x; }
+  // round two floats and pack them into one 32-bit word, x in the low half
+  __device__ static inline uint32_t pack2(float x, float y) {
+    const f16x2 h = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
 };
 
 struct BF16 {
@@ -81,11 +91,34 @@ struct BF16 {
     }
   }
   __device__ static inline storage round(float x) { return (__bf16)x; }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    const bf16x2 h = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
 };
 
-// 16-byte global load / store.
-__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Round n floats (n a multiple of 4) to E's storage type and store them at
+// p with the widest aligned vector stores (16 bytes for 8 half-width or 4
+// single-width elements).
+template <typename E, int N>
+__device__ inline void store_rounded(typename E::storage* p, const float* x) {
+  static_assert(N % 4 == 0, "store_rounded needs a multiple of 4 elements");
+  if constexpr (sizeof(typename E::storage) == 4) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<f32x4*>(p + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+  } else if constexpr (N % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 8)
+      st16(p + i, u32x4{E::pack2(x[i], x[i + 1]), E::pack2(x[i + 2], x[i + 3]),
+                        E::pack2(x[i + 4], x[i + 5]), E::pack2(x[i + 6], x[i + 7])});
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<u32x2*>(p + i) = u32x2{E::pack2(x[i], x[i + 1]), E::pack2(x[i + 2], x[i + 3])};
+  }
+}
+
 
 // Cross-lane moves inside a 16-lane DPP row.
 template <int CTRL>
@@ -112,6 +145,21 @@ __device__ inline float group_sum(float v) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum / sum over all 64 lanes of a wave; every lane receives it.
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Value of a wave-uniform lane's register (v_readlane with an SGPR index).
+__device__ inline int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
 // Scalar (wave-uniform) copy of a value.
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -56,15 +56,41 @@ def test_supported_shapes(native):
     assert lib.pkv_supported(7, 128, 16) == 0
 
 
-def test_workspace_bytes(native):
+def test_workspace_bytes_and_plan(native):
+    import torch
+    f16, bf16 = torch.float16, torch.bfloat16
     # one partition (short contexts): no workspace
-    assert native.workspace_bytes(4, 4, 4, 64, 16, 64) == 0
-    # long contexts: fp32 (m, l) + [head_dim] per (seq, q head, partition)
-    parts = -(-32768 // 512)
-    assert native.workspace_bytes(8, 64, 8, 128, 32, 32768) == 8 * 64 * parts * 130 * 4
-    assert native.workspace_bytes(8, 64, 8, 128, 32, 32768, 1024) == 8 * 64 * 32 * 130 * 4
+    assert native.workspace_bytes(4, 4, 4, 64, 16, 4, 64, torch.float32) == 0
+    assert native.plan(4, 4, 4, 64, 16, 4, 64, torch.float32) == (64, 1, native.PATH_VALU, False)
+    # many (sequence, head) units: one partition per sequence, longest first
+    # (the order is computed inside the decode kernel: no workspace)
+    assert native.plan(64, 40, 40, 128, 16, 128, 2048, f16) == (2048, 1, native.PATH_VALU, True)
+    assert native.workspace_bytes(64, 40, 40, 128, 16, 128, 2048, f16) == 0
+    # more than 1024 sequences: a separate order kernel writes the order to the workspace
+    assert native.plan(2000, 8, 8, 128, 16, 8, 128, f16)[3]
+    assert native.workspace_bytes(2000, 8, 8, 128, 16, 8, 128, f16) == 2000 * 4
+    assert native.plan(256, 32, 8, 128, 16, 256, 4096, bf16) == (4096, 1, native.PATH_MFMA, True)
+    # few units, long contexts: split so that every compute unit gets work
+    p, parts, path, srt = native.plan(8, 64, 8, 128, 32, 1024, 32768, bf16)
+    assert path == native.PATH_MFMA and parts > 1 and p * parts >= 32768 and p % 32 == 0
+    assert native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16) == \
+        8 * 64 * parts * 130 * 4
+    # an explicit partition size
+    assert native.plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 4096) == \
+        (4096, 8, native.PATH_MFMA, False)
+    assert native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 4096) == \
+        8 * 64 * 8 * 130 * 4
+    # 2048 workgroups: more than two rounds of resident ones, so longest first
+    assert native.plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024) == \
+        (1024, 32, native.PATH_MFMA, True)
+    # the table width caps the context: 10 blocks of 16 tokens
+    assert native.plan(2, 4, 4, 128, 16, 10, 100000, f16, 64)[1] == 3
     with pytest.raises(ValueError):
-        native.workspace_bytes(8, 64, 8, 128, 32, 32768, 100)   # not a multiple of 32
+        native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 100)   # not a multiple of 32
+    with pytest.raises(ValueError):
+        native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 8192)  # above 256 tiles
+    with pytest.raises(native.PagedKVError):
+        native.plan(2, 4, 4, 96, 16, 10, 100, f16)                          # head_dim 96
 
 
 def _decode(lib, **over):
