@@ -293,3 +293,19 @@ def test_decode_many_sequences_longest_first(dtype, hq, hkv, partition):
     dt = {torch.float16: 1, torch.bfloat16: 2}[dtype]
     assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), dt, partition)[3]
     _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), partition=partition)
+
+
+def test_decode_batch_above_fused_order_limit():
+    """More than 1024 sequences: the longest-first order comes from the
+    separate order kernel through the workspace."""
+    say("decode order kernel")
+    num_seqs, hq, hkv, hd, bs = 1500, 2, 2, 64, 16
+    rng = np.random.default_rng(1200)
+    lens = rng.integers(1, 97, num_seqs)
+    q, ks, vs, nblk = pins.random_case(rng, num_seqs, hq, hkv, hd, lens, bs, extra_blocks=3)
+    kp, vp, tables, L, _ = pins.page(ks, vs, bs, nblk, rng)
+    from paged_kv_cache_389_amd import plan, workspace_bytes
+    assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1)[3]
+    assert workspace_bytes(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1) >= \
+        4 * num_seqs
+    _check_decode(q, kp, vp, tables, L, hkv, torch.float16, 0.125)
