@@ -109,9 +109,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
   const int part = blockIdx.x, g = blockIdx.y;
   __shared__ OrderScratch sm_order;
-  const int s = a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs, a.len_cap,
-                                                    blockIdx.z, sm_order)
-                                  : sequence_of(a, blockIdx.z);
+  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
+                                                            a.len_cap, blockIdx.z, sm_order)
+                                          : sequence_of(a, blockIdx.z));
   const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
   const int n = lane & 15, g4 = lane >> 4;
   const int G = a.group;
@@ -121,13 +121,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
   // independent loads first: the length, the query group, this wave's table entries
   int L = a.context_lens[s];
-  u32x4 qb[KSTEPS];   // Q^T in the B layout: head n, dims 32*kk + 8*g4 .. +8 (zero past G)
-  {
+  // Q^T in the B layout: lane (n, g4) holds head n, dims 32*kk + 8*g4 .. +8
+  // (zero past G).  Wave 0 loads it; it is kept in LDS, indexed by lane, and
+  // every wave reads its lane's 16 bytes per step (saves 16 VGPRs a wave)
+  __shared__ u32x4 sm_q[KSTEPS][kWave];
+  u32x4 qload[KSTEPS];
+  if (wave == 0) {
     const int hn = n < G ? n : G - 1;
     const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
-      qb[kk] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+      qload[kk] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
   }
   int tbl;
   {
@@ -143,14 +147,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     return;
   }
   if (tok_begin >= L) return;
+  if (wave == 0) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) sm_q[kk][lane] = qload[kk];
+  }
+  __syncthreads();
   const int tok_end = min(L, tok_begin + P);
   const int nparts = (L + P - 1) / P;
   const int n_units = (tok_end + 15) / 16 - unit_begin;   // <= 4 * 64
   const int mine = n_units > wave ? (n_units - wave + NW - 1) / NW : 0;
 
-  const size_t block_stride = (size_t)a.num_kv_heads * BS * HD;
-  const T* kbase = static_cast<const T*>(a.k_cache) + (size_t)g * BS * HD + n * HD + g4 * 8;
-  const T* vbase = static_cast<const T*>(a.v_cache) + (size_t)g * BS * HD + (4 * g4) * HD + n * DPL;
+  // tile addresses: a buffer descriptor over the 16-token tile, built in
+  // scalar registers, plus a constant 32-bit per-lane byte offset, so no
+  // per-tile address arithmetic runs on the vector ALU
+  const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
+  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
+  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
+  const uint32_t koff = (uint32_t)((n * HD + g4 * 8) * sizeof(T));
+  const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
 
   f32x4 acc[DPL];
 #pragma unroll
@@ -168,18 +182,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
       bad = 1;
       phys = 0;
     }
-    const size_t toff = (size_t)phys * block_stride + (size_t)(u % TPB) * 16 * HD;
+    const size_t toff = (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * HD * sizeof(T);
+    constexpr uint32_t kTileBytes = 16 * HD * sizeof(T);
+    const rsrc_t kt = make_rsrc(kbase + toff, kTileBytes);
+    const rsrc_t vt = make_rsrc(vbase + toff, kTileBytes);
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = ld16(kbase + toff + kk * 32);
+    for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const T* vp = vbase + toff + r * HD;
       if constexpr (VW == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
         vv[r][0] = x[0];
         vv[r][1] = x[1];
       } else {
-        const u32x4 x = ld16(vp);
+        const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
         vv[r][0] = x[0];
         vv[r][1] = x[1];
         vv[r][2] = x[2];
@@ -190,6 +206,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
   auto compute_tile = [&](int i, const u32x4* ka, uint32_t (*vv)[VW]) {
     const int u = unit_begin + wave + NW * i;
+    // read Q^T from LDS for this tile; the compiler barrier keeps the reads
+    // from being hoisted out of the loop (which would pin Q in registers)
+    __asm__ volatile("" ::: "memory");
+    u32x4 qb[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm_q[kk][lane];
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
@@ -209,9 +231,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
       }
     }
-    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     const float mn = fmaxf(m, mb);
     const float mu = (mn == -INFINITY) ? 0.f : mn;
     const float corr = fast_exp2(m - mu);
@@ -266,8 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   }
 
   // the four token groups of a head column hold partial sums of l
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = rows_sum(l);
 
   // merge the 4 waves in LDS
   __shared__ float sm_m[NW][GMAX], sm_l[NW][GMAX];

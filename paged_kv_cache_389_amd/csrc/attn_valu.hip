@@ -60,9 +60,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
   const int part = blockIdx.x, h = blockIdx.y;
   __shared__ OrderScratch sm_order;
-  const int s = a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs, a.len_cap,
-                                                    blockIdx.z, sm_order)
-                                  : sequence_of(a, blockIdx.z);
+  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
+                                                            a.len_cap, blockIdx.z, sm_order)
+                                          : sequence_of(a, blockIdx.z));
   const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
   const int row = lane / LPR, col = lane % LPR;
   const int P = a.part_tokens;
@@ -93,9 +93,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int n_units = (tok_end + UT - 1) / UT - unit_begin;   // <= 4 * 64
   const int mine = n_units > wave ? (n_units - wave + NW - 1) / NW : 0;
 
-  const T* kbase = static_cast<const T*>(a.k_cache) + (size_t)g * BS * HD + row * HD + col * VEC;
-  const T* vbase = static_cast<const T*>(a.v_cache) + (size_t)g * BS * HD + row * HD + col * VEC;
-  const size_t block_stride = (size_t)a.num_kv_heads * BS * HD;
+  // unit addresses: a buffer descriptor over the unit's tile rows, built in
+  // scalar registers, plus a constant 32-bit per-lane byte offset, so no
+  // per-unit address arithmetic runs on the vector ALU
+  const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
+  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
+  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
+  const uint32_t loff = (uint32_t)((row * HD + col * VEC) * sizeof(T));
 
   float m = -INFINITY, l = 0.f, o[VEC];
 #pragma unroll
@@ -110,11 +114,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       bad = 1;
       phys = 0;
     }
-    const size_t off = (size_t)phys * block_stride + (size_t)(u % UPB) * UT * HD;
+    const size_t off = (size_t)phys * block_bytes + (size_t)(u % UPB) * UT * HD * sizeof(T);
+    constexpr uint32_t kUnitBytes = UT * HD * sizeof(T);
+    const rsrc_t kt = make_rsrc(kbase + off, kUnitBytes);
+    const rsrc_t vt = make_rsrc(vbase + off, kUnitBytes);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) kr[c] = ld16(kbase + off + c * RPI * HD);
+    for (int c = 0; c < CH; ++c) kr[c] = bld16(kt, loff, c * RPI * HD * sizeof(T));
 #pragma unroll
-    for (int c = 0; c < CH; ++c) vr[c] = ld16(vbase + off + c * RPI * HD);
+    for (int c = 0; c < CH; ++c) vr[c] = bld16(vt, loff, c * RPI * HD * sizeof(T));
   };
 
   // fold the wave's i-th unit into the online state

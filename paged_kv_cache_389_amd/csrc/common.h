@@ -130,17 +130,57 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
+// Row-pair exchanges of gfx950 (v_permlane16_swap / v_permlane32_swap with
+// the same register as both operands).  swap16 returns, in every lane, the
+// value of its own 16-lane row and of the partner row (rows 0<->1, 2<->3);
+// swap32 the same for the two 32-lane halves.  op(first, second) therefore
+// combines each lane with lane ^ 16 (resp. lane ^ 32), with the operands in
+// the same order in both partners, so both get bit-identical results.
+struct Pair {
+  float lo, hi;
+};
+__device__ inline Pair swap16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ inline Pair swap32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Max / sum over the four 16-lane rows (lanes with equal lane % 16).
+__device__ inline float rows_max(float v) {
+  Pair p = swap16(v);
+  v = fmaxf(p.lo, p.hi);
+  p = swap32(v);
+  return fmaxf(p.lo, p.hi);
+}
+__device__ inline float rows_sum(float v) {
+  Pair p = swap16(v);
+  v = p.lo + p.hi;
+  p = swap32(v);
+  return p.lo + p.hi;
+}
+
 // Sum over aligned groups of N lanes (N a power of two, 1..64); every lane
 // of a group receives the group's sum.  Steps inside a 16-lane row use DPP;
-// the 32- and 64-lane steps use cross-row shuffles.
+// the 32- and 64-lane steps use the row-pair exchanges.
 template <int N>
 __device__ inline float group_sum(float v) {
   if constexpr (N >= 2) v += dpp<kDppXor1>(v);
   if constexpr (N >= 4) v += dpp<kDppXor2>(v);
   if constexpr (N >= 8) v += dpp<kDppRowHalfMirror>(v);   // quads uniform: mirror == xor 4
   if constexpr (N >= 16) v += dpp<kDppRowMirror>(v);      // halves uniform: mirror == xor 8
-  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
+  if constexpr (N >= 32) {
+    const Pair p = swap16(v);
+    v = p.lo + p.hi;
+  }
+  if constexpr (N >= 64) {
+    const Pair p = swap32(v);
+    v = p.lo + p.hi;
+  }
   return v;
 }
 
@@ -156,6 +196,21 @@ __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// Raw buffer descriptor over `bytes` bytes at a wave-uniform base (four
+// scalar registers; word 3 is the GFX9-family raw-buffer format).  Loads
+// through it take one VGPR of per-lane byte offset, do their address
+// arithmetic in scalar registers, and return zero past `bytes`.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4 bld16(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, const_off, 0));
+}
+__device__ inline u32x2 bld8(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, const_off, 0));
 }
 
 // Value of a wave-uniform lane's register (v_readlane with an SGPR index).
