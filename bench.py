@@ -201,9 +201,11 @@ def bench_one(name, args, with_cpu):
         "data": "synthetic (seeded N(0,1) values, random block placement)",
         "config": {"workload": name, **WORKLOAD_DESC[name], "seed": wl.seed,
                    "placement": args.placement,
-                   "partition_tokens": plan[0], "max_parts": plan[1],
                    "path": ["auto", "valu", "mfma", "contiguous"][args.path],
-                   "kernel": ["auto", "valu", "mfma"][plan[2]], "longest_first": plan[3]},
+                   "kernel": ["auto", "valu", "mfma"][plan["path"]],
+                   "grid": ["partitions", "balanced"][plan["grid"]],
+                   "partition_tokens": plan["partition_tokens"], "max_parts": plan["max_parts"],
+                   "ranges": plan["ranges"], "longest_first": bool(plan["longest_first"])},
         "queries_per_s": round(wl.num_seqs / (ms_per_step / 1e3), 1),
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 5),

@@ -88,43 +88,67 @@ const char* pkv_last_error(void);
  * head_dim in {64, 128, 256}; block_size in {8, 16, 32}. */
 int pkv_supported(pkv_dtype dtype, int head_dim, int block_size);
 
+/* How a decode call divides its work (pkv_plan.grid). */
+typedef enum {
+  PKV_GRID_PARTITIONS = 0, /* one workgroup per (partition, head, sequence) */
+  PKV_GRID_BALANCED = 1    /* one workgroup per resident slot, equal shares of all tiles */
+} pkv_grid;
+
+/* The plan of a decode call (filled by pkv_paged_attention_plan). */
+typedef struct {
+  int path;              /* PKV_PATH_VALU or PKV_PATH_MFMA */
+  int grid;              /* pkv_grid */
+  int partition_tokens;  /* partitions grid: tokens per partition (0 for balanced) */
+  int max_parts;         /* partitions grid: partitions per sequence (0 for balanced) */
+  int ranges;            /* balanced grid: waves, one range of tiles each (0 for partitions) */
+  int longest_first;     /* partitions grid: 1 if sequences are visited longest first */
+  size_t workspace_bytes;
+} pkv_plan;
+
 /*
- * How a decode call with these sizes would run: the kernel variant and the
- * partition size.  Long contexts are cut into partitions of
- * `partition_tokens` tokens; each partition's partial softmax state (running
- * max, running sum and unnormalised output, all fp32) goes to the workspace
- * and a second kernel merges them.  With partition_tokens == 0 the library
- * chooses: one partition per sequence unless the (sequence, head) units of
- * work are too few to give every compute unit about four workgroups, and
- * never partitions shorter than 512 tokens.  An explicit partition_tokens
- * must be a multiple of 32 and of block_size and at most 256 units of the
- * chosen kernel (4096 tokens for 16-bit types with head_dim 128).
- * `path` is a pkv_decode_path.
+ * How a decode call with these sizes would run.
  *
- * When the grid holds more than about two rounds of resident workgroups, a
- * small kernel first orders the sequences longest first (stable within
- * half-octave length bins) and the decode grid visits them in that order,
- * so long sequences do not start last and finish alone.  The order only
- * changes when each sequence is computed, never its result.
+ * Kernel: grouped query heads (2 <= Hq/Hkv <= 16, fp16/bf16, head_dim 64 or
+ * 128, block_size 16 or 32) run on the MFMA kernel, which reads each KV tile
+ * once for the whole group; everything else on the vector-ALU kernel.
  *
- * Writes the chosen partition size, the number of partitions the grid
- * covers per sequence, the kernel variant (PKV_PATH_VALU or PKV_PATH_MFMA)
- * and whether the longest-first order is used (0/1) to the non-NULL out
- * pointers.  Returns PKV_OK or the status pkv_paged_attention_decode_ex
- * would return for these sizes.  Host only.
+ * Grid PARTITIONS (the default): contexts are cut into partitions of partition_tokens
+ * tokens (0: one partition per sequence unless the (sequence, head) units
+ * are too few to give every compute unit about four workgroups, never
+ * shorter than 512 tokens), one workgroup each, merged by the same second
+ * kernel when a context has several.  An explicit partition_tokens must be a
+ * multiple of 32 and of block_size and at most 256 units of the kernel (4096
+ * tokens for 16-bit types with head_dim 128).  When the grid holds more than
+ * about two rounds of resident workgroups, sequences are visited longest
+ * first (stable within half-octave length bins), computed inside the
+ * kernel for up to 1024 sequences and by a small order kernel beyond.
+ *
+ * Grid BALANCED, on request (partition_tokens == -1, at most 1024
+ * sequences): the tiles (16 tokens for MFMA, 4-32 for VALU) of every
+ * (sequence, head) pair are laid end to end, sequence major, and cut into
+ * equal ranges, one per wave the device holds at once; each wave walks its
+ * range alone (no barrier, no LDS merge), so all waves start together and
+ * finish together whatever the length mix.  A pair cut by a range boundary
+ * leaves partial softmax states (running max, running sum, unnormalised
+ * output, fp32) in the workspace, and a second kernel merges them; it also
+ * writes the zero rows of empty sequences.
+ *
+ * The plan only changes the order of floating-point operations inside one
+ * output row, never which tokens contribute.  Writes the plan to *out (if
+ * not NULL).  Returns PKV_OK or the status pkv_paged_attention_decode_ex
+ * would return for these sizes.  Host only; queries the current device's
+ * compute-unit count and kernel occupancy (once, then cached).
  */
 int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_blocks_per_seq, int max_context_len,
-                             pkv_dtype dtype, int partition_tokens, int path,
-                             int* out_partition_tokens, int* out_max_parts, int* out_path,
-                             int* out_sorted);
+                             pkv_dtype dtype, int partition_tokens, int path, pkv_plan* out);
 
 /*
- * Workspace bytes pkv_paged_attention_decode(_ex) needs for these sizes:
- * num_seqs * num_q_heads * max_parts * (head_dim + 2) * 4 when the plan has
- * several partitions, plus num_seqs * 4 when it uses the longest-first
- * order; 0 when it needs neither.  Returns (size_t)-1 for invalid sizes.
- * Host only.
+ * Workspace bytes pkv_paged_attention_decode(_ex) needs for these sizes (the
+ * plan's workspace_bytes): the partial states (head_dim + 2 fp32 each) of
+ * the plan's grid and its small integer arrays, each part rounded to 16
+ * bytes; 0 for a partitions grid with one partition per sequence and no
+ * order kernel.  Returns (size_t)-1 for invalid sizes.  Host only.
  */
 size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                            int head_dim, int block_size, int max_blocks_per_seq,

@@ -23,6 +23,17 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
 
+GRID_PARTITIONS, GRID_BALANCED = 0, 1
+
+
+class _Plan(ctypes.Structure):
+    """Mirror of ``pkv_plan`` in include/pagedkv.h."""
+    _fields_ = [("path", ctypes.c_int), ("grid", ctypes.c_int),
+                ("partition_tokens", ctypes.c_int), ("max_parts", ctypes.c_int),
+                ("ranges", ctypes.c_int), ("longest_first", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 class NativeLibraryMissing(ImportError):
     pass
 
@@ -52,9 +63,8 @@ def _load():
     lib.pkv_supported.argtypes = [i32, i32, i32]
     lib.pkv_paged_attention_workspace_bytes.restype = sz
     lib.pkv_paged_attention_workspace_bytes.argtypes = [i32] * 10
-    ip = ctypes.POINTER(ctypes.c_int)
     lib.pkv_paged_attention_plan.restype = i32
-    lib.pkv_paged_attention_plan.argtypes = [i32] * 10 + [ip, ip, ip, ip]
+    lib.pkv_paged_attention_plan.argtypes = [i32] * 10 + [ctypes.POINTER(_Plan)]
     lib.pkv_paged_attention_decode.restype = i32
     lib.pkv_paged_attention_decode.argtypes = [
         vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
@@ -118,15 +128,15 @@ def _dtype_code(dtype):
 
 def plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
          max_context_len, dtype, partition_tokens=0, path=PATH_AUTO):
-    """(partition_tokens, max_parts, path, sorted) a decode call with these
-    sizes would use (see ``pkv_paged_attention_plan``)."""
-    pt, mp, pa, so = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    """The plan of a decode call with these sizes, as a dict with the fields
+    of ``pkv_plan``: path, grid, partition_tokens, max_parts, ranges,
+    longest_first, workspace_bytes (see ``pkv_paged_attention_plan``)."""
+    out = _Plan()
     st = lib.pkv_paged_attention_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                       max_blocks_per_seq, max_context_len, _dtype_code(dtype),
-                                      partition_tokens, path, ctypes.byref(pt), ctypes.byref(mp),
-                                      ctypes.byref(pa), ctypes.byref(so))
+                                      partition_tokens, path, ctypes.byref(out))
     _check("paged_attention_plan", st)
-    return pt.value, mp.value, pa.value, bool(so.value)
+    return {name: getattr(out, name) for name, _ in _Plan._fields_}
 
 
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

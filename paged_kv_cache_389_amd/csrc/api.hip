@@ -20,6 +20,7 @@ constexpr int kMinAutoPartition = 512;  // the library never splits finer than t
 constexpr int kWgPerCu = 4;             // split until about this many workgroups per CU
 constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxDevices = 64;
+constexpr int kBalancedRequest = -1;    // partition_tokens value that asks for the balanced grid
 
 int elem_size(pkv_dtype d) { return d == PKV_F32 ? 4 : 2; }
 bool dtype_ok(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
@@ -47,16 +48,40 @@ int compute_units() {
   return n;
 }
 
-// The kernel a decode call runs and how it cuts contexts into partitions.
+// The kernel a decode call runs and how its grid divides the work.
 struct Plan {
   bool mfma = false;
-  int part_tokens = 0;   // tokens per partition
-  int max_parts = 0;     // partitions the grid covers per sequence
+  int grid_mode = kGridPartitions;
+  int part_tokens = 0;   // partitions grid: tokens per partition
+  int max_parts = 1;     // partitions grid: partitions the grid covers per sequence
+  int ranges = 0;        // balanced grid: waves (4 per workgroup), one range each
+  int unit_group = 1;    // balanced grid: query heads per work unit
   int len_cap = 0;       // context lengths are clamped to this
-  bool sort = false;     // visit sequences longest first
+  bool sort = false;     // partitions grid: visit sequences longest first
   bool sort_kernel = false;  // ... through the order kernel (large batches)
   int status = PKV_OK;
 };
+
+// Workgroups of the balanced kernel resident on the whole device (cached
+// per device and kernel; a fallback when the runtime cannot say).
+int resident_workgroups(bool mfma, Elem e, int head_dim, int block_size, int group) {
+  constexpr int kKeys = 2 * 3 * 3 * 3 * 3;   // kernel x dtype x head_dim x block_size x GMAX
+  static int cached[kMaxDevices][kKeys];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  const int gmax = group <= 4 ? 0 : (group <= 8 ? 1 : 2);
+  const int hdk = head_dim == 64 ? 0 : (head_dim == 128 ? 1 : 2);
+  const int bsk = block_size == 8 ? 0 : (block_size == 16 ? 1 : 2);
+  const int key = (((((mfma ? 1 : 0) * 3 + (int)e) * 3 + hdk) * 3 + bsk) * 3 + gmax);
+  int per_cu = dev >= 0 ? __atomic_load_n(&cached[dev][key], __ATOMIC_RELAXED) : 0;
+  if (per_cu <= 0) {
+    per_cu = mfma ? decode_mfma_occupancy(e, head_dim, block_size, group)
+                  : decode_valu_occupancy(e, head_dim, block_size);
+    if (per_cu <= 0) per_cu = mfma ? 3 : 4;
+    if (dev >= 0) __atomic_store_n(&cached[dev][key], per_cu, __ATOMIC_RELAXED);
+  }
+  return per_cu * compute_units();
+}
 
 Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                int max_blocks_per_seq, int max_context_len, pkv_dtype dtype, int requested,
@@ -77,9 +102,33 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
 
   const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
   pl.len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
+  const int unit = pl.mfma ? 16 : valu_unit_tokens(e, head_dim, block_size);
+  const int units_per_seq = pl.mfma ? num_kv_heads : num_q_heads;
+
+  // Balanced grid on request (partition_tokens == -1): equal shares of all
+  // tiles, one workgroup per resident slot, so every workgroup starts at
+  // once and ends at about the same time whatever the length mix.  It needs
+  // the tile prefix of the batch in LDS (at most kBalancedMaxSeqs
+  // sequences, an int total).
+  const int64_t seq_tiles = (pl.len_cap + unit - 1) / unit;
+  if (requested == kBalancedRequest) {
+    if (num_seqs > kBalancedMaxSeqs || (int64_t)num_seqs * seq_tiles >= (1ll << 31) - 1) {
+      pl.status = PKV_EUNSUPPORTED;
+      return pl;
+    }
+    pl.grid_mode = kGridBalanced;
+    pl.unit_group = pl.mfma ? group : 1;
+    // one range per resident wave, at most one per 4 tiles of the largest
+    // possible batch, a multiple of 32 (8 XCDs x 4 waves)
+    const int64_t waves = 4 * (int64_t)resident_workgroups(pl.mfma, e, head_dim, block_size, group);
+    const int64_t tiles_upper = (int64_t)num_seqs * units_per_seq * seq_tiles;
+    int64_t r = waves < tiles_upper / 4 ? waves : tiles_upper / 4;
+    r = r / 32 * 32;
+    pl.ranges = (int)(r < 32 ? 32 : r);
+    return pl;
+  }
 
   // a wave handles at most 64 units of a partition
-  const int unit = pl.mfma ? 16 : valu_unit_tokens(e, head_dim, block_size);
   const int p_max = 256 * unit / kPartAlign * kPartAlign;
   int p;
   if (requested > 0) {
@@ -91,7 +140,7 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
   } else {
     // one partition per (sequence, head) unit unless those units are too
     // few to give every compute unit several workgroups
-    const int64_t units = (int64_t)num_seqs * (pl.mfma ? num_kv_heads : num_q_heads);
+    const int64_t units = (int64_t)num_seqs * units_per_seq;
     const int64_t target = (int64_t)kWgPerCu * compute_units();
     const int64_t parts = units >= target ? 1 : (target + units - 1) / units;
     const int len = pl.len_cap > 0 ? pl.len_cap : 1;
@@ -104,24 +153,46 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
   // Longest first pays off once the grid is more than about two rounds of
   // resident workgroups (the VALU kernel keeps 4 per compute unit, the MFMA
   // kernel 3); with fewer, nearly every workgroup starts at once anyway.
-  const int64_t wgs = (int64_t)pl.max_parts * (pl.mfma ? num_kv_heads : num_q_heads) * num_seqs;
+  const int64_t wgs = (int64_t)pl.max_parts * units_per_seq * num_seqs;
   const int64_t resident = (int64_t)(pl.mfma ? 3 : 4) * compute_units();
   pl.sort = num_seqs > 1 && wgs > 2 * resident;
   pl.sort_kernel = pl.sort && num_seqs > kFusedOrderMax;
   return pl;
 }
 
-// Workspace layout: partial outputs [B][Hq][max_parts][HD] fp32, then
-// partial (max, sum) [B][Hq][max_parts][2] fp32 (both only with several
-// partitions), then the sequence order [B] int32 (only when sorting).
-size_t partials_bytes(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
-  if (max_parts <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * max_parts * (size_t)(head_dim + 2) * sizeof(float);
+// Workspace layout, each part 16-byte aligned:
+//  partitions grid: partial outputs [B][Hq][max_parts][HD] fp32 and partial
+//    (max, sum) [B][Hq][max_parts][2] fp32 (only with several partitions),
+//    then the sequence order [B] int32 (only with the order kernel);
+//  balanced grid: partial outputs [2*ranges][unit_group][HD] fp32, partial
+//    (max, sum) [2*ranges][unit_group][2] fp32, the tile prefix [B+1] int32.
+struct Layout {
+  size_t part_o = 0, part_ml = 0, extra = 0, total = 0;   // byte offsets, size
+};
+
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+Layout workspace_layout(int num_seqs, int num_q_heads, int head_dim, const Plan& pl) {
+  Layout lo;
+  size_t states = 0;
+  if (pl.grid_mode == kGridBalanced)
+    states = (size_t)2 * pl.ranges * pl.unit_group;
+  else if (pl.max_parts > 1)
+    states = (size_t)num_seqs * num_q_heads * pl.max_parts;
+  lo.part_o = 0;
+  lo.part_ml = align16(states * head_dim * sizeof(float));
+  lo.extra = lo.part_ml + align16(states * 2 * sizeof(float));
+  size_t extra_bytes = 0;
+  if (pl.grid_mode == kGridBalanced)
+    extra_bytes = (size_t)(num_seqs + 1) * sizeof(int32_t);
+  else if (pl.sort_kernel)
+    extra_bytes = (size_t)num_seqs * sizeof(int32_t);
+  lo.total = extra_bytes ? lo.extra + align16(extra_bytes) : (states ? lo.extra : 0);
+  return lo;
 }
 
 size_t workspace_for(int num_seqs, int num_q_heads, int head_dim, const Plan& pl) {
-  return partials_bytes(num_seqs, num_q_heads, head_dim, pl.max_parts) +
-         (pl.sort_kernel ? (size_t)num_seqs * sizeof(int32_t) : 0);
+  return workspace_layout(num_seqs, num_q_heads, head_dim, pl).total;
 }
 
 }  // namespace
@@ -154,7 +225,7 @@ size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int nu
                                            int partition_tokens, int path) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      partition_tokens < kBalancedRequest || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
       num_q_heads % num_kv_heads)
     return (size_t)-1;
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -165,21 +236,24 @@ size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int nu
 
 int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_blocks_per_seq, int max_context_len,
-                             pkv_dtype dtype, int partition_tokens, int path,
-                             int* out_partition_tokens, int* out_max_parts, int* out_path,
-                             int* out_sorted) {
+                             pkv_dtype dtype, int partition_tokens, int path, pkv_plan* out) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      partition_tokens < kBalancedRequest || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
       num_q_heads % num_kv_heads)
     return PKV_EINVAL;
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                             max_blocks_per_seq, max_context_len, dtype, partition_tokens, path);
   if (pl.status != PKV_OK) return pl.status;
-  if (out_partition_tokens) *out_partition_tokens = pl.part_tokens;
-  if (out_max_parts) *out_max_parts = pl.max_parts;
-  if (out_path) *out_path = pl.mfma ? PKV_PATH_MFMA : PKV_PATH_VALU;
-  if (out_sorted) *out_sorted = pl.sort ? 1 : 0;
+  if (out) {
+    out->path = pl.mfma ? PKV_PATH_MFMA : PKV_PATH_VALU;
+    out->grid = pl.grid_mode == kGridBalanced ? PKV_GRID_BALANCED : PKV_GRID_PARTITIONS;
+    out->partition_tokens = pl.grid_mode == kGridBalanced ? 0 : pl.part_tokens;
+    out->max_parts = pl.grid_mode == kGridBalanced ? 0 : pl.max_parts;
+    out->ranges = pl.ranges;
+    out->longest_first = pl.sort ? 1 : 0;
+    out->workspace_bytes = workspace_for(num_seqs, num_q_heads, head_dim, pl);
+  }
   return PKV_OK;
 }
 
@@ -193,7 +267,8 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                                   void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0 || partition < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS)
+      max_context_len < 0 || partition < kBalancedRequest || path < PKV_PATH_AUTO ||
+      path > PKV_PATH_CONTIGUOUS)
     return PKV_EINVAL;
   if (num_q_heads % num_kv_heads) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
@@ -208,8 +283,8 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                             max_blocks_per_seq, max_context_len, dtype, partition, path);
   if (pl.status != PKV_OK) return pl.status;
-  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, pl);
-  const size_t partials = partials_bytes(num_seqs, num_q_heads, head_dim, pl.max_parts);
+  const Layout lo = workspace_layout(num_seqs, num_q_heads, head_dim, pl);
+  const size_t need = lo.total;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
   const bool use_mfma = pl.mfma;
@@ -221,14 +296,15 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.part_o = partials ? static_cast<float*>(workspace) : nullptr;
-  a.part_ml = partials ? static_cast<float*>(workspace) +
-                             (size_t)num_seqs * num_q_heads * pl.max_parts * head_dim
-                       : nullptr;
-  a.seq_order = pl.sort_kernel
-                    ? reinterpret_cast<const int32_t*>(static_cast<char*>(workspace) + partials)
-                    : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = need ? reinterpret_cast<float*>(ws + lo.part_o) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float*>(ws + lo.part_ml) : nullptr;
+  a.seq_order = pl.sort_kernel ? reinterpret_cast<const int32_t*>(ws + lo.extra) : nullptr;
+  a.tile_start = pl.grid_mode == kGridBalanced ? reinterpret_cast<int32_t*>(ws + lo.extra) : nullptr;
   a.order_mode = pl.sort_kernel ? 1 : (pl.sort ? 2 : 0);
+  a.grid_mode = pl.grid_mode;
+  a.ranges = pl.ranges;
+  a.unit_group = pl.unit_group;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -251,7 +327,7 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   err = use_mfma ? launch_decode_mfma(e, head_dim, block_size, a, st)
                  : launch_decode_valu(e, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
-  if (pl.max_parts > 1) {
+  if (pl.grid_mode == kGridBalanced || pl.max_parts > 1) {
     err = launch_decode_reduce(e, head_dim, a, st);
     if (err != hipSuccess) return fail_hip(err);
   }

@@ -39,6 +39,7 @@
 #include "common.h"
 #include "decode.h"
 #include "order.h"
+#include "balance.h"
 
 namespace pkv {
 
@@ -95,67 +96,60 @@ __device__ inline uint32_t pair_of(int e, const uint32_t* x, const uint32_t* y) 
   return __builtin_amdgcn_perm(y[e >> 1], x[e >> 1], sel);
 }
 
-template <typename E, int HD, int BS, int GMAX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(DecodeArgs a) {
+// LDS of one workgroup: Q^T (B layout, indexed by lane) and the four
+// waves' softmax states for up to GMAX heads.
+template <int HD, int GMAX>
+struct MfmaShared {
+  static constexpr int OS = HD + 4;   // padded row stride of the output tiles
+  u32x4 q[HD / 32][kWave];
+  float m[4][GMAX], l[4][GMAX];
+  __attribute__((aligned(16))) float o[4][GMAX][OS];
+  int bad[4];
+};
+
+// One wave's state for the 16 head columns: acc[e] holds O^T rows
+// (4*g4 + r)*DPL + e (r < 4) of head column n = lane % 16; m and l are the
+// column's running max (log2 units) and, per token group g4, partial sum.
+template <int DPL>
+struct MfmaState {
+  f32x4 acc[DPL];
+  float m, l;
+  int bad;
+};
+
+// Write Q^T of the G query heads of KV head g of sequence s into q (B
+// layout: lane (n, g4) holds head n, dims 32*kk + 8*g4 .. +8; zero past G).
+template <typename E, int HD>
+__device__ inline void mfma_load_q(const DecodeArgs& a, int s, int g, u32x4 (*q)[kWave]) {
+  using T = typename E::storage;
+  const int lane = threadIdx.x % kWave, n = lane & 15, g4 = lane >> 4;
+  const int G = a.group;
+  const int hn = n < G ? n : G - 1;
+  const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
+#pragma unroll
+  for (int kk = 0; kk < HD / 32; ++kk)
+    q[kk][lane] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+}
+
+// Fold tiles ta + first, ta + first + stride, ... (< tb) of KV head g of
+// sequence s (context length L > 0; tile = 16 tokens) into the calling
+// wave's state, with Q^T read from q (LDS).
+template <typename E, int HD, int BS>
+__device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
+                                       int first, int stride, const u32x4 (*q)[kWave],
+                                       MfmaState<HD / 16>& st) {
   using T = typename E::storage;
   using Ops = MfmaOps<E>;
-  constexpr int NW = 4;
   constexpr int KSTEPS = HD / 32;      // QK MFMAs per tile
   constexpr int DPL = HD / 16;         // V dims per lane per token == PV MFMAs per tile
   constexpr int VW = DPL / 2;          // dwords of V per lane per token
   constexpr int TPB = BS / 16;         // tiles per block
-  constexpr int OS = HD + 4;           // padded row stride of the LDS output tiles
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
 
-  const int part = blockIdx.x, g = blockIdx.y;
-  __shared__ OrderScratch sm_order;
-  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
-                                                            a.len_cap, blockIdx.z, sm_order)
-                                          : sequence_of(a, blockIdx.z));
-  const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
+  const int lane = threadIdx.x % kWave;
   const int n = lane & 15, g4 = lane >> 4;
-  const int G = a.group;
-  const int P = a.part_tokens;
-  const int tok_begin = part * P;
-  const int unit_begin = tok_begin / 16;
-
-  // independent loads first: the length, the query group, this wave's table entries
-  int L = a.context_lens[s];
-  // Q^T in the B layout: lane (n, g4) holds head n, dims 32*kk + 8*g4 .. +8
-  // (zero past G).  Wave 0 loads it; it is kept in LDS, indexed by lane, and
-  // every wave reads its lane's 16 bytes per step (saves 16 VGPRs a wave)
-  __shared__ u32x4 sm_q[KSTEPS][kWave];
-  u32x4 qload[KSTEPS];
-  if (wave == 0) {
-    const int hn = n < G ? n : G - 1;
-    const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      qload[kk] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
-  }
-  int tbl;
-  {
-    const int blk = min((unit_begin + wave + NW * lane) / TPB, a.max_blocks - 1);
-    tbl = a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
-  }
-
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G) * HD;
-  if (L == 0) {
-    if (part == 0)
-      for (int i = tid; i < G * HD; i += 256) out[i] = E::round(0.f);
-    return;
-  }
-  if (tok_begin >= L) return;
-  if (wave == 0) {
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) sm_q[kk][lane] = qload[kk];
-  }
-  __syncthreads();
-  const int tok_end = min(L, tok_begin + P);
-  const int nparts = (L + P - 1) / P;
-  const int n_units = (tok_end + 15) / 16 - unit_begin;   // <= 4 * 64
-  const int mine = n_units > wave ? (n_units - wave + NW - 1) / NW : 0;
+  const int tok_end = L;
+  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
   // tile addresses: a buffer descriptor over the 16-token tile, built in
   // scalar registers, plus a constant 32-bit per-lane byte offset, so no
@@ -168,104 +162,112 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
   f32x4 acc[DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-  int bad = 0;
+  for (int e = 0; e < DPL; ++e) acc[e] = st.acc[e];
+  float m = st.m, l = st.l;
+  int bad = st.bad;
 
-  // issue the loads of the wave's i-th 16-token tile: K in the A layout
-  // (token row n, dims 32*kk + 8*g4 .. +8), V row-wise (tokens 4*g4 + r,
-  // dims n*DPL .. +DPL)
-  auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VW]) {
-    const int u = unit_begin + wave + NW * i;
-    int phys = lane_value(tbl, i);
-    if ((unsigned)phys >= (unsigned)a.num_blocks) {
-      bad = 1;
-      phys = 0;
+  // passes of at most 64 of the wave's tiles: their table entries fit one VGPR
+  for (int pass = ta + first; pass < tb; pass += kWave * stride) {
+    const int mine = min(kWave, (tb - pass + stride - 1) / stride);
+    int tbl;
+    {
+      const int blk = min((pass + stride * lane) / TPB, a.max_blocks - 1);
+      tbl = a.contiguous ? s * a.max_blocks + blk : table[blk];
     }
-    const size_t toff = (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * HD * sizeof(T);
-    constexpr uint32_t kTileBytes = 16 * HD * sizeof(T);
-    const rsrc_t kt = make_rsrc(kbase + toff, kTileBytes);
-    const rsrc_t vt = make_rsrc(vbase + toff, kTileBytes);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (VW == 2) {
-        const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
-        vv[r][0] = x[0];
-        vv[r][1] = x[1];
-      } else {
-        const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
-        vv[r][0] = x[0];
-        vv[r][1] = x[1];
-        vv[r][2] = x[2];
-        vv[r][3] = x[3];
+
+    // issue the loads of the wave's i-th tile of the pass: K in the A layout
+    // (token row n, dims 32*kk + 8*g4 .. +8), V row-wise (tokens 4*g4 + r,
+    // dims n*DPL .. +DPL)
+    auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VW]) {
+      const int u = pass + stride * i;
+      int phys = lane_value(tbl, i);
+      if ((unsigned)phys >= (unsigned)a.num_blocks) {
+        bad = 1;
+        phys = 0;
       }
-    }
-  };
-
-  auto compute_tile = [&](int i, const u32x4* ka, uint32_t (*vv)[VW]) {
-    const int u = unit_begin + wave + NW * i;
-    // read Q^T from LDS for this tile; the compiler barrier keeps the reads
-    // from being hoisted out of the loop (which would pin Q in registers)
-    __asm__ volatile("" ::: "memory");
-    u32x4 qb[KSTEPS];
+      const size_t toff = (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * HD * sizeof(T);
+      constexpr uint32_t kTileBytes = 16 * HD * sizeof(T);
+      const rsrc_t kt = make_rsrc(kbase + toff, kTileBytes);
+      const rsrc_t vt = make_rsrc(vbase + toff, kTileBytes);
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm_q[kk][lane];
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
-    float sc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
-    if (u * 16 + 16 > tok_end) {
-      // the partition's last tile: mask by index, and zero the value rows
-      // past the context so a non-finite value there cannot reach the product
-      const int t0 = u * 16 + 4 * g4;
+      for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (t0 + r >= tok_end) {
-          sc[r] = -INFINITY;
-#pragma unroll
-          for (int w = 0; w < VW; ++w) vv[r][w] = 0u;
+        if constexpr (VW == 2) {
+          const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
+          vv[r][0] = x[0];
+          vv[r][1] = x[1];
+        } else {
+          const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
+          vv[r][0] = x[0];
+          vv[r][1] = x[1];
+          vv[r][2] = x[2];
+          vv[r][3] = x[3];
         }
       }
-    }
-    const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const float mn = fmaxf(m, mb);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float corr = fast_exp2(m - mu);
-    m = mn;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);   // exp2(-inf) == 0
-    l = __builtin_fmaf(l, corr, (p[0] + p[1]) + (p[2] + p[3]));
-    if (__any(corr != 1.f)) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] *= corr;
-    }
+    };
 
-    // P^T in the B layout: tokens 4*g4 + r of head n
-    const u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
-    u32x2 pr = {0u, 0u};
-    if constexpr (Ops::kSplit) {
-      pr[0] = Ops::pack2(p[0] - Ops::widen_lo(pb[0]), p[1] - Ops::widen_hi(pb[0]));
-      pr[1] = Ops::pack2(p[2] - Ops::widen_lo(pb[1]), p[3] - Ops::widen_hi(pb[1]));
-    }
-    // V^T in the A layout, one MFMA per lane-dim e
+    auto compute_tile = [&](int i, const u32x4* ka, uint32_t (*vv)[VW]) {
+      const int u = pass + stride * i;
+      // read Q^T from LDS for this tile; the compiler barrier keeps the reads
+      // from being hoisted out of the loop (which would pin Q in registers)
+      __asm__ volatile("" ::: "memory");
+      u32x4 qb[KSTEPS];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const u32x2 va = {pair_of(e, vv[0], vv[1]), pair_of(e, vv[2], vv[3])};
-      acc[e] = Ops::pv(va, pb, acc[e]);
-      if constexpr (Ops::kSplit) acc[e] = Ops::pv(va, pr, acc[e]);
-    }
-  };
+      for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = q[kk][lane];
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
+      if (u * 16 + 16 > tok_end) {
+        // the sequence's last tile: mask by index, and zero the value rows
+        // past the context so a non-finite value there cannot reach the product
+        const int t0 = u * 16 + 4 * g4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (t0 + r >= tok_end) {
+            sc[r] = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < VW; ++w) vv[r][w] = 0u;
+          }
+        }
+      }
+      const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const float mn = fmaxf(m, mb);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float corr = fast_exp2(m - mu);
+      m = mn;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);   // exp2(-inf) == 0
+      l = __builtin_fmaf(l, corr, (p[0] + p[1]) + (p[2] + p[3]));
+      if (__any(corr != 1.f)) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] *= corr;
+      }
 
-  // two register buffers: the loads of tile i+1 are in flight while tile i
-  // is computed
-  u32x4 kA[KSTEPS], kB[KSTEPS];
-  uint32_t vA[4][VW], vB[4][VW];
-  if (mine > 0) {
+      // P^T in the B layout: tokens 4*g4 + r of head n
+      const u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
+      u32x2 pr = {0u, 0u};
+      if constexpr (Ops::kSplit) {
+        pr[0] = Ops::pack2(p[0] - Ops::widen_lo(pb[0]), p[1] - Ops::widen_hi(pb[0]));
+        pr[1] = Ops::pack2(p[2] - Ops::widen_lo(pb[1]), p[3] - Ops::widen_hi(pb[1]));
+      }
+      // V^T in the A layout, one MFMA per lane-dim e
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const u32x2 va = {pair_of(e, vv[0], vv[1]), pair_of(e, vv[2], vv[3])};
+        acc[e] = Ops::pv(va, pb, acc[e]);
+        if constexpr (Ops::kSplit) acc[e] = Ops::pv(va, pr, acc[e]);
+      }
+    };
+
+    // two register buffers: the loads of tile i+1 are in flight while tile i
+    // is computed
+    u32x4 kA[KSTEPS], kB[KSTEPS];
+    uint32_t vA[4][VW], vB[4][VW];
     load_tile(0, kA, vA);
     int i = 0;
     // steady state: the loads of the next tile are always issued, so the
@@ -284,65 +286,236 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
       compute_tile(i, kA, vA);
     }
   }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) st.acc[e] = acc[e];
+  st.m = m;
+  st.l = l;
+  st.bad = bad;
+}
+
+template <int DPL>
+__device__ inline void mfma_state_init(MfmaState<DPL>& st) {
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) st.acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.bad = 0;
+}
+
+// Attention of the G query heads of KV head g of sequence s (context length
+// L > 0) over its 16-token tiles [ta, tb), by the four waves of the
+// workgroup (tile round-robin), merged in LDS.  The merged states are
+// normalised and rounded into `out` (the group's first head) when `out` is
+// not null, else stored unnormalised to the partial states
+// state0 + hh * hh_stride (hh < G).
+template <typename E, int HD, int BS, int GMAX>
+__device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
+                                  typename E::storage* out, size_t state0, size_t hh_stride,
+                                  MfmaShared<HD, GMAX>& sm) {
+  constexpr int NW = 4;
+  constexpr int DPL = HD / 16;
+  const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int G = a.group;
+
+  if (wave == 0) mfma_load_q<E, HD>(a, s, g, sm.q);
+  MfmaState<DPL> st;
+  mfma_state_init(st);
+  __syncthreads();   // Q^T is in LDS
+  mfma_accumulate<E, HD, BS>(a, s, g, L, ta, tb, wave, NW, sm.q, st);
 
   // the four token groups of a head column hold partial sums of l
-  l = rows_sum(l);
+  const float l = rows_sum(st.l);
 
   // merge the 4 waves in LDS
-  __shared__ float sm_m[NW][GMAX], sm_l[NW][GMAX];
-  __shared__ __attribute__((aligned(16))) float sm_o[NW][GMAX][OS];
-  __shared__ int sm_bad[NW];
   if (n < G) {
     if (g4 == 0) {
-      sm_m[wave][n] = m;
-      sm_l[wave][n] = l;
+      sm.m[wave][n] = st.m;
+      sm.l[wave][n] = l;
     }
 #pragma unroll
     for (int e = 0; e < DPL; ++e)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[wave][n][(4 * g4 + r) * DPL + e] = acc[e][r];
+      for (int r = 0; r < 4; ++r) sm.o[wave][n][(4 * g4 + r) * DPL + e] = st.acc[e][r];
   }
-  const int any_bad = __any(bad);
-  if (lane == 0) sm_bad[wave] = any_bad;
+  const int any_bad = __any(st.bad);
+  if (lane == 0) sm.bad[wave] = any_bad;
   __syncthreads();
 
-  const int all_bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
+  const int all_bad = sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3];
   for (int idx = tid; idx < G * (HD / 4); idx += 256) {
     const int hh = idx / (HD / 4), d = (idx % (HD / 4)) * 4;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][hh]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ls = 0.f;
     f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float wt = fast_exp2(sm_m[w][hh] - M);   // M is finite: the partition has a token
-      Ls = __builtin_fmaf(wt, sm_l[w][hh], Ls);
-      O += wt * *reinterpret_cast<const f32x4*>(&sm_o[w][hh][d]);
+      const float wt = fast_exp2(sm.m[w][hh] - Mu);
+      Ls = __builtin_fmaf(wt, sm.l[w][hh], Ls);
+      O += wt * *reinterpret_cast<const f32x4*>(&sm.o[w][hh][d]);
     }
     if (all_bad) O = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    if (nparts == 1) {
+    if (out) {
       const float inv = 1.f / Ls;
       float r[4] = {O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
       store_rounded<E, 4>(out + hh * HD + d, r);
     } else {
-      const size_t pidx = ((size_t)s * a.num_q_heads + (size_t)g * G + hh) * a.max_parts + part;
-      *reinterpret_cast<f32x4*>(a.part_o + pidx * HD + d) = O;
-      if (d == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * pidx) = f32x2{M, Ls};
+      const size_t stt = state0 + hh * hh_stride;
+      *reinterpret_cast<f32x4*>(a.part_o + stt * HD + d) = O;
+      if (d == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * stt) = f32x2{M, Ls};
     }
+  }
+  __syncthreads();   // LDS is free for the next piece
+}
+
+// Partitions mode: grid (max_parts, Hkv, B); partition `part` of KV head g
+// of the sequence of grid row z.
+template <typename E, int HD, int BS, int GMAX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
+    DecodeArgs a) {
+  using T = typename E::storage;
+  __shared__ OrderScratch sm_order;
+  __shared__ MfmaShared<HD, GMAX> sm;
+  const int part = blockIdx.x, g = blockIdx.y, G = a.group;
+  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
+                                                            a.len_cap, blockIdx.z, sm_order)
+                                          : sequence_of(a, blockIdx.z));
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G) * HD;
+  const int P = a.part_tokens;
+  if (L == 0) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < G * HD; i += 256) out[i] = E::round(0.f);
+    return;
+  }
+  if (part * P >= L) return;
+  const int nparts = (L + P - 1) / P;
+  const int ta = part * P / 16;
+  const int tb = (min(L, part * P + P) + 15) / 16;
+  const size_t state0 = ((size_t)s * a.num_q_heads + (size_t)g * G) * a.max_parts + part;
+  mfma_piece<E, HD, BS, GMAX>(a, s, g, L, ta, tb, nparts == 1 ? out : nullptr, state0,
+                              a.max_parts, sm);
+}
+
+// Balanced mode: every wave of the grid owns one equal range of the tiles
+// of all (sequence, KV head) units laid end to end (sequence major) and
+// walks its pieces alone, with Q^T in its own LDS slot: no barrier after the
+// tile prefix, so all waves stream from the first cycle to about the same
+// last cycle.  Each wave stores its G heads straight from registers: lane
+// (n, g4) holds, for r < 4, the DPL consecutive dims (4*g4 + r)*DPL .. of
+// head n.
+template <typename E, int HD, int BS, int GMAX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
+decode_mfma_balanced_kernel(DecodeArgs a) {
+  using T = typename E::storage;
+  constexpr int DPL = HD / 16;
+  __shared__ TilePrefix sm_prefix;
+  __shared__ u32x4 sm_q[4][HD / 32][kWave];
+  tile_prefix(a, 16, sm_prefix);
+  const int B = a.num_seqs, G = a.group;
+  const int Ts = sm_prefix.start[B];
+  const int64_t T_all = (int64_t)Ts * a.num_kv_heads;
+  const int R = effective_ranges(T_all, a.ranges);
+  const int wave = uniform(threadIdx.x / kWave);
+  const int w = range_of_wave(blockIdx.x, wave, R, a.ranges);
+  if (w < 0) return;
+  const int lane = threadIdx.x % kWave, n = lane & 15, g4 = lane >> 4;
+  RangeWalk walk{range_begin(T_all, w, R), range_begin(T_all, w + 1, R),
+                 range_begin(T_all, w, R), a.num_kv_heads, B, w};
+  Piece p;
+  while (walk.next(sm_prefix, p)) {
+    const int s = uniform(p.s), g = uniform(p.hu);
+    int L = a.context_lens[s];
+    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+    __asm__ volatile("" ::: "memory");   // the previous piece's Q^T reads come first
+    mfma_load_q<E, HD>(a, s, g, sm_q[wave]);
+    MfmaState<DPL> st;
+    mfma_state_init(st);
+    mfma_accumulate<E, HD, BS>(a, s, g, L, uniform(p.ta), uniform(p.tb), 0, 1, sm_q[wave], st);
+    const float l = rows_sum(st.l);
+    if (n < G) {
+      const bool bad = __any(st.bad);
+      if (p.whole) {
+        T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G + n) * HD;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[DPL];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) v[e] = bad ? __builtin_nanf("") : st.acc[e][r] * inv;
+          store_rounded<E, DPL>(out + (4 * g4 + r) * DPL, v);
+        }
+      } else {
+        const size_t stt = (size_t)p.slot * G + n;
+        float* po = a.part_o + stt * HD;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int e = 0; e < DPL; e += 4)
+            *reinterpret_cast<f32x4*>(po + (4 * g4 + r) * DPL + e) =
+                bad ? f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                            __builtin_nanf("")}
+                    : f32x4{st.acc[e][r], st.acc[e + 1][r], st.acc[e + 2][r], st.acc[e + 3][r]};
+        if (g4 == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * stt) = f32x2{st.m, l};
+      }
+    }
+  }
+}
+
+template <typename E, int HD, int BS, int GMAX>
+static void launch_mfma_g(const DecodeArgs& a, hipStream_t st) {
+  if (a.grid_mode == kGridBalanced) {
+    hipLaunchKernelGGL((decode_mfma_balanced_kernel<E, HD, BS, GMAX>), dim3(a.ranges / 4), dim3(256),
+                       0, st, a);
+  } else {
+    dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, GMAX>), grid, dim3(256), 0, st, a);
   }
 }
 
 template <typename E, int HD, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
   if (a.group <= 4)
-    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, 4>), grid, dim3(256), 0, st, a);
+    launch_mfma_g<E, HD, BS, 4>(a, st);
   else if (a.group <= 8)
-    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, 8>), grid, dim3(256), 0, st, a);
+    launch_mfma_g<E, HD, BS, 8>(a, st);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, 16>), grid, dim3(256), 0, st, a);
+    launch_mfma_g<E, HD, BS, 16>(a, st);
   return hipGetLastError();
+}
+
+template <typename E, int HD, int BS>
+static int occupancy_t(int group) {
+  int n = 0;
+  const void* f = group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<E, HD, BS, 4>)
+                  : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<E, HD, BS, 8>)
+                               : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<E, HD, BS, 16>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess) return 0;
+  return n;
+}
+
+template <typename E>
+static int occupancy_e(int hd, int bs, int group) {
+  switch (hd * 100 + bs) {
+    case 6416: return occupancy_t<E, 64, 16>(group);
+    case 6432: return occupancy_t<E, 64, 32>(group);
+    case 12816: return occupancy_t<E, 128, 16>(group);
+    case 12832: return occupancy_t<E, 128, 32>(group);
+  }
+  return 0;
+}
+
+int decode_mfma_occupancy(Elem e, int hd, int bs, int group) {
+  switch (e) {
+    case Elem::F16: return occupancy_e<F16>(hd, bs, group);
+    case Elem::BF16: return occupancy_e<BF16>(hd, bs, group);
+    default: break;
+  }
+  return 0;
 }
 
 template <typename E, int HD>

@@ -1,4 +1,4 @@
-// Merge of the per-partition softmax states of a split context.
+// Merge of the partial softmax states of a split context.
 //
 // A partition p of one (sequence, query head) left its running max m_p (in
 // log2 units), its running sum l_p and its unnormalised output o_p[HD], all
@@ -9,46 +9,39 @@
 // reduce of a paged decode kernel for long contexts.
 //
 // One wave per (sequence, query head), four per workgroup.  Lane j owns the
-// weight of partition c0 + j of the current chunk of 64 partitions.  The
-// partial outputs are read as float4: one load instruction covers
-// 64 / (HD/4) partitions side by side, so all of a chunk's loads are issued
-// back to back, and the partitions held by different lane groups are summed
-// with shuffles at the end.
+// weight of state c0 + j of the current chunk of 64 states.  The partial
+// outputs are read as float4: one load instruction covers 64 / (HD/4)
+// states side by side, so all of a chunk's loads are issued back to back,
+// and the states held by different lane groups are summed with shuffles at
+// the end.  The states come from the partitions of the partition grid, or
+// from the ranges that cut a unit in the balanced grid.
 #include "common.h"
 #include "decode.h"
 
 namespace pkv {
 
-template <typename E, int HD>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  using T = typename E::storage;
+// Merge `n` partial states of one query head into out[HD]; state(j) gives
+// the index of the j-th state in part_o / part_ml.  One wave.
+template <typename E, int HD, typename StateOf>
+__device__ inline void merge_states(const DecodeArgs& a, int n, StateOf state,
+                                    typename E::storage* out) {
   constexpr int F4 = HD / 4;            // float4 per partial row
-  constexpr int PPL = kWave / F4;       // partitions per load instruction (1, 2 or 4)
+  constexpr int PPL = kWave / F4;       // states per load instruction (1, 2 or 4)
   static_assert(PPL >= 1 && PPL * F4 == kWave, "unsupported head_dim");
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
-  if (h >= a.num_q_heads) return;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;   // the partition kernel wrote the output itself
-
-  const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
-  const float* ml = a.part_ml + 2 * base;
-  const float* po = a.part_o + base * HD;
+  const int lane = threadIdx.x % kWave;
 
   float M = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
+  for (int p = lane; p < n; p += kWave) M = fmaxf(M, a.part_ml[2 * state(p)]);
   M = wave_max(M);
 
   const int d4 = lane % F4, psub = lane / F4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float Ls = 0.f;
-  for (int c0 = 0; c0 < nparts; c0 += kWave) {
-    const int nc = min(kWave, nparts - c0);
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const int nc = min(kWave, n - c0);
     float w = 0.f;
     if (lane < nc) {
-      const f32x2 mlp = *reinterpret_cast<const f32x2*>(ml + 2 * (c0 + lane));
+      const f32x2 mlp = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * state(c0 + lane));
       w = fast_exp2(mlp[0] - M);
       Ls = __builtin_fmaf(w, mlp[1], Ls);
     }
@@ -60,7 +53,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * PPL + psub;
         wv[u] = __shfl(w, j < nc ? j : 0, 64);
-        v[u] = j < nc ? *reinterpret_cast<const f32x4*>(po + (size_t)(c0 + j) * HD + 4 * d4)
+        v[u] = j < nc ? *reinterpret_cast<const f32x4*>(a.part_o + state(c0 + j) * HD + 4 * d4)
                       : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
@@ -79,15 +72,66 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   if (psub == 0) {
     const float inv = 1.f / Ls;
     float r[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD + 4 * d4;
-    store_rounded<E, 4>(out, r);
+    store_rounded<E, 4>(out + 4 * d4, r);
   }
+}
+
+// Partitions mode: one wave per (sequence, query head), four per workgroup.
+template <typename E, int HD>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  using T = typename E::storage;
+  const int tid = threadIdx.x, wave = tid / kWave;
+  const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
+  if (h >= a.num_q_heads) return;
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  if (nparts <= 1) return;   // the partition kernel wrote the output itself
+  const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
+  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
+  merge_states<E, HD>(a, nparts, [&](int j) { return base + j; }, out);
+}
+
+// Balanced mode: one wave per (sequence, query head).  The head's unit
+// covers tiles [S, E) of the end-to-end layout; the ranges wf .. wl that
+// cut it left one state each (wf's last piece, the others' first), and a
+// unit inside a single range was written by the decode kernel.  Sequences
+// with no tokens get a zero row here.
+template <typename E, int HD>
+__global__ __launch_bounds__(256) void decode_reduce_balanced_kernel(DecodeArgs a) {
+  using T = typename E::storage;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
+  if (h >= a.num_q_heads) return;
+  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
+  const int ug = a.unit_group;                 // query heads per unit
+  const int U = a.num_q_heads / ug;            // units per sequence
+  const int hu = h / ug, hh = h % ug;
+  const int Ts = a.tile_start[a.num_seqs];
+  const int nt = a.tile_start[s + 1] - a.tile_start[s];
+  const int64_t S = (int64_t)U * a.tile_start[s] + (int64_t)hu * nt;
+  const int64_t E_ = S + nt;
+  if (nt == 0) {
+    for (int d = lane; d < HD; d += kWave) out[d] = E::round(0.f);
+    return;
+  }
+  const int64_t T_all = (int64_t)Ts * U;
+  const int R = effective_ranges(T_all, a.ranges);
+  const int wf = range_of(S, T_all, R), wl = range_of(E_ - 1, T_all, R);
+  if (wf == wl) return;
+  const int first_slot = 2 * wf + (S > range_begin(T_all, wf, R) ? 1 : 0);
+  merge_states<E, HD>(
+      a, wl - wf + 1,
+      [&](int j) { return (size_t)(j == 0 ? first_slot : 2 * (wf + j)) * ug + hh; }, out);
 }
 
 template <typename E, int HD>
 static hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
   dim3 grid((a.num_q_heads + 3) / 4, a.num_seqs);
-  hipLaunchKernelGGL((decode_reduce_kernel<E, HD>), grid, dim3(256), 0, st, a);
+  if (a.grid_mode == kGridBalanced)
+    hipLaunchKernelGGL((decode_reduce_balanced_kernel<E, HD>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<E, HD>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@
 #include "common.h"
 #include "decode.h"
 #include "order.h"
+#include "balance.h"
 
 namespace pkv {
 
@@ -50,48 +51,62 @@ int valu_unit_tokens(Elem e, int head_dim, int block_size) {
   return (lpb < 4 ? lpb : 4) * rpi;
 }
 
+// LDS of one workgroup: the four waves' softmax states.
+template <int HD>
+struct ValuShared {
+  float m[4], l[4];
+  __attribute__((aligned(16))) float o[4][HD];
+  int bad[4];
+};
+
+// One lane's online softmax state: running max m (log2 units), running sum
+// l and unnormalised output o over its columns; bad is set when a table
+// entry fell outside the pool.
+template <int VEC>
+struct ValuState {
+  float m, l, o[VEC];
+  int bad;
+};
+
+// What a wave must read before streaming a piece: its lane's 16 bytes of
+// the query row and the physical blocks of its first 64 units.
+struct ValuMeta {
+  u32x4 q;
+  int tbl;
+};
+
+// Issue the loads of a piece's ValuMeta (units ta + first + stride*i).
 template <typename E, int HD, int BS>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+__device__ inline ValuMeta valu_meta(const DecodeArgs& a, int s, int h, int ta, int first,
+                                     int stride) {
+  using T = typename E::storage;
+  using Tl = ValuTiling<E, HD, BS>;
+  const int lane = threadIdx.x % kWave, col = lane % Tl::LPR;
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + h) * HD;
+  ValuMeta mt;
+  mt.q = ld16(qrow + col * Tl::VEC);
+  const int blk = min((ta + first + stride * lane) / Tl::UPB, a.max_blocks - 1);
+  mt.tbl = a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
+  return mt;
+}
+
+// Fold units ta + first, ta + first + stride, ... (< tb) of query head h of
+// sequence s (context length L > 0; unit = UT tokens) into the calling
+// wave's state, given the piece's ValuMeta.  Row group `row` of the wave
+// sees every RPI-th token.
+template <typename E, int HD, int BS>
+__device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
+                                       int first, int stride, const ValuMeta& meta,
+                                       ValuState<ValuTiling<E, HD, BS>::VEC>& st) {
   using T = typename E::storage;
   using Tl = ValuTiling<E, HD, BS>;
   constexpr int VEC = Tl::VEC, LPR = Tl::LPR, RPI = Tl::RPI, CH = Tl::CH, UT = Tl::UT,
                 UPB = Tl::UPB;
-  constexpr int NW = 4;
-
-  const int part = blockIdx.x, h = blockIdx.y;
-  __shared__ OrderScratch sm_order;
-  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
-                                                            a.len_cap, blockIdx.z, sm_order)
-                                          : sequence_of(a, blockIdx.z));
-  const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
+  const int lane = threadIdx.x % kWave;
   const int row = lane / LPR, col = lane % LPR;
-  const int P = a.part_tokens;
-  const int tok_begin = part * P;
-  const int unit_begin = tok_begin / UT;
   const int g = h / a.group;
-
-  // independent loads first: the length, the query slice, this wave's table entries
-  int L = a.context_lens[s];
-  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + h) * HD;
-  const u32x4 qv = ld16(qrow + col * VEC);
-  int tbl;
-  {
-    const int blk = min((unit_begin + wave + NW * lane) / UPB, a.max_blocks - 1);
-    tbl = a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
-  }
-
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
-  if (L == 0) {
-    if (part == 0)
-      for (int d = tid; d < HD; d += 256) out[d] = E::round(0.f);
-    return;
-  }
-  if (tok_begin >= L) return;
-  const int tok_end = min(L, tok_begin + P);
-  const int nparts = (L + P - 1) / P;
-  const int n_units = (tok_end + UT - 1) / UT - unit_begin;   // <= 4 * 64
-  const int mine = n_units > wave ? (n_units - wave + NW - 1) / NW : 0;
+  const int tok_end = L;
+  const u32x4 qv = meta.q;
 
   // unit addresses: a buffer descriptor over the unit's tile rows, built in
   // scalar registers, plus a constant 32-bit per-lane byte offset, so no
@@ -100,90 +115,101 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
   const uint32_t loff = (uint32_t)((row * HD + col * VEC) * sizeof(T));
+  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
-  float m = -INFINITY, l = 0.f, o[VEC];
+  float m = st.m, l = st.l, o[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) o[e] = 0.f;
-  int bad = 0;
+  for (int e = 0; e < VEC; ++e) o[e] = st.o[e];
+  int bad = st.bad;
 
-  // issue the loads of the wave's i-th unit
-  auto load_unit = [&](int i, u32x4* kr, u32x4* vr) {
-    const int u = unit_begin + wave + NW * i;
-    int phys = lane_value(tbl, i);
-    if ((unsigned)phys >= (unsigned)a.num_blocks) {
-      bad = 1;
-      phys = 0;
+  // passes of at most 64 of the wave's units: their table entries fit one
+  // VGPR (the first pass's come with the meta)
+  for (int pass = ta + first; pass < tb; pass += kWave * stride) {
+    const int mine = min(kWave, (tb - pass + stride - 1) / stride);
+    int tbl = meta.tbl;
+    if (pass != ta + first) {
+      const int blk = min((pass + stride * lane) / UPB, a.max_blocks - 1);
+      tbl = a.contiguous ? s * a.max_blocks + blk : table[blk];
     }
-    const size_t off = (size_t)phys * block_bytes + (size_t)(u % UPB) * UT * HD * sizeof(T);
-    constexpr uint32_t kUnitBytes = UT * HD * sizeof(T);
-    const rsrc_t kt = make_rsrc(kbase + off, kUnitBytes);
-    const rsrc_t vt = make_rsrc(vbase + off, kUnitBytes);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) kr[c] = bld16(kt, loff, c * RPI * HD * sizeof(T));
-#pragma unroll
-    for (int c = 0; c < CH; ++c) vr[c] = bld16(vt, loff, c * RPI * HD * sizeof(T));
-  };
 
-  // fold the wave's i-th unit into the online state
-  auto compute_unit = [&](int i, const u32x4* kr, const u32x4* vr) {
-    const int u = unit_begin + wave + NW * i;
-    float sc[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) sc[c] = group_sum<LPR>(E::dot16(kr[c], qv, 0.f)) * a.scale_log2e;
-    if ((u + 1) * UT <= tok_end) {
-      // every token of the unit is inside the partition
-      float mb = sc[0];
-#pragma unroll
-      for (int c = 1; c < CH; ++c) mb = fmaxf(mb, sc[c]);
-      const float mn = fmaxf(m, mb);
-      const float corr = fast_exp2(m - mn);
-      m = mn;
-      l *= corr;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] *= corr;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const float p = fast_exp2(sc[c] - mn);
-        l += p;
-        float vf[VEC];
-        E::unpack16(vr[c], vf);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
+    // issue the loads of the wave's i-th unit of the pass
+    auto load_unit = [&](int i, u32x4* kr, u32x4* vr) {
+      const int u = pass + stride * i;
+      int phys = lane_value(tbl, i);
+      if ((unsigned)phys >= (unsigned)a.num_blocks) {
+        bad = 1;
+        phys = 0;
       }
-    } else {
-      // the partition's last unit: tokens at or past tok_end are masked by
-      // index, never by arithmetic, so whatever those slots hold cannot
-      // reach the result
-      const int t0 = u * UT + row;
-      float mb = -INFINITY;
+      const size_t off = (size_t)phys * block_bytes + (size_t)(u % UPB) * UT * HD * sizeof(T);
+      constexpr uint32_t kUnitBytes = UT * HD * sizeof(T);
+      const rsrc_t kt = make_rsrc(kbase + off, kUnitBytes);
+      const rsrc_t vt = make_rsrc(vbase + off, kUnitBytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) kr[c] = bld16(kt, loff, c * RPI * HD * sizeof(T));
+#pragma unroll
+      for (int c = 0; c < CH; ++c) vr[c] = bld16(vt, loff, c * RPI * HD * sizeof(T));
+    };
+
+    // fold the wave's i-th unit into the online state
+    auto compute_unit = [&](int i, const u32x4* kr, const u32x4* vr) {
+      const int u = pass + stride * i;
+      float sc[CH];
 #pragma unroll
       for (int c = 0; c < CH; ++c)
-        if (t0 + c * RPI < tok_end) mb = fmaxf(mb, sc[c]);
-      const float mn = fmaxf(m, mb);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float corr = fast_exp2(m - mu);
-      m = mn;
-      l *= corr;
+        sc[c] = group_sum<LPR>(E::dot16(kr[c], qv, 0.f)) * a.scale_log2e;
+      if ((u + 1) * UT <= tok_end) {
+        // every token of the unit is inside the context
+        float mb = sc[0];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] *= corr;
+        for (int c = 1; c < CH; ++c) mb = fmaxf(mb, sc[c]);
+        const float mn = fmaxf(m, mb);
+        const float corr = fast_exp2(m - mn);
+        m = mn;
+        l *= corr;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        if (t0 + c * RPI < tok_end) {
-          const float p = fast_exp2(sc[c] - mu);
+        for (int e = 0; e < VEC; ++e) o[e] *= corr;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const float p = fast_exp2(sc[c] - mn);
           l += p;
           float vf[VEC];
           E::unpack16(vr[c], vf);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
         }
+      } else {
+        // the sequence's last unit: tokens at or past the context length are
+        // masked by index, never by arithmetic, so whatever those slots hold
+        // cannot reach the result
+        const int t0 = u * UT + row;
+        float mb = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (t0 + c * RPI < tok_end) mb = fmaxf(mb, sc[c]);
+        const float mn = fmaxf(m, mb);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        const float corr = fast_exp2(m - mu);
+        m = mn;
+        l *= corr;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] *= corr;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          if (t0 + c * RPI < tok_end) {
+            const float p = fast_exp2(sc[c] - mu);
+            l += p;
+            float vf[VEC];
+            E::unpack16(vr[c], vf);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
+          }
+        }
       }
-    }
-  };
+    };
 
-  // two register buffers: the loads of unit i+1 are in flight while unit i
-  // is computed
-  u32x4 kA[CH], vA[CH], kB[CH], vB[CH];
-  if (mine > 0) {
+    // two register buffers: the loads of unit i+1 are in flight while unit i
+    // is computed
+    u32x4 kA[CH], vA[CH], kB[CH], vB[CH];
     load_unit(0, kA, vA);
     int i = 0;
     // steady state: the loads of the next unit are always issued, so the
@@ -202,75 +228,200 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       compute_unit(i, kA, vA);
     }
   }
+  st.m = m;
+  st.l = l;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) st.o[e] = o[e];
+  st.bad = bad;
+}
 
-  // merge the wave's RPI row groups (lanes that differ in `row`)
+// Merge the wave's RPI row groups (lanes that differ in `row`): afterwards
+// every lane holds the wave's state for its columns.
+template <int VEC, int LPR>
+__device__ inline void valu_row_merge(ValuState<VEC>& st) {
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {
-    const float mo = __shfl_xor(m, off, 64);
-    const float lo = __shfl_xor(l, off, 64);
-    const float mn = fmaxf(m, mo);
+    const float mo = __shfl_xor(st.m, off, 64);
+    const float lo = __shfl_xor(st.l, off, 64);
+    const float mn = fmaxf(st.m, mo);
     const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float wa = fast_exp2(m - mu), wb = fast_exp2(mo - mu);
-    l = l * wa + lo * wb;
+    const float wa = fast_exp2(st.m - mu), wb = fast_exp2(mo - mu);
+    st.l = st.l * wa + lo * wb;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = o[e] * wa + __shfl_xor(o[e], off, 64) * wb;
-    m = mn;
+    for (int e = 0; e < VEC; ++e) st.o[e] = st.o[e] * wa + __shfl_xor(st.o[e], off, 64) * wb;
+    st.m = mn;
   }
+}
 
-  // merge the 4 waves in LDS
-  __shared__ float sm_m[NW], sm_l[NW];
-  __shared__ __attribute__((aligned(16))) float sm_o[NW][HD];
-  __shared__ int sm_bad[NW];
-  if (lane == 0) {
-    sm_m[wave] = m;
-    sm_l[wave] = l;
-  }
-  if (row == 0) {
-#pragma unroll
-    for (int e = 0; e < VEC; e += 4)
-      *reinterpret_cast<f32x4*>(&sm_o[wave][col * VEC + e]) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-  }
-  const int any_bad = __any(bad);
-  if (lane == 0) sm_bad[wave] = any_bad;
-  __syncthreads();
-  if (wave != 0 || row != 0) return;
-
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w]);
-  float wt[NW], Ls = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    wt[w] = fast_exp2(sm_m[w] - M);   // M is finite: this partition has a token
-    Ls = __builtin_fmaf(wt[w], sm_l[w], Ls);
-  }
-  float O[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; e += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&sm_o[w][col * VEC + e]);
-    O[e] = acc[0];
-    O[e + 1] = acc[1];
-    O[e + 2] = acc[2];
-    O[e + 3] = acc[3];
-  }
-  if (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) {
+// Store a merged state's VEC columns at col*VEC: normalised and rounded into
+// out when out is not null, else unnormalised to po and (max, sum) to pml.
+template <typename E, int VEC>
+__device__ inline void valu_emit(float M, float Ls, float* O, bool bad, int col,
+                                 typename E::storage* out, float* po, float* pml) {
+  if (bad) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) O[e] = __builtin_nanf("");
   }
-  if (nparts == 1) {
+  if (out) {
     const float inv = 1.f / Ls;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) O[e] *= inv;
     store_rounded<E, VEC>(out + col * VEC, O);
   } else {
-    const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + part;
-    float* po = a.part_o + pidx * HD + col * VEC;
 #pragma unroll
     for (int e = 0; e < VEC; e += 4)
-      *reinterpret_cast<f32x4*>(po + e) = f32x4{O[e], O[e + 1], O[e + 2], O[e + 3]};
-    if (col == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * pidx) = f32x2{M, Ls};
+      *reinterpret_cast<f32x4*>(po + col * VEC + e) = f32x4{O[e], O[e + 1], O[e + 2], O[e + 3]};
+    if (col == 0) *reinterpret_cast<f32x2*>(pml) = f32x2{M, Ls};
+  }
+}
+
+// Attention of query head h of sequence s (context length L > 0) over its
+// units [ta, tb), by the four waves of the workgroup (unit round-robin),
+// merged in LDS.  Result as in valu_emit.
+template <typename E, int HD, int BS>
+__device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
+                                  typename E::storage* out, float* po, float* pml,
+                                  ValuShared<HD>& sm) {
+  using Tl = ValuTiling<E, HD, BS>;
+  constexpr int VEC = Tl::VEC, LPR = Tl::LPR;
+  constexpr int NW = 4;
+  const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
+  const int row = lane / LPR, col = lane % LPR;
+  ValuState<VEC> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) st.o[e] = 0.f;
+  st.bad = 0;
+  const ValuMeta meta = valu_meta<E, HD, BS>(a, s, h, ta, wave, NW);
+  valu_accumulate<E, HD, BS>(a, s, h, L, ta, tb, wave, NW, meta, st);
+  valu_row_merge<VEC, LPR>(st);
+
+  // merge the 4 waves in LDS
+  if (lane == 0) {
+    sm.m[wave] = st.m;
+    sm.l[wave] = st.l;
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<f32x4*>(&sm.o[wave][col * VEC + e]) =
+          f32x4{st.o[e], st.o[e + 1], st.o[e + 2], st.o[e + 3]};
+  }
+  const int any_bad = __any(st.bad);
+  if (lane == 0) sm.bad[wave] = any_bad;
+  __syncthreads();
+  if (wave == 0 && row == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float wt[NW], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      wt[w] = fast_exp2(sm.m[w] - Mu);
+      Ls = __builtin_fmaf(wt[w], sm.l[w], Ls);
+    }
+    float O[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        acc += wt[w] * *reinterpret_cast<const f32x4*>(&sm.o[w][col * VEC + e]);
+      O[e] = acc[0];
+      O[e + 1] = acc[1];
+      O[e + 2] = acc[2];
+      O[e + 3] = acc[3];
+    }
+    valu_emit<E, VEC>(M, Ls, O, sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3], col, out, po, pml);
+  }
+  __syncthreads();   // the LDS states are free for the next piece
+}
+
+// Partitions mode: grid (max_parts, Hq, B); partition `part` of query head
+// h of the sequence of grid row z.
+template <typename E, int HD, int BS>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  using T = typename E::storage;
+  constexpr int UT = ValuTiling<E, HD, BS>::UT;
+  __shared__ OrderScratch sm_order;
+  __shared__ ValuShared<HD> sm;
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
+                                                            a.len_cap, blockIdx.z, sm_order)
+                                          : sequence_of(a, blockIdx.z));
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
+  const int P = a.part_tokens;
+  if (L == 0) {
+    if (part == 0)
+      for (int d = threadIdx.x; d < HD; d += 256) out[d] = E::round(0.f);
+    return;
+  }
+  if (part * P >= L) return;
+  const int nparts = (L + P - 1) / P;
+  const int ta = part * P / UT;
+  const int tb = (min(L, part * P + P) + UT - 1) / UT;
+  const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + part;
+  valu_piece<E, HD, BS>(a, s, h, L, ta, tb, nparts == 1 ? out : nullptr,
+                        a.part_o + pidx * HD, a.part_ml + 2 * pidx, sm);
+}
+
+// Balanced mode: every wave of the grid owns one equal range of the unit
+// tiles laid end to end (sequence major) and walks its pieces alone: no
+// barrier and no LDS after the tile prefix, so all waves stream from the
+// first cycle to about the same last cycle.
+template <typename E, int HD, int BS>
+__global__ __launch_bounds__(256) void decode_valu_balanced_kernel(DecodeArgs a) {
+  using T = typename E::storage;
+  using Tl = ValuTiling<E, HD, BS>;
+  constexpr int VEC = Tl::VEC, LPR = Tl::LPR, UT = Tl::UT;
+  __shared__ TilePrefix sm_prefix;
+  tile_prefix(a, UT, sm_prefix);
+  const int B = a.num_seqs;
+  const int Ts = sm_prefix.start[B];
+  const int64_t T_all = (int64_t)Ts * a.num_q_heads;
+  const int R = effective_ranges(T_all, a.ranges);
+  const int w = range_of_wave(blockIdx.x, uniform(threadIdx.x / kWave), R, a.ranges);
+  if (w < 0) return;
+  const int lane = threadIdx.x % kWave, row = lane / LPR, col = lane % LPR;
+  RangeWalk walk{range_begin(T_all, w, R), range_begin(T_all, w + 1, R),
+                 range_begin(T_all, w, R), a.num_q_heads, B, w};
+  // the next piece's length, query slice and first table entries are read
+  // while the current piece streams, so a piece starts with its tile loads
+  Piece p, pn;
+  if (!walk.next(sm_prefix, p)) return;
+  ValuMeta meta = valu_meta<E, HD, BS>(a, uniform(p.s), uniform(p.hu), uniform(p.ta), 0, 1);
+  int L = a.context_lens[uniform(p.s)];
+  for (;;) {
+    const bool more = walk.next(sm_prefix, pn);
+    ValuMeta meta_n = meta;
+    int L_n = 0;
+    if (more) {
+      meta_n = valu_meta<E, HD, BS>(a, uniform(pn.s), uniform(pn.hu), uniform(pn.ta), 0, 1);
+      L_n = a.context_lens[uniform(pn.s)];
+    }
+    const int s = uniform(p.s), h = uniform(p.hu);
+    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+    ValuState<VEC> st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st.o[e] = 0.f;
+    st.bad = 0;
+    valu_accumulate<E, HD, BS>(a, s, h, L, uniform(p.ta), uniform(p.tb), 0, 1, meta, st);
+    valu_row_merge<VEC, LPR>(st);
+    if (row == 0) {
+      T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
+      valu_emit<E, VEC>(st.m, st.l, st.o, __any(st.bad), col, p.whole ? out : nullptr,
+                        a.part_o + (size_t)p.slot * HD, a.part_ml + 2 * (size_t)p.slot);
+    }
+    if (!more) break;
+    p = pn;
+    meta = meta_n;
+    L = L_n;
   }
 }
 
@@ -278,9 +429,24 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
 template <typename E, int HD, int BS>
 static hipError_t launch_valu_t(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.max_parts, a.num_q_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
+  if (a.grid_mode == kGridBalanced) {
+    hipLaunchKernelGGL((decode_valu_balanced_kernel<E, HD, BS>), dim3(a.ranges / 4), dim3(256), 0, st,
+                       a);
+  } else {
+    dim3 grid(a.max_parts, a.num_q_heads, a.num_seqs);
+    hipLaunchKernelGGL((decode_valu_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
+}
+
+template <typename E, int HD, int BS>
+static int occupancy_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&decode_valu_balanced_kernel<E, HD, BS>), 256, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
 }
 
 template <typename E, int HD>
@@ -301,6 +467,31 @@ static hipError_t launch_valu_e(int hd, int bs, const DecodeArgs& a, hipStream_t
     case 256: return launch_valu_hd<E, 256>(bs, a, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename E>
+static int occupancy_e(int hd, int bs) {
+  switch (hd * 100 + bs) {
+    case 6408: return occupancy_t<E, 64, 8>();
+    case 6416: return occupancy_t<E, 64, 16>();
+    case 6432: return occupancy_t<E, 64, 32>();
+    case 12808: return occupancy_t<E, 128, 8>();
+    case 12816: return occupancy_t<E, 128, 16>();
+    case 12832: return occupancy_t<E, 128, 32>();
+    case 25608: return occupancy_t<E, 256, 8>();
+    case 25616: return occupancy_t<E, 256, 16>();
+    case 25632: return occupancy_t<E, 256, 32>();
+  }
+  return 0;
+}
+
+int decode_valu_occupancy(Elem e, int hd, int bs) {
+  switch (e) {
+    case Elem::F32: return occupancy_e<F32>(hd, bs);
+    case Elem::F16: return occupancy_e<F16>(hd, bs);
+    case Elem::BF16: return occupancy_e<BF16>(hd, bs);
+  }
+  return 0;
 }
 
 bool decode_valu_supported(Elem e, int hd, int bs) {

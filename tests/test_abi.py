@@ -59,32 +59,57 @@ def test_supported_shapes(native):
 def test_workspace_bytes_and_plan(native):
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
-    # one partition (short contexts): no workspace
-    assert native.workspace_bytes(4, 4, 4, 64, 16, 4, 64, torch.float32) == 0
-    assert native.plan(4, 4, 4, 64, 16, 4, 64, torch.float32) == (64, 1, native.PATH_VALU, False)
-    # many (sequence, head) units: one partition per sequence, longest first
-    # (the order is computed inside the decode kernel: no workspace)
-    assert native.plan(64, 40, 40, 128, 16, 128, 2048, f16) == (2048, 1, native.PATH_VALU, True)
-    assert native.workspace_bytes(64, 40, 40, 128, 16, 128, 2048, f16) == 0
-    # more than 1024 sequences: a separate order kernel writes the order to the workspace
-    assert native.plan(2000, 8, 8, 128, 16, 8, 128, f16)[3]
-    assert native.workspace_bytes(2000, 8, 8, 128, 16, 8, 128, f16) == 2000 * 4
-    assert native.plan(256, 32, 8, 128, 16, 256, 4096, bf16) == (4096, 1, native.PATH_MFMA, True)
+    P, B = native.GRID_PARTITIONS, native.GRID_BALANCED
+
+    def plan(*a, **k):
+        p = native.plan(*a, **k)
+        assert p["workspace_bytes"] == native.workspace_bytes(*a, **k)
+        return p
+
+    # default: partitions grid, one partition per (sequence, head) when there
+    # are enough of them, visited longest first (order computed in-kernel)
+    p = plan(64, 40, 40, 128, 16, 128, 2048, f16)
+    assert (p["path"], p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
+        (native.PATH_VALU, P, 2048, 1, 1)
+    assert p["workspace_bytes"] == 0
+    p = plan(256, 32, 8, 128, 16, 256, 4096, bf16)
+    assert (p["path"], p["grid"], p["max_parts"], p["workspace_bytes"]) == \
+        (native.PATH_MFMA, P, 1, 0)
     # few units, long contexts: split so that every compute unit gets work
-    p, parts, path, srt = native.plan(8, 64, 8, 128, 32, 1024, 32768, bf16)
-    assert path == native.PATH_MFMA and parts > 1 and p * parts >= 32768 and p % 32 == 0
-    assert native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16) == \
-        8 * 64 * parts * 130 * 4
-    # an explicit partition size
-    assert native.plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 4096) == \
-        (4096, 8, native.PATH_MFMA, False)
-    assert native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 4096) == \
-        8 * 64 * 8 * 130 * 4
+    p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16)
+    assert p["max_parts"] > 1 and p["partition_tokens"] * p["max_parts"] >= 32768
+    assert p["workspace_bytes"] == 8 * 64 * p["max_parts"] * (128 + 2) * 4
+    # balanced grid on request (-1): 2 partial states per range and the tile prefix
+    p = plan(64, 40, 40, 128, 16, 128, 2048, f16, -1)
+    assert (p["grid"], p["partition_tokens"], p["max_parts"]) == (B, 0, 0)
+    assert p["ranges"] >= 32 and p["ranges"] % 32 == 0
+    assert p["workspace_bytes"] == 2 * p["ranges"] * (128 + 2) * 4 + 65 * 4 + 12
+    p = plan(256, 32, 8, 128, 16, 256, 4096, bf16, -1)
+    assert (p["path"], p["grid"]) == (native.PATH_MFMA, B)
+    assert p["workspace_bytes"] == 2 * p["ranges"] * 4 * 128 * 4 + 2 * p["ranges"] * 4 * 2 * 4 \
+        + 257 * 4 + 12
+    # small batches get fewer ranges (about 4 tiles each at the least, 32 minimum)
+    assert plan(4, 4, 4, 64, 16, 4, 64, torch.float32, -1)["ranges"] == 32
+    # the balanced grid holds at most 1024 sequences
+    with pytest.raises(native.PagedKVError):
+        native.plan(1025, 4, 4, 64, 16, 4, 64, torch.float32, -1)
+    # explicit partition size: partitions grid
+    p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 4096)
+    assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
+        (P, 4096, 8, 0)
+    assert p["workspace_bytes"] == 8 * 64 * 8 * 128 * 4 + 8 * 64 * 8 * 2 * 4
     # 2048 workgroups: more than two rounds of resident ones, so longest first
-    assert native.plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024) == \
-        (1024, 32, native.PATH_MFMA, True)
+    p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024)
+    assert (p["grid"], p["max_parts"], p["longest_first"]) == (P, 32, 1)
+    # more than 1024 sequences: partitions grid, order kernel writes the order
+    p = plan(2000, 8, 8, 128, 16, 8, 128, f16)
+    assert (p["grid"], p["max_parts"], p["longest_first"]) == (P, 1, 1)
+    assert p["workspace_bytes"] == 2000 * 4
+    # one partition per sequence, no order: no workspace
+    p = plan(2000, 1, 1, 128, 16, 8, 128, f16)
+    assert (p["grid"], p["longest_first"], p["workspace_bytes"]) == (P, 0, 0)
     # the table width caps the context: 10 blocks of 16 tokens
-    assert native.plan(2, 4, 4, 128, 16, 10, 100000, f16, 64)[1] == 3
+    assert plan(2, 4, 4, 128, 16, 10, 100000, f16, 64)["max_parts"] == 3
     with pytest.raises(ValueError):
         native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 100)   # not a multiple of 32
     with pytest.raises(ValueError):
@@ -115,7 +140,9 @@ def _decode(lib, **over):
     (dict(part=48), -1),         # not a multiple of 32
     (dict(path=2, Hq=2, Hkv=2), -2),   # MFMA needs grouped heads
     (dict(path=2, dtype=0), -2),       # MFMA needs 16-bit types
-    (dict(maxL=4096, maxb=256), -3),   # several partitions and no workspace
+    (dict(maxL=4096, maxb=256, part=-1), -3),   # balanced grid and no workspace
+    (dict(maxL=4096, maxb=256, part=512), -3),   # several partitions and no workspace
+    (dict(part=-2), -1),
     (dict(path=7), -1),
 ])
 def test_decode_rejects_bad_arguments_before_launch(native, over, status):

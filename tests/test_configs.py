@@ -3,7 +3,8 @@
 Each workload is built at the size and with the seed the benchmark uses, and
 its step runs through the C ABI in the benchmark's launch configuration
 (library-chosen partition size and kernel), then again with a forced split
-so the partition + reduce path is covered at full size too:
+and with the balanced grid, so the partition + reduce and the balanced +
+reduce paths are covered at full size too:
 
 * cache writes (reshape_and_cache) and block copies (copy_blocks) are
   compared with the oracle's byte for byte over the WHOLE K and V buffers;
@@ -117,7 +118,7 @@ def test_full_size_step_matches_oracle(name):
     v_o = torch.from_numpy(v_host).view(wl.dtype)
     want = oracle.decode(wl.q.cpu(), k_o, v_o, wl.block_tables, wl.context_lens, wl.scale,
                          wl.num_kv_heads, seqs=seqs)
-    for partition in (0, split):
+    for partition in (0, split, -1):
         say("full-size decode", name, "partition", partition, pk.plan(
             wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
             wl.block_tables.shape[1], wl.max_context_len, wl.dtype, partition))

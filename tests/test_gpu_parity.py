@@ -150,14 +150,15 @@ SHAPES = [  # (hq, hkv, hd, bs)
 ]
 
 
+@pytest.mark.parametrize("grid", [0, -1], ids=["partitions", "balanced"])
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_ID.get)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "hq%d_hkv%d_hd%d_bs%d" % s)
-def test_decode_ragged_lengths(dtype, shape):
+def test_decode_ragged_lengths(dtype, shape, grid):
     hq, hkv, hd, bs = shape
-    say("decode ragged", DT_ID[dtype], shape)
+    say("decode ragged", DT_ID[dtype], shape, grid)
     lens = [1, bs - 1, bs, bs + 1, 63, 64, 65, 200]
     q, kp, vp, tables, L = _case(7 + hd + bs + hq, lens, hq, hkv, hd, bs)
-    _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd))
+    _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), partition=grid)
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=DT_ID.get)
@@ -227,25 +228,29 @@ def test_decode_poisoned_slots_never_reach_the_result(hq, hkv):
     assert torch.equal(g1.view(torch.int16), g2.view(torch.int16))
 
 
+@pytest.mark.parametrize("grid", [0, -1], ids=["partitions", "balanced"])
 @pytest.mark.parametrize("path", [1, 2], ids=["valu", "mfma"])
-def test_decode_zero_length_gives_zeros(path):
-    say("decode L=0", path)
+def test_decode_zero_length_gives_zeros(path, grid):
+    say("decode L=0", path, grid)
     q, kp, vp, tables, L = _case(800, [0, 9, 0], 8, 2, 128, 16)
     dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, torch.bfloat16)
-    got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.1, path=path)
+    got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.1, path=path,
+                     partition=grid)
     assert not got[0].any() and not got[2].any()
     want = oracle.decode(qt, kt, vt, tables, L, 0.1, 2)
     assert max_err(got, want) <= 2e-2
 
 
+@pytest.mark.parametrize("grid", [0, -1], ids=["partitions", "balanced"])
 @pytest.mark.parametrize("path", [1, 2], ids=["valu", "mfma"])
-def test_decode_bad_table_entry_gives_nan_not_a_fault(path):
-    say("decode bad table", path)
+def test_decode_bad_table_entry_gives_nan_not_a_fault(path, grid):
+    say("decode bad table", path, grid)
     q, kp, vp, tables, L = _case(900, [40, 40], 8, 2, 128, 16)
     tables = tables.copy()
     tables[1, 1] = kp.shape[0] + 1000          # outside the pool
     dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, torch.float16)
-    got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.1, path=path)
+    got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.1, path=path,
+                     partition=grid)
     assert torch.isnan(got[1]).all()
     want = oracle.decode(qt, kt, vt, tables, L, 0.1, 2, seqs=[0])
     assert max_err(got[:1], want[:1]) <= 2e-2
@@ -277,21 +282,27 @@ def test_decode_contiguous_control_matches_paged():
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=DT_ID.get)
-@pytest.mark.parametrize("hq,hkv,partition", [(4, 4, 0), (8, 2, 0), (8, 2, 64), (2, 2, 32)])
+@pytest.mark.parametrize("hq,hkv,partition", [(4, 4, 0), (8, 2, 0), (8, 2, 64), (2, 2, 32),
+                                              (4, 4, -1), (8, 2, -1)])
 def test_decode_many_sequences_longest_first(dtype, hq, hkv, partition):
-    """Enough (sequence, head) workgroups that the library first orders the
-    sequences longest first; lengths log-uniform so the order is far from
-    the index order.  With partition 64 the split path runs under the order
-    too."""
+    """Partitions grid with enough workgroups that the kernel visits the
+    sequences longest first (order computed inside the kernel); lengths
+    log-uniform so the order is far from the index order; partitions 64 and
+    32 run the split path under the order too.  Partition -1 is the balanced
+    grid on the same batch."""
     say("decode longest-first", DT_ID[dtype], hq, hkv, partition)
     num_seqs, hd, bs = 800, 128, 16
     rng = np.random.default_rng(1100 + hq + partition)
     lens = np.clip(np.rint(np.exp(rng.uniform(0, math.log(300), num_seqs))), 1, 300).astype(int)
     q, ks, vs, nblk = pins.random_case(rng, num_seqs, hq, hkv, hd, lens, bs, extra_blocks=3)
     kp, vp, tables, L, _ = pins.page(ks, vs, bs, nblk, rng)
-    from paged_kv_cache_389_amd import plan
+    from paged_kv_cache_389_amd import GRID_BALANCED, plan
     dt = {torch.float16: 1, torch.bfloat16: 2}[dtype]
-    assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), dt, partition)[3]
+    p = plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), dt, partition)
+    if partition >= 0:
+        assert p["longest_first"]
+    else:
+        assert p["grid"] == GRID_BALANCED
     _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), partition=partition)
 
 
@@ -305,7 +316,39 @@ def test_decode_batch_above_fused_order_limit():
     q, ks, vs, nblk = pins.random_case(rng, num_seqs, hq, hkv, hd, lens, bs, extra_blocks=3)
     kp, vp, tables, L, _ = pins.page(ks, vs, bs, nblk, rng)
     from paged_kv_cache_389_amd import plan, workspace_bytes
-    assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1)[3]
+    assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1)["longest_first"]
     assert workspace_bytes(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1) >= \
         4 * num_seqs
     _check_decode(q, kp, vp, tables, L, hkv, torch.float16, 0.125)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=DT_ID.get)
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (16, 2)])
+def test_decode_balanced_long_sequence_cut_by_many_ranges(dtype, hq, hkv):
+    """Balanced grid: one long sequence and a few short ones, so every range
+    boundary cuts a (head, sequence) unit and the reduce merges dozens of
+    partial states per head; also empty sequences among them."""
+    say("decode balanced long", DT_ID[dtype], hq, hkv)
+    lens = [9000, 0, 3, 777, 0, 16]
+    q, kp, vp, tables, L = _case(1300 + hq, lens, hq, hkv, 128, 16)
+    got, _ = _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(128), partition=-1)
+    assert not got[1].any() and not got[4].any()
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2)])
+def test_decode_balanced_determinism_and_placement(hq, hkv):
+    """Balanced grid: bit-identical results across runs and across physical
+    placements of the same logical sequences."""
+    say("decode balanced placement", hq, hkv)
+    rng = np.random.default_rng(1400)
+    lens = [700, 33, 1200, 5, 2000, 1]
+    q, ks, vs, nblk = pins.random_case(rng, len(lens), hq, hkv, 128, lens, 16, extra_blocks=40)
+    outs = []
+    for rep in range(2):
+        kp, vp, tables, L, _ = pins.page(ks, vs, 16, nblk, rng)
+        dev, _ = upload_case(q, kp, vp, tables, L, torch.float16)
+        for _ in range(2):
+            outs.append(decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
+                                   0.088, partition=-1).cpu())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
