@@ -57,6 +57,7 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="one line per workload")
     p.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA, 3 contiguous")
+    p.add_argument("--grid", type=int, default=0, help="0 auto, 1 direct, 2 planned")
     p.add_argument("--placement", default="random", choices=["random", "sequential"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -112,16 +113,16 @@ def step_bytes(wl, dev):
     return wl.decode_bytes(), writes + copies
 
 
-def run_gpu(wl, dev, steps, warmup, partition, path):
+def run_gpu(wl, dev, steps, warmup, partition, path, grid):
     from paged_kv_cache_389_amd import _native as pk
     tables = None if path == 3 else dev["tables"]
     max_blocks = -(-wl.max_context_len // wl.block_size) if tables is None else tables.shape[1]
     ws_len = pk.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                 wl.block_size, max_blocks, wl.max_context_len, wl.dtype,
-                                partition, path)
+                                partition, path, grid)
     ws = torch.empty(max(ws_len, 1), dtype=torch.uint8, device="cuda")
     plan = pk.plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-                   max_blocks, wl.max_context_len, wl.dtype, partition, path)
+                   max_blocks, wl.max_context_len, wl.dtype, partition, path, grid)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
 
@@ -134,7 +135,7 @@ def run_gpu(wl, dev, steps, warmup, partition, path):
             ev[i][0].record()
         pk.paged_attention_decode(dev["out"], dev["q"], dev["k"], dev["v"], tables, dev["lens"],
                                   wl.scale, wl.max_context_len, workspace=ws,
-                                  partition_tokens=partition, path=path)
+                                  partition_tokens=partition, path=path, grid=grid)
         if i is not None:
             ev[i][1].record()
 
@@ -182,7 +183,8 @@ def cpu_baseline(wl, budget_s):
 def bench_one(name, args, with_cpu):
     wl, dev = build_inputs(name, args.placement)
     alg_decode, alg_writes = step_bytes(wl, dev)
-    wall, decode_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition, args.path)
+    wall, decode_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition, args.path,
+                                    args.grid)
     ms_per_step = wall / args.steps * 1e3
     dec_ms = float(np.mean(decode_ms))
     achieved = alg_decode / (dec_ms / 1e3) / 1e9
@@ -203,9 +205,9 @@ def bench_one(name, args, with_cpu):
                    "placement": args.placement,
                    "path": ["auto", "valu", "mfma", "contiguous"][args.path],
                    "kernel": ["auto", "valu", "mfma"][plan["path"]],
-                   "grid": ["partitions", "balanced"][plan["grid"]],
+                   "grid": {1: "direct", 2: "planned"}[plan["grid"]],
                    "partition_tokens": plan["partition_tokens"], "max_parts": plan["max_parts"],
-                   "ranges": plan["ranges"], "longest_first": bool(plan["longest_first"])},
+                   "longest_first": bool(plan["longest_first"])},
         "queries_per_s": round(wl.num_seqs / (ms_per_step / 1e3), 1),
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 5),

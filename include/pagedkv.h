@@ -88,20 +88,21 @@ const char* pkv_last_error(void);
  * head_dim in {64, 128, 256}; block_size in {8, 16, 32}. */
 int pkv_supported(pkv_dtype dtype, int head_dim, int block_size);
 
-/* How a decode call divides its work (pkv_plan.grid). */
+/* How a decode call divides its work (the grid argument; pkv_plan.grid
+ * reports DIRECT or PLANNED). */
 typedef enum {
-  PKV_GRID_PARTITIONS = 0, /* one workgroup per (partition, head, sequence) */
-  PKV_GRID_BALANCED = 1    /* one workgroup per resident slot, equal shares of all tiles */
+  PKV_GRID_AUTO = 0,     /* the library chooses (see pkv_paged_attention_plan) */
+  PKV_GRID_DIRECT = 1,   /* one workgroup per (head unit, partition, sequence) in index order */
+  PKV_GRID_PLANNED = 2   /* a planning kernel lists the partitions, largest first */
 } pkv_grid;
 
 /* The plan of a decode call (filled by pkv_paged_attention_plan). */
 typedef struct {
   int path;              /* PKV_PATH_VALU or PKV_PATH_MFMA */
   int grid;              /* pkv_grid */
-  int partition_tokens;  /* partitions grid: tokens per partition (0 for balanced) */
-  int max_parts;         /* partitions grid: partitions per sequence (0 for balanced) */
-  int ranges;            /* balanced grid: waves, one range of tiles each (0 for partitions) */
-  int longest_first;     /* partitions grid: 1 if sequences are visited longest first */
+  int partition_tokens;  /* P: tokens per partition at most */
+  int max_parts;         /* ceil(min(max_context_len, table capacity) / P) */
+  int longest_first;     /* 1 if workgroups start longest sequence / partition first */
   size_t workspace_bytes;
 } pkv_plan;
 
@@ -112,26 +113,27 @@ typedef struct {
  * 128, block_size 16 or 32) run on the MFMA kernel, which reads each KV tile
  * once for the whole group; everything else on the vector-ALU kernel.
  *
- * Grid PARTITIONS (the default): contexts are cut into partitions of partition_tokens
- * tokens (0: one partition per sequence unless the (sequence, head) units
- * are too few to give every compute unit about four workgroups, never
- * shorter than 512 tokens), one workgroup each, merged by the same second
- * kernel when a context has several.  An explicit partition_tokens must be a
- * multiple of 32 and of block_size and at most 256 units of the kernel (4096
- * tokens for 16-bit types with head_dim 128).  When the grid holds more than
- * about two rounds of resident workgroups, sequences are visited longest
- * first (stable within half-octave length bins), computed inside the
- * kernel for up to 1024 sequences and by a small order kernel beyond.
+ * Partitions: a context of L tokens is cut into n = ceil(L / P) partitions
+ * of equal size (rounded up to a multiple of max(32, block_size) tokens, the
+ * last one shorter), one workgroup per partition and head unit (a KV head
+ * for MFMA, a query head for VALU), merged by a second kernel when n > 1.
+ * partition_tokens == 0 lets the library choose P (one partition per
+ * sequence unless the (sequence, head) units are too few to give every
+ * compute unit about two workgroups, never below 512 tokens and at most 256
+ * units of the kernel: 4096 tokens for 16-bit types with head_dim 128); an
+ * explicit P must be a multiple of 32 and of block_size and at most 2^20.
  *
- * Grid BALANCED, on request (partition_tokens == -1, at most 1024
- * sequences): the tiles (16 tokens for MFMA, 4-32 for VALU) of every
- * (sequence, head) pair are laid end to end, sequence major, and cut into
- * equal ranges, one per wave the device holds at once; each wave walks its
- * range alone (no barrier, no LDS merge), so all waves start together and
- * finish together whatever the length mix.  A pair cut by a range boundary
- * leaves partial softmax states (running max, running sum, unnormalised
- * output, fp32) in the workspace, and a second kernel merges them; it also
- * writes the zero rows of empty sequences.
+ * Grid DIRECT: workgroups in (head unit, partition, sequence) order.  When
+ * the grid holds more than one round of resident workgroups and the batch
+ * at most 1024 sequences, each workgroup ranks the lengths itself and
+ * sequence row z is the z-th longest (half-octave bins, stable), so the
+ * longest sequences start first.  Grid PLANNED (PKV_GRID_AUTO picks it for
+ * such grids with more than 1024 sequences; at most 65535 partitions per
+ * sequence and 2^31 - 1 workgroups): a one-workgroup kernel first lists
+ * the (sequence, partition) items largest partition first (half-octave
+ * size bins, stable, a sequence's partitions together) in the workspace,
+ * and the decode grid follows the list, skipping the empty partitions of
+ * the direct grid.  In both the head unit is the fastest index.
  *
  * The plan only changes the order of floating-point operations inside one
  * output row, never which tokens contribute.  Writes the plan to *out (if
@@ -141,19 +143,21 @@ typedef struct {
  */
 int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_blocks_per_seq, int max_context_len,
-                             pkv_dtype dtype, int partition_tokens, int path, pkv_plan* out);
+                             pkv_dtype dtype, int partition_tokens, int path, int grid,
+                             pkv_plan* out);
 
 /*
  * Workspace bytes pkv_paged_attention_decode(_ex) needs for these sizes (the
- * plan's workspace_bytes): the partial states (head_dim + 2 fp32 each) of
- * the plan's grid and its small integer arrays, each part rounded to 16
- * bytes; 0 for a partitions grid with one partition per sequence and no
- * order kernel.  Returns (size_t)-1 for invalid sizes.  Host only.
+ * plan's workspace_bytes): with max_parts > 1 the partial states (head_dim
+ * + 2 fp32 per sequence, query head and partition), and with the planned
+ * grid its work list (16 bytes per sequence and partition, plus 8 bytes per
+ * sequence), each part rounded to 16 bytes; 0 for a direct grid with one
+ * partition per sequence.  Returns (size_t)-1 for invalid sizes.  Host only.
  */
 size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                            int head_dim, int block_size, int max_blocks_per_seq,
                                            int max_context_len, pkv_dtype dtype,
-                                           int partition_tokens, int path);
+                                           int partition_tokens, int path, int grid);
 
 /*
  * paged_attention_decode: out[s][h][:] = softmax(scale * K_s q[s][h]) V_s
@@ -206,9 +210,9 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Same as pkv_paged_attention_decode with an explicit partition size
- * (0 = library choice; see pkv_paged_attention_plan for the rules) and
- * kernel variant (pkv_decode_path).  Used for tuning sweeps and for the
- * contiguous-layout control. */
+ * (0 = library choice; see pkv_paged_attention_plan for the rules), kernel
+ * variant (pkv_decode_path) and grid (pkv_grid).  Used for tuning sweeps,
+ * tests of every grid and the contiguous-layout control. */
 int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_tables,
                                   const int32_t* context_lens, float scale, int num_seqs,
@@ -216,7 +220,7 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                                   int block_size, int num_blocks, int max_blocks_per_seq,
                                   int max_context_len, pkv_dtype dtype, void* workspace,
                                   size_t workspace_bytes, int partition_tokens, int path,
-                                  void* stream);
+                                  int grid, void* stream);
 
 /*
  * reshape_and_cache: for every token j with slot = slot_mapping[j] >= 0,

@@ -23,15 +23,14 @@ _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: P
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
 
-GRID_PARTITIONS, GRID_BALANCED = 0, 1
+GRID_AUTO, GRID_DIRECT, GRID_PLANNED = 0, 1, 2
 
 
 class _Plan(ctypes.Structure):
     """Mirror of ``pkv_plan`` in include/pagedkv.h."""
     _fields_ = [("path", ctypes.c_int), ("grid", ctypes.c_int),
                 ("partition_tokens", ctypes.c_int), ("max_parts", ctypes.c_int),
-                ("ranges", ctypes.c_int), ("longest_first", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("longest_first", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class NativeLibraryMissing(ImportError):
@@ -62,16 +61,16 @@ def _load():
     lib.pkv_supported.restype = i32
     lib.pkv_supported.argtypes = [i32, i32, i32]
     lib.pkv_paged_attention_workspace_bytes.restype = sz
-    lib.pkv_paged_attention_workspace_bytes.argtypes = [i32] * 10
+    lib.pkv_paged_attention_workspace_bytes.argtypes = [i32] * 11
     lib.pkv_paged_attention_plan.restype = i32
-    lib.pkv_paged_attention_plan.argtypes = [i32] * 10 + [ctypes.POINTER(_Plan)]
+    lib.pkv_paged_attention_plan.argtypes = [i32] * 11 + [ctypes.POINTER(_Plan)]
     lib.pkv_paged_attention_decode.restype = i32
     lib.pkv_paged_attention_decode.argtypes = [
         vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.pkv_paged_attention_decode_ex.restype = i32
     lib.pkv_paged_attention_decode_ex.argtypes = [
         vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
-        i32, i32, vp]
+        i32, i32, i32, vp]
     lib.pkv_reshape_and_cache.restype = i32
     lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_copy_blocks.restype = i32
@@ -127,24 +126,24 @@ def _dtype_code(dtype):
 
 
 def plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-         max_context_len, dtype, partition_tokens=0, path=PATH_AUTO):
+         max_context_len, dtype, partition_tokens=0, path=PATH_AUTO, grid=GRID_AUTO):
     """The plan of a decode call with these sizes, as a dict with the fields
-    of ``pkv_plan``: path, grid, partition_tokens, max_parts, ranges,
-    longest_first, workspace_bytes (see ``pkv_paged_attention_plan``)."""
+    of ``pkv_plan``: path, grid, partition_tokens, max_parts, longest_first,
+    workspace_bytes (see ``pkv_paged_attention_plan``)."""
     out = _Plan()
     st = lib.pkv_paged_attention_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                       max_blocks_per_seq, max_context_len, _dtype_code(dtype),
-                                      partition_tokens, path, ctypes.byref(out))
+                                      partition_tokens, path, grid, ctypes.byref(out))
     _check("paged_attention_plan", st)
     return {name: getattr(out, name) for name, _ in _Plan._fields_}
 
 
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, max_context_len, dtype, partition_tokens=0,
-                    path=PATH_AUTO) -> int:
+                    path=PATH_AUTO, grid=GRID_AUTO) -> int:
     n = lib.pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                 block_size, max_blocks_per_seq, max_context_len,
-                                                _dtype_code(dtype), partition_tokens, path)
+                                                _dtype_code(dtype), partition_tokens, path, grid)
     if n == _SIZE_MAX:
         raise ValueError("invalid sizes for the decode workspace")
     return int(n)
@@ -152,7 +151,7 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                            max_context_len, workspace=None, partition_tokens=0,
-                           path=PATH_AUTO, stream=None):
+                           path=PATH_AUTO, grid=GRID_AUTO, stream=None):
     """``out[s, h] = softmax(scale * K_s q[s, h]) V_s`` over each sequence's
     paged KV (see ``pkv_paged_attention_decode``).  ``max_context_len`` is a
     host-side bound of ``context_lens``.  ``workspace`` is a uint8 device
@@ -184,7 +183,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     if block_tables is not None and block_tables.shape[0] != num_seqs:
         raise ValueError("block_tables must have num_seqs rows")
     need = workspace_bytes(num_seqs, hq, hkv, hd, bs, max_blocks, int(max_context_len), q.dtype,
-                           partition_tokens, path)
+                           partition_tokens, path, grid)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
@@ -195,7 +194,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), tables_ptr, _ptr(context_lens),
             ctypes.c_float(scale), num_seqs, hq, hkv, hd, bs, nb, max_blocks,
             int(max_context_len), _DTYPE_CODE[q.dtype], ws_ptr, ws_len, int(partition_tokens),
-            int(path), _stream(q, stream))
+            int(path), int(grid), _stream(q, stream))
     _check("paged_attention_decode", st)
     return out
 

@@ -17,10 +17,11 @@ thread_local std::string g_last_error;
 
 constexpr int kPartAlign = 32;          // tokens; partitions are whole 32-token spans
 constexpr int kMinAutoPartition = 512;  // the library never splits finer than this
-constexpr int kWgPerCu = 4;             // split until about this many workgroups per CU
+constexpr int kWgPerCu = 2;             // split until about this many workgroups per CU
 constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxDevices = 64;
-constexpr int kBalancedRequest = -1;    // partition_tokens value that asks for the balanced grid
+constexpr int kMaxItemParts = 65535;    // a work item packs (part, n) into 16 bits each
+constexpr int kMaxPartition = 1 << 20;  // tokens; explicit partition sizes up to this
 
 int elem_size(pkv_dtype d) { return d == PKV_F32 ? 4 : 2; }
 bool dtype_ok(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
@@ -51,19 +52,17 @@ int compute_units() {
 // The kernel a decode call runs and how its grid divides the work.
 struct Plan {
   bool mfma = false;
-  int grid_mode = kGridPartitions;
-  int part_tokens = 0;   // partitions grid: tokens per partition
-  int max_parts = 1;     // partitions grid: partitions the grid covers per sequence
-  int ranges = 0;        // balanced grid: waves (4 per workgroup), one range each
-  int unit_group = 1;    // balanced grid: query heads per work unit
+  int part_tokens = 0;   // P: tokens per partition at most
+  int part_align = 32;   // partition sizes are multiples of this
+  int max_parts = 1;     // partitions per sequence at most
   int len_cap = 0;       // context lengths are clamped to this
-  bool sort = false;     // partitions grid: visit sequences longest first
-  bool sort_kernel = false;  // ... through the order kernel (large batches)
+  bool planned = false;  // work items listed largest first by the planning kernel
+  bool sorted = false;   // direct grid: each workgroup ranks the sequences by length
   int status = PKV_OK;
 };
 
-// Workgroups of the balanced kernel resident on the whole device (cached
-// per device and kernel; a fallback when the runtime cannot say).
+// Decode workgroups resident on the whole device (cached per device and
+// kernel; a fallback when the runtime cannot say).
 int resident_workgroups(bool mfma, Elem e, int head_dim, int block_size, int group) {
   constexpr int kKeys = 2 * 3 * 3 * 3 * 3;   // kernel x dtype x head_dim x block_size x GMAX
   static int cached[kMaxDevices][kKeys];
@@ -85,7 +84,7 @@ int resident_workgroups(bool mfma, Elem e, int head_dim, int block_size, int gro
 
 Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                int max_blocks_per_seq, int max_context_len, pkv_dtype dtype, int requested,
-               int path) {
+               int path, int grid) {
   Plan pl;
   const Elem e = to_elem(dtype);
   if (!decode_valu_supported(e, head_dim, block_size)) {
@@ -104,35 +103,14 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
   pl.len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
   const int unit = pl.mfma ? 16 : valu_unit_tokens(e, head_dim, block_size);
   const int units_per_seq = pl.mfma ? num_kv_heads : num_q_heads;
+  pl.part_align = block_size > kPartAlign ? block_size : kPartAlign;
 
-  // Balanced grid on request (partition_tokens == -1): equal shares of all
-  // tiles, one workgroup per resident slot, so every workgroup starts at
-  // once and ends at about the same time whatever the length mix.  It needs
-  // the tile prefix of the batch in LDS (at most kBalancedMaxSeqs
-  // sequences, an int total).
-  const int64_t seq_tiles = (pl.len_cap + unit - 1) / unit;
-  if (requested == kBalancedRequest) {
-    if (num_seqs > kBalancedMaxSeqs || (int64_t)num_seqs * seq_tiles >= (1ll << 31) - 1) {
-      pl.status = PKV_EUNSUPPORTED;
-      return pl;
-    }
-    pl.grid_mode = kGridBalanced;
-    pl.unit_group = pl.mfma ? group : 1;
-    // one range per resident wave, at most one per 4 tiles of the largest
-    // possible batch, a multiple of 32 (8 XCDs x 4 waves)
-    const int64_t waves = 4 * (int64_t)resident_workgroups(pl.mfma, e, head_dim, block_size, group);
-    const int64_t tiles_upper = (int64_t)num_seqs * units_per_seq * seq_tiles;
-    int64_t r = waves < tiles_upper / 4 ? waves : tiles_upper / 4;
-    r = r / 32 * 32;
-    pl.ranges = (int)(r < 32 ? 32 : r);
-    return pl;
-  }
-
-  // a wave handles at most 64 units of a partition
-  const int p_max = 256 * unit / kPartAlign * kPartAlign;
+  // the library's partitions give each of the 4 waves at most 64 units (one
+  // vector of table entries); an explicit size may take several passes
+  const int p_max = 256 * unit / pl.part_align * pl.part_align;
   int p;
   if (requested > 0) {
-    if (requested % kPartAlign || requested % block_size || requested > p_max) {
+    if (requested % pl.part_align || requested > kMaxPartition) {
       pl.status = PKV_EINVAL;
       return pl;
     }
@@ -144,56 +122,72 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
     const int64_t target = (int64_t)kWgPerCu * compute_units();
     const int64_t parts = units >= target ? 1 : (target + units - 1) / units;
     const int len = pl.len_cap > 0 ? pl.len_cap : 1;
-    p = round_up((int)((len + parts - 1) / parts), kPartAlign);
-    if (p < kMinAutoPartition) p = round_up(len < kMinAutoPartition ? len : kMinAutoPartition, kPartAlign);
+    p = round_up((int)((len + parts - 1) / parts), pl.part_align);
+    if (p < kMinAutoPartition)
+      p = round_up(len < kMinAutoPartition ? len : kMinAutoPartition, pl.part_align);
     if (p > p_max) p = p_max;
   }
   pl.part_tokens = p;
   pl.max_parts = pl.len_cap > 0 ? (pl.len_cap + p - 1) / p : 1;
-  // Longest first pays off once the grid is more than about two rounds of
-  // resident workgroups (the VALU kernel keeps 4 per compute unit, the MFMA
-  // kernel 3); with fewer, nearly every workgroup starts at once anyway.
-  const int64_t wgs = (int64_t)pl.max_parts * units_per_seq * num_seqs;
-  const int64_t resident = (int64_t)(pl.mfma ? 3 : 4) * compute_units();
-  pl.sort = num_seqs > 1 && wgs > 2 * resident;
-  pl.sort_kernel = pl.sort && num_seqs > kFusedOrderMax;
+  const int64_t direct_x = (int64_t)pl.max_parts * units_per_seq;
+  if (direct_x > INT32_MAX) {   // the direct grid's x is units * parts
+    pl.status = PKV_EUNSUPPORTED;
+    return pl;
+  }
+  // Longest first pays off once the grid holds more than one round of
+  // resident workgroups; with fewer, every workgroup starts at once anyway.  The direct grid ranks up to kFusedOrderMax sequences inside
+  // each workgroup (no extra launch); larger batches are planned.
+  const int64_t wgs = direct_x * num_seqs;
+  const bool plannable = wgs <= INT32_MAX && pl.max_parts <= kMaxItemParts;
+  const int64_t resident = resident_workgroups(pl.mfma, e, head_dim, block_size, group);
+  const bool longest_first = num_seqs > 1 && wgs > resident;
+  if (grid == PKV_GRID_PLANNED) {
+    if (!plannable) {
+      pl.status = PKV_EUNSUPPORTED;
+      return pl;
+    }
+    pl.planned = true;
+  } else if (longest_first) {
+    if (num_seqs <= kFusedOrderMax)
+      pl.sorted = true;
+    else if (grid == PKV_GRID_AUTO && plannable)
+      pl.planned = true;
+  }
   return pl;
 }
 
-// Workspace layout, each part 16-byte aligned:
-//  partitions grid: partial outputs [B][Hq][max_parts][HD] fp32 and partial
-//    (max, sum) [B][Hq][max_parts][2] fp32 (only with several partitions),
-//    then the sequence order [B] int32 (only with the order kernel);
-//  balanced grid: partial outputs [2*ranges][unit_group][HD] fp32, partial
-//    (max, sum) [2*ranges][unit_group][2] fp32, the tile prefix [B+1] int32.
+// Workspace layout, each part 16-byte aligned: with several partitions the
+// partial outputs [B][Hq][max_parts][HD] fp32 and the partial (max, sum)
+// [B][Hq][max_parts][2] fp32; then for the planned grid the planner's
+// scratch [2B] int32, the items [B * max_parts][4] int32 and their count.
 struct Layout {
-  size_t part_o = 0, part_ml = 0, extra = 0, total = 0;   // byte offsets, size
+  size_t part_o = 0, part_ml = 0, scratch = 0, items = 0, count = 0, total = 0;
 };
 
 size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
-Layout workspace_layout(int num_seqs, int num_q_heads, int head_dim, const Plan& pl) {
+Layout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                        const Plan& pl) {
   Layout lo;
-  size_t states = 0;
-  if (pl.grid_mode == kGridBalanced)
-    states = (size_t)2 * pl.ranges * pl.unit_group;
-  else if (pl.max_parts > 1)
-    states = (size_t)num_seqs * num_q_heads * pl.max_parts;
+  const size_t states = pl.max_parts > 1 ? (size_t)num_seqs * num_q_heads * pl.max_parts : 0;
   lo.part_o = 0;
   lo.part_ml = align16(states * head_dim * sizeof(float));
-  lo.extra = lo.part_ml + align16(states * 2 * sizeof(float));
-  size_t extra_bytes = 0;
-  if (pl.grid_mode == kGridBalanced)
-    extra_bytes = (size_t)(num_seqs + 1) * sizeof(int32_t);
-  else if (pl.sort_kernel)
-    extra_bytes = (size_t)num_seqs * sizeof(int32_t);
-  lo.total = extra_bytes ? lo.extra + align16(extra_bytes) : (states ? lo.extra : 0);
+  lo.scratch = lo.part_ml + align16(states * 2 * sizeof(float));
+  if (!pl.planned) {
+    lo.total = lo.scratch;
+    return lo;
+  }
+  lo.items = lo.scratch + align16((size_t)2 * num_seqs * sizeof(int32_t));
+  lo.count = lo.items + (size_t)num_seqs * pl.max_parts * 4 * sizeof(int32_t);
+  lo.total = lo.count + 16;
   return lo;
 }
 
-size_t workspace_for(int num_seqs, int num_q_heads, int head_dim, const Plan& pl) {
-  return workspace_layout(num_seqs, num_q_heads, head_dim, pl).total;
+size_t workspace_for(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                     const Plan& pl) {
+  return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, pl).total;
 }
+
 
 }  // namespace
 
@@ -222,37 +216,37 @@ int pkv_supported(pkv_dtype dtype, int head_dim, int block_size) {
 size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                            int head_dim, int block_size, int max_blocks_per_seq,
                                            int max_context_len, pkv_dtype dtype,
-                                           int partition_tokens, int path) {
+                                           int partition_tokens, int path, int grid) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      partition_tokens < kBalancedRequest || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
-      num_q_heads % num_kv_heads)
+      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED || num_q_heads % num_kv_heads)
     return (size_t)-1;
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                            max_blocks_per_seq, max_context_len, dtype, partition_tokens, path);
+                            max_blocks_per_seq, max_context_len, dtype, partition_tokens, path, grid);
   if (pl.status != PKV_OK) return (size_t)-1;
-  return workspace_for(num_seqs, num_q_heads, head_dim, pl);
+  return workspace_for(num_seqs, num_q_heads, num_kv_heads, head_dim, pl);
 }
 
 int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_blocks_per_seq, int max_context_len,
-                             pkv_dtype dtype, int partition_tokens, int path, pkv_plan* out) {
+                             pkv_dtype dtype, int partition_tokens, int path, int grid,
+                             pkv_plan* out) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      partition_tokens < kBalancedRequest || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
-      num_q_heads % num_kv_heads)
+      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED || num_q_heads % num_kv_heads)
     return PKV_EINVAL;
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                            max_blocks_per_seq, max_context_len, dtype, partition_tokens, path);
+                            max_blocks_per_seq, max_context_len, dtype, partition_tokens, path, grid);
   if (pl.status != PKV_OK) return pl.status;
   if (out) {
     out->path = pl.mfma ? PKV_PATH_MFMA : PKV_PATH_VALU;
-    out->grid = pl.grid_mode == kGridBalanced ? PKV_GRID_BALANCED : PKV_GRID_PARTITIONS;
-    out->partition_tokens = pl.grid_mode == kGridBalanced ? 0 : pl.part_tokens;
-    out->max_parts = pl.grid_mode == kGridBalanced ? 0 : pl.max_parts;
-    out->ranges = pl.ranges;
-    out->longest_first = pl.sort ? 1 : 0;
-    out->workspace_bytes = workspace_for(num_seqs, num_q_heads, head_dim, pl);
+    out->grid = pl.planned ? PKV_GRID_PLANNED : PKV_GRID_DIRECT;
+    out->partition_tokens = pl.part_tokens;
+    out->max_parts = pl.max_parts;
+    out->longest_first = pl.planned || pl.sorted ? 1 : 0;
+    out->workspace_bytes = workspace_for(num_seqs, num_q_heads, num_kv_heads, head_dim, pl);
   }
   return PKV_OK;
 }
@@ -263,12 +257,12 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                                   int num_q_heads, int num_kv_heads, int head_dim,
                                   int block_size, int num_blocks, int max_blocks_per_seq,
                                   int max_context_len, pkv_dtype dtype, void* workspace,
-                                  size_t workspace_bytes, int partition, int path,
+                                  size_t workspace_bytes, int partition, int path, int grid,
                                   void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0 || partition < kBalancedRequest || path < PKV_PATH_AUTO ||
-      path > PKV_PATH_CONTIGUOUS)
+      max_context_len < 0 || partition < 0 || path < PKV_PATH_AUTO ||
+      path > PKV_PATH_CONTIGUOUS || grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED)
     return PKV_EINVAL;
   if (num_q_heads % num_kv_heads) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
@@ -281,9 +275,9 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
 
   const Elem e = to_elem(dtype);
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                            max_blocks_per_seq, max_context_len, dtype, partition, path);
+                            max_blocks_per_seq, max_context_len, dtype, partition, path, grid);
   if (pl.status != PKV_OK) return pl.status;
-  const Layout lo = workspace_layout(num_seqs, num_q_heads, head_dim, pl);
+  const Layout lo = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, pl);
   const size_t need = lo.total;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
@@ -297,14 +291,12 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   char* ws = static_cast<char*>(workspace);
-  a.part_o = need ? reinterpret_cast<float*>(ws + lo.part_o) : nullptr;
-  a.part_ml = need ? reinterpret_cast<float*>(ws + lo.part_ml) : nullptr;
-  a.seq_order = pl.sort_kernel ? reinterpret_cast<const int32_t*>(ws + lo.extra) : nullptr;
-  a.tile_start = pl.grid_mode == kGridBalanced ? reinterpret_cast<int32_t*>(ws + lo.extra) : nullptr;
-  a.order_mode = pl.sort_kernel ? 1 : (pl.sort ? 2 : 0);
-  a.grid_mode = pl.grid_mode;
-  a.ranges = pl.ranges;
-  a.unit_group = pl.unit_group;
+  a.part_o = pl.max_parts > 1 ? reinterpret_cast<float*>(ws + lo.part_o) : nullptr;
+  a.part_ml = pl.max_parts > 1 ? reinterpret_cast<float*>(ws + lo.part_ml) : nullptr;
+  a.items = pl.planned ? reinterpret_cast<const int32_t*>(ws + lo.items) : nullptr;
+  a.item_count = pl.planned ? reinterpret_cast<const int32_t*>(ws + lo.count) : nullptr;
+  a.planned = pl.planned ? 1 : 0;
+  a.sorted = pl.sorted ? 1 : 0;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -314,20 +306,23 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
   a.max_blocks = max_blocks_per_seq;
   a.len_cap = pl.len_cap;
   a.part_tokens = pl.part_tokens;
+  a.part_align = pl.part_align;
   a.max_parts = pl.max_parts;
   a.contiguous = contiguous ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (pl.sort_kernel) {
-    err = launch_seq_order(context_lens, num_seqs, pl.len_cap,
-                           const_cast<int32_t*>(a.seq_order), st);
+  if (pl.planned) {
+    err = launch_plan_items(context_lens, num_seqs, pl.len_cap, pl.part_tokens, pl.part_align,
+                            reinterpret_cast<int32_t*>(ws + lo.scratch),
+                            reinterpret_cast<int32_t*>(ws + lo.items),
+                            reinterpret_cast<int32_t*>(ws + lo.count), st);
     if (err != hipSuccess) return fail_hip(err);
   }
   err = use_mfma ? launch_decode_mfma(e, head_dim, block_size, a, st)
                  : launch_decode_valu(e, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
-  if (pl.grid_mode == kGridBalanced || pl.max_parts > 1) {
+  if (pl.max_parts > 1) {
     err = launch_decode_reduce(e, head_dim, a, st);
     if (err != hipSuccess) return fail_hip(err);
   }
@@ -344,7 +339,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                        scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                        block_size, num_blocks, max_blocks_per_seq,
                                        max_context_len, dtype, workspace, workspace_bytes, 0,
-                                       PKV_PATH_AUTO, stream);
+                                       PKV_PATH_AUTO, PKV_GRID_AUTO, stream);
 }
 
 int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -38,10 +38,11 @@
 // KV head h / G.
 #include "common.h"
 #include "decode.h"
-#include "order.h"
-#include "balance.h"
 
 namespace pkv {
+
+// Register stages of the tile pipeline (see mfma_accumulate).
+constexpr int kMfmaStages = 2;
 
 template <typename E>
 struct MfmaOps;
@@ -132,11 +133,22 @@ __device__ inline void mfma_load_q(const DecodeArgs& a, int s, int g, u32x4 (*q)
 }
 
 // Fold tiles ta + first, ta + first + stride, ... (< tb) of KV head g of
-// sequence s (context length L > 0; tile = 16 tokens) into the calling
-// wave's state, with Q^T read from q (LDS).
-template <typename E, int HD, int BS>
+// sequence s (tile = 16 tokens; tokens at or past L > 0 are masked) into
+// the calling wave's state, with Q^T read from q (LDS).
+// The physical blocks of the first pass of tiles ta + first + stride * i
+// (lane i), read along with the query: the index is clamped to the table
+// row, so the load is in bounds whatever the length.
+template <int BS>
+__device__ inline int mfma_first_blocks(const DecodeArgs& a, int s, int ta, int first,
+                                        int stride) {
+  const int lane = threadIdx.x % kWave;
+  const int blk = min((ta + first + stride * lane) / (BS / 16), a.max_blocks - 1);
+  return a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
+}
+
+template <typename E, int HD, int BS, int NS = kMfmaStages>
 __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
-                                       int first, int stride, const u32x4 (*q)[kWave],
+                                       int first, int stride, int tbl0, const u32x4 (*q)[kWave],
                                        MfmaState<HD / 16>& st) {
   using T = typename E::storage;
   using Ops = MfmaOps<E>;
@@ -169,8 +181,8 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
   // passes of at most 64 of the wave's tiles: their table entries fit one VGPR
   for (int pass = ta + first; pass < tb; pass += kWave * stride) {
     const int mine = min(kWave, (tb - pass + stride - 1) / stride);
-    int tbl;
-    {
+    int tbl = tbl0;
+    if (pass != ta + first) {
       const int blk = min((pass + stride * lane) / TPB, a.max_blocks - 1);
       tbl = a.contiguous ? s * a.max_blocks + blk : table[blk];
     }
@@ -178,17 +190,19 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
     // issue the loads of the wave's i-th tile of the pass: K in the A layout
     // (token row n, dims 32*kk + 8*g4 .. +8), V row-wise (tokens 4*g4 + r,
     // dims n*DPL .. +DPL)
+    // (tiles i >= mine get an empty descriptor: their loads return zeros
+    // without a memory access, so every step issues the same loads)
     auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VW]) {
+      const bool live = i < mine;
       const int u = pass + stride * i;
-      int phys = lane_value(tbl, i);
-      if ((unsigned)phys >= (unsigned)a.num_blocks) {
-        bad = 1;
-        phys = 0;
-      }
+      int phys = lane_value(tbl, i < kWave ? i : kWave - 1);
+      if (live && (unsigned)phys >= (unsigned)a.num_blocks) bad = 1;
+      if (!live || (unsigned)phys >= (unsigned)a.num_blocks) phys = 0;
       const size_t toff = (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * HD * sizeof(T);
       constexpr uint32_t kTileBytes = 16 * HD * sizeof(T);
-      const rsrc_t kt = make_rsrc(kbase + toff, kTileBytes);
-      const rsrc_t vt = make_rsrc(vbase + toff, kTileBytes);
+      const uint32_t nbytes = live ? kTileBytes : 0u;
+      const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
+      const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
 #pragma unroll
@@ -264,26 +278,18 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
       }
     };
 
-    // two register buffers: the loads of tile i+1 are in flight while tile i
-    // is computed
-    u32x4 kA[KSTEPS], kB[KSTEPS];
-    uint32_t vA[4][VW], vB[4][VW];
-    load_tile(0, kA, vA);
-    int i = 0;
-    // steady state: the loads of the next tile are always issued, so the
-    // wait before each tile's math covers only that tile's own loads
-    for (; i + 2 < mine; i += 2) {
-      load_tile(i + 1, kB, vB);
-      compute_tile(i, kA, vA);
-      load_tile(i + 2, kA, vA);
-      compute_tile(i + 1, kB, vB);
-    }
-    if (i + 1 < mine) {
-      load_tile(i + 1, kB, vB);
-      compute_tile(i, kA, vA);
-      compute_tile(i + 1, kB, vB);
-    } else {
-      compute_tile(i, kA, vA);
+    // NS register stages: the loads of tiles i+1 .. i+NS-1 are in flight
+    // while tile i is computed
+    u32x4 kb[NS][KSTEPS];
+    uint32_t vb[NS][4][VW];
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
+    for (int i0 = 0; i0 < mine; i0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        load_tile(i0 + j + NS - 1, kb[(j + NS - 1) % NS], vb[(j + NS - 1) % NS]);
+        if (i0 + j < mine) compute_tile(i0 + j, kb[j], vb[j]);
+      }
     }
   }
 #pragma unroll
@@ -302,27 +308,26 @@ __device__ inline void mfma_state_init(MfmaState<DPL>& st) {
   st.bad = 0;
 }
 
-// Attention of the G query heads of KV head g of sequence s (context length
-// L > 0) over its 16-token tiles [ta, tb), by the four waves of the
+// Attention of the G query heads of KV head g of sequence s over its
+// 16-token tiles [ta, tb) (tokens at or past L > 0 masked), by the four waves of the
 // workgroup (tile round-robin), merged in LDS.  The merged states are
 // normalised and rounded into `out` (the group's first head) when `out` is
 // not null, else stored unnormalised to the partial states
 // state0 + hh * hh_stride (hh < G).
 template <typename E, int HD, int BS, int GMAX>
 __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
-                                  typename E::storage* out, size_t state0, size_t hh_stride,
-                                  MfmaShared<HD, GMAX>& sm) {
+                                  int tbl0, typename E::storage* out, size_t state0,
+                                  size_t hh_stride, MfmaShared<HD, GMAX>& sm) {
   constexpr int NW = 4;
   constexpr int DPL = HD / 16;
   const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
   const int n = lane & 15, g4 = lane >> 4;
   const int G = a.group;
 
-  if (wave == 0) mfma_load_q<E, HD>(a, s, g, sm.q);
   MfmaState<DPL> st;
   mfma_state_init(st);
   __syncthreads();   // Q^T is in LDS
-  mfma_accumulate<E, HD, BS>(a, s, g, L, ta, tb, wave, NW, sm.q, st);
+  mfma_accumulate<E, HD, BS>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q, st);
 
   // the four token groups of a head column hold partial sums of l
   const float l = rows_sum(st.l);
@@ -371,110 +376,37 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
   __syncthreads();   // LDS is free for the next piece
 }
 
-// Partitions mode: grid (max_parts, Hkv, B); partition `part` of KV head g
-// of the sequence of grid row z.
+// One workgroup per (work item, KV head g): the grid is described with
+// DecodeArgs.
 template <typename E, int HD, int BS, int GMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
     DecodeArgs a) {
   using T = typename E::storage;
-  __shared__ OrderScratch sm_order;
   __shared__ MfmaShared<HD, GMAX> sm;
-  const int part = blockIdx.x, g = blockIdx.y, G = a.group;
-  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
-                                                            a.len_cap, blockIdx.z, sm_order)
-                                          : sequence_of(a, blockIdx.z));
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  __shared__ OrderScratch sm_order;
+  const WorkItem w = work_item(a, a.num_kv_heads, sm_order);
+  if (!w.valid) return;
+  const int s = uniform(w.s), g = w.unit, G = a.group;
+  const int wave = uniform(threadIdx.x / kWave);
   T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G) * HD;
-  const int P = a.part_tokens;
-  if (L == 0) {
-    if (part == 0)
-      for (int i = threadIdx.x; i < G * HD; i += 256) out[i] = E::round(0.f);
+  if (w.t1 <= w.t0) {   // empty context: zero row
+    for (int i = threadIdx.x; i < G * HD; i += 256) out[i] = E::round(0.f);
     return;
   }
-  if (part * P >= L) return;
-  const int nparts = (L + P - 1) / P;
-  const int ta = part * P / 16;
-  const int tb = (min(L, part * P + P) + 15) / 16;
-  const size_t state0 = ((size_t)s * a.num_q_heads + (size_t)g * G) * a.max_parts + part;
-  mfma_piece<E, HD, BS, GMAX>(a, s, g, L, ta, tb, nparts == 1 ? out : nullptr, state0,
+  // the query heads and the blocks of the first tiles are read together
+  const int ta = w.t0 / 16, tb = (w.t1 + 15) / 16;
+  const int tbl0 = mfma_first_blocks<BS>(a, s, ta, wave, 4);
+  if (wave == 0) mfma_load_q<E, HD>(a, s, g, sm.q);
+  const size_t state0 = ((size_t)s * a.num_q_heads + (size_t)g * G) * a.max_parts + w.part;
+  mfma_piece<E, HD, BS, GMAX>(a, s, g, w.t1, ta, tb, tbl0, w.n == 1 ? out : nullptr, state0,
                               a.max_parts, sm);
-}
-
-// Balanced mode: every wave of the grid owns one equal range of the tiles
-// of all (sequence, KV head) units laid end to end (sequence major) and
-// walks its pieces alone, with Q^T in its own LDS slot: no barrier after the
-// tile prefix, so all waves stream from the first cycle to about the same
-// last cycle.  Each wave stores its G heads straight from registers: lane
-// (n, g4) holds, for r < 4, the DPL consecutive dims (4*g4 + r)*DPL .. of
-// head n.
-template <typename E, int HD, int BS, int GMAX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
-decode_mfma_balanced_kernel(DecodeArgs a) {
-  using T = typename E::storage;
-  constexpr int DPL = HD / 16;
-  __shared__ TilePrefix sm_prefix;
-  __shared__ u32x4 sm_q[4][HD / 32][kWave];
-  tile_prefix(a, 16, sm_prefix);
-  const int B = a.num_seqs, G = a.group;
-  const int Ts = sm_prefix.start[B];
-  const int64_t T_all = (int64_t)Ts * a.num_kv_heads;
-  const int R = effective_ranges(T_all, a.ranges);
-  const int wave = uniform(threadIdx.x / kWave);
-  const int w = range_of_wave(blockIdx.x, wave, R, a.ranges);
-  if (w < 0) return;
-  const int lane = threadIdx.x % kWave, n = lane & 15, g4 = lane >> 4;
-  RangeWalk walk{range_begin(T_all, w, R), range_begin(T_all, w + 1, R),
-                 range_begin(T_all, w, R), a.num_kv_heads, B, w};
-  Piece p;
-  while (walk.next(sm_prefix, p)) {
-    const int s = uniform(p.s), g = uniform(p.hu);
-    int L = a.context_lens[s];
-    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-    __asm__ volatile("" ::: "memory");   // the previous piece's Q^T reads come first
-    mfma_load_q<E, HD>(a, s, g, sm_q[wave]);
-    MfmaState<DPL> st;
-    mfma_state_init(st);
-    mfma_accumulate<E, HD, BS>(a, s, g, L, uniform(p.ta), uniform(p.tb), 0, 1, sm_q[wave], st);
-    const float l = rows_sum(st.l);
-    if (n < G) {
-      const bool bad = __any(st.bad);
-      if (p.whole) {
-        T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G + n) * HD;
-        const float inv = 1.f / l;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v[DPL];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) v[e] = bad ? __builtin_nanf("") : st.acc[e][r] * inv;
-          store_rounded<E, DPL>(out + (4 * g4 + r) * DPL, v);
-        }
-      } else {
-        const size_t stt = (size_t)p.slot * G + n;
-        float* po = a.part_o + stt * HD;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int e = 0; e < DPL; e += 4)
-            *reinterpret_cast<f32x4*>(po + (4 * g4 + r) * DPL + e) =
-                bad ? f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                            __builtin_nanf("")}
-                    : f32x4{st.acc[e][r], st.acc[e + 1][r], st.acc[e + 2][r], st.acc[e + 3][r]};
-        if (g4 == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * stt) = f32x2{st.m, l};
-      }
-    }
-  }
 }
 
 template <typename E, int HD, int BS, int GMAX>
 static void launch_mfma_g(const DecodeArgs& a, hipStream_t st) {
-  if (a.grid_mode == kGridBalanced) {
-    hipLaunchKernelGGL((decode_mfma_balanced_kernel<E, HD, BS, GMAX>), dim3(a.ranges / 4), dim3(256),
-                       0, st, a);
-  } else {
-    dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, GMAX>), grid, dim3(256), 0, st, a);
-  }
+  const dim3 grid = a.planned ? dim3(a.num_kv_heads * a.max_parts * a.num_seqs)
+                              : dim3(a.num_kv_heads * a.max_parts, 1, a.num_seqs);
+  hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, GMAX>), grid, dim3(256), 0, st, a);
 }
 
 template <typename E, int HD, int BS>
@@ -491,9 +423,9 @@ static hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t st) {
 template <typename E, int HD, int BS>
 static int occupancy_t(int group) {
   int n = 0;
-  const void* f = group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<E, HD, BS, 4>)
-                  : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<E, HD, BS, 8>)
-                               : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<E, HD, BS, 16>);
+  const void* f = group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, HD, BS, 4>)
+                  : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, HD, BS, 8>)
+                               : reinterpret_cast<const void*>(&decode_mfma_kernel<E, HD, BS, 16>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess) return 0;
   return n;
 }

@@ -8,13 +8,16 @@
 // merge).  The pages do not describe this step; it is the split-context
 // reduce of a paged decode kernel for long contexts.
 //
+// A second kernel merges them: the states of one launch are visible to the
+// next launch on the stream without any fence inside the decode kernel (a
+// device-wide fence per partition costs far more than the launch).
+//
 // One wave per (sequence, query head), four per workgroup.  Lane j owns the
 // weight of state c0 + j of the current chunk of 64 states.  The partial
 // outputs are read as float4: one load instruction covers 64 / (HD/4)
 // states side by side, so all of a chunk's loads are issued back to back,
 // and the states held by different lane groups are summed with shuffles at
-// the end.  The states come from the partitions of the partition grid, or
-// from the ranges that cut a unit in the balanced grid.
+// the end.
 #include "common.h"
 #include "decode.h"
 
@@ -76,7 +79,8 @@ __device__ inline void merge_states(const DecodeArgs& a, int n, StateOf state,
   }
 }
 
-// Partitions mode: one wave per (sequence, query head), four per workgroup.
+// One wave per (sequence, query head), four per workgroup; contexts of one
+// partition were written by the decode kernel.
 template <typename E, int HD>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   using T = typename E::storage;
@@ -85,53 +89,17 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   if (h >= a.num_q_heads) return;
   int L = a.context_lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;   // the partition kernel wrote the output itself
+  const int nparts = num_parts(L, a.part_tokens);
+  if (nparts <= 1) return;
   const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
   T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
   merge_states<E, HD>(a, nparts, [&](int j) { return base + j; }, out);
 }
 
-// Balanced mode: one wave per (sequence, query head).  The head's unit
-// covers tiles [S, E) of the end-to-end layout; the ranges wf .. wl that
-// cut it left one state each (wf's last piece, the others' first), and a
-// unit inside a single range was written by the decode kernel.  Sequences
-// with no tokens get a zero row here.
-template <typename E, int HD>
-__global__ __launch_bounds__(256) void decode_reduce_balanced_kernel(DecodeArgs a) {
-  using T = typename E::storage;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
-  if (h >= a.num_q_heads) return;
-  T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
-  const int ug = a.unit_group;                 // query heads per unit
-  const int U = a.num_q_heads / ug;            // units per sequence
-  const int hu = h / ug, hh = h % ug;
-  const int Ts = a.tile_start[a.num_seqs];
-  const int nt = a.tile_start[s + 1] - a.tile_start[s];
-  const int64_t S = (int64_t)U * a.tile_start[s] + (int64_t)hu * nt;
-  const int64_t E_ = S + nt;
-  if (nt == 0) {
-    for (int d = lane; d < HD; d += kWave) out[d] = E::round(0.f);
-    return;
-  }
-  const int64_t T_all = (int64_t)Ts * U;
-  const int R = effective_ranges(T_all, a.ranges);
-  const int wf = range_of(S, T_all, R), wl = range_of(E_ - 1, T_all, R);
-  if (wf == wl) return;
-  const int first_slot = 2 * wf + (S > range_begin(T_all, wf, R) ? 1 : 0);
-  merge_states<E, HD>(
-      a, wl - wf + 1,
-      [&](int j) { return (size_t)(j == 0 ? first_slot : 2 * (wf + j)) * ug + hh; }, out);
-}
-
 template <typename E, int HD>
 static hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
   dim3 grid((a.num_q_heads + 3) / 4, a.num_seqs);
-  if (a.grid_mode == kGridBalanced)
-    hipLaunchKernelGGL((decode_reduce_balanced_kernel<E, HD>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_reduce_kernel<E, HD>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_reduce_kernel<E, HD>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -27,8 +27,6 @@
 // each partition stores (m, l, o) in fp32 and attn_reduce.hip merges them.
 #include "common.h"
 #include "decode.h"
-#include "order.h"
-#include "balance.h"
 
 namespace pkv {
 
@@ -91,8 +89,8 @@ __device__ inline ValuMeta valu_meta(const DecodeArgs& a, int s, int h, int ta, 
 }
 
 // Fold units ta + first, ta + first + stride, ... (< tb) of query head h of
-// sequence s (context length L > 0; unit = UT tokens) into the calling
-// wave's state, given the piece's ValuMeta.  Row group `row` of the wave
+// sequence s (unit = UT tokens; tokens at or past L > 0 are masked) into the
+// calling wave's state, given the piece's ValuMeta.  Row group `row` of the wave
 // sees every RPI-th token.
 template <typename E, int HD, int BS>
 __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
@@ -275,13 +273,13 @@ __device__ inline void valu_emit(float M, float Ls, float* O, bool bad, int col,
   }
 }
 
-// Attention of query head h of sequence s (context length L > 0) over its
-// units [ta, tb), by the four waves of the workgroup (unit round-robin),
+// Attention of query head h of sequence s over its units [ta, tb) (tokens
+// at or past L > 0 masked), by the four waves of the workgroup (unit round-robin),
 // merged in LDS.  Result as in valu_emit.
 template <typename E, int HD, int BS>
 __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
-                                  typename E::storage* out, float* po, float* pml,
-                                  ValuShared<HD>& sm) {
+                                  const ValuMeta& meta, typename E::storage* out, float* po,
+                                  float* pml, ValuShared<HD>& sm) {
   using Tl = ValuTiling<E, HD, BS>;
   constexpr int VEC = Tl::VEC, LPR = Tl::LPR;
   constexpr int NW = 4;
@@ -293,7 +291,6 @@ __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int 
 #pragma unroll
   for (int e = 0; e < VEC; ++e) st.o[e] = 0.f;
   st.bad = 0;
-  const ValuMeta meta = valu_meta<E, HD, BS>(a, s, h, ta, wave, NW);
   valu_accumulate<E, HD, BS>(a, s, h, L, ta, tb, wave, NW, meta, st);
   valu_row_merge<VEC, LPR>(st);
 
@@ -339,103 +336,37 @@ __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int 
   __syncthreads();   // the LDS states are free for the next piece
 }
 
-// Partitions mode: grid (max_parts, Hq, B); partition `part` of query head
-// h of the sequence of grid row z.
+// One workgroup per (work item, query head h): the grid is described with
+// DecodeArgs.
 template <typename E, int HD, int BS>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   using T = typename E::storage;
   constexpr int UT = ValuTiling<E, HD, BS>::UT;
-  __shared__ OrderScratch sm_order;
   __shared__ ValuShared<HD> sm;
-  const int part = blockIdx.x, h = blockIdx.y;
-  const int s = uniform(a.order_mode == 2 ? sorted_sequence(a.context_lens, a.num_seqs,
-                                                            a.len_cap, blockIdx.z, sm_order)
-                                          : sequence_of(a, blockIdx.z));
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  __shared__ OrderScratch sm_order;
+  const WorkItem w = work_item(a, a.num_q_heads, sm_order);
+  if (!w.valid) return;
+  const int s = uniform(w.s), h = w.unit;
   T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
-  const int P = a.part_tokens;
-  if (L == 0) {
-    if (part == 0)
-      for (int d = threadIdx.x; d < HD; d += 256) out[d] = E::round(0.f);
+  if (w.t1 <= w.t0) {   // empty context: zero row
+    for (int d = threadIdx.x; d < HD; d += 256) out[d] = E::round(0.f);
     return;
   }
-  if (part * P >= L) return;
-  const int nparts = (L + P - 1) / P;
-  const int ta = part * P / UT;
-  const int tb = (min(L, part * P + P) + UT - 1) / UT;
-  const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + part;
-  valu_piece<E, HD, BS>(a, s, h, L, ta, tb, nparts == 1 ? out : nullptr,
+  // the query slice and the blocks of the first units are read together
+  const int ta = w.t0 / UT, tb = (w.t1 + UT - 1) / UT;
+  const ValuMeta meta = valu_meta<E, HD, BS>(a, s, h, ta, uniform(threadIdx.x / kWave), 4);
+  const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + w.part;
+  valu_piece<E, HD, BS>(a, s, h, w.t1, ta, tb, meta, w.n == 1 ? out : nullptr,
                         a.part_o + pidx * HD, a.part_ml + 2 * pidx, sm);
-}
-
-// Balanced mode: every wave of the grid owns one equal range of the unit
-// tiles laid end to end (sequence major) and walks its pieces alone: no
-// barrier and no LDS after the tile prefix, so all waves stream from the
-// first cycle to about the same last cycle.
-template <typename E, int HD, int BS>
-__global__ __launch_bounds__(256) void decode_valu_balanced_kernel(DecodeArgs a) {
-  using T = typename E::storage;
-  using Tl = ValuTiling<E, HD, BS>;
-  constexpr int VEC = Tl::VEC, LPR = Tl::LPR, UT = Tl::UT;
-  __shared__ TilePrefix sm_prefix;
-  tile_prefix(a, UT, sm_prefix);
-  const int B = a.num_seqs;
-  const int Ts = sm_prefix.start[B];
-  const int64_t T_all = (int64_t)Ts * a.num_q_heads;
-  const int R = effective_ranges(T_all, a.ranges);
-  const int w = range_of_wave(blockIdx.x, uniform(threadIdx.x / kWave), R, a.ranges);
-  if (w < 0) return;
-  const int lane = threadIdx.x % kWave, row = lane / LPR, col = lane % LPR;
-  RangeWalk walk{range_begin(T_all, w, R), range_begin(T_all, w + 1, R),
-                 range_begin(T_all, w, R), a.num_q_heads, B, w};
-  // the next piece's length, query slice and first table entries are read
-  // while the current piece streams, so a piece starts with its tile loads
-  Piece p, pn;
-  if (!walk.next(sm_prefix, p)) return;
-  ValuMeta meta = valu_meta<E, HD, BS>(a, uniform(p.s), uniform(p.hu), uniform(p.ta), 0, 1);
-  int L = a.context_lens[uniform(p.s)];
-  for (;;) {
-    const bool more = walk.next(sm_prefix, pn);
-    ValuMeta meta_n = meta;
-    int L_n = 0;
-    if (more) {
-      meta_n = valu_meta<E, HD, BS>(a, uniform(pn.s), uniform(pn.hu), uniform(pn.ta), 0, 1);
-      L_n = a.context_lens[uniform(pn.s)];
-    }
-    const int s = uniform(p.s), h = uniform(p.hu);
-    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-    ValuState<VEC> st;
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) st.o[e] = 0.f;
-    st.bad = 0;
-    valu_accumulate<E, HD, BS>(a, s, h, L, uniform(p.ta), uniform(p.tb), 0, 1, meta, st);
-    valu_row_merge<VEC, LPR>(st);
-    if (row == 0) {
-      T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;
-      valu_emit<E, VEC>(st.m, st.l, st.o, __any(st.bad), col, p.whole ? out : nullptr,
-                        a.part_o + (size_t)p.slot * HD, a.part_ml + 2 * (size_t)p.slot);
-    }
-    if (!more) break;
-    p = pn;
-    meta = meta_n;
-    L = L_n;
-  }
 }
 
 // ------------------------------------------------------------------ dispatch
 
 template <typename E, int HD, int BS>
 static hipError_t launch_valu_t(const DecodeArgs& a, hipStream_t st) {
-  if (a.grid_mode == kGridBalanced) {
-    hipLaunchKernelGGL((decode_valu_balanced_kernel<E, HD, BS>), dim3(a.ranges / 4), dim3(256), 0, st,
-                       a);
-  } else {
-    dim3 grid(a.max_parts, a.num_q_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_valu_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
-  }
+  const dim3 grid = a.planned ? dim3(a.num_q_heads * a.max_parts * a.num_seqs)
+                              : dim3(a.num_q_heads * a.max_parts, 1, a.num_seqs);
+  hipLaunchKernelGGL((decode_valu_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -443,7 +374,7 @@ template <typename E, int HD, int BS>
 static int occupancy_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_valu_balanced_kernel<E, HD, BS>), 256, 0) !=
+          &n, reinterpret_cast<const void*>(&decode_valu_kernel<E, HD, BS>), 256, 0) !=
       hipSuccess)
     return 0;
   return n;

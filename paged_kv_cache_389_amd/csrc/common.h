@@ -7,6 +7,7 @@
 namespace pkv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -218,5 +219,17 @@ __device__ inline int lane_value(int v, int lane) { return __builtin_amdgcn_read
 
 // Scalar (wave-uniform) copy of a value.
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Read of an int at a wave-uniform address that nothing writes during the
+// kernel, through the constant address space so that it is issued as a
+// scalar-memory read: its wait is counted apart from the vector loads
+// issued after it, which therefore need not wait for it.
+__device__ inline int load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+// Four ints at a 16-byte aligned uniform address, the same way.
+__device__ inline i32x4 load_uniform4(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) i32x4*)p;
+}
 
 }  // namespace pkv

@@ -5,21 +5,34 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+#include "order.h"
+
 namespace pkv {
 
-// How the decode grid divides the work.
-//  kGridPartitions: one workgroup per (partition, head unit, sequence); a
-//    partition is part_tokens tokens; several partitions per sequence are
-//    merged by the partition reduce.
-//  kGridBalanced: a fixed number of workgroups (about the resident count),
-//    each streaming an equal share of all tiles of all (head unit, sequence)
-//    pairs laid end to end; a unit cut by a share boundary leaves partial
-//    states in its workgroups' slots, merged by the balanced reduce.
-enum GridMode { kGridPartitions = 0, kGridBalanced = 1 };
-
-constexpr int kBalancedMaxSeqs = 1024;   // the in-kernel tile prefix holds 4 per thread
+// Partitions.  A context of L > 0 tokens is cut into n = ceil(L / P)
+// partitions of equal size, rounded up to `align` tokens (the last one
+// shorter), so no partition is a small remainder; P (part_tokens) is a
+// multiple of align, hence every partition holds at most P tokens and the
+// last one at least one.  A context of L <= 0 tokens has one (empty)
+// partition, which writes the zero row.
+__host__ __device__ inline int num_parts(int L, int P) { return L <= 0 ? 1 : (L + P - 1) / P; }
+__host__ __device__ inline int part_size(int L, int n, int align) {
+  const int ps = (L + n - 1) / n;
+  return (ps + align - 1) / align * align;
+}
 
 // Everything a decode launch needs.  Passed by value as the kernel argument.
+//
+// Grid.  Direct: (units * max_parts, 1, B), workgroup (x, z) computes
+// partition x / units of head unit x % units of sequence z, or of the z-th
+// longest sequence when `sorted` (each workgroup ranks the lengths itself,
+// as the hardware starts workgroups in index order).  Planned: a
+// small kernel first lists the (sequence, partition) work items, largest
+// partition first, and workgroup x computes unit x % units of item
+// x / units (units * items the grid's x; the items past the count exit at
+// once).  In both the head unit is the fastest index: workgroup b runs on
+// XCD b % 8, so every XCD gets the same share of each item.
 struct DecodeArgs {
   void* out;                  // [B][Hq][HD] element type
   const void* q;              // [B][Hq][HD]
@@ -27,14 +40,12 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* context_lens;  // [B]
-  const int32_t* seq_order;   // [B] sequence of grid row z (longest first), or null
-  int order_mode;             // 0: row z is sequence z; 1: read seq_order;
-                              // 2: compute the longest-first order in the kernel
-  // partial softmax states: partitions mode [B][Hq][max_parts], balanced mode
-  // [2 * ranges][group]; o has HD floats per state, ml 2 (max in log2 units, sum)
+  const int32_t* items;       // planned grid: [item capacity][4] (s, part << 16 | n, t0, t1)
+  const int32_t* item_count;  // planned grid: number of listed items
+  // partial softmax states of split contexts, [B][Hq][max_parts]: o has HD
+  // floats per state, ml 2 (max in log2 units, sum)
   float* part_o;
   float* part_ml;
-  int32_t* tile_start;        // balanced mode: [B + 1] tile prefix over sequences
   float scale_log2e;          // scale * log2(e): scores are kept in log2 units
   int num_seqs;
   int num_q_heads;
@@ -43,60 +54,54 @@ struct DecodeArgs {
   int num_blocks;
   int max_blocks;             // row stride of block_tables
   int len_cap;                // lengths are clamped to this (<= max_blocks*BS)
-  int part_tokens;            // partitions mode: tokens per partition
-  int max_parts;              // partitions mode: partitions the grid covers per sequence
+  int part_tokens;            // P: tokens per partition at most
+  int part_align;             // partition sizes are multiples of this
+  int max_parts;              // ceil(len_cap / P): partitions per sequence at most
   int contiguous;             // 1: ignore tables; block j of seq s is s*max_blocks + j
-  int grid_mode;              // GridMode
-  int ranges;                 // balanced mode: waves (a multiple of 32), one range each
-  int unit_group;             // balanced mode: query heads per work unit (1 or group)
+  int planned;                // 1: planned grid, 0: direct grid
+  int sorted;                 // direct grid: row z is the z-th longest sequence (B <= 1024)
 };
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
 
-// Sequence handled by grid row z when the order comes from memory (mode 1;
-// an out-of-range entry falls back to z itself) or is the identity.
-__device__ inline int sequence_of(const DecodeArgs& a, int z) {
-  if (a.order_mode != 1) return z;
-  const int s = a.seq_order[z];
-  return (unsigned)s < (unsigned)a.num_seqs ? s : z;
-}
+// The work of one decode workgroup: tokens [t0, t1) (partition `part` of
+// n) of head unit `unit` of sequence s, or nothing (valid false: an item
+// slot past the list, or a partition past the context).  t1 == 0 only for
+// an empty context, whose single partition writes the zero row.
+struct WorkItem {
+  int s, part, n, t0, t1, unit;
+  bool valid;
+};
 
-// ---------------------------------------------------------- balanced mode
-//
-// Tiles of all work units laid end to end, sequence major: with U head units
-// per sequence and nt_s = ceil(L_s / tile_tokens) tiles per unit, unit
-// (s, hu) covers tiles [U*start[s] + hu*nt_s, U*start[s] + (hu+1)*nt_s) of
-// T = U*Ts, where start[] is the prefix of nt over sequences and Ts =
-// start[B].  Sequence-major keeps the heads of a sequence, and neighbouring
-// sequences (which may share prompt blocks), in neighbouring ranges.  With R = min(ranges, T) ranges (so none is empty), range
-// w covers [T*w/R, T*(w+1)/R).  A range leaves a partial state for its
-// first unit when that unit began before the range (slot 2w) and for its
-// last unit when that unit ends after it (slot 2w+1); a range that lies
-// inside one unit leaves one state, in slot 2w.
-
-__device__ inline int effective_ranges(int64_t T, int ranges) {
-  return T < ranges ? (int)T : ranges;
-}
-
-__device__ inline int64_t range_begin(int64_t T, int w, int R) { return T * w / R; }
-
-// The range holding tile r (0 <= r < T).
-__device__ inline int range_of(int64_t r, int64_t T, int R) {
-  return (int)(((r + 1) * R - 1) / T);
-}
-
-// Range handled by wave `wave` (of 4) of workgroup b (-1: none).  The
-// dispatcher places workgroup b on XCD b % 8, so with all ranges in use
-// (`ranges`, a multiple of 32) XCD x gets the contiguous ranges
-// x*R/8 .. (x+1)*R/8 - 1 and neighbouring units (sequences that share
-// blocks) share its L2.
-__device__ inline int range_of_wave(int b, int wave, int R, int ranges) {
-  if (R == ranges) {
-    const int wgs = ranges / 4;
-    return ((b % 8) * (wgs / 8) + b / 8) * 4 + wave;
+__device__ inline WorkItem work_item(const DecodeArgs& a, int units, OrderScratch& sm) {
+  WorkItem w;
+  w.unit = blockIdx.x % units;
+  const int k = blockIdx.x / units;
+  if (a.planned) {
+    // scalar reads: the count and the item are fetched together
+    const int cnt = load_uniform(a.item_count);
+    const i32x4 it = load_uniform4(a.items + 4 * (size_t)k);
+    w.s = it[0];
+    w.part = it[1] >> 16;
+    w.n = it[1] & 0xffff;
+    w.t0 = it[2];
+    w.t1 = it[3];
+    w.valid = k < cnt;
+  } else {
+    // every thread takes this branch or none (a.sorted is uniform): the
+    // ranking has barriers
+    w.s = a.sorted ? uniform(sorted_sequence(a.context_lens, a.num_seqs, a.len_cap, blockIdx.z, sm))
+                   : (int)blockIdx.z;
+    w.part = k;
+    int L = load_uniform(a.context_lens + w.s);
+    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+    w.n = num_parts(L, a.part_tokens);
+    const int ps = part_size(L, w.n, a.part_align);
+    w.t0 = k * ps;
+    w.t1 = min(L, w.t0 + ps);
+    w.valid = k < w.n;
   }
-  const int w = b * 4 + wave;
-  return w < R ? w : -1;
+  return w;
 }
 
 // Launchers (one translation unit each).  Return hipSuccess or the launch error.
@@ -110,15 +115,17 @@ bool decode_valu_supported(Elem e, int head_dim, int block_size);
 // 64 units per pass); the MFMA kernel's unit is 16 tokens.
 int valu_unit_tokens(Elem e, int head_dim, int block_size);
 bool decode_mfma_supported(Elem e, int head_dim, int block_size);
-// Workgroups of the balanced-mode kernel resident per compute unit (0 if
-// the runtime cannot say).
+// Decode workgroups resident per compute unit (0 if the runtime cannot say).
 int decode_valu_occupancy(Elem e, int head_dim, int block_size);
 int decode_mfma_occupancy(Elem e, int head_dim, int block_size, int group);
 
-// Writes order[0..num_seqs) = the sequence indices, longest context first
-// (stable within half-octave length bins).
-hipError_t launch_seq_order(const int32_t* lens, int num_seqs, int len_cap, int32_t* order,
-                            hipStream_t stream);
+// Writes the work items of a planned grid (see DecodeArgs): items[4k ..
+// 4k+3] = (s, part << 16 | n, t0, t1) for k < *count, largest partition
+// first (half-octave size bins; stable, and a sequence's partitions
+// together), using scratch[2 * num_seqs].
+hipError_t launch_plan_items(const int32_t* lens, int num_seqs, int len_cap, int part_tokens,
+                             int part_align, int32_t* scratch, int32_t* items, int32_t* count,
+                             hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

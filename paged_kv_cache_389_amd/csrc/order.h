@@ -1,10 +1,9 @@
-// Longest-first order of a decode batch, shared by the order kernel and the
-// decode kernels (which compute it themselves for batches of at most
-// kFusedOrderMax sequences, saving a launch).
-//
-// Lengths are binned by half octaves below the batch's length bound
-// (bin b holds lengths in (cap * 2^-(b+1)/2, cap * 2^-b/2], 32 bins); the
-// order is bin 0 first and, inside a bin, increasing sequence index.
+// Longest-first orders: lengths are binned by half octaves below a bound
+// (bin b holds lengths in (cap * 2^-(b+1)/2, cap * 2^-b/2], 32 bins; bin 0
+// is the longest), and an order lists bin 0 first and, inside a bin,
+// increasing index.  The work planner bins partition sizes this way; the
+// decode kernels of the direct grid rank sequences by length themselves
+// for batches of at most kFusedOrderMax sequences (sorted_sequence).
 #pragma once
 
 #include "common.h"

@@ -21,13 +21,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def decode_gpu(q, kc, vc, tables, lens, scale, max_len=None, partition=0, path=0):
+def decode_gpu(q, kc, vc, tables, lens, scale, max_len=None, partition=0, path=0, grid=0):
     """Run paged_attention_decode on device tensors; returns the output."""
     out = torch.empty_like(q)
     if max_len is None:
         max_len = int(lens.max().item()) if lens.numel() else 0
     pk.paged_attention_decode(out, q, kc, vc, tables, lens, scale, max_len,
-                              partition_tokens=partition, path=path)
+                              partition_tokens=partition, path=path, grid=grid)
     torch.cuda.synchronize()
     return out
 

@@ -59,74 +59,82 @@ def test_supported_shapes(native):
 def test_workspace_bytes_and_plan(native):
     import torch
     f16, bf16 = torch.float16, torch.bfloat16
-    P, B = native.GRID_PARTITIONS, native.GRID_BALANCED
+    D, PL = native.GRID_DIRECT, native.GRID_PLANNED
 
     def plan(*a, **k):
         p = native.plan(*a, **k)
         assert p["workspace_bytes"] == native.workspace_bytes(*a, **k)
         return p
 
-    # default: partitions grid, one partition per (sequence, head) when there
-    # are enough of them, visited longest first (order computed in-kernel)
+    def items_bytes(B, max_parts):   # planner scratch, items, count
+        return (2 * B * 4 + 15) // 16 * 16 + B * max_parts * 16 + 16
+
+    # one partition per (sequence, head) when there are enough of them; the
+    # grid holds more than one round of resident workgroups (the host
+    # assumes 4 VALU / 3 MFMA per compute unit and 256 units without a
+    # device), so the workgroups rank the sequences longest first
     p = plan(64, 40, 40, 128, 16, 128, 2048, f16)
     assert (p["path"], p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
-        (native.PATH_VALU, P, 2048, 1, 1)
+        (native.PATH_VALU, D, 2048, 1, 1)
     assert p["workspace_bytes"] == 0
     p = plan(256, 32, 8, 128, 16, 256, 4096, bf16)
-    assert (p["path"], p["grid"], p["max_parts"], p["workspace_bytes"]) == \
-        (native.PATH_MFMA, P, 1, 0)
-    # few units, long contexts: split so that every compute unit gets work
+    assert (p["path"], p["grid"], p["max_parts"], p["longest_first"], p["workspace_bytes"]) == \
+        (native.PATH_MFMA, D, 1, 1, 0)
+    # few units, long contexts: split so that every compute unit gets about
+    # two workgroups (512 of them: one round, so not ranked)
     p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16)
-    assert p["max_parts"] > 1 and p["partition_tokens"] * p["max_parts"] >= 32768
-    assert p["workspace_bytes"] == 8 * 64 * p["max_parts"] * (128 + 2) * 4
-    # balanced grid on request (-1): 2 partial states per range and the tile prefix
-    p = plan(64, 40, 40, 128, 16, 128, 2048, f16, -1)
-    assert (p["grid"], p["partition_tokens"], p["max_parts"]) == (B, 0, 0)
-    assert p["ranges"] >= 32 and p["ranges"] % 32 == 0
-    assert p["workspace_bytes"] == 2 * p["ranges"] * (128 + 2) * 4 + 65 * 4 + 12
-    p = plan(256, 32, 8, 128, 16, 256, 4096, bf16, -1)
-    assert (p["path"], p["grid"]) == (native.PATH_MFMA, B)
-    assert p["workspace_bytes"] == 2 * p["ranges"] * 4 * 128 * 4 + 2 * p["ranges"] * 4 * 2 * 4 \
-        + 257 * 4 + 12
-    # small batches get fewer ranges (about 4 tiles each at the least, 32 minimum)
-    assert plan(4, 4, 4, 64, 16, 4, 64, torch.float32, -1)["ranges"] == 32
-    # the balanced grid holds at most 1024 sequences
-    with pytest.raises(native.PagedKVError):
-        native.plan(1025, 4, 4, 64, 16, 4, 64, torch.float32, -1)
-    # explicit partition size: partitions grid
+    assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
+        (D, 4096, 8, 0)
+    assert p["workspace_bytes"] == 8 * 64 * 8 * (128 + 2) * 4
+    # explicit partition size; 512 workgroups fit one round
     p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 4096)
     assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
-        (P, 4096, 8, 0)
+        (D, 4096, 8, 0)
     assert p["workspace_bytes"] == 8 * 64 * 8 * 128 * 4 + 8 * 64 * 8 * 2 * 4
-    # 2048 workgroups: more than two rounds of resident ones, so longest first
+    # 2048 workgroups: ranked longest first; the planned grid on request
+    # adds the work list after the partial states
     p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024)
-    assert (p["grid"], p["max_parts"], p["longest_first"]) == (P, 32, 1)
-    # more than 1024 sequences: partitions grid, order kernel writes the order
+    assert (p["grid"], p["max_parts"], p["longest_first"]) == (D, 32, 1)
+    assert p["workspace_bytes"] == 8 * 64 * 32 * (128 + 2) * 4
+    p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024, grid=PL)
+    assert (p["grid"], p["max_parts"], p["longest_first"]) == (PL, 32, 1)
+    assert p["workspace_bytes"] == 8 * 64 * 32 * (128 + 2) * 4 + \
+        items_bytes(8, 32)
+    # more than 1024 sequences to rank: planned in one workgroup
     p = plan(2000, 8, 8, 128, 16, 8, 128, f16)
-    assert (p["grid"], p["max_parts"], p["longest_first"]) == (P, 1, 1)
-    assert p["workspace_bytes"] == 2000 * 4
-    # one partition per sequence, no order: no workspace
-    p = plan(2000, 1, 1, 128, 16, 8, 128, f16)
-    assert (p["grid"], p["longest_first"], p["workspace_bytes"]) == (P, 0, 0)
+    assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
+        (PL, 128, 1, 1)
+    assert p["workspace_bytes"] == items_bytes(2000, 1)
+    # ... unless the direct grid is asked for
+    p = plan(2000, 8, 8, 128, 16, 8, 128, f16, grid=D)
+    assert (p["grid"], p["longest_first"], p["workspace_bytes"]) == (D, 0, 0)
+    # one partition per sequence in one round: direct, no workspace
+    p = plan(1000, 1, 1, 128, 16, 8, 128, f16)
+    assert (p["grid"], p["longest_first"], p["workspace_bytes"]) == (D, 0, 0)
     # the table width caps the context: 10 blocks of 16 tokens
     assert plan(2, 4, 4, 128, 16, 10, 100000, f16, 64)["max_parts"] == 3
     with pytest.raises(ValueError):
         native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 100)   # not a multiple of 32
+    # explicit partitions may exceed one pass of table entries per wave, up
+    # to 2^20 tokens
+    assert plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 8192)["max_parts"] == 4
     with pytest.raises(ValueError):
-        native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, 8192)  # above 256 tiles
+        native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, (1 << 20) + 32)
+    with pytest.raises(ValueError):
+        native.workspace_bytes(8, 64, 8, 128, 32, 1024, 32768, bf16, -1)    # negative
     with pytest.raises(native.PagedKVError):
         native.plan(2, 4, 4, 96, 16, 10, 100, f16)                          # head_dim 96
 
 
 def _decode(lib, **over):
     args = dict(out=1, q=1, k=1, v=1, tables=1, lens=1, scale=1.0, B=2, Hq=4, Hkv=2, hd=128,
-                bs=16, nb=64, maxb=8, maxL=100, dtype=1, ws=None, wsb=0, part=0, path=0)
+                bs=16, nb=64, maxb=8, maxL=100, dtype=1, ws=None, wsb=0, part=0, path=0, grid=0)
     args.update(over)
     a = args
     return lib.pkv_paged_attention_decode_ex(
         a["out"], a["q"], a["k"], a["v"], a["tables"], a["lens"], ctypes.c_float(a["scale"]),
         a["B"], a["Hq"], a["Hkv"], a["hd"], a["bs"], a["nb"], a["maxb"], a["maxL"], a["dtype"],
-        a["ws"], a["wsb"], a["part"], a["path"], None)
+        a["ws"], a["wsb"], a["part"], a["path"], a["grid"], None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -140,9 +148,11 @@ def _decode(lib, **over):
     (dict(part=48), -1),         # not a multiple of 32
     (dict(path=2, Hq=2, Hkv=2), -2),   # MFMA needs grouped heads
     (dict(path=2, dtype=0), -2),       # MFMA needs 16-bit types
-    (dict(maxL=4096, maxb=256, part=-1), -3),   # balanced grid and no workspace
     (dict(maxL=4096, maxb=256, part=512), -3),   # several partitions and no workspace
-    (dict(part=-2), -1),
+    (dict(B=4000, Hq=4, Hkv=4, maxL=64, maxb=4), -3),   # planned grid and no workspace
+    (dict(part=-1), -1),
+    (dict(grid=3), -1),
+    (dict(grid=2), -3),          # planned grid on request and no workspace
     (dict(path=7), -1),
 ])
 def test_decode_rejects_bad_arguments_before_launch(native, over, status):

@@ -2,9 +2,9 @@
 
 Each workload is built at the size and with the seed the benchmark uses, and
 its step runs through the C ABI in the benchmark's launch configuration
-(library-chosen partition size and kernel), then again with a forced split
-and with the balanced grid, so the partition + reduce and the balanced +
-reduce paths are covered at full size too:
+(library-chosen partition size, kernel and grid), then again with a forced
+split on the direct and on the planned grid, so the partition + reduce path
+is covered at full size on both grids:
 
 * cache writes (reshape_and_cache) and block copies (copy_blocks) are
   compared with the oracle's byte for byte over the WHOLE K and V buffers;
@@ -66,10 +66,10 @@ def _sample(wl, n):
     return sorted(picks[:n])
 
 
-def _decode(wl, kc, vc, tables, lens, partition):
+def _decode(wl, kc, vc, tables, lens, partition, grid):
     out = torch.empty_like(wl.q)
     pk.paged_attention_decode(out, wl.q, kc, vc, tables, lens, wl.scale, wl.max_context_len,
-                              partition_tokens=partition)
+                              partition_tokens=partition, grid=grid)
     torch.cuda.synchronize()
     return out
 
@@ -118,14 +118,15 @@ def test_full_size_step_matches_oracle(name):
     v_o = torch.from_numpy(v_host).view(wl.dtype)
     want = oracle.decode(wl.q.cpu(), k_o, v_o, wl.block_tables, wl.context_lens, wl.scale,
                          wl.num_kv_heads, seqs=seqs)
-    for partition in (0, split, -1):
-        say("full-size decode", name, "partition", partition, pk.plan(
+
+    for partition, grid in ((0, pk.GRID_AUTO), (split, pk.GRID_DIRECT), (split, pk.GRID_PLANNED)):
+        say("full-size decode", name, "partition", partition, "grid", grid, pk.plan(
             wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-            wl.block_tables.shape[1], wl.max_context_len, wl.dtype, partition))
-        got = _decode(wl, kc, vc, tables, lens, partition)
-        again = _decode(wl, kc, vc, tables, lens, partition)
+            wl.block_tables.shape[1], wl.max_context_len, wl.dtype, partition, 0, grid))
+        got = _decode(wl, kc, vc, tables, lens, partition, grid)
+        again = _decode(wl, kc, vc, tables, lens, partition, grid)
         assert torch.equal(_bits(got), _bits(again)), "decode is not deterministic"
         g = got.cpu().double().numpy()[seqs]
         err = float(np.abs(g - want[seqs]).max())
         assert np.isfinite(g).all()
-        assert err <= TOL[wl.dtype], f"{name} partition {partition}: max abs err {err}"
+        assert err <= TOL[wl.dtype], f"{name} partition {partition} grid {grid}: max abs err {err}"

@@ -14,6 +14,7 @@ import torch
 import oracle
 import pins
 from gpu_helpers import (DEV, INT_VIEW, TOL, decode_gpu, max_err, say, upload_case)
+from paged_kv_cache_389_amd import _native as pk
 
 pytestmark = pytest.mark.gpu
 
@@ -134,10 +135,11 @@ def _case(seed, lens, hq, hkv, hd, bs, extra_blocks=5, poison=True):
     return q, kp, vp, tables, L
 
 
-def _check_decode(q, kp, vp, tables, L, hkv, dtype, scale, partition=0, path=0, tol=None):
+def _check_decode(q, kp, vp, tables, L, hkv, dtype, scale, partition=0, path=0, grid=0,
+                  tol=None):
     dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, dtype)
     got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], scale,
-                     partition=partition, path=path)
+                     partition=partition, path=path, grid=grid)
     want = oracle.decode(qt, kt, vt, tables, L, scale, hkv)
     err = max_err(got, want)
     assert err <= (TOL[dtype] if tol is None else tol), f"max abs err {err}"
@@ -150,7 +152,10 @@ SHAPES = [  # (hq, hkv, hd, bs)
 ]
 
 
-@pytest.mark.parametrize("grid", [0, -1], ids=["partitions", "balanced"])
+GRIDS = {"direct": 1, "planned": 2}
+
+
+@pytest.mark.parametrize("grid", GRIDS.values(), ids=GRIDS.keys())
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_ID.get)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "hq%d_hkv%d_hd%d_bs%d" % s)
 def test_decode_ragged_lengths(dtype, shape, grid):
@@ -158,21 +163,44 @@ def test_decode_ragged_lengths(dtype, shape, grid):
     say("decode ragged", DT_ID[dtype], shape, grid)
     lens = [1, bs - 1, bs, bs + 1, 63, 64, 65, 200]
     q, kp, vp, tables, L = _case(7 + hd + bs + hq, lens, hq, hkv, hd, bs)
-    _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), partition=grid)
+    _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), grid=grid)
 
 
+@pytest.mark.parametrize("grid", GRIDS.values(), ids=GRIDS.keys())
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=DT_ID.get)
 @pytest.mark.parametrize("path", [1, 2], ids=["valu", "mfma"])
 @pytest.mark.parametrize("partition", [32, 64, 96, 512])
-def test_decode_split_context(dtype, path, partition):
-    """Several partitions per sequence, merged by the reduce kernel, with
-    lengths around partition boundaries."""
-    say("decode split", DT_ID[dtype], path, partition)
+def test_decode_split_context(dtype, path, partition, grid):
+    """Several partitions per sequence (equal sizes, rounded to 32 tokens),
+    merged by the reduce kernel, with lengths around partition boundaries."""
+    say("decode split", DT_ID[dtype], path, partition, grid)
     hq, hkv, hd, bs = 8, 2, 128, 16 if partition % 32 == 0 else 32
     lens = [1, partition - 1, partition, partition + 1, 3 * partition + 5, 1000, 17]
     q, kp, vp, tables, L = _case(300 + partition + path, lens, hq, hkv, hd, bs)
     _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd),
-                  partition=partition, path=path)
+                  partition=partition, path=path, grid=grid)
+
+
+@pytest.mark.parametrize("path", [1, 2], ids=["valu", "mfma"])
+def test_decode_split_context_any_workspace_contents(path):
+    """The workspace needs no initialisation: one full of random bytes, used
+    for several split calls in a row, gives the oracle's result every time."""
+    say("decode split garbage workspace", path)
+    hq, hkv, hd, bs = 8, 2, 128, 16
+    lens = [1, 95, 96, 97, 1000, 333]
+    q, kp, vp, tables, L = _case(350 + path, lens, hq, hkv, hd, bs)
+    dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, torch.bfloat16)
+    want = oracle.decode(qt, kt, vt, tables, L, 0.1, hkv)
+    need = pk.workspace_bytes(len(lens), hq, hkv, hd, bs, tables.shape[1], int(L.max()),
+                              torch.bfloat16, 96, path)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=gen)
+    for _ in range(3):
+        out = torch.empty_like(dev["q"])
+        pk.paged_attention_decode(out, dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
+                                  0.1, int(L.max()), workspace=ws, partition_tokens=96, path=path)
+        torch.cuda.synchronize()
+        assert max_err(out, want) <= 2e-2
 
 
 def test_decode_split_context_fp32():
@@ -228,20 +256,20 @@ def test_decode_poisoned_slots_never_reach_the_result(hq, hkv):
     assert torch.equal(g1.view(torch.int16), g2.view(torch.int16))
 
 
-@pytest.mark.parametrize("grid", [0, -1], ids=["partitions", "balanced"])
+@pytest.mark.parametrize("grid", GRIDS.values(), ids=GRIDS.keys())
 @pytest.mark.parametrize("path", [1, 2], ids=["valu", "mfma"])
 def test_decode_zero_length_gives_zeros(path, grid):
     say("decode L=0", path, grid)
     q, kp, vp, tables, L = _case(800, [0, 9, 0], 8, 2, 128, 16)
     dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, torch.bfloat16)
     got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.1, path=path,
-                     partition=grid)
+                     grid=grid)
     assert not got[0].any() and not got[2].any()
     want = oracle.decode(qt, kt, vt, tables, L, 0.1, 2)
     assert max_err(got, want) <= 2e-2
 
 
-@pytest.mark.parametrize("grid", [0, -1], ids=["partitions", "balanced"])
+@pytest.mark.parametrize("grid", GRIDS.values(), ids=GRIDS.keys())
 @pytest.mark.parametrize("path", [1, 2], ids=["valu", "mfma"])
 def test_decode_bad_table_entry_gives_nan_not_a_fault(path, grid):
     say("decode bad table", path, grid)
@@ -250,7 +278,7 @@ def test_decode_bad_table_entry_gives_nan_not_a_fault(path, grid):
     tables[1, 1] = kp.shape[0] + 1000          # outside the pool
     dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, torch.float16)
     got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.1, path=path,
-                     partition=grid)
+                     grid=grid)
     assert torch.isnan(got[1]).all()
     want = oracle.decode(qt, kt, vt, tables, L, 0.1, 2, seqs=[0])
     assert max_err(got[:1], want[:1]) <= 2e-2
@@ -281,65 +309,65 @@ def test_decode_contiguous_control_matches_paged():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("grid", [0, 2], ids=["auto", "planned"])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=DT_ID.get)
-@pytest.mark.parametrize("hq,hkv,partition", [(4, 4, 0), (8, 2, 0), (8, 2, 64), (2, 2, 32),
-                                              (4, 4, -1), (8, 2, -1)])
-def test_decode_many_sequences_longest_first(dtype, hq, hkv, partition):
-    """Partitions grid with enough workgroups that the kernel visits the
-    sequences longest first (order computed inside the kernel); lengths
-    log-uniform so the order is far from the index order; partitions 64 and
-    32 run the split path under the order too.  Partition -1 is the balanced
-    grid on the same batch."""
-    say("decode longest-first", DT_ID[dtype], hq, hkv, partition)
+@pytest.mark.parametrize("hq,hkv,partition", [(4, 4, 0), (8, 2, 0), (8, 2, 64), (2, 2, 32)])
+def test_decode_many_sequences_longest_first(dtype, hq, hkv, partition, grid):
+    """A large batch, longest first: ranked inside the direct grid's
+    workgroups (auto, where the grid is large enough) or listed by the
+    planner; lengths log-uniform so the order is far from the index order;
+    partitions 64 and 32 run the split path under the order too."""
+    say("decode longest first", DT_ID[dtype], hq, hkv, partition, grid)
     num_seqs, hd, bs = 800, 128, 16
     rng = np.random.default_rng(1100 + hq + partition)
     lens = np.clip(np.rint(np.exp(rng.uniform(0, math.log(300), num_seqs))), 1, 300).astype(int)
     q, ks, vs, nblk = pins.random_case(rng, num_seqs, hq, hkv, hd, lens, bs, extra_blocks=3)
     kp, vp, tables, L, _ = pins.page(ks, vs, bs, nblk, rng)
-    from paged_kv_cache_389_amd import GRID_BALANCED, plan
+    from paged_kv_cache_389_amd import plan
     dt = {torch.float16: 1, torch.bfloat16: 2}[dtype]
-    p = plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), dt, partition)
-    if partition >= 0:
-        assert p["longest_first"]
-    else:
-        assert p["grid"] == GRID_BALANCED
-    _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), partition=partition)
+    p = plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), dt, partition, 0, grid)
+    if grid == 2 or hq == hkv:
+        assert p["longest_first"], p
+    _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(hd), partition=partition,
+                  grid=grid)
 
 
-def test_decode_batch_above_fused_order_limit():
-    """More than 1024 sequences: the longest-first order comes from the
-    separate order kernel through the workspace."""
-    say("decode order kernel")
-    num_seqs, hq, hkv, hd, bs = 1500, 2, 2, 64, 16
+def test_decode_planned_batch_of_several_chunks():
+    """More than 1024 sequences: the planner works in chunks of 1024, with
+    empty sequences among them."""
+    say("decode planned chunks")
+    num_seqs, hq, hkv, hd, bs = 2500, 2, 2, 64, 16
     rng = np.random.default_rng(1200)
-    lens = rng.integers(1, 97, num_seqs)
+    lens = rng.integers(0, 97, num_seqs)
+    lens[::37] = 0
     q, ks, vs, nblk = pins.random_case(rng, num_seqs, hq, hkv, hd, lens, bs, extra_blocks=3)
     kp, vp, tables, L, _ = pins.page(ks, vs, bs, nblk, rng)
-    from paged_kv_cache_389_amd import plan, workspace_bytes
-    assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1)["longest_first"]
-    assert workspace_bytes(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1) >= \
-        4 * num_seqs
-    _check_decode(q, kp, vp, tables, L, hkv, torch.float16, 0.125)
+    from paged_kv_cache_389_amd import GRID_PLANNED, plan
+    assert plan(num_seqs, hq, hkv, hd, bs, tables.shape[1], int(L.max()), 1)["grid"] == \
+        GRID_PLANNED
+    got, _ = _check_decode(q, kp, vp, tables, L, hkv, torch.float16, 0.125, partition=32)
+    assert not got[lens == 0].any()
 
 
+@pytest.mark.parametrize("grid", GRIDS.values(), ids=GRIDS.keys())
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=DT_ID.get)
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (16, 2)])
-def test_decode_balanced_long_sequence_cut_by_many_ranges(dtype, hq, hkv):
-    """Balanced grid: one long sequence and a few short ones, so every range
-    boundary cuts a (head, sequence) unit and the reduce merges dozens of
-    partial states per head; also empty sequences among them."""
-    say("decode balanced long", DT_ID[dtype], hq, hkv)
+def test_decode_long_sequence_many_partitions(dtype, hq, hkv, grid):
+    """One long sequence cut into dozens of partitions among short and empty
+    ones; the reduce merges dozens of partial states per head."""
+    say("decode long many partitions", DT_ID[dtype], hq, hkv, grid)
     lens = [9000, 0, 3, 777, 0, 16]
     q, kp, vp, tables, L = _case(1300 + hq, lens, hq, hkv, 128, 16)
-    got, _ = _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(128), partition=-1)
+    got, _ = _check_decode(q, kp, vp, tables, L, hkv, dtype, 1.0 / math.sqrt(128), partition=256,
+                           grid=grid)
     assert not got[1].any() and not got[4].any()
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2)])
-def test_decode_balanced_determinism_and_placement(hq, hkv):
-    """Balanced grid: bit-identical results across runs and across physical
+def test_decode_planned_determinism_and_placement(hq, hkv):
+    """Planned grid: bit-identical results across runs and across physical
     placements of the same logical sequences."""
-    say("decode balanced placement", hq, hkv)
+    say("decode planned placement", hq, hkv)
     rng = np.random.default_rng(1400)
     lens = [700, 33, 1200, 5, 2000, 1]
     q, ks, vs, nblk = pins.random_case(rng, len(lens), hq, hkv, 128, lens, 16, extra_blocks=40)
@@ -349,6 +377,6 @@ def test_decode_balanced_determinism_and_placement(hq, hkv):
         dev, _ = upload_case(q, kp, vp, tables, L, torch.float16)
         for _ in range(2):
             outs.append(decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
-                                   0.088, partition=-1).cpu())
+                                   0.088, partition=256, grid=2).cpu())
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
