@@ -7,11 +7,15 @@ seeded, and resident in HBM before the timed region.
 
 Prints ONE JSON line.  ``value`` is whole-step throughput in algorithmic
 bytes per second (GB/s): the K/V bytes the attention must read plus q, out,
-tables, lengths and the cache writes.  ``roofline`` reports the decode
-call's own achieved HBM bandwidth (its algorithmic bytes over its average
-duration, timed with HIP events on the launch stream) against the MI355X
-HBM3E peak of 8 TB/s.  ``cpu_baseline`` times the float64 CPU oracle on a
-bounded sample of the same workload.
+tables, lengths and the cache writes.  ``roofline`` reports the attention
+kernel's own achieved HBM bandwidth (the decode call's algorithmic bytes
+over the kernel's average duration, timed with HIP events that the library
+records around that launch on its stream) against the MI355X HBM3E peak of
+8 TB/s, with the HBM bytes per launch that rocprofv3 counters measured
+(``traffic``, from profiles/decode_traffic.json while the kernel sources
+are unchanged, else null).  ``decode_ms`` times the whole decode call
+(planning kernel and partition merge included).  ``cpu_baseline`` times the
+float64 CPU oracle on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
 """
@@ -63,7 +67,101 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    p.add_argument("--counters", metavar="OUT_JSON",
+                   help="no run: turn rocprofv3 --pmc databases of FETCH_SIZE and WRITE_SIZE "
+                        "(this workload, then the copy calibration) into HBM bytes per launch, "
+                        "merged into OUT_JSON")
+    p.add_argument("--fetch-db")
+    p.add_argument("--write-db")
+    p.add_argument("--cal-fetch-db")
+    p.add_argument("--cal-write-db")
+    p.add_argument("--cal-mib", type=int, default=1024)
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources of the library (names and bytes): counter
+    figures are only used while the kernels they were taken on are built."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "paged_kv_cache_389_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch of the attention kernel from the committed
+    counter summary, or None if there is none for this workload or the
+    kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_digest():
+        return None
+    w = rec.get("workloads", {}).get(name)
+    return None if w is None else w.get("hbm_bytes_per_launch")
+
+
+def _counter_means(db):
+    """{(kernel name, counter): mean per dispatch} from a rocprofv3 database."""
+    import glob
+    import sqlite3
+    files = [db] if db.endswith(".db") else glob.glob(os.path.join(db, "**", "*.db"),
+                                                       recursive=True)
+    acc = {}
+    for f in files:
+        con = sqlite3.connect(f)
+        cols = [c[1] for c in con.execute("pragma table_info(counters_collection)")]
+        ki, ci, vi = cols.index("kernel_name"), cols.index("counter_name"), cols.index("value")
+        for r in con.execute("select * from counters_collection"):
+            acc.setdefault((r[ki], r[ci]), []).append(float(r[vi]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def counters_to_traffic(args):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the attention kernel,
+    each divided by what the same counter reads per byte of a plain copy of
+    known size, give its HBM bytes per launch."""
+    def pick(means, counter, want):
+        rows = [(v, k) for (k, c), v in means.items() if c == counter and want(k)]
+        if not rows:
+            raise SystemExit(f"no {counter} rows")
+        return max(rows)
+    is_decode = lambda k: "decode_mfma_kernel" in k or "decode_valu_kernel" in k
+    is_other = lambda k: "pkv::" not in k
+    cal_bytes = args.cal_mib << 20
+    f_fetch = pick(_counter_means(args.cal_fetch_db), "FETCH_SIZE", is_other)[0] * 1024 / cal_bytes
+    f_write = pick(_counter_means(args.cal_write_db), "WRITE_SIZE", is_other)[0] * 1024 / cal_bytes
+    fetch, kname = pick(_counter_means(args.fetch_db), "FETCH_SIZE", is_decode)
+    write, _ = pick(_counter_means(args.write_db), "WRITE_SIZE", is_decode)
+    from paged_kv_cache_389_amd import workloads
+    wl = workloads.make(args.workload, device="cpu")
+    try:
+        with open(args.counters) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("sources_sha256") != kernel_sources_digest():
+        rec = {"sources_sha256": kernel_sources_digest(), "workloads": {}}
+    rec["calibration"] = {"copy_mib": args.cal_mib, "fetch_counter_per_byte": round(f_fetch, 4),
+                          "write_counter_per_byte": round(f_write, 4)}
+    rec["workloads"][args.workload] = {
+        "kernel": kname.split("(")[0], "fetch_kib_per_launch": round(fetch, 1),
+        "write_kib_per_launch": round(write, 1),
+        "hbm_bytes_per_launch": int(fetch * 1024 / f_fetch + write * 1024 / f_write),
+        "alg_bytes_per_launch": wl.decode_bytes()}
+    with open(args.counters, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec["workloads"][args.workload]))
 
 
 def copy_calibration(mib, reps=5):
@@ -125,6 +223,7 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
                    max_blocks, wl.max_context_len, wl.dtype, partition, path, grid)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    kev = [(pk.HipEvent(), pk.HipEvent()) for _ in range(steps)]
 
     def one_step(i=None):
         if dev["pairs"] is not None:
@@ -135,7 +234,8 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
             ev[i][0].record()
         pk.paged_attention_decode(dev["out"], dev["q"], dev["k"], dev["v"], tables, dev["lens"],
                                   wl.scale, wl.max_context_len, workspace=ws,
-                                  partition_tokens=partition, path=path, grid=grid)
+                                  partition_tokens=partition, path=path, grid=grid,
+                                  kernel_events=None if i is None else kev[i])
         if i is not None:
             ev[i][1].record()
 
@@ -148,7 +248,8 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     decode_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, decode_ms, plan
+    kernel_ms = [a.elapsed_ms(b) for a, b in kev]
+    return wall, decode_ms, kernel_ms, plan
 
 
 def cpu_baseline(wl, budget_s):
@@ -183,11 +284,13 @@ def cpu_baseline(wl, budget_s):
 def bench_one(name, args, with_cpu):
     wl, dev = build_inputs(name, args.placement)
     alg_decode, alg_writes = step_bytes(wl, dev)
-    wall, decode_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition, args.path,
-                                    args.grid)
+    wall, decode_ms, kernel_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition,
+                                               args.path, args.grid)
     ms_per_step = wall / args.steps * 1e3
     dec_ms = float(np.mean(decode_ms))
-    achieved = alg_decode / (dec_ms / 1e3) / 1e9
+    ker_ms = float(np.mean(kernel_ms))
+    achieved = alg_decode / (ker_ms / 1e3) / 1e9
+    kname = ("decode_mfma_kernel" if plan["path"] == 2 else "decode_valu_kernel")
     line = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + queries/s",
         "value": round((alg_decode + alg_writes) / (ms_per_step / 1e3) / 1e9, 2),
@@ -212,11 +315,12 @@ def bench_one(name, args, with_cpu):
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 5),
         "decode_ms_min": round(float(np.min(decode_ms)), 5),
+        "kernel_ms": round(ker_ms, 5),
         "bytes": {"decode_alg": alg_decode, "writes_alg": alg_writes,
                   "kv_logical": wl.kv_bytes()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attention_decode call (main kernel + partition reduce)"},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(name), "kernel": kname},
     }
     if name == "sharing_fp16":
         line["bytes"]["kv_unique"] = wl.unique_kv_bytes()
@@ -227,6 +331,9 @@ def bench_one(name, args, with_cpu):
 
 def main():
     args = parse()
+    if args.counters:
+        counters_to_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path needs no communication; see the sharding notes)", file=sys.stderr)

@@ -222,6 +222,21 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                                   size_t workspace_bytes, int partition_tokens, int path,
                                   int grid, void* stream);
 
+/* Same as pkv_paged_attention_decode_ex, and records begin_event on `stream`
+ * right before the attention kernel is launched and end_event right after
+ * it (before the partition merge and after the planning kernel), so that
+ * hipEventElapsedTime gives the attention kernel's own duration.  The events
+ * are hipEvent_t handles the caller created; either may be NULL.  For
+ * measurement; the result is the same as pkv_paged_attention_decode_ex's. */
+int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, float scale, int num_seqs,
+                                     int num_q_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int num_blocks, int max_blocks_per_seq,
+                                     int max_context_len, pkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, int partition_tokens, int path,
+                                     int grid, void* begin_event, void* end_event, void* stream);
+
 /*
  * reshape_and_cache: for every token j with slot = slot_mapping[j] >= 0,
  *   k_cache[slot / block_size][g][slot % block_size][:] = k[j][g][:]

@@ -18,7 +18,7 @@ CPU implementation.
 
 _NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
-           "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED")
+           "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")
 
 __all__ = list(_NATIVE) + ["block_manager", "workloads"]
 

@@ -71,6 +71,10 @@ def _load():
     lib.pkv_paged_attention_decode_ex.argtypes = [
         vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
         i32, i32, i32, vp]
+    lib.pkv_paged_attention_decode_timed.restype = i32
+    lib.pkv_paged_attention_decode_timed.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+        i32, i32, i32, vp, vp, vp]
     lib.pkv_reshape_and_cache.restype = i32
     lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_copy_blocks.restype = i32
@@ -84,7 +88,8 @@ EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_supported",
     "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_plan",
     "pkv_paged_attention_decode",
-    "pkv_paged_attention_decode_ex", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_paged_attention_decode_ex", "pkv_paged_attention_decode_timed",
+    "pkv_reshape_and_cache", "pkv_copy_blocks",
 )
 
 
@@ -151,11 +156,13 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                            max_context_len, workspace=None, partition_tokens=0,
-                           path=PATH_AUTO, grid=GRID_AUTO, stream=None):
+                           path=PATH_AUTO, grid=GRID_AUTO, stream=None, kernel_events=None):
     """``out[s, h] = softmax(scale * K_s q[s, h]) V_s`` over each sequence's
     paged KV (see ``pkv_paged_attention_decode``).  ``max_context_len`` is a
     host-side bound of ``context_lens``.  ``workspace`` is a uint8 device
-    tensor; when None one of the required size is allocated."""
+    tensor; when None one of the required size is allocated.
+    ``kernel_events`` = (begin, end) :class:`HipEvent` pair recorded around
+    the attention kernel itself (``pkv_paged_attention_decode_timed``)."""
     for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (context_lens, "context_lens")):
         _dev(t, n)
@@ -190,11 +197,13 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     tables_ptr = _ptr(block_tables) if block_tables is not None else None
     with torch.cuda.device(q.device):
-        st = lib.pkv_paged_attention_decode_ex(
+        ev0, ev1 = (kernel_events[0].handle, kernel_events[1].handle) if kernel_events \
+            else (None, None)
+        st = lib.pkv_paged_attention_decode_timed(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), tables_ptr, _ptr(context_lens),
             ctypes.c_float(scale), num_seqs, hq, hkv, hd, bs, nb, max_blocks,
             int(max_context_len), _DTYPE_CODE[q.dtype], ws_ptr, ws_len, int(partition_tokens),
-            int(path), int(grid), _stream(q, stream))
+            int(path), int(grid), ev0, ev1, _stream(q, stream))
     _check("paged_attention_decode", st)
     return out
 
@@ -240,3 +249,38 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
                                  src_dst_pairs.shape[0], hkv, hd, bs, nb,
                                  _DTYPE_CODE[k_cache.dtype], _stream(k_cache, stream))
     _check("copy_blocks", st)
+
+
+class HipEvent:
+    """A timing hipEvent_t of the HIP runtime that torch loaded, for
+    ``kernel_events`` (the library records it; read it with
+    :meth:`elapsed_ms`)."""
+
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            HipEvent._hip = hip
+        self.handle = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise PagedKVError("hipEventCreate failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        """Milliseconds from this event to ``end`` (both recorded; waits for end)."""
+        hip = HipEvent._hip
+        if hip.hipEventSynchronize(end.handle) != 0:
+            raise PagedKVError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise PagedKVError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.handle:
+            HipEvent._hip.hipEventDestroy(self.handle)

@@ -251,14 +251,14 @@ int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, in
   return PKV_OK;
 }
 
-int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
-                                  const void* v_cache, const int32_t* block_tables,
-                                  const int32_t* context_lens, float scale, int num_seqs,
-                                  int num_q_heads, int num_kv_heads, int head_dim,
-                                  int block_size, int num_blocks, int max_blocks_per_seq,
-                                  int max_context_len, pkv_dtype dtype, void* workspace,
-                                  size_t workspace_bytes, int partition, int path, int grid,
-                                  void* stream) {
+int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, float scale, int num_seqs,
+                                     int num_q_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int num_blocks, int max_blocks_per_seq,
+                                     int max_context_len, pkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, int partition, int path, int grid,
+                                     void* begin_event, void* end_event, void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0 || partition < 0 || path < PKV_PATH_AUTO ||
@@ -319,14 +319,33 @@ int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
                             reinterpret_cast<int32_t*>(ws + lo.count), st);
     if (err != hipSuccess) return fail_hip(err);
   }
+  if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
+    return fail_hip(err);
   err = use_mfma ? launch_decode_mfma(e, head_dim, block_size, a, st)
                  : launch_decode_valu(e, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
+  if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
+    return fail_hip(err);
   if (pl.max_parts > 1) {
     err = launch_decode_reduce(e, head_dim, a, st);
     if (err != hipSuccess) return fail_hip(err);
   }
   return PKV_OK;
+}
+
+int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, float scale, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_context_len, pkv_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, int partition, int path, int grid,
+                                  void* stream) {
+  return pkv_paged_attention_decode_timed(out, q, k_cache, v_cache, block_tables, context_lens,
+                                          scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          block_size, num_blocks, max_blocks_per_seq,
+                                          max_context_len, dtype, workspace, workspace_bytes,
+                                          partition, path, grid, nullptr, nullptr, stream);
 }
 
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
