@@ -56,8 +56,8 @@ struct Plan {
   int part_align = 32;   // partition sizes are multiples of this
   int max_parts = 1;     // partitions per sequence at most
   int len_cap = 0;       // context lengths are clamped to this
-  bool planned = false;  // work items listed largest first by the planning kernel
-  bool sorted = false;   // direct grid: each workgroup ranks the sequences by length
+  int planned = 0;       // 0 direct; 1 planned, found in each workgroup; 2 planned, listed
+                         // by the planning kernel
   int status = PKV_OK;
 };
 
@@ -134,24 +134,24 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
     pl.status = PKV_EUNSUPPORTED;
     return pl;
   }
-  // Longest first pays off once the grid holds more than one round of
-  // resident workgroups; with fewer, every workgroup starts at once anyway.  The direct grid ranks up to kFusedOrderMax sequences inside
-  // each workgroup (no extra launch); larger batches are planned.
+  // Largest first pays off once the grid holds more than one round of
+  // resident workgroups; with fewer, every workgroup starts at once anyway.
+  // Each workgroup finds its own item for up to kFusedOrderMax sequences (no
+  // extra launch); larger batches are listed by the planning kernel.
   const int64_t wgs = direct_x * num_seqs;
   const bool plannable = wgs <= INT32_MAX && pl.max_parts <= kMaxItemParts;
   const int64_t resident = resident_workgroups(pl.mfma, e, head_dim, block_size, group);
-  const bool longest_first = num_seqs > 1 && wgs > resident;
-  if (grid == PKV_GRID_PLANNED) {
+  const bool want = grid == PKV_GRID_PLANNED ||
+                    (grid == PKV_GRID_AUTO && num_seqs > 1 && wgs > resident);
+  if (want) {
     if (!plannable) {
-      pl.status = PKV_EUNSUPPORTED;
-      return pl;
+      if (grid == PKV_GRID_PLANNED) {
+        pl.status = PKV_EUNSUPPORTED;
+        return pl;
+      }
+    } else {
+      pl.planned = num_seqs <= kFusedOrderMax ? 1 : 2;
     }
-    pl.planned = true;
-  } else if (longest_first) {
-    if (num_seqs <= kFusedOrderMax)
-      pl.sorted = true;
-    else if (grid == PKV_GRID_AUTO && plannable)
-      pl.planned = true;
   }
   return pl;
 }
@@ -173,7 +173,7 @@ Layout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int hea
   lo.part_o = 0;
   lo.part_ml = align16(states * head_dim * sizeof(float));
   lo.scratch = lo.part_ml + align16(states * 2 * sizeof(float));
-  if (!pl.planned) {
+  if (pl.planned != 2) {
     lo.total = lo.scratch;
     return lo;
   }
@@ -245,7 +245,7 @@ int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, in
     out->grid = pl.planned ? PKV_GRID_PLANNED : PKV_GRID_DIRECT;
     out->partition_tokens = pl.part_tokens;
     out->max_parts = pl.max_parts;
-    out->longest_first = pl.planned || pl.sorted ? 1 : 0;
+    out->longest_first = pl.planned ? 1 : 0;
     out->workspace_bytes = workspace_for(num_seqs, num_q_heads, num_kv_heads, head_dim, pl);
   }
   return PKV_OK;
@@ -293,10 +293,9 @@ int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cac
   char* ws = static_cast<char*>(workspace);
   a.part_o = pl.max_parts > 1 ? reinterpret_cast<float*>(ws + lo.part_o) : nullptr;
   a.part_ml = pl.max_parts > 1 ? reinterpret_cast<float*>(ws + lo.part_ml) : nullptr;
-  a.items = pl.planned ? reinterpret_cast<const int32_t*>(ws + lo.items) : nullptr;
-  a.item_count = pl.planned ? reinterpret_cast<const int32_t*>(ws + lo.count) : nullptr;
-  a.planned = pl.planned ? 1 : 0;
-  a.sorted = pl.sorted ? 1 : 0;
+  a.items = pl.planned == 2 ? reinterpret_cast<const int32_t*>(ws + lo.items) : nullptr;
+  a.item_count = pl.planned == 2 ? reinterpret_cast<const int32_t*>(ws + lo.count) : nullptr;
+  a.planned = pl.planned;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -312,7 +311,7 @@ int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cac
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (pl.planned) {
+  if (pl.planned == 2) {
     err = launch_plan_items(context_lens, num_seqs, pl.len_cap, pl.part_tokens, pl.part_align,
                             reinterpret_cast<int32_t*>(ws + lo.scratch),
                             reinterpret_cast<int32_t*>(ws + lo.items),

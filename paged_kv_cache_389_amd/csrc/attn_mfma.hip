@@ -383,8 +383,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     DecodeArgs a) {
   using T = typename E::storage;
   __shared__ MfmaShared<HD, GMAX> sm;
-  __shared__ OrderScratch sm_order;
-  const WorkItem w = work_item(a, a.num_kv_heads, sm_order);
+  __shared__ PlanScratch sm_plan;
+  const WorkItem w = work_item(a, a.num_kv_heads, sm_plan);
   if (!w.valid) return;
   const int s = uniform(w.s), g = w.unit, G = a.group;
   const int wave = uniform(threadIdx.x / kWave);

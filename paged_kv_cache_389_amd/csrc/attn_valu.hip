@@ -343,8 +343,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   using T = typename E::storage;
   constexpr int UT = ValuTiling<E, HD, BS>::UT;
   __shared__ ValuShared<HD> sm;
-  __shared__ OrderScratch sm_order;
-  const WorkItem w = work_item(a, a.num_q_heads, sm_order);
+  __shared__ PlanScratch sm_plan;
+  const WorkItem w = work_item(a, a.num_q_heads, sm_plan);
   if (!w.valid) return;
   const int s = uniform(w.s), h = w.unit;
   T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * HD;

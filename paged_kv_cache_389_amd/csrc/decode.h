@@ -10,18 +10,6 @@
 
 namespace pkv {
 
-// Partitions.  A context of L > 0 tokens is cut into n = ceil(L / P)
-// partitions of equal size, rounded up to `align` tokens (the last one
-// shorter), so no partition is a small remainder; P (part_tokens) is a
-// multiple of align, hence every partition holds at most P tokens and the
-// last one at least one.  A context of L <= 0 tokens has one (empty)
-// partition, which writes the zero row.
-__host__ __device__ inline int num_parts(int L, int P) { return L <= 0 ? 1 : (L + P - 1) / P; }
-__host__ __device__ inline int part_size(int L, int n, int align) {
-  const int ps = (L + n - 1) / n;
-  return (ps + align - 1) / align * align;
-}
-
 // Everything a decode launch needs.  Passed by value as the kernel argument.
 //
 // Grid.  Direct: (units * max_parts, 1, B), workgroup (x, z) computes
@@ -58,8 +46,8 @@ struct DecodeArgs {
   int part_align;             // partition sizes are multiples of this
   int max_parts;              // ceil(len_cap / P): partitions per sequence at most
   int contiguous;             // 1: ignore tables; block j of seq s is s*max_blocks + j
-  int planned;                // 1: planned grid, 0: direct grid
-  int sorted;                 // direct grid: row z is the z-th longest sequence (B <= 1024)
+  int planned;                // 0: direct grid; 1: planned, each workgroup finds its item
+                              // (B <= 1024); 2: planned, items listed by the planning kernel
 };
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
@@ -73,11 +61,11 @@ struct WorkItem {
   bool valid;
 };
 
-__device__ inline WorkItem work_item(const DecodeArgs& a, int units, OrderScratch& sm) {
+__device__ inline WorkItem work_item(const DecodeArgs& a, int units, PlanScratch& sm) {
   WorkItem w;
   w.unit = blockIdx.x % units;
   const int k = blockIdx.x / units;
-  if (a.planned) {
+  if (a.planned == 2) {
     // scalar reads: the count and the item are fetched together
     const int cnt = load_uniform(a.item_count);
     const i32x4 it = load_uniform4(a.items + 4 * (size_t)k);
@@ -87,11 +75,18 @@ __device__ inline WorkItem work_item(const DecodeArgs& a, int units, OrderScratc
     w.t0 = it[2];
     w.t1 = it[3];
     w.valid = k < cnt;
+  } else if (a.planned == 1) {
+    // every thread takes this branch or none: the planning has barriers
+    int item[5];
+    w.valid = plan_item(a.context_lens, a.num_seqs, a.len_cap, a.part_tokens, a.part_align, k, sm,
+                        item);
+    w.s = uniform(item[0]);
+    w.part = uniform(item[1]);
+    w.n = uniform(item[2]);
+    w.t0 = uniform(item[3]);
+    w.t1 = uniform(item[4]);
   } else {
-    // every thread takes this branch or none (a.sorted is uniform): the
-    // ranking has barriers
-    w.s = a.sorted ? uniform(sorted_sequence(a.context_lens, a.num_seqs, a.len_cap, blockIdx.z, sm))
-                   : (int)blockIdx.z;
+    w.s = blockIdx.z;
     w.part = k;
     int L = load_uniform(a.context_lens + w.s);
     L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);

@@ -72,16 +72,17 @@ def test_workspace_bytes_and_plan(native):
     # one partition per (sequence, head) when there are enough of them; the
     # grid holds more than one round of resident workgroups (the host
     # assumes 4 VALU / 3 MFMA per compute unit and 256 units without a
-    # device), so the workgroups rank the sequences longest first
+    # device), so the work is planned largest first, each workgroup finding
+    # its own item (no workspace)
     p = plan(64, 40, 40, 128, 16, 128, 2048, f16)
     assert (p["path"], p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
-        (native.PATH_VALU, D, 2048, 1, 1)
+        (native.PATH_VALU, PL, 2048, 1, 1)
     assert p["workspace_bytes"] == 0
     p = plan(256, 32, 8, 128, 16, 256, 4096, bf16)
     assert (p["path"], p["grid"], p["max_parts"], p["longest_first"], p["workspace_bytes"]) == \
-        (native.PATH_MFMA, D, 1, 1, 0)
+        (native.PATH_MFMA, PL, 1, 1, 0)
     # few units, long contexts: split so that every compute unit gets about
-    # two workgroups (512 of them: one round, so not ranked)
+    # two workgroups (512 of them: one round, so direct)
     p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16)
     assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
         (D, 4096, 8, 0)
@@ -91,16 +92,15 @@ def test_workspace_bytes_and_plan(native):
     assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
         (D, 4096, 8, 0)
     assert p["workspace_bytes"] == 8 * 64 * 8 * 128 * 4 + 8 * 64 * 8 * 2 * 4
-    # 2048 workgroups: ranked longest first; the planned grid on request
-    # adds the work list after the partial states
+    # 2048 workgroups: planned, partial states only; the direct grid on request
     p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024)
-    assert (p["grid"], p["max_parts"], p["longest_first"]) == (D, 32, 1)
-    assert p["workspace_bytes"] == 8 * 64 * 32 * (128 + 2) * 4
-    p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024, grid=PL)
     assert (p["grid"], p["max_parts"], p["longest_first"]) == (PL, 32, 1)
-    assert p["workspace_bytes"] == 8 * 64 * 32 * (128 + 2) * 4 + \
-        items_bytes(8, 32)
-    # more than 1024 sequences to rank: planned in one workgroup
+    assert p["workspace_bytes"] == 8 * 64 * 32 * (128 + 2) * 4
+    p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16, 1024, grid=D)
+    assert (p["grid"], p["max_parts"], p["longest_first"]) == (D, 32, 0)
+    assert p["workspace_bytes"] == 8 * 64 * 32 * (128 + 2) * 4
+    # more than 1024 sequences: the planning kernel lists the items in the
+    # workspace
     p = plan(2000, 8, 8, 128, 16, 8, 128, f16)
     assert (p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
         (PL, 128, 1, 1)
@@ -152,7 +152,6 @@ def _decode(lib, **over):
     (dict(B=4000, Hq=4, Hkv=4, maxL=64, maxb=4), -3),   # planned grid and no workspace
     (dict(part=-1), -1),
     (dict(grid=3), -1),
-    (dict(grid=2), -3),          # planned grid on request and no workspace
     (dict(path=7), -1),
 ])
 def test_decode_rejects_bad_arguments_before_launch(native, over, status):
