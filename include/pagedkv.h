@@ -117,11 +117,13 @@ typedef struct {
  * of equal size (rounded up to a multiple of max(32, block_size) tokens, the
  * last one shorter), one workgroup per partition and head unit (a KV head
  * for MFMA, a query head for VALU), merged by a second kernel when n > 1.
- * partition_tokens == 0 lets the library choose P (one partition per
- * sequence unless the (sequence, head) units are too few to give every
- * compute unit about two workgroups, never below 512 tokens and at most 256
- * units of the kernel: 4096 tokens for 16-bit types with head_dim 128); an
- * explicit P must be a multiple of 32 and of block_size and at most 2^20.
+ * partition_tokens == 0 lets the library choose P: when the (sequence, head)
+ * units are too few to give every compute unit about two workgroups, the
+ * contexts are cut to do so (never below 512 tokens); otherwise contexts
+ * longer than half the length bound are cut in two (never below 2048
+ * tokens), so that no single long context ends the launch alone; at most
+ * 256 units of the kernel (4096 tokens for 16-bit types with head_dim 128).
+ * An explicit P must be a multiple of 32 and of block_size and at most 2^20.
  *
  * Grid DIRECT: workgroups in (head unit, partition, sequence) order.  When
  * the grid holds more than one round of resident workgroups and the batch

@@ -18,6 +18,7 @@ thread_local std::string g_last_error;
 constexpr int kPartAlign = 32;          // tokens; partitions are whole 32-token spans
 constexpr int kMinAutoPartition = 512;  // the library never splits finer than this
 constexpr int kWgPerCu = 2;             // split until about this many workgroups per CU
+constexpr int kSplitFloor = 2048;       // tokens; many-unit batches split no finer
 constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxItemParts = 65535;    // a work item packs (part, n) into 16 bits each
@@ -116,15 +117,24 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
     }
     p = requested;
   } else {
-    // one partition per (sequence, head) unit unless those units are too
-    // few to give every compute unit several workgroups
+    // Few (sequence, head) units: cut the contexts so that every compute
+    // unit gets about kWgPerCu workgroups.  Many units: the grid is full
+    // anyway, but a context much longer than the others would be one long
+    // workgroup that ends last, so contexts longer than half the bound are
+    // cut in two (never below kSplitFloor tokens per partition).
     const int64_t units = (int64_t)num_seqs * units_per_seq;
     const int64_t target = (int64_t)kWgPerCu * compute_units();
-    const int64_t parts = units >= target ? 1 : (target + units - 1) / units;
     const int len = pl.len_cap > 0 ? pl.len_cap : 1;
-    p = round_up((int)((len + parts - 1) / parts), pl.part_align);
-    if (p < kMinAutoPartition)
-      p = round_up(len < kMinAutoPartition ? len : kMinAutoPartition, pl.part_align);
+    if (units >= target) {
+      p = round_up((len + 1) / 2, pl.part_align);
+      if (p < kSplitFloor) p = kSplitFloor;
+      if (p >= len) p = round_up(len, pl.part_align);
+    } else {
+      const int64_t parts = (target + units - 1) / units;
+      p = round_up((int)((len + parts - 1) / parts), pl.part_align);
+      if (p < kMinAutoPartition)
+        p = round_up(len < kMinAutoPartition ? len : kMinAutoPartition, pl.part_align);
+    }
     if (p > p_max) p = p_max;
   }
   pl.part_tokens = p;

@@ -78,9 +78,11 @@ def test_workspace_bytes_and_plan(native):
     assert (p["path"], p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
         (native.PATH_VALU, PL, 2048, 1, 1)
     assert p["workspace_bytes"] == 0
+    # ... and contexts longer than half the bound are cut in two
     p = plan(256, 32, 8, 128, 16, 256, 4096, bf16)
-    assert (p["path"], p["grid"], p["max_parts"], p["longest_first"], p["workspace_bytes"]) == \
-        (native.PATH_MFMA, PL, 1, 1, 0)
+    assert (p["path"], p["grid"], p["partition_tokens"], p["max_parts"], p["longest_first"]) == \
+        (native.PATH_MFMA, PL, 2048, 2, 1)
+    assert p["workspace_bytes"] == 256 * 32 * 2 * (128 + 2) * 4
     # few units, long contexts: split so that every compute unit gets about
     # two workgroups (512 of them: one round, so direct)
     p = plan(8, 64, 8, 128, 32, 1024, 32768, bf16)
