@@ -146,7 +146,11 @@ __device__ inline int mfma_first_blocks(const DecodeArgs& a, int s, int ta, int 
   return a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
 }
 
-template <typename E, int HD, int BS, int NS = kMfmaStages>
+//
+// With kWaitQ the workgroup's Q^T is still being written to LDS: every wave
+// passes one barrier, right after issuing the loads of its first tiles
+// (or at once if it has none), so those loads overlap the query's.
+template <typename E, int HD, int BS, bool kWaitQ = false, int NS = kMfmaStages>
 __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
                                        int first, int stride, int tbl0, const u32x4 (*q)[kWave],
                                        MfmaState<HD / 16>& st) {
@@ -179,6 +183,7 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
   int bad = st.bad;
 
   // passes of at most 64 of the wave's tiles: their table entries fit one VGPR
+  if (kWaitQ && ta + first >= tb) __syncthreads();   // no tiles: the barrier alone
   for (int pass = ta + first; pass < tb; pass += kWave * stride) {
     const int mine = min(kWave, (tb - pass + stride - 1) / stride);
     int tbl = tbl0;
@@ -284,6 +289,7 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
     uint32_t vb[NS][4][VW];
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
+    if (kWaitQ && pass == ta + first) __syncthreads();   // Q^T is in LDS
     for (int i0 = 0; i0 < mine; i0 += NS) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -326,8 +332,7 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
 
   MfmaState<DPL> st;
   mfma_state_init(st);
-  __syncthreads();   // Q^T is in LDS
-  mfma_accumulate<E, HD, BS>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q, st);
+  mfma_accumulate<E, HD, BS, true>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q, st);
 
   // the four token groups of a head column hold partial sums of l
   const float l = rows_sum(st.l);
