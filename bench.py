@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
 DEFAULT_WORKLOAD = "opt13b_fp16"
 DTYPE_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 WORKLOAD_DESC = {
@@ -76,6 +77,8 @@ def parse():
     p.add_argument("--cal-fetch-db")
     p.add_argument("--cal-write-db")
     p.add_argument("--cal-mib", type=int, default=1024)
+    p.add_argument("--swap", type=int, default=0, metavar="BLOCKS",
+                   help="measure swap_blocks of this many K+V block pairs each way instead")
     return p.parse_args()
 
 
@@ -252,6 +255,68 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
     return wall, decode_ms, kernel_ms, plan
 
 
+def bench_swap(args):
+    """swap_blocks between the device cache and a pool in pinned host memory.
+
+    Blocks of the llama-3-8B decode shape (8 KV heads x 16 tokens x 128,
+    bf16: 32 KiB per K block and as much per V block); ``--swap`` pairs of
+    distinct, randomly placed blocks go out (device -> host) and back in
+    (host -> device) each step.  Throughput is K+V bytes moved over the
+    kernel's time (torch events around the launch on the current stream),
+    set against the host link's published peak (PCIe 5.0 x16, 64 GB/s per
+    direction) and against a DMA copy of one contiguous buffer of the same
+    size."""
+    from paged_kv_cache_389_amd import _native as pk
+    n = args.swap
+    hkv, bs, hd, dt = 8, 16, 128, torch.bfloat16
+    g = torch.Generator().manual_seed(389)
+    dev_blocks, host_blocks = max(2 * n, 4096), n + n // 4
+    kd = torch.randn((dev_blocks, hkv, bs, hd), generator=g).to(dt).cuda()
+    vd = torch.randn((dev_blocks, hkv, bs, hd), generator=g).to(dt).cuda()
+    kh = torch.zeros((host_blocks, hkv, bs, hd), dtype=dt).pin_memory()
+    vh = torch.zeros((host_blocks, hkv, bs, hd), dtype=dt).pin_memory()
+    d_sel = torch.randperm(dev_blocks, generator=g)[:n]
+    h_sel = torch.randperm(host_blocks, generator=g)[:n]
+    out_pairs = torch.stack([d_sel, h_sel], 1).cuda()
+    in_pairs = torch.stack([h_sel, torch.randperm(dev_blocks, generator=g)[:n]], 1).cuda()
+    moved = 2 * n * hkv * bs * hd * 2
+    flat_d = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    flat_h = torch.empty(moved, dtype=torch.uint8).pin_memory()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_out = timed(lambda: pk.swap_blocks(kd, vd, kh, vh, out_pairs))
+    ms_in = timed(lambda: pk.swap_blocks(kh, vh, kd, vd, in_pairs))
+    ms_dma_out = timed(lambda: flat_h.copy_(flat_d, non_blocking=True))
+    ms_dma_in = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
+    gbs = lambda ms: round(moved / (ms / 1e3) / 1e9, 2)
+    both = 2 * moved / ((ms_out + ms_in) / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "swap_blocks: K+V bytes moved per second, device <-> pinned host",
+        "value": round(both, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_out + ms_in, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, random distinct block pairs)",
+        "config": {"workload": "swap_llama3_8b_blocks", "pairs": n, "num_kv_heads": hkv,
+                   "block_size": bs, "head_dim": hd, "bytes_each_way": moved},
+        "out_gbs": gbs(ms_out), "in_gbs": gbs(ms_in),
+        "dma_contiguous_out_gbs": gbs(ms_dma_out), "dma_contiguous_in_gbs": gbs(ms_dma_in),
+        "roofline": {"bound": "host-link", "achieved": round(both, 2), "peak": HOST_LINK_GBS,
+                     "unit": "GB/s", "frac": round(both / HOST_LINK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel"}}), flush=True)
+
+
 def cpu_baseline(wl, budget_s):
     """The float64 oracle, single-threaded, over whole sequences (all heads)
     in index order until the time budget is used; throughput in the same
@@ -343,6 +408,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.swap:
+        bench_swap(args)
         return
     names = sorted(WORKLOAD_DESC) if args.sweep else [args.workload]
     for name in names:

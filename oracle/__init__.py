@@ -22,6 +22,7 @@ data, closed forms, invariants and hand-worked fixtures.
 """
 
 from .paged_attention import decode, decode_one, kv_head_of
-from .cache_ops import copy_blocks, reshape_and_cache
+from .cache_ops import copy_blocks, reshape_and_cache, swap_blocks
 
-__all__ = ["decode", "decode_one", "kv_head_of", "copy_blocks", "reshape_and_cache"]
+__all__ = ["decode", "decode_one", "kv_head_of", "copy_blocks", "reshape_and_cache",
+           "swap_blocks"]

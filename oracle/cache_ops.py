@@ -1,4 +1,4 @@
-"""Oracle: the two cache-writing operations, applied to host arrays in place.
+"""Oracle: the cache-writing operations, applied to host arrays in place.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -49,3 +49,18 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
     for src, dst in np.asarray(src_dst_pairs).reshape(-1, 2).tolist():
         k_cache[int(dst)] = k_cache[int(src)]
         v_cache[int(dst)] = v_cache[int(src)]
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs):
+    """Move whole blocks between two pools: ``dst[dst_i] = src[src_i]`` for K
+    and V.
+
+    When memory runs short the engine evicts whole sequences by swapping
+    their blocks out to CPU memory, and brings them back later ("vLLM and
+    PagedAttention: How Ideas from Operating Systems Accelerated LLM
+    Inference", paragraph on the engine).  Either pool may be the device
+    cache; the copy is of bytes only.
+    """
+    for src, dst in np.asarray(src_dst_pairs).reshape(-1, 2).tolist():
+        dst_k[int(dst)] = src_k[int(src)]
+        dst_v[int(dst)] = src_v[int(src)]

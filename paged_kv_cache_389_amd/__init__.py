@@ -6,7 +6,9 @@ Device calls (hand-written gfx950 HIP kernels behind the C ABI in
 * :func:`paged_attention_decode` - single-query attention over a KV cache kept
   in fixed-size physical blocks reached through per-sequence block tables;
 * :func:`reshape_and_cache` - write new tokens' K/V rows into their slots;
-* :func:`copy_blocks` - copy whole blocks (the copy of copy-on-write).
+* :func:`copy_blocks` - copy whole blocks (the copy of copy-on-write);
+* :func:`swap_blocks` - move whole blocks between the device cache and a
+  pool in pinned host memory (eviction by swapping).
 
 Host side: :mod:`.block_manager` (block pool, tables, reference counts, fork,
 copy-on-write) and :mod:`.workloads` (seeded synthetic inputs).
@@ -16,7 +18,8 @@ The device calls load ``libpagedkv.so`` on first use and raise
 CPU implementation.
 """
 
-_NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_bytes", "plan",
+_NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "swap_blocks",
+           "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
            "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")
 

@@ -79,6 +79,8 @@ def _load():
     lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_copy_blocks.restype = i32
     lib.pkv_copy_blocks.argtypes = [vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
+    lib.pkv_swap_blocks.restype = i32
+    lib.pkv_swap_blocks.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, i32, vp]
     return lib
 
 
@@ -89,7 +91,7 @@ EXPORTED = (
     "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_plan",
     "pkv_paged_attention_decode",
     "pkv_paged_attention_decode_ex", "pkv_paged_attention_decode_timed",
-    "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
 )
 
 
@@ -249,6 +251,44 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
                                  src_dst_pairs.shape[0], hkv, hd, bs, nb,
                                  _DTYPE_CODE[k_cache.dtype], _stream(k_cache, stream))
     _check("copy_blocks", st)
+
+
+def _reachable(t: torch.Tensor, name: str):
+    """A tensor the device can address: HIP device memory or pinned host memory."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" and not (t.device.type == "cpu" and t.is_pinned()):
+        raise ValueError(f"{name} must be on a HIP device or in pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, stream=None):
+    """``dst[pair[1]] = src[pair[0]]`` for whole blocks of the K and V pools,
+    between the device cache and a pool in pinned host memory (either way;
+    ``pkv_swap_blocks``).  ``src_dst_pairs`` is int64 [n, 2] on the device.
+    Asynchronous on the current stream of the device pool."""
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        _reachable(t, n)
+    _dev(src_dst_pairs, "src_dst_pairs")
+    dt = src_k.dtype
+    if dt not in _DTYPE_CODE or any(t.dtype != dt for t in (src_v, dst_k, dst_v)):
+        raise ValueError("pools must share one supported dtype")
+    if src_k.dim() != 4 or src_v.shape != src_k.shape or dst_k.dim() != 4 or \
+            dst_v.shape != dst_k.shape or dst_k.shape[1:] != src_k.shape[1:]:
+        raise ValueError("pools must be [num_blocks, num_kv_heads, block_size, head_dim] alike")
+    if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or \
+            src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    nsrc, hkv, bs, hd = src_k.shape
+    ndst = dst_k.shape[0]
+    dev = src_dst_pairs.device
+    with torch.cuda.device(dev):
+        st = lib.pkv_swap_blocks(_ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v),
+                                 _ptr(src_dst_pairs), src_dst_pairs.shape[0], hkv, hd, bs, nsrc,
+                                 ndst, _DTYPE_CODE[dt], _stream(src_dst_pairs, stream))
+    _check("swap_blocks", st)
 
 
 class HipEvent:

@@ -23,6 +23,9 @@ Behaviour, from the pages:
   only then is the token written ("Memory Optimization ...", section
   "Advanced Capabilities: Memory Sharing with Copy-on-Write"; "vLLM and
   PagedAttention ...", paragraph on sharing).
+* When device memory runs short, whole sequences are evicted by swapping
+  their blocks to a pool in CPU memory and brought back later ("vLLM and
+  PagedAttention ...", paragraph on the engine).
 
 Readings where the pages are silent:
 
@@ -31,6 +34,9 @@ Readings where the pages are silent:
 * Slot numbering: slot ``b * block_size + o`` is offset ``o`` of block ``b``.
 * Free blocks are handed out from the end of a free list; its initial order
   may be given (a seeded permutation gives random placement).
+* A swap moves a group of sequences that holds every reference to its
+  blocks (a prompt and its forks): each distinct block moves once, keeps its
+  count, and every table of the group is rewritten.
 """
 
 from __future__ import annotations
@@ -45,22 +51,25 @@ class OutOfBlocks(RuntimeError):
 class Sequence:
     """One sequence's logical view: its block table and its token count."""
 
-    __slots__ = ("seq_id", "table", "length")
+    __slots__ = ("seq_id", "table", "length", "on_host")
 
     def __init__(self, seq_id: int):
         self.seq_id = seq_id
         self.table: list[int] = []
         self.length = 0
+        self.on_host = False   # the table indexes the host pool (swapped out)
 
     def __repr__(self):
-        return f"Sequence(id={self.seq_id}, len={self.length}, table={self.table})"
+        where = "host" if self.on_host else "device"
+        return f"Sequence(id={self.seq_id}, len={self.length}, {where} table={self.table})"
 
 
 class BlockManager:
     """A pool of ``num_blocks`` physical blocks of ``block_size`` token slots."""
 
-    def __init__(self, num_blocks: int, block_size: int, free_order=None):
-        if num_blocks <= 0 or block_size <= 0:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None,
+                 num_host_blocks: int = 0):
+        if num_blocks <= 0 or block_size <= 0 or num_host_blocks < 0:
             raise ValueError("num_blocks and block_size must be positive")
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
@@ -76,6 +85,10 @@ class BlockManager:
         self._next_id = 0
         # copy-on-write pairs (src, dst) emitted since the last take_copy_pairs()
         self._pending_copies: list[tuple[int, int]] = []
+        # the host pool that swapped-out blocks live in
+        self.num_host_blocks = int(num_host_blocks)
+        self._host_free = list(range(self.num_host_blocks - 1, -1, -1))
+        self.host_refcount = np.zeros(self.num_host_blocks, dtype=np.int64)
 
     # ------------------------------------------------------------------ pool
     @property
@@ -113,6 +126,8 @@ class BlockManager:
         Raises :class:`OutOfBlocks` without changing any state if the pool
         cannot supply the block.
         """
+        if seq.on_host:
+            raise ValueError("the sequence is swapped out; swap it in first")
         bs = self.block_size
         offset = seq.length % bs
         if offset == 0:
@@ -154,9 +169,73 @@ class BlockManager:
     def free(self, seq: Sequence) -> None:
         """Drop the sequence's hold on its blocks; unreferenced blocks return."""
         for b in reversed(seq.table):
-            self._release(b)
+            if seq.on_host:
+                self.host_refcount[b] -= 1
+                if self.host_refcount[b] == 0:
+                    self._host_free.append(b)
+            else:
+                self._release(b)
         seq.table = []
         seq.length = 0
+        seq.on_host = False
+
+    # ------------------------------------------------------------------ swap
+    def _group_blocks(self, seqs, on_host: bool):
+        """Distinct blocks of the group in first-use order, checked to be
+        held by the group alone."""
+        order, count = [], {}
+        for s in seqs:
+            if s.on_host != on_host:
+                raise ValueError(f"sequence {s.seq_id} is not on the "
+                                 f"{'host' if on_host else 'device'}")
+            for b in s.table:
+                if b not in count:
+                    order.append(b)
+                    count[b] = 0
+                count[b] += 1
+        refs = self.host_refcount if on_host else self.refcount
+        for b in order:
+            if count[b] != refs[b]:
+                raise ValueError(f"block {b} is also held outside the group")
+        return order
+
+    def _move(self, seqs, order, to_host: bool) -> np.ndarray:
+        src_refs, dst_refs = ((self.refcount, self.host_refcount) if to_host
+                              else (self.host_refcount, self.refcount))
+        src_free, dst_free = ((self._free, self._host_free) if to_host
+                              else (self._host_free, self._free))
+        mapping = {}
+        for b in order:
+            d = dst_free.pop()
+            dst_refs[d] = src_refs[b]
+            src_refs[b] = 0
+            src_free.append(b)
+            mapping[b] = d
+        for s in seqs:
+            s.table = [mapping[b] for b in s.table]
+            s.on_host = to_host
+        return np.array([(b, mapping[b]) for b in order], dtype=np.int64).reshape(-1, 2)
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Move the group's blocks to the host pool.  Returns int64 [n, 2]
+        (device block, host block) pairs, one per distinct block, for
+        swap_blocks; raises :class:`OutOfBlocks` (state unchanged) when the
+        host pool is short."""
+        seqs = list(seqs)
+        order = self._group_blocks(seqs, on_host=False)
+        if len(order) > len(self._host_free):
+            raise OutOfBlocks(f"need {len(order)} host blocks, {len(self._host_free)} free")
+        return self._move(seqs, order, to_host=True)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Move the group's blocks back to the device pool.  Returns int64
+        [n, 2] (host block, device block) pairs; raises :class:`OutOfBlocks`
+        (state unchanged) when the device pool is short."""
+        seqs = list(seqs)
+        order = self._group_blocks(seqs, on_host=True)
+        if len(order) > len(self._free):
+            raise OutOfBlocks(f"need {len(order)} device blocks, {len(self._free)} free")
+        return self._move(seqs, order, to_host=False)
 
     def take_copy_pairs(self) -> np.ndarray:
         """Copy-on-write pairs emitted since the last call, as int64 [n, 2]."""

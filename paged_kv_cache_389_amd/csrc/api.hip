@@ -400,8 +400,31 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int first = 0; first < num_pairs; first += kMaxGridYZ) {
     const int n = num_pairs - first < kMaxGridYZ ? num_pairs - first : kMaxGridYZ;
-    hipError_t err = launch_copy_blocks(k_cache, v_cache, src_dst_pairs + 2 * (size_t)first, n,
-                                        block_bytes, num_blocks, st);
+    hipError_t err = launch_copy_blocks(k_cache, v_cache, k_cache, v_cache,
+                                        src_dst_pairs + 2 * (size_t)first, n, block_bytes,
+                                        num_blocks, num_blocks, st);
+    if (err != hipSuccess) return fail_hip(err);
+  }
+  return PKV_OK;
+}
+
+int pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                    const int64_t* src_dst_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                    int block_size, int num_src_blocks, int num_dst_blocks, pkv_dtype dtype,
+                    void* stream) {
+  if (!dtype_ok(dtype) || num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_src_blocks <= 0 || num_dst_blocks <= 0)
+    return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !src_dst_pairs) return PKV_EINVAL;
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_size(dtype);
+  if (block_bytes % 16) return PKV_EUNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int first = 0; first < num_pairs; first += kMaxGridYZ) {
+    const int n = num_pairs - first < kMaxGridYZ ? num_pairs - first : kMaxGridYZ;
+    hipError_t err = launch_copy_blocks(dst_k, dst_v, src_k, src_v,
+                                        src_dst_pairs + 2 * (size_t)first, n, block_bytes,
+                                        num_src_blocks, num_dst_blocks, st);
     if (err != hipSuccess) return fail_hip(err);
   }
   return PKV_OK;

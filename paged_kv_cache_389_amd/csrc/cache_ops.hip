@@ -34,23 +34,29 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-// Grid (chunks, 2, pairs): y selects the K or the V cache; each workgroup
-// copies one chunk of 256 threads x 4 vectors (16 KiB) of one block.
+// Grid (chunks, 2, pairs): y selects the K or the V pool; each workgroup
+// copies one chunk of 256 threads x 4 vectors (16 KiB) of one block from
+// block src of the source pools to block dst of the destination pools.
+// Pairs naming a block outside its pool are skipped.
 //
-// Passage: copy-on-write copies the shared block's content into a new block
+// Passages: copy-on-write copies the shared block's content into a new block
 // ("Memory Optimization ...", section "Advanced Capabilities: Memory Sharing
 // with Copy-on-Write"); one block is copied, not the whole cache ("vLLM and
-// PagedAttention ...", paragraph on sharing).
+// PagedAttention ...", paragraph on sharing).  The engine evicts whole
+// sequences by swapping their blocks to CPU memory (same page, paragraph on
+// the engine): the same copy between a device pool and a pool in pinned
+// host memory, which the kernel reads or writes directly over the host link.
 constexpr int kCopyUnroll = 4;
-__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* k_cache, u32x4* v_cache,
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* dst_k, u32x4* dst_v,
+                                                          const u32x4* src_k, const u32x4* src_v,
                                                           const int64_t* __restrict__ pairs,
-                                                          int64_t block_vecs, int num_blocks) {
+                                                          int64_t block_vecs, int num_src,
+                                                          int num_dst) {
   const int64_t src = pairs[2 * (size_t)blockIdx.z];
   const int64_t dst = pairs[2 * (size_t)blockIdx.z + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  u32x4* cache = blockIdx.y == 0 ? k_cache : v_cache;
-  const u32x4* from = cache + src * block_vecs;
-  u32x4* to = cache + dst * block_vecs;
+  if (src < 0 || src >= num_src || dst < 0 || dst >= num_dst) return;
+  const u32x4* from = (blockIdx.y == 0 ? src_k : src_v) + src * block_vecs;
+  u32x4* to = (blockIdx.y == 0 ? dst_k : dst_v) + dst * block_vecs;
   const int64_t base = (int64_t)blockIdx.x * 256 * kCopyUnroll + threadIdx.x;
   u32x4 buf[kCopyUnroll];
 #pragma unroll
@@ -77,13 +83,15 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
-                              size_t block_bytes, int num_blocks, hipStream_t st) {
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int64_t* pairs, int num_pairs, size_t block_bytes, int num_src,
+                              int num_dst, hipStream_t st) {
   const int64_t block_vecs = (int64_t)(block_bytes / 16);
   const int64_t per_wg = 256 * kCopyUnroll;
   dim3 grid((unsigned)((block_vecs + per_wg - 1) / per_wg), 2, (unsigned)num_pairs);
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, st, static_cast<u32x4*>(k_cache),
-                     static_cast<u32x4*>(v_cache), pairs, block_vecs, num_blocks);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, st, static_cast<u32x4*>(dst_k),
+                     static_cast<u32x4*>(dst_v), static_cast<const u32x4*>(src_k),
+                     static_cast<const u32x4*>(src_v), pairs, block_vecs, num_src, num_dst);
   return hipGetLastError();
 }
 

@@ -126,7 +126,10 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                     int row_bytes, int block_size, int num_blocks,
                                     hipStream_t stream);
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
-                              size_t block_bytes, int num_blocks, hipStream_t stream);
+// dst pools[pairs[i][1]] = src pools[pairs[i][0]] for K and V (pools may be
+// the same, for copy-on-write).
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int64_t* pairs, int num_pairs, size_t block_bytes, int num_src,
+                              int num_dst, hipStream_t stream);
 
 }  // namespace pkv

@@ -26,7 +26,8 @@ def native():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for call in ("pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks"):
+    for call in ("pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks",
+                 "pkv_swap_blocks"):
         assert call in names
 
 
@@ -174,6 +175,13 @@ def test_cache_ops_reject_bad_arguments(native):
     assert lib.pkv_copy_blocks(1, 1, None, 3, 8, 128, 16, 64, 1, None) == -1
     assert lib.pkv_copy_blocks(1, 1, 1, -1, 8, 128, 16, 64, 1, None) == -1
     assert lib.pkv_copy_blocks(1, 1, 1, 3, 8, 128, 16, 64, 5, None) == -1
+    # swap_blocks: (dst_k, dst_v, src_k, src_v, pairs, n, hkv, hd, bs, n_src, n_dst, dtype, stream)
+    assert lib.pkv_swap_blocks(None, None, None, None, None, 0, 8, 128, 16, 64, 32, 1, None) == 0
+    assert lib.pkv_swap_blocks(1, 1, 1, None, 1, 3, 8, 128, 16, 64, 32, 1, None) == -1
+    assert lib.pkv_swap_blocks(1, 1, 1, 1, 1, -1, 8, 128, 16, 64, 32, 1, None) == -1
+    assert lib.pkv_swap_blocks(1, 1, 1, 1, 1, 3, 8, 128, 16, 64, 0, 1, None) == -1
+    assert lib.pkv_swap_blocks(1, 1, 1, 1, 1, 3, 8, 128, 16, 64, 32, 7, None) == -1
+    assert lib.pkv_swap_blocks(1, 1, 1, 1, 1, 3, 1, 1, 1, 64, 32, 1, None) == -2
 
 
 def test_binding_rejects_cpu_tensors(native):
@@ -185,3 +193,7 @@ def test_binding_rejects_cpu_tensors(native):
     with pytest.raises(ValueError):
         native.reshape_and_cache(x, x, torch.zeros(4, 2, 2, 8), torch.zeros(4, 2, 2, 8),
                                  torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError):   # pageable host pools are not device-addressable
+        native.swap_blocks(torch.zeros(4, 1, 2, 8), torch.zeros(4, 1, 2, 8),
+                           torch.zeros(4, 1, 2, 8), torch.zeros(4, 1, 2, 8),
+                           torch.zeros(1, 2, dtype=torch.int64))

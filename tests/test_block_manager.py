@@ -176,3 +176,92 @@ def test_write_then_attend_slot_is_last_position():
     for i, slot in enumerate(wl.step.slot_mapping):
         L = int(wl.context_lens[i])
         assert slot == wl.block_tables[i, (L - 1) // 4] * 4 + (L - 1) % 4
+
+
+# ------------------------------------------------------------------- swap
+
+def _gather(pool, seq, bs):
+    """A sequence's logical rows [L, ...] read through its table."""
+    rows = [pool[seq.table[t // bs], :, t % bs] for t in range(seq.length)]
+    return np.stack(rows) if rows else pool[:0, :, 0]
+
+
+def test_swap_round_trip_keeps_content_sharing_and_counts():
+    """A prompt and its forks swapped out, the freed device blocks reused and
+    overwritten, then swapped back in: every sequence reads the same rows,
+    sharing is kept (each distinct block moved once, with its count), and the
+    pools' free lists and counts stay consistent."""
+    import oracle
+    rng = np.random.default_rng(51)
+    bs, hkv, hd, nb, nh = 4, 2, 3, 24, 12
+    bm = BlockManager(nb, bs, free_order=rng.permutation(nb), num_host_blocks=nh)
+    prompt = bm.new_sequence()
+    bm.extend(prompt, 10)
+    kids = [bm.fork(prompt) for _ in range(3)]
+    for i, k in enumerate(kids):
+        bm.extend(k, i + 1)                    # copy-on-write on the shared tail
+    other = bm.new_sequence()
+    bm.extend(other, 5)
+    group = [prompt] + kids
+    dev_k = rng.integers(-900, 900, (nb, hkv, bs, hd)).astype(np.int16)
+    dev_v = rng.integers(-900, 900, (nb, hkv, bs, hd)).astype(np.int16)
+    host_k = np.zeros((nh, hkv, bs, hd), np.int16)
+    host_v = np.zeros((nh, hkv, bs, hd), np.int16)
+    want = [(_gather(dev_k, s, bs), _gather(dev_v, s, bs)) for s in group + [other]]
+    distinct = {b for s in group for b in s.table}
+    counts = {b: int(bm.refcount[b]) for b in distinct}
+
+    out = bm.swap_out(group)
+    assert sorted(out[:, 0].tolist()) == sorted(distinct)
+    assert len(set(out[:, 1].tolist())) == len(out)
+    assert all(bm.host_refcount[h] == counts[d] for d, h in out.tolist())
+    assert all(s.on_host for s in group) and not other.on_host
+    check_invariants(bm, [other])
+    oracle.swap_blocks(dev_k, dev_v, host_k, host_v, out)
+    # the device blocks are free again: another sequence takes and overwrites them
+    filler = bm.new_sequence()
+    bm.extend(filler, bs * len(distinct))
+    for b in filler.table:
+        dev_k[b] = -1
+        dev_v[b] = -1
+    bm.free(filler)
+
+    back = bm.swap_in(group)
+    assert sorted(back[:, 0].tolist()) == sorted(out[:, 1].tolist())
+    oracle.swap_blocks(host_k, host_v, dev_k, dev_v, back)
+    assert not bm.host_refcount.any() and bm.num_host_blocks == len(bm._host_free)
+    check_invariants(bm, group + [other])
+    for s, (k, v) in zip(group + [other], want):
+        assert np.array_equal(_gather(dev_k, s, bs), k)
+        assert np.array_equal(_gather(dev_v, s, bs), v)
+
+
+def test_swap_needs_the_whole_sharing_group():
+    bm = BlockManager(16, 4, num_host_blocks=16)
+    prompt = bm.new_sequence()
+    bm.extend(prompt, 6)
+    kid = bm.fork(prompt)
+    with pytest.raises(ValueError):
+        bm.swap_out([kid])                     # the prompt still holds the blocks
+    assert not kid.on_host and bm.refcount[prompt.table[0]] == 2
+
+
+def test_swap_out_of_host_blocks_leaves_state_unchanged():
+    bm = BlockManager(16, 4, num_host_blocks=2)
+    s = bm.new_sequence()
+    bm.extend(s, 9)                            # three blocks
+    table, free = list(s.table), bm.free_blocks()
+    with pytest.raises(OutOfBlocks):
+        bm.swap_out([s])
+    assert s.table == table and not s.on_host and bm.free_blocks() == free
+
+
+def test_swapped_out_sequence_cannot_append_and_frees_host_blocks():
+    bm = BlockManager(8, 4, num_host_blocks=8)
+    s = bm.new_sequence()
+    bm.extend(s, 5)
+    bm.swap_out([s])
+    with pytest.raises(ValueError):
+        bm.append_slot(s)
+    bm.free(s)
+    assert not bm.host_refcount.any() and len(bm._host_free) == 8 and bm.num_free == 8

@@ -163,3 +163,32 @@ def test_copy_on_write_end_to_end():
     assert np.array_equal(kc[dst, :, 3], new[0])
     assert np.array_equal(kc[shared], k0[shared])
     assert kids[1].table[-1] == shared and bm.refcount[shared] == 2
+
+
+# ------------------------------------------------------------ swap_blocks
+
+def test_swap_blocks_golden(golden_dir):
+    g = _load(golden_dir, "swap_blocks_small.json")
+    sk, sv = np.array(g["src_k"], np.int32), np.array(g["src_v"], np.int32)
+    dk, dv = np.array(g["dst_k"], np.int32), np.array(g["dst_v"], np.int32)
+    s0 = sk.copy()
+    oracle.swap_blocks(sk, sv, dk, dv, np.array(g["src_dst_pairs"], np.int64))
+    assert np.array_equal(dk, np.array(g["expected_dst_k"], np.int32))
+    assert np.array_equal(dv, np.array(g["expected_dst_v"], np.int32))
+    assert np.array_equal(sk, s0)
+
+
+def test_swap_blocks_out_and_back_is_identity():
+    """Swapping blocks out to another pool and back to their places restores
+    the pool byte for byte; unnamed blocks of both pools are untouched."""
+    rng = np.random.default_rng(61)
+    dev = rng.integers(-2**15, 2**15, (9, 2, 4, 8)).astype(np.int16)
+    host = rng.integers(-2**15, 2**15, (5, 2, 4, 8)).astype(np.int16)
+    d0, h0 = dev.copy(), host.copy()
+    out = np.array([[8, 0], [2, 3], [5, 1]], np.int64)
+    oracle.swap_blocks(dev, dev, host, host, out)   # K and V pools aliased: one array
+    assert np.array_equal(host[[0, 3, 1]], d0[[8, 2, 5]])
+    assert np.array_equal(host[[2, 4]], h0[[2, 4]])
+    dev[[8, 2, 5]] = 0
+    oracle.swap_blocks(host, host, dev, dev, out[:, ::-1])
+    assert np.array_equal(dev, d0)
