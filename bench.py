@@ -50,6 +50,11 @@ WORKLOAD_DESC = {
     "sharing_fp16": dict(num_seqs=256, prompts=32, fanout=8, heads="32/32", head_dim=128,
                          block_size=16, context_lens="1024+U[1,15]+U[0,256]",
                          pool_blocks=8192),
+    "beam_search_fp16": dict(num_seqs=128, requests=16, beam_width=8, heads="32/32",
+                             head_dim=128, block_size=16,
+                             context_lens="prompt U[256,1024] + 64 beam steps",
+                             pool_blocks=8192, timed_step="step 64 (its copy-on-write pairs, "
+                                                          "128 new tokens, decode)"),
 }
 
 
@@ -66,6 +71,8 @@ def parse():
     p.add_argument("--placement", default="random", choices=["random", "sequential"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--cpu-pool", type=int, default=min(16, len(os.sched_getaffinity(0))),
+                   help="worker processes of the pooled oracle baseline (<= 1: none)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
     p.add_argument("--counters", metavar="OUT_JSON",
@@ -317,33 +324,97 @@ def bench_swap(args):
                      "kernel": "copy_blocks_kernel"}}), flush=True)
 
 
-def cpu_baseline(wl, budget_s):
-    """The float64 oracle, single-threaded, over whole sequences (all heads)
-    in index order until the time budget is used; throughput in the same
-    unit as the metric (algorithmic KV GB/s of the sample)."""
-    import oracle
-    from threadpoolctl import threadpool_limits
+def _oracle_inputs(wl, seqs):
+    """The oracle's inputs for a set of sequences as host numpy arrays (the
+    blocks they reference, compacted, in a type that holds the workload's
+    values exactly: float16 stays float16, bfloat16 becomes float32)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_helpers import compact_pool
-    done, secs, kv = [], 0.0, 0
-    row = 2 * wl.num_kv_heads * wl.head_dim * wl.esize
+    kc, vc, tables = compact_pool(wl, seqs)
+    host = (lambda t: t.numpy()) if wl.dtype != torch.bfloat16 else \
+        (lambda t: t.float().numpy())
+    return host(wl.q.cpu()), host(kc), host(vc), tables
+
+
+def _time_oracle(q, kc, vc, tables, lens, scale, hkv, seqs, row, budget_s):
+    """Single-threaded oracle over ``seqs`` in order until ``budget_s``;
+    returns (sequences done, KV bytes, seconds)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    done, secs, kv = 0, 0.0, 0
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
-        q_cpu = wl.q.cpu()
-        for s in range(wl.num_seqs):
-            kc, vc, tables = compact_pool(wl, [s])
+        for s in seqs:
             t = time.perf_counter()
-            oracle.decode(q_cpu, kc, vc, tables, wl.context_lens, wl.scale, wl.num_kv_heads,
-                          seqs=[s])
+            oracle.decode(q, kc, vc, tables, lens, scale, hkv, seqs=[s])
             secs += time.perf_counter() - t
-            done.append(s)
-            kv += int(wl.context_lens[s]) * row
+            done += 1
+            kv += int(lens[s]) * row
             if secs >= budget_s:
                 break
-    return {"value": round(kv / secs / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(secs, 3), "queries_per_s": round(len(done) * wl.num_q_heads / secs, 3),
-            "sample": f"{len(done)} of {wl.num_seqs} sequences x all {wl.num_q_heads} query heads "
-                      f"(decode only, float64 numpy, one thread)"}
+    return done, kv, secs
+
+
+def _pool_worker(path):
+    """One process of the pooled CPU baseline: load its share (untimed),
+    then time the oracle over it."""
+    z = np.load(path)
+    return _time_oracle(z["q"], z["kc"], z["vc"], z["tables"], z["lens"], float(z["scale"]),
+                        int(z["hkv"]), [int(x) for x in z["seqs"]], int(z["row"]), float("inf"))
+
+
+def cpu_baseline(wl, budget_s, pool_workers=0):
+    """The float64 oracle over whole sequences (all heads), throughput in the
+    metric's unit (algorithmic KV GB/s of the sample).  One thread, in index
+    order until the time budget is used; then, with ``pool_workers`` > 1, a
+    process pool of that many single-threaded workers over the same number of
+    sequences per worker (capped at the batch), each worker timing its own
+    share after loading it: the pooled rate is the sample's bytes over the
+    slowest worker's time."""
+    row = 2 * wl.num_kv_heads * wl.head_dim * wl.esize
+    order = list(range(wl.num_seqs))
+    q, kc, vc, tables = _oracle_inputs(wl, order)
+    done, kv, secs = _time_oracle(q, kc, vc, tables, wl.context_lens, wl.scale,
+                                  wl.num_kv_heads, order, row, budget_s)
+    res = {"value": round(kv / secs / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "seconds": round(secs, 3), "queries_per_s": round(done / secs, 3),
+           "sample": f"{done} of {wl.num_seqs} sequences x all {wl.num_q_heads} query heads "
+                     f"(decode only, float64 numpy, one thread)"}
+    if pool_workers > 1:
+        res["pool"] = _cpu_pool(wl, row, order[:min(wl.num_seqs, done * pool_workers)],
+                                pool_workers)
+    return res
+
+
+def _cpu_pool(wl, row, seqs, workers):
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    # longest first, dealt round-robin, so the workers' shares are alike
+    seqs = sorted(seqs, key=lambda s: -int(wl.context_lens[s]))
+    shares = [seqs[w::workers] for w in range(workers)]
+    shares = [sh for sh in shares if sh]
+    tmp = tempfile.mkdtemp(dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        paths = []
+        for w, sh in enumerate(shares):
+            path = os.path.join(tmp, f"share{w}.npz")
+            q, kc, vc, tables = _oracle_inputs(wl, sh)   # only this share's blocks
+            np.savez(path, q=q, kc=kc, vc=vc, tables=tables, lens=wl.context_lens,
+                     scale=wl.scale, hkv=wl.num_kv_heads, seqs=np.array(sh), row=row)
+            paths.append(path)
+        with cf.ProcessPoolExecutor(len(paths), mp_context=mp.get_context("spawn")) as ex:
+            results = list(ex.map(_pool_worker, paths))
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    kv = sum(r[1] for r in results)
+    slowest = max(r[2] for r in results)
+    return {"value": round(kv / slowest / 1e9, 6), "unit": "GB/s", "cores": len(paths),
+            "kind": "oracle", "seconds": round(slowest, 3),
+            "queries_per_s": round(len(seqs) / slowest, 3),
+            "sample": f"{len(seqs)} of {wl.num_seqs} sequences over {len(paths)} single-threaded "
+                      f"worker processes (rate = sample bytes / slowest worker's oracle time)"}
 
 
 def bench_one(name, args, with_cpu):
@@ -381,16 +452,25 @@ def bench_one(name, args, with_cpu):
         "decode_ms": round(dec_ms, 5),
         "decode_ms_min": round(float(np.min(decode_ms)), 5),
         "kernel_ms": round(ker_ms, 5),
+        "kernel_ms_median": round(float(np.median(kernel_ms)), 5),
+        "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
+        "gbs_at_median": round(alg_decode / (float(np.median(kernel_ms)) / 1e3) / 1e9, 2),
         "bytes": {"decode_alg": alg_decode, "writes_alg": alg_writes,
                   "kv_logical": wl.kv_bytes()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(name), "kernel": kname},
     }
-    if name == "sharing_fp16":
+    if name in ("sharing_fp16", "beam_search_fp16"):
         line["bytes"]["kv_unique"] = wl.unique_kv_bytes()
+    if name == "beam_search_fp16":
+        from paged_kv_cache_389_amd import workloads
+        pairs = [len(h.copy_pairs) for h in wl.history]
+        line["beam"] = {"copy_pairs_timed_step": pairs[-1],
+                        "copy_pairs_per_step_mean": round(float(np.mean(pairs)), 2),
+                        "block_saving_vs_unshared": round(workloads.sharing_saving(wl), 4)}
     if with_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s, args.cpu_pool)
     return line
 
 

@@ -29,6 +29,12 @@ Five workload shapes (names used throughout the tests and the benchmark):
     through reference counts, then diverge by 0-256 generated tokens; the
     first append into the shared partly filled last block triggers
     copy-on-write.  32 heads (MHA), head_dim 128, block_size 16, pool of 8192.
+``beam_search_fp16``
+    16 requests with prompts of 256-1024 tokens, each decoded with 8 beams
+    for 64 steps: every step appends one token to every beam (copy-on-write
+    where beams share a partly filled last block), then each request's beams
+    are re-drawn from their parents (forks of the chosen, frees of the
+    dropped).  32 heads (MHA), head_dim 128, block_size 16, pool of 8192.
 
 Values are N(0, 1) float32 draws cast (round to nearest even) to the
 workload dtype.  Integer draws use numpy's PCG64 seeded with the workload
@@ -57,6 +63,11 @@ class DecodeStepInputs:
     seq_index: np.ndarray           # int64 [n_tokens], sequence of each token
     new_k: torch.Tensor | None = None   # [n_tokens, Hkv, hd]
     new_v: torch.Tensor | None = None
+    # multi-step workloads whose batch changes between steps (beam search):
+    # the tables and lengths the step's decode runs over, after its writes
+    block_tables: np.ndarray | None = None   # int32 [n_seqs, W]
+    context_lens: np.ndarray | None = None   # int32 [n_seqs]
+    physical_blocks: int = 0                 # device blocks held after the step
 
 
 @dataclass
@@ -276,6 +287,104 @@ def build_sharing(name="sharing_fp16", *, dtype="fp16", num_prompts=32, fanout=8
     return wl
 
 
+def build_beam_search(name="beam_search_fp16", *, dtype="fp16", num_requests=16,
+                      beam_width=8, prompt_lens=(256, 1024), steps=64, num_q_heads=32,
+                      num_kv_heads=32, head_dim=128, block_size=16, num_blocks=8192,
+                      selection_temp=2.0, seed=6, device="cpu", tensors=True):
+    """Beam-search workload: repeated fork and free over shared prefixes.
+
+    Each request's prompt (length uniform in ``prompt_lens``) is written once
+    and forked into ``beam_width`` beams that hold all of its blocks; the
+    prompt's own hold is dropped.  Step ``t`` (1..``steps``) appends one token
+    to every beam, request by request, beam by beam; the block manager turns
+    appends into shared partly filled blocks into copy-on-write pairs.  The
+    step's decode runs over all beams after its writes.  Between steps each
+    request re-draws its beams: every new beam picks a parent among the
+    current ones with probability proportional to ``exp(selection_temp * z)``,
+    ``z ~ N(0, 1)`` per current beam (a stand-in for the beams' scores);
+    parents that nobody picked are freed, a parent picked ``c`` times is kept
+    and forked ``c - 1`` times, and the new batch lists the beams parent by
+    parent.  ``history`` holds every step's pairs, slots, new rows, and the
+    tables and lengths its decode reads; the workload's own tables, lengths
+    and ``q`` are those of the last step.  ``tensors=False`` skips every
+    tensor draw (integer structure only).
+    """
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    rng = np.random.default_rng(seed)
+    lo, hi = prompt_lens
+    plens = rng.integers(lo, hi + 1, size=num_requests)
+    width = -(-(int(plens.max()) + steps) // block_size)
+    bm = BlockManager(num_blocks, block_size, free_order=rng.permutation(num_blocks))
+    beams = []                       # per request: its current beams, in batch order
+    for r in range(num_requests):
+        parent = bm.new_sequence()
+        bm.extend(parent, int(plens[r]))
+        beams.append([bm.fork(parent) for _ in range(beam_width)])
+        bm.free(parent)
+    num_seqs = num_requests * beam_width
+    g = _gen(device, seed)
+    pool_shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    k_cache = v_cache = None
+    if tensors:
+        k_cache = _randn(pool_shape, dt, g, device)
+        v_cache = _randn(pool_shape, dt, g, device)
+    history, lineage = [], []
+    for t in range(1, steps + 1):
+        batch = [b for req in beams for b in req]
+        slots = np.array([bm.append_slot(b) for b in batch], np.int64)
+        st = DecodeStepInputs(copy_pairs=bm.take_copy_pairs(), slot_mapping=slots,
+                              seq_index=np.arange(num_seqs, dtype=np.int64),
+                              block_tables=bm.block_table_array(batch, width=width),
+                              context_lens=bm.context_lens(batch),
+                              physical_blocks=bm.num_blocks - bm.num_free)
+        if tensors:
+            st.new_k = _randn((num_seqs, num_kv_heads, head_dim), dt, g, device)
+            st.new_v = _randn((num_seqs, num_kv_heads, head_dim), dt, g, device)
+        history.append(st)
+        if t == steps:
+            break
+        # re-draw the beams of every request from their parents
+        parents_of_step = []
+        for r in range(num_requests):
+            z = rng.standard_normal(beam_width)
+            w = np.exp(selection_temp * (z - z.max()))
+            picks = rng.choice(beam_width, size=beam_width, p=w / w.sum())
+            count = np.bincount(picks, minlength=beam_width)
+            old = beams[r]
+            for i in range(beam_width):
+                if count[i] == 0:
+                    bm.free(old[i])
+            new, par = [], []
+            for i in range(beam_width):
+                if count[i]:
+                    new.append(old[i])
+                    new.extend(bm.fork(old[i]) for _ in range(count[i] - 1))
+                    par.extend([r * beam_width + i] * int(count[i]))
+            beams[r] = new
+            parents_of_step.extend(par)
+        lineage.append(np.array(parents_of_step, np.int64))
+    final = history[-1]
+    q = _randn((num_seqs, num_q_heads, head_dim), dt, g, device) if tensors else None
+    wl = Workload(
+        name=name, dtype=dt, num_seqs=num_seqs, num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+        num_blocks=num_blocks, scale=1.0 / math.sqrt(head_dim), seed=seed,
+        context_lens=final.context_lens, block_tables=final.block_tables, q=q,
+        k_cache=k_cache, v_cache=v_cache, step=final, history=history,
+        meta={"prompt_lens": plens, "beam_width": beam_width, "steps": steps,
+              "parents": lineage, "utilisation": bm.utilisation([b for q_ in beams for b in q_])})
+    return wl
+
+
+def sharing_saving(wl, step=None) -> float:
+    """1 - physical / logical blocks of a multi-step workload's step (default:
+    the last): the share of block memory that sharing saves against giving
+    every sequence its own copy of its blocks."""
+    st = wl.history[-1] if step is None else wl.history[step]
+    logical = int(((st.context_lens.astype(np.int64) + wl.block_size - 1) // wl.block_size).sum())
+    return 1.0 - st.physical_blocks / logical if logical else 0.0
+
+
 # Full-size presets -------------------------------------------------------
 
 def tiny_fp32(seed=1, device="cpu", **kw):
@@ -312,12 +421,17 @@ def sharing_fp16(seed=5, device="cpu", **kw):
     return build_sharing("sharing_fp16", seed=seed, device=device, **kw)
 
 
+def beam_search_fp16(seed=6, device="cpu", **kw):
+    return build_beam_search("beam_search_fp16", seed=seed, device=device, **kw)
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "opt13b_fp16": opt13b_fp16,
     "llama3_8b_gqa_bf16": llama3_8b_gqa_bf16,
     "long_context_gqa_bf16": long_context_gqa_bf16,
     "sharing_fp16": sharing_fp16,
+    "beam_search_fp16": beam_search_fp16,
 }
 
 

@@ -265,3 +265,60 @@ def test_swapped_out_sequence_cannot_append_and_frees_host_blocks():
         bm.append_slot(s)
     bm.free(s)
     assert not bm.host_refcount.any() and len(bm._host_free) == 8 and bm.num_free == 8
+
+
+@pytest.mark.parametrize("seed,width,temp", [(6, 8, 2.0), (7, 4, 0.5), (8, 3, 5.0)])
+def test_beam_search_tokens_follow_the_beams_lineage(seed, width, temp):
+    """Replaying the beam-search workload's history with the oracle's cache
+    ops on slot ids: after every step, each beam reads, through its table,
+    its request's prompt followed by the tokens of its own ancestry (the
+    parent chain the selection drew), one per step. Also: copy pairs are
+    fresh distinct blocks, held blocks never exceed the pool, and beams keep
+    their count per request."""
+    import oracle
+    bs = 8
+    wl = workloads.build_beam_search(num_requests=5, beam_width=width, prompt_lens=(1, 40),
+                                     steps=30, num_kv_heads=1, head_dim=4, block_size=bs,
+                                     num_blocks=512, selection_temp=temp, seed=seed,
+                                     tensors=False)
+    nb = wl.num_blocks
+    # every slot starts holding its own number (the prompt's content)
+    k = np.arange(nb * bs, dtype=np.int64).reshape(nb, 1, bs, 1).repeat(4, axis=3)
+    v = -k
+    plens = wl.meta["prompt_lens"]
+    first = wl.history[0]
+    # the prompt's own blocks: step 1's tables with its copies traced back
+    origin = {int(d): int(s_) for s_, d in first.copy_pairs}
+    expect = []
+    for i in range(wl.num_seqs):
+        r = i // width
+        t = [origin.get(int(b), int(b)) for b in first.block_tables[i]]
+        expect.append([t[p // bs] * bs + p % bs for p in range(int(plens[r]))])
+    n_pairs = 0
+    for step, st in enumerate(wl.history, start=1):
+        if step > 1:
+            parents = wl.meta["parents"][step - 2]
+            assert len(parents) == wl.num_seqs
+            assert np.array_equal(np.bincount(parents // width, minlength=5), [width] * 5)
+            assert all(parents[i] // width == i // width for i in range(wl.num_seqs))
+            expect = [list(expect[p]) for p in parents]
+        pairs = st.copy_pairs
+        n_pairs += len(pairs)
+        if len(pairs):
+            assert len(set(pairs[:, 1].tolist())) == len(pairs)
+            assert not set(pairs[:, 1].tolist()) & set(pairs[:, 0].tolist())
+        oracle.copy_blocks(k, v, pairs)
+        ids = 10**7 * step + np.arange(wl.num_seqs, dtype=np.int64)
+        new = np.repeat(ids[:, None, None], 4, axis=2)
+        oracle.reshape_and_cache(new, -new, k, v, st.slot_mapping)
+        for i in range(wl.num_seqs):
+            expect[i].append(int(ids[i]))
+            L = int(st.context_lens[i])
+            assert L == len(expect[i])
+            tab = st.block_tables[i]
+            got = [int(k[tab[p // bs], 0, p % bs, 0]) for p in range(L)]
+            assert got == expect[i], f"step {step} beam {i}"
+            assert all(int(v[tab[p // bs], 0, p % bs, 3]) == -e for p, e in enumerate(expect[i]))
+        assert 0 < st.physical_blocks <= nb
+    assert n_pairs > 0
+    assert 0.0 < workloads.sharing_saving(wl) < 1.0

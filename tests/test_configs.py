@@ -1,4 +1,4 @@
-"""Parity at the five workloads' full sizes (GPU).
+"""Parity at the workloads' full sizes (GPU).
 
 Each workload is built at the size and with the seed the benchmark uses, and
 its step runs through the C ABI in the benchmark's launch configuration
@@ -8,7 +8,7 @@ is covered at full size on both grids:
 
 * cache writes (reshape_and_cache) and block copies (copy_blocks) are
   compared with the oracle's byte for byte over the WHOLE K and V buffers;
-  the sharing workload replays its entire history (every step's
+  the sharing and beam-search workloads replay their entire history (every step's
   copy-on-write pairs, then its new tokens) on both sides;
 * attention is compared with the float64 oracle on sampled sequences (the
   longest, the shortest and seeded random ones, all query heads), within
@@ -34,6 +34,7 @@ CASES = {
     "llama3_8b_gqa_bf16": (8, 1024),
     "long_context_gqa_bf16": (2, 1024),
     "sharing_fp16": (8, 512),
+    "beam_search_fp16": (8, 512),
 }
 
 
@@ -96,8 +97,8 @@ def test_full_size_step_matches_oracle(name):
                                  torch.from_numpy(st.slot_mapping).to(DEV))
             n_tok += len(st.slot_mapping)
     torch.cuda.synchronize()
-    if name == "sharing_fp16":
-        assert n_pairs > 0 and n_tok > 0, "the sharing workload must copy and write"
+    if name in ("sharing_fp16", "beam_search_fp16"):
+        assert n_pairs > 0 and n_tok > 0, "the sharing workloads must copy and write"
     if name == "llama3_8b_gqa_bf16":
         assert n_tok == wl.num_seqs
 
