@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA, 3 contiguous")
     p.add_argument("--grid", type=int, default=0, help="0 auto, 1 direct, 2 planned")
+    p.add_argument("--kv-cache", default="auto", choices=["auto", "e4m3"],
+                   help="e4m3: quantise the pools to 8-bit codes and time the 8-bit path")
     p.add_argument("--placement", default="random", choices=["random", "sequential"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -213,24 +215,57 @@ def build_inputs(name, placement):
 
 
 def step_bytes(wl, dev):
-    row = wl.num_kv_heads * wl.head_dim * wl.esize
+    """Algorithmic bytes of the step: (decode, cache writes + copies).  With
+    an 8-bit cache the K/V rows cost one byte per element (q and out keep
+    the workload type) and the quantising write reads source rows and
+    writes code rows."""
+    row_src = wl.num_kv_heads * wl.head_dim * wl.esize
+    row = wl.num_kv_heads * wl.head_dim * (1 if dev.get("kv_fp8") else wl.esize)
     n_tok = 0 if dev["slots"] is None else int(dev["slots"].numel())
     n_pair = 0 if dev["pairs"] is None else int(dev["pairs"].shape[0])
-    writes = 2 * (2 * n_tok * row) + 8 * n_tok
+    writes = 2 * (n_tok * row_src + n_tok * row) + 8 * n_tok
     copies = 2 * (2 * n_pair * row * wl.block_size) + 16 * n_pair
-    return wl.decode_bytes(), writes + copies
+    decode = wl.decode_bytes()
+    if dev.get("kv_fp8"):
+        decode -= wl.kv_bytes() - wl.kv_bytes() // wl.esize
+    return decode, writes + copies
+
+
+def quantise_pools(wl, dev):
+    """Replace the workload's K/V pools by E4M3 code pools (one scale per
+    cache: its largest magnitude over 448), written by the library's
+    quantising cache write over every slot; set-up, not timed."""
+    from paged_kv_cache_389_amd import _native as pk
+    nb, hkv, bs, hd = dev["k"].shape
+    k_scale = float(dev["k"].abs().amax().float()) / 448.0
+    v_scale = float(dev["v"].abs().amax().float()) / 448.0
+    kc = torch.empty((nb, hkv, bs, hd), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    chunk = max(1, (1 << 27) // (hkv * hd * wl.esize) // bs)   # blocks per chunk (~128 MiB)
+    for b0 in range(0, nb, chunk):
+        b1 = min(nb, b0 + chunk)
+        rows_k = dev["k"][b0:b1].permute(0, 2, 1, 3).reshape(-1, hkv, hd).contiguous()
+        rows_v = dev["v"][b0:b1].permute(0, 2, 1, 3).reshape(-1, hkv, hd).contiguous()
+        slots = torch.arange(b0 * bs, b1 * bs, dtype=torch.int64, device="cuda")
+        pk.reshape_and_cache_fp8(rows_k, rows_v, kc, vc, slots, k_scale, v_scale)
+    torch.cuda.synchronize()
+    dev["k"], dev["v"] = kc, vc
+    wl.k_cache = wl.v_cache = None
+    dev.update(kv_fp8=True, k_scale=k_scale, v_scale=v_scale)
 
 
 def run_gpu(wl, dev, steps, warmup, partition, path, grid):
     from paged_kv_cache_389_amd import _native as pk
     tables = None if path == 3 else dev["tables"]
     max_blocks = -(-wl.max_context_len // wl.block_size) if tables is None else tables.shape[1]
+    fp8 = bool(dev.get("kv_fp8"))
+    code = pk._DTYPE_CODE[wl.dtype] | (pk.KV_E4M3 if fp8 else 0)
     ws_len = pk.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                wl.block_size, max_blocks, wl.max_context_len, wl.dtype,
+                                wl.block_size, max_blocks, wl.max_context_len, code,
                                 partition, path, grid)
     ws = torch.empty(max(ws_len, 1), dtype=torch.uint8, device="cuda")
     plan = pk.plan(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-                   max_blocks, wl.max_context_len, wl.dtype, partition, path, grid)
+                   max_blocks, wl.max_context_len, code, partition, path, grid)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     kev = [(pk.HipEvent(), pk.HipEvent()) for _ in range(steps)]
@@ -239,13 +274,25 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
         if dev["pairs"] is not None:
             pk.copy_blocks(dev["k"], dev["v"], dev["pairs"])
         if dev["slots"] is not None:
-            pk.reshape_and_cache(dev["new_k"], dev["new_v"], dev["k"], dev["v"], dev["slots"])
+            if fp8:
+                pk.reshape_and_cache_fp8(dev["new_k"], dev["new_v"], dev["k"], dev["v"],
+                                         dev["slots"], dev["k_scale"], dev["v_scale"])
+            else:
+                pk.reshape_and_cache(dev["new_k"], dev["new_v"], dev["k"], dev["v"],
+                                     dev["slots"])
         if i is not None:
             ev[i][0].record()
-        pk.paged_attention_decode(dev["out"], dev["q"], dev["k"], dev["v"], tables, dev["lens"],
-                                  wl.scale, wl.max_context_len, workspace=ws,
-                                  partition_tokens=partition, path=path, grid=grid,
-                                  kernel_events=None if i is None else kev[i])
+        if fp8:
+            pk.paged_attention_decode_fp8(dev["out"], dev["q"], dev["k"], dev["v"], tables,
+                                          dev["lens"], wl.scale, dev["k_scale"], dev["v_scale"],
+                                          wl.max_context_len, workspace=ws,
+                                          partition_tokens=partition, path=path, grid=grid,
+                                          kernel_events=None if i is None else kev[i])
+        else:
+            pk.paged_attention_decode(dev["out"], dev["q"], dev["k"], dev["v"], tables,
+                                      dev["lens"], wl.scale, wl.max_context_len, workspace=ws,
+                                      partition_tokens=partition, path=path, grid=grid,
+                                      kernel_events=None if i is None else kev[i])
         if i is not None:
             ev[i][1].record()
 
@@ -419,6 +466,9 @@ def _cpu_pool(wl, row, seqs, workers):
 
 def bench_one(name, args, with_cpu):
     wl, dev = build_inputs(name, args.placement)
+    if args.kv_cache == "e4m3":
+        with_cpu = False   # the oracle baseline times the 16-bit pools
+        quantise_pools(wl, dev)
     alg_decode, alg_writes = step_bytes(wl, dev)
     wall, decode_ms, kernel_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition,
                                                args.path, args.grid)
@@ -440,7 +490,9 @@ def bench_one(name, args, with_cpu):
         "vs_baseline": None,
         "dtype": DTYPE_NAME[wl.dtype],
         "data": "synthetic (seeded N(0,1) values, random block placement)",
-        "config": {"workload": name, **WORKLOAD_DESC[name], "seed": wl.seed,
+        "config": {"workload": name + ("_kv_e4m3" if dev.get("kv_fp8") else ""),
+                   **WORKLOAD_DESC[name], "seed": wl.seed,
+                   "kv_cache": "e4m3" if dev.get("kv_fp8") else DTYPE_NAME[wl.dtype],
                    "placement": args.placement,
                    "path": ["auto", "valu", "mfma", "contiguous"][args.path],
                    "kernel": ["auto", "valu", "mfma"][plan["path"]],
@@ -456,10 +508,11 @@ def bench_one(name, args, with_cpu):
         "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
         "gbs_at_median": round(alg_decode / (float(np.median(kernel_ms)) / 1e3) / 1e9, 2),
         "bytes": {"decode_alg": alg_decode, "writes_alg": alg_writes,
-                  "kv_logical": wl.kv_bytes()},
+                  "kv_logical": wl.kv_bytes() // (wl.esize if dev.get("kv_fp8") else 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(name), "kernel": kname},
+                     "traffic": recorded_traffic(name + ("_kv_e4m3" if dev.get("kv_fp8") else "")),
+                     "kernel": kname},
     }
     if name in ("sharing_fp16", "beam_search_fp16"):
         line["bytes"]["kv_unique"] = wl.unique_kv_bytes()

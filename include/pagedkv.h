@@ -2,7 +2,7 @@
  * pagedkv.h - C ABI of libpagedkv.so: the paged KV-cache decode path on
  * AMD Instinct MI355X (gfx950).
  *
- * Three operations, each one or two hand-written HIP kernels:
+ * The operations, each one or two hand-written HIP kernels:
  *
  *   pkv_paged_attention_decode  single-query attention of every sequence in
  *                               a batch over its KV cache, which lives in
@@ -11,7 +11,11 @@
  *   pkv_reshape_and_cache       write new tokens' key/value rows into the
  *                               cache slots the block manager assigned;
  *   pkv_copy_blocks             copy whole physical blocks (the copy step of
- *                               copy-on-write).
+ *                               copy-on-write);
+ *   pkv_swap_blocks             move whole blocks between the device cache and
+ *                               a pool in pinned host memory;
+ *   pkv_reshape_and_cache_fp8,  the same write and attention over an 8-bit
+ *   pkv_paged_attention_decode_fp8  (E4M3) cache.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -30,7 +34,8 @@
  *   and one physical block is num_kv_heads*block_size*head_dim contiguous
  *   elements.
  * - Slot numbering: slot = physical_block * block_size + offset.
- * - Element type is given by `dtype`; q, out, k, v and both caches share it.
+ * - Element type is given by `dtype`; q, out, k, v and both caches share it
+ *   (except in the _fp8 calls, whose caches hold 8-bit codes).
  *   Attention accumulates in fp32 and rounds the result to nearest even.
  * - Return value: PKV_OK (0) or a negative pkv_status.  Argument errors are
  *   detected on the host before anything is enqueued.  PKV_EHIP reports a
@@ -53,10 +58,17 @@ extern "C" {
 #endif
 
 typedef enum {
-  PKV_F32 = 0,  /* IEEE binary32 */
-  PKV_F16 = 1,  /* IEEE binary16 */
-  PKV_BF16 = 2  /* bfloat16 */
+  PKV_F32 = 0,   /* IEEE binary32 */
+  PKV_F16 = 1,   /* IEEE binary16 */
+  PKV_BF16 = 2,  /* bfloat16 */
+  PKV_E4M3 = 3   /* 8-bit OCP E4M3 cache codes (copy and swap calls, which move bytes) */
 } pkv_dtype;
+
+/* OR-ed into the dtype argument of pkv_supported, pkv_paged_attention_plan
+ * and pkv_paged_attention_workspace_bytes: the caches hold E4M3 codes (the
+ * 8-bit cache of pkv_paged_attention_decode_fp8); the low bits stay the
+ * type of q and out. */
+#define PKV_KV_E4M3 0x100
 
 typedef enum {
   PKV_OK = 0,
@@ -85,7 +97,8 @@ const char* pkv_status_string(int status);
 const char* pkv_last_error(void);
 
 /* Supported shapes: nonzero if (dtype, head_dim, block_size) is compiled in.
- * head_dim in {64, 128, 256}; block_size in {8, 16, 32}. */
+ * head_dim in {64, 128, 256}; block_size in {8, 16, 32}; with PKV_KV_E4M3,
+ * all but head_dim 64 with block_size 8. */
 int pkv_supported(pkv_dtype dtype, int head_dim, int block_size);
 
 /* How a decode call divides its work (the grid argument; pkv_plan.grid
@@ -316,6 +329,54 @@ int pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src
                     const int64_t* src_dst_pairs, int num_pairs, int num_kv_heads, int head_dim,
                     int block_size, int num_src_blocks, int num_dst_blocks, pkv_dtype dtype,
                     void* stream);
+
+/*
+ * An 8-bit KV cache (E4M3 codes with one scale per cache).
+ *
+ * Passage: quantising the KV cache to INT8/FP8 is named among the memory
+ * features of serving libraries ("Memory Optimization in LLM Serving with
+ * PagedAttention", section "Broader Context").  The pages fix nothing more;
+ * the readings: OCP E4M3 codes (sign, 4-bit exponent with bias 7, 3-bit
+ * fraction; largest finite 448, NaN 0x7F, no infinity), one float scale for
+ * the K cache and one for the V cache, and a stored code c meaning
+ * value(c) * scale.
+ *
+ * reshape_and_cache_fp8: as pkv_reshape_and_cache, but the caches are uint8
+ * [num_blocks][num_kv_heads][block_size][head_dim] and each element x of k
+ * (v) is stored as the code of the float32 quotient x / k_scale (v_scale):
+ * NaN -> 0x7F, magnitudes above 448 (infinity included) saturate to +-448,
+ * everything else rounds to the nearest code, ties to the even one; zero
+ * keeps its sign.  k and v are of type `dtype` (PKV_F32, PKV_F16 or
+ * PKV_BF16), [num_tokens][num_kv_heads][head_dim]; head_dim must be a
+ * multiple of 16.  Slots behave as in pkv_reshape_and_cache.  Scales must
+ * be finite and nonzero (else PKV_EINVAL).
+ */
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks, pkv_dtype dtype,
+                              float k_scale, float v_scale, void* stream);
+
+/*
+ * paged_attention_decode_fp8: pkv_paged_attention_decode_timed over E4M3
+ * caches: the keys and values of the attention are value(code) * k_scale
+ * and value(code) * v_scale.  q and out are of type `dtype` (PKV_F32,
+ * PKV_F16 or PKV_BF16); k_cache and v_cache are uint8 codes in the cache
+ * layout.  The scales multiply outside the dot products (scores by
+ * scale * k_scale, the output by v_scale), which is exact up to rounding
+ * order.  The workspace size is pkv_paged_attention_workspace_bytes with
+ * dtype | PKV_KV_E4M3.  Runs the vector-ALU kernel (path AUTO or VALU;
+ * MFMA and CONTIGUOUS return PKV_EUNSUPPORTED).  Everything else, events
+ * included, as pkv_paged_attention_decode_timed.
+ */
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, float k_scale,
+                                   float v_scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int num_blocks,
+                                   int max_blocks_per_seq, int max_context_len, pkv_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, int partition_tokens,
+                                   int path, int grid, void* begin_event, void* end_event,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

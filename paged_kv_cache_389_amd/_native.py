@@ -17,9 +17,12 @@ import torch  # loads torch's HIP runtime first, so the library shares it
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_E4M3 = 0, 1, 2, 3
+KV_E4M3 = 0x100   # OR-ed into a q dtype code: the caches hold E4M3 codes
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_CONTIGUOUS = 0, 1, 2, 3
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+# element types of caches the byte-moving calls accept (uint8: E4M3 codes)
+_CACHE_CODE = {**_DTYPE_CODE, torch.uint8: PKV_E4M3}
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
 
@@ -81,6 +84,13 @@ def _load():
     lib.pkv_copy_blocks.argtypes = [vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_swap_blocks.restype = i32
     lib.pkv_swap_blocks.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pkv_reshape_and_cache_fp8.restype = i32
+    lib.pkv_reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32,
+                                              f32, f32, vp]
+    lib.pkv_paged_attention_decode_fp8.restype = i32
+    lib.pkv_paged_attention_decode_fp8.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, f32, f32, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+        vp, sz, i32, i32, i32, vp, vp, vp]
     return lib
 
 
@@ -92,6 +102,7 @@ EXPORTED = (
     "pkv_paged_attention_decode",
     "pkv_paged_attention_decode_ex", "pkv_paged_attention_decode_timed",
     "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
+    "pkv_reshape_and_cache_fp8", "pkv_paged_attention_decode_fp8",
 )
 
 
@@ -238,7 +249,7 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     """Copy whole blocks ``cache[dst] = cache[src]`` for each int64 pair row."""
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (src_dst_pairs, "src_dst_pairs")):
         _dev(t, n)
-    if k_cache.dtype not in _DTYPE_CODE or v_cache.dtype != k_cache.dtype:
+    if k_cache.dtype not in _CACHE_CODE or v_cache.dtype != k_cache.dtype:
         raise ValueError("caches must share one supported dtype")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
@@ -249,7 +260,7 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     with torch.cuda.device(k_cache.device):
         st = lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src_dst_pairs),
                                  src_dst_pairs.shape[0], hkv, hd, bs, nb,
-                                 _DTYPE_CODE[k_cache.dtype], _stream(k_cache, stream))
+                                 _CACHE_CODE[k_cache.dtype], _stream(k_cache, stream))
     _check("copy_blocks", st)
 
 
@@ -273,7 +284,7 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, stream=None):
         _reachable(t, n)
     _dev(src_dst_pairs, "src_dst_pairs")
     dt = src_k.dtype
-    if dt not in _DTYPE_CODE or any(t.dtype != dt for t in (src_v, dst_k, dst_v)):
+    if dt not in _CACHE_CODE or any(t.dtype != dt for t in (src_v, dst_k, dst_v)):
         raise ValueError("pools must share one supported dtype")
     if src_k.dim() != 4 or src_v.shape != src_k.shape or dst_k.dim() != 4 or \
             dst_v.shape != dst_k.shape or dst_k.shape[1:] != src_k.shape[1:]:
@@ -287,8 +298,84 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, stream=None):
     with torch.cuda.device(dev):
         st = lib.pkv_swap_blocks(_ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v),
                                  _ptr(src_dst_pairs), src_dst_pairs.shape[0], hkv, hd, bs, nsrc,
-                                 ndst, _DTYPE_CODE[dt], _stream(src_dst_pairs, stream))
+                                 ndst, _CACHE_CODE[dt], _stream(src_dst_pairs, stream))
     _check("swap_blocks", st)
+
+
+def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=None):
+    """Quantising cache write (``pkv_reshape_and_cache_fp8``): rows of ``k``
+    and ``v`` ([num_tokens, Hkv, hd], float32/float16/bfloat16) become E4M3
+    codes of ``x / k_scale`` and ``x / v_scale`` in the uint8 caches."""
+    for t, n in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (slot_mapping, "slot_mapping")):
+        _dev(t, n)
+    if k.dtype not in _DTYPE_CODE or v.dtype != k.dtype:
+        raise ValueError("k and v must share one supported dtype")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("8-bit caches must be uint8 tensors of E4M3 codes")
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must both be [num_tokens, num_kv_heads, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, hkv, bs, hd = k_cache.shape
+    if k.shape[1:] != (hkv, hd):
+        raise ValueError("k/v rows do not match the cache's [num_kv_heads, head_dim]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k.shape[0],):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    with torch.cuda.device(k.device):
+        st = lib.pkv_reshape_and_cache_fp8(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(slot_mapping), k.shape[0], hkv, hd, bs, nb,
+                                           _DTYPE_CODE[k.dtype], ctypes.c_float(k_scale),
+                                           ctypes.c_float(v_scale), _stream(k, stream))
+    _check("reshape_and_cache_fp8", st)
+
+
+def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                               k_scale, v_scale, max_context_len, workspace=None,
+                               partition_tokens=0, path=PATH_AUTO, grid=GRID_AUTO, stream=None,
+                               kernel_events=None):
+    """Decode attention over E4M3 caches (``pkv_paged_attention_decode_fp8``):
+    keys and values are ``value(code) * k_scale`` and ``value(code) *
+    v_scale``; otherwise as :func:`paged_attention_decode`."""
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (context_lens, "context_lens"), (block_tables, "block_tables")):
+        _dev(t, n)
+    if q.dtype not in _DTYPE_CODE or out.dtype != q.dtype:
+        raise ValueError("q and out must share one supported dtype")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("8-bit caches must be uint8 tensors of E4M3 codes")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    num_seqs, hq, hd = q.shape
+    nb, hkv, bs, hd2 = k_cache.shape
+    if hd2 != hd:
+        raise ValueError("head_dim of q and caches differ")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (num_seqs,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must have num_seqs rows")
+    max_blocks = block_tables.shape[1]
+    need = workspace_bytes(num_seqs, hq, hkv, hd, bs, max_blocks, int(max_context_len),
+                           _DTYPE_CODE[q.dtype] | KV_E4M3, partition_tokens, path, grid)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(q.device):
+        ev0, ev1 = (kernel_events[0].handle, kernel_events[1].handle) if kernel_events \
+            else (None, None)
+        st = lib.pkv_paged_attention_decode_fp8(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), ctypes.c_float(scale), ctypes.c_float(k_scale),
+            ctypes.c_float(v_scale), num_seqs, hq, hkv, hd, bs, nb, max_blocks,
+            int(max_context_len), _DTYPE_CODE[q.dtype], ws_ptr, ws_len, int(partition_tokens),
+            int(path), int(grid), ev0, ev1, _stream(q, stream))
+    _check("paged_attention_decode_fp8", st)
+    return out
 
 
 class HipEvent:

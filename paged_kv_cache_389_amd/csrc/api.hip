@@ -24,9 +24,18 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxItemParts = 65535;    // a work item packs (part, n) into 16 bits each
 constexpr int kMaxPartition = 1 << 20;  // tokens; explicit partition sizes up to this
 
-int elem_size(pkv_dtype d) { return d == PKV_F32 ? 4 : 2; }
+int elem_size(int d) { return d == PKV_F32 ? 4 : (d == PKV_E4M3 ? 1 : 2); }
+// types of q, out and unquantised caches
 bool dtype_ok(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
-Elem to_elem(pkv_dtype d) {
+// cache element types the byte-moving calls accept
+bool cache_dtype_ok(int d) { return dtype_ok(d) || d == PKV_E4M3; }
+// plan / workspace / supported: a q type, optionally with PKV_KV_E4M3
+bool plan_dtype_ok(int d) {
+  return dtype_ok(d & 0xFF) && ((d & ~0xFF) == 0 || (d & ~0xFF) == PKV_KV_E4M3);
+}
+bool finite_nonzero(float x) { return x == x && x != 0.f && x - x == 0.f; }
+Elem to_elem(int d) {
+  d &= 0xFF;
   return d == PKV_F32 ? Elem::F32 : (d == PKV_F16 ? Elem::F16 : Elem::BF16);
 }
 
@@ -64,31 +73,37 @@ struct Plan {
 
 // Decode workgroups resident on the whole device (cached per device and
 // kernel; a fallback when the runtime cannot say).
-int resident_workgroups(bool mfma, Elem e, int head_dim, int block_size, int group) {
-  constexpr int kKeys = 2 * 3 * 3 * 3 * 3;   // kernel x dtype x head_dim x block_size x GMAX
+int resident_workgroups(bool mfma, Elem e, bool kv_fp8, int head_dim, int block_size,
+                        int group) {
+  constexpr int kKeys = 2 * 3 * 2 * 3 * 3 * 3;   // kernel x dtype x cache x hd x bs x GMAX
   static int cached[kMaxDevices][kKeys];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
   const int gmax = group <= 4 ? 0 : (group <= 8 ? 1 : 2);
   const int hdk = head_dim == 64 ? 0 : (head_dim == 128 ? 1 : 2);
   const int bsk = block_size == 8 ? 0 : (block_size == 16 ? 1 : 2);
-  const int key = (((((mfma ? 1 : 0) * 3 + (int)e) * 3 + hdk) * 3 + bsk) * 3 + gmax);
+  const int key =
+      ((((((mfma ? 1 : 0) * 3 + (int)e) * 2 + (kv_fp8 ? 1 : 0)) * 3 + hdk) * 3 + bsk) * 3 + gmax);
   int per_cu = dev >= 0 ? __atomic_load_n(&cached[dev][key], __ATOMIC_RELAXED) : 0;
   if (per_cu <= 0) {
-    per_cu = mfma ? decode_mfma_occupancy(e, head_dim, block_size, group)
-                  : decode_valu_occupancy(e, head_dim, block_size);
+    per_cu = mfma ? decode_mfma_occupancy(e, kv_fp8, head_dim, block_size, group)
+                  : decode_valu_occupancy(e, kv_fp8, head_dim, block_size);
     if (per_cu <= 0) per_cu = mfma ? 3 : 4;
     if (dev >= 0) __atomic_store_n(&cached[dev][key], per_cu, __ATOMIC_RELAXED);
   }
   return per_cu * compute_units();
 }
 
+// dtype: the type of q and out, with PKV_KV_E4M3 for an 8-bit cache (no
+// contiguous control).
 Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-               int max_blocks_per_seq, int max_context_len, pkv_dtype dtype, int requested,
+               int max_blocks_per_seq, int max_context_len, int dtype, int requested,
                int path, int grid) {
   Plan pl;
   const Elem e = to_elem(dtype);
-  if (!decode_valu_supported(e, head_dim, block_size)) {
+  const bool kv_fp8 = (dtype & PKV_KV_E4M3) != 0;
+  if (!decode_valu_supported(e, kv_fp8, head_dim, block_size) ||
+      (kv_fp8 && path == PKV_PATH_CONTIGUOUS)) {
     pl.status = PKV_EUNSUPPORTED;
     return pl;
   }
@@ -102,7 +117,7 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
 
   const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
   pl.len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
-  const int unit = pl.mfma ? 16 : valu_unit_tokens(e, head_dim, block_size);
+  const int unit = pl.mfma ? 16 : valu_unit_tokens(e, kv_fp8, head_dim, block_size);
   const int units_per_seq = pl.mfma ? num_kv_heads : num_q_heads;
   pl.part_align = block_size > kPartAlign ? block_size : kPartAlign;
 
@@ -150,7 +165,7 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
   // extra launch); larger batches are listed by the planning kernel.
   const int64_t wgs = direct_x * num_seqs;
   const bool plannable = wgs <= INT32_MAX && pl.max_parts <= kMaxItemParts;
-  const int64_t resident = resident_workgroups(pl.mfma, e, head_dim, block_size, group);
+  const int64_t resident = resident_workgroups(pl.mfma, e, kv_fp8, head_dim, block_size, group);
   const bool want = grid == PKV_GRID_PLANNED ||
                     (grid == PKV_GRID_AUTO && num_seqs > 1 && wgs > resident);
   if (want) {
@@ -219,15 +234,17 @@ const char* pkv_status_string(int status) {
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 int pkv_supported(pkv_dtype dtype, int head_dim, int block_size) {
-  if (!dtype_ok(dtype)) return 0;
-  return decode_valu_supported(to_elem(dtype), head_dim, block_size) ? 1 : 0;
+  if (!plan_dtype_ok(dtype)) return 0;
+  return decode_valu_supported(to_elem(dtype), (dtype & PKV_KV_E4M3) != 0, head_dim, block_size)
+             ? 1
+             : 0;
 }
 
 size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                            int head_dim, int block_size, int max_blocks_per_seq,
                                            int max_context_len, pkv_dtype dtype,
                                            int partition_tokens, int path, int grid) {
-  if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+  if (!plan_dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
       grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED || num_q_heads % num_kv_heads)
@@ -242,7 +259,7 @@ int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, in
                              int block_size, int max_blocks_per_seq, int max_context_len,
                              pkv_dtype dtype, int partition_tokens, int path, int grid,
                              pkv_plan* out) {
-  if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+  if (!plan_dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
       grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED || num_q_heads % num_kv_heads)
@@ -261,20 +278,26 @@ int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, in
   return PKV_OK;
 }
 
-int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cache,
-                                     const void* v_cache, const int32_t* block_tables,
-                                     const int32_t* context_lens, float scale, int num_seqs,
-                                     int num_q_heads, int num_kv_heads, int head_dim,
-                                     int block_size, int num_blocks, int max_blocks_per_seq,
-                                     int max_context_len, pkv_dtype dtype, void* workspace,
-                                     size_t workspace_bytes, int partition, int path, int grid,
-                                     void* begin_event, void* end_event, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every decode entry point: kv_fp8 says the caches hold E4M3 codes with the
+// given scales (ignored otherwise).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                bool kv_fp8, float k_scale, float v_scale, int num_seqs, int num_q_heads,
+                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                int max_blocks_per_seq, int max_context_len, int dtype, void* workspace,
+                size_t workspace_bytes, int partition, int path, int grid, void* begin_event,
+                void* end_event, void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0 || partition < 0 || path < PKV_PATH_AUTO ||
       path > PKV_PATH_CONTIGUOUS || grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED)
     return PKV_EINVAL;
   if (num_q_heads % num_kv_heads) return PKV_EINVAL;
+  if (kv_fp8 && (!finite_nonzero(k_scale) || !finite_nonzero(v_scale))) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   const bool contiguous = path == PKV_PATH_CONTIGUOUS;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_tables && !contiguous))
@@ -285,7 +308,8 @@ int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cac
 
   const Elem e = to_elem(dtype);
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                            max_blocks_per_seq, max_context_len, dtype, partition, path, grid);
+                            max_blocks_per_seq, max_context_len,
+                            kv_fp8 ? (dtype | PKV_KV_E4M3) : dtype, partition, path, grid);
   if (pl.status != PKV_OK) return pl.status;
   const Layout lo = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, pl);
   const size_t need = lo.total;
@@ -306,7 +330,8 @@ int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cac
   a.items = pl.planned == 2 ? reinterpret_cast<const int32_t*>(ws + lo.items) : nullptr;
   a.item_count = pl.planned == 2 ? reinterpret_cast<const int32_t*>(ws + lo.count) : nullptr;
   a.planned = pl.planned;
-  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2e = (float)((double)scale * (kv_fp8 ? (double)k_scale : 1.0) * 1.4426950408889634);
+  a.v_scale = kv_fp8 ? v_scale : 1.f;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -330,8 +355,8 @@ int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cac
   }
   if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
     return fail_hip(err);
-  err = use_mfma ? launch_decode_mfma(e, head_dim, block_size, a, st)
-                 : launch_decode_valu(e, head_dim, block_size, a, st);
+  err = use_mfma ? launch_decode_mfma(e, kv_fp8, head_dim, block_size, a, st)
+                 : launch_decode_valu(e, kv_fp8, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
   if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
     return fail_hip(err);
@@ -340,6 +365,40 @@ int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cac
     if (err != hipSuccess) return fail_hip(err);
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode_timed(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, float scale, int num_seqs,
+                                     int num_q_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int num_blocks, int max_blocks_per_seq,
+                                     int max_context_len, pkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, int partition, int path, int grid,
+                                     void* begin_event, void* end_event, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, false, 1.f, 1.f,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, dtype, workspace, workspace_bytes,
+                     partition, path, grid, begin_event, end_event, stream);
+}
+
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, float k_scale,
+                                   float v_scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int num_blocks,
+                                   int max_blocks_per_seq, int max_context_len, pkv_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, int partition,
+                                   int path, int grid, void* begin_event, void* end_event,
+                                   void* stream) {
+  if (path == PKV_PATH_CONTIGUOUS) return PKV_EUNSUPPORTED;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, true, k_scale,
+                     v_scale, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, dtype, workspace,
+                     workspace_bytes, partition, path, grid, begin_event, end_event, stream);
 }
 
 int pkv_paged_attention_decode_ex(void* out, const void* q, const void* k_cache,
@@ -387,10 +446,27 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   return err == hipSuccess ? PKV_OK : fail_hip(err);
 }
 
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks, pkv_dtype dtype,
+                              float k_scale, float v_scale, void* stream) {
+  if (!dtype_ok(dtype) || num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || !finite_nonzero(k_scale) || !finite_nonzero(v_scale))
+    return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_EINVAL;
+  if (head_dim % 16) return PKV_EUNSUPPORTED;
+  hipError_t err = launch_reshape_and_cache_fp8(to_elem(dtype), k, v, k_cache, v_cache,
+                                                slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                                block_size, num_blocks, k_scale, v_scale,
+                                                static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : fail_hip(err);
+}
+
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int num_pairs,
                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
                     pkv_dtype dtype, void* stream) {
-  if (!dtype_ok(dtype) || num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+  if (!cache_dtype_ok(dtype) || num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0)
     return PKV_EINVAL;
   if (num_pairs == 0) return PKV_OK;
@@ -412,7 +488,7 @@ int pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src
                     const int64_t* src_dst_pairs, int num_pairs, int num_kv_heads, int head_dim,
                     int block_size, int num_src_blocks, int num_dst_blocks, pkv_dtype dtype,
                     void* stream) {
-  if (!dtype_ok(dtype) || num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+  if (!cache_dtype_ok(dtype) || num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_src_blocks <= 0 || num_dst_blocks <= 0)
     return PKV_EINVAL;
   if (num_pairs == 0) return PKV_OK;

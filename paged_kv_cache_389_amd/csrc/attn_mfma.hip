@@ -89,6 +89,16 @@ struct MfmaOps<BF16> {
   __device__ static inline float widen_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 };
 
+// Two E4M3 codes (bytes 2*kHi, 2*kHi + 1 of w) as a pair of E's 16-bit
+// values, element 0 from the lower byte (exact: every code is a 16-bit value)
+template <typename E, bool kHi>
+__device__ inline uint32_t codes_to_pair(uint32_t w) {
+  if constexpr (__is_same(E, F16))
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, kHi));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, kHi));
+}
+
 // {lo16 = 16-bit element e of x, hi16 = element e of y}; e is a constant
 // after unrolling
 __device__ inline uint32_t pair_of(int e, const uint32_t* x, const uint32_t* y) {
@@ -118,9 +128,21 @@ struct MfmaState {
   int bad;
 };
 
+// Head dim of element i < 8 of k-step kk in lane group g4, for the A
+// operand (K) and the B operand (Q^T) alike.  16-bit caches: dims 32*kk +
+// 8*g4 + i.  8-bit caches: a lane reads 16 contiguous codes at 64*(kk/2) +
+// 16*g4 and feeds the first 8 to k-step 2*(kk/2), the next 8 to the step
+// after.  Both orders cover every dim once, and a dot product does not
+// depend on the order of its terms.
+template <typename C>
+__device__ constexpr int mfma_dim0(int kk, int g4) {
+  return sizeof(typename C::storage) == 1 ? 64 * (kk / 2) + 16 * g4 + 8 * (kk % 2)
+                                          : 32 * kk + 8 * g4;
+}
+
 // Write Q^T of the G query heads of KV head g of sequence s into q (B
-// layout: lane (n, g4) holds head n, dims 32*kk + 8*g4 .. +8; zero past G).
-template <typename E, int HD>
+// layout: lane (n, g4) holds head n, the dims mfma_dim0 gives; zero past G).
+template <typename E, typename C, int HD>
 __device__ inline void mfma_load_q(const DecodeArgs& a, int s, int g, u32x4 (*q)[kWave]) {
   using T = typename E::storage;
   const int lane = threadIdx.x % kWave, n = lane & 15, g4 = lane >> 4;
@@ -129,7 +151,7 @@ __device__ inline void mfma_load_q(const DecodeArgs& a, int s, int g, u32x4 (*q)
   const T* qh = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + (size_t)g * G + hn) * HD;
 #pragma unroll
   for (int kk = 0; kk < HD / 32; ++kk)
-    q[kk][lane] = (n < G) ? ld16(qh + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+    q[kk][lane] = (n < G) ? ld16(qh + mfma_dim0<C>(kk, g4)) : u32x4{0, 0, 0, 0};
 }
 
 // Fold tiles ta + first, ta + first + stride, ... (< tb) of KV head g of
@@ -150,17 +172,25 @@ __device__ inline int mfma_first_blocks(const DecodeArgs& a, int s, int ta, int 
 // With kWaitQ the workgroup's Q^T is still being written to LDS: every wave
 // passes one barrier, right after issuing the loads of its first tiles
 // (or at once if it has none), so those loads overlap the query's.
-template <typename E, int HD, int BS, bool kWaitQ = false, int NS = kMfmaStages>
+//
+// C is the cache element: E itself, or E4M3 codes, which are loaded at half
+// the width and turned into E's 16-bit values right before the products
+// (the scales are applied outside: K's in scale_log2e, V's on the output).
+template <typename E, typename C, int HD, int BS, bool kWaitQ = false, int NS = kMfmaStages>
 __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
                                        int first, int stride, int tbl0, const u32x4 (*q)[kWave],
                                        MfmaState<HD / 16>& st) {
-  using T = typename E::storage;
+  using T = typename C::storage;       // cache element
   using Ops = MfmaOps<E>;
+  constexpr bool k8 = sizeof(T) == 1;
   constexpr int KSTEPS = HD / 32;      // QK MFMAs per tile
   constexpr int DPL = HD / 16;         // V dims per lane per token == PV MFMAs per tile
-  constexpr int VW = DPL / 2;          // dwords of V per lane per token
+  constexpr int VW = DPL / 2;          // dwords of 16-bit V per lane per token
+  constexpr int KL = k8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per tile
+  constexpr int VL = k8 ? VW / 2 : VW;           // dwords of V loaded per lane per token
   constexpr int TPB = BS / 16;         // tiles per block
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
+  static_assert(!k8 || KSTEPS % 2 == 0, "8-bit K loads cover two k-steps");
 
   const int lane = threadIdx.x % kWave;
   const int n = lane & 15, g4 = lane >> 4;
@@ -173,7 +203,7 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
   const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
-  const uint32_t koff = (uint32_t)((n * HD + g4 * 8) * sizeof(T));
+  const uint32_t koff = (uint32_t)((n * HD + mfma_dim0<C>(0, g4)) * sizeof(T));
   const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
 
   f32x4 acc[DPL];
@@ -197,7 +227,7 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
     // dims n*DPL .. +DPL)
     // (tiles i >= mine get an empty descriptor: their loads return zeros
     // without a memory access, so every step issues the same loads)
-    auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VW]) {
+    auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VL]) {
       const bool live = i < mine;
       const int u = pass + stride * i;
       int phys = lane_value(tbl, i < kWave ? i : kWave - 1);
@@ -209,10 +239,12 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
       const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
       const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
+      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (VW == 2) {
+        if constexpr (VL == 1) {
+          vv[r][0] = bld4(vt, voff, r * HD * sizeof(T));
+        } else if constexpr (VL == 2) {
           const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
@@ -226,8 +258,36 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
       }
     };
 
-    auto compute_tile = [&](int i, const u32x4* ka, uint32_t (*vv)[VW]) {
+    auto compute_tile = [&](int i, const u32x4* kl, uint32_t (*vl)[VL]) {
       const int u = pass + stride * i;
+      // the tile's operands in E's 16-bit values (8-bit codes converted here,
+      // after their loads have landed)
+      u32x4 ka[KSTEPS];
+      uint32_t vv[4][VW];
+      if constexpr (k8) {
+#pragma unroll
+        for (int kk = 0; kk < KL; ++kk) {
+          ka[2 * kk] = u32x4{codes_to_pair<E, false>(kl[kk][0]), codes_to_pair<E, true>(kl[kk][0]),
+                             codes_to_pair<E, false>(kl[kk][1]), codes_to_pair<E, true>(kl[kk][1])};
+          ka[2 * kk + 1] =
+              u32x4{codes_to_pair<E, false>(kl[kk][2]), codes_to_pair<E, true>(kl[kk][2]),
+                    codes_to_pair<E, false>(kl[kk][3]), codes_to_pair<E, true>(kl[kk][3])};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int w = 0; w < VL; ++w) {
+            vv[r][2 * w] = codes_to_pair<E, false>(vl[r][w]);
+            vv[r][2 * w + 1] = codes_to_pair<E, true>(vl[r][w]);
+          }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = kl[kk];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int w = 0; w < VW; ++w) vv[r][w] = vl[r][w];
+      }
       // read Q^T from LDS for this tile; the compiler barrier keeps the reads
       // from being hoisted out of the loop (which would pin Q in registers)
       __asm__ volatile("" ::: "memory");
@@ -285,8 +345,8 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
 
     // NS register stages: the loads of tiles i+1 .. i+NS-1 are in flight
     // while tile i is computed
-    u32x4 kb[NS][KSTEPS];
-    uint32_t vb[NS][4][VW];
+    u32x4 kb[NS][KL];
+    uint32_t vb[NS][4][VL];
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
     if (kWaitQ && pass == ta + first) __syncthreads();   // Q^T is in LDS
@@ -320,7 +380,7 @@ __device__ inline void mfma_state_init(MfmaState<DPL>& st) {
 // normalised and rounded into `out` (the group's first head) when `out` is
 // not null, else stored unnormalised to the partial states
 // state0 + hh * hh_stride (hh < G).
-template <typename E, int HD, int BS, int GMAX>
+template <typename E, typename C, int HD, int BS, int GMAX>
 __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
                                   int tbl0, typename E::storage* out, size_t state0,
                                   size_t hh_stride, MfmaShared<HD, GMAX>& sm) {
@@ -332,7 +392,7 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
 
   MfmaState<DPL> st;
   mfma_state_init(st);
-  mfma_accumulate<E, HD, BS, true>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q, st);
+  mfma_accumulate<E, C, HD, BS, true>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q, st);
 
   // the four token groups of a head column hold partial sums of l
   const float l = rows_sum(st.l);
@@ -367,6 +427,7 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
       Ls = __builtin_fmaf(wt, sm.l[w][hh], Ls);
       O += wt * *reinterpret_cast<const f32x4*>(&sm.o[w][hh][d]);
     }
+    if constexpr (!__is_same(E, C)) O *= a.v_scale;   // 8-bit V: code units -> values
     if (all_bad) O = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     if (out) {
       const float inv = 1.f / Ls;
@@ -383,7 +444,7 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
 
 // One workgroup per (work item, KV head g): the grid is described with
 // DecodeArgs.
-template <typename E, int HD, int BS, int GMAX>
+template <typename E, typename C, int HD, int BS, int GMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
     DecodeArgs a) {
   using T = typename E::storage;
@@ -401,74 +462,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   // the query heads and the blocks of the first tiles are read together
   const int ta = w.t0 / 16, tb = (w.t1 + 15) / 16;
   const int tbl0 = mfma_first_blocks<BS>(a, s, ta, wave, 4);
-  if (wave == 0) mfma_load_q<E, HD>(a, s, g, sm.q);
+  if (wave == 0) mfma_load_q<E, C, HD>(a, s, g, sm.q);
   const size_t state0 = ((size_t)s * a.num_q_heads + (size_t)g * G) * a.max_parts + w.part;
-  mfma_piece<E, HD, BS, GMAX>(a, s, g, w.t1, ta, tb, tbl0, w.n == 1 ? out : nullptr, state0,
-                              a.max_parts, sm);
+  mfma_piece<E, C, HD, BS, GMAX>(a, s, g, w.t1, ta, tb, tbl0, w.n == 1 ? out : nullptr, state0,
+                                 a.max_parts, sm);
 }
 
-template <typename E, int HD, int BS, int GMAX>
+template <typename E, typename C, int HD, int BS, int GMAX>
 static void launch_mfma_g(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid = a.planned ? dim3(a.num_kv_heads * a.max_parts * a.num_seqs)
                               : dim3(a.num_kv_heads * a.max_parts, 1, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<E, HD, BS, GMAX>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<E, C, HD, BS, GMAX>), grid, dim3(256), 0, st, a);
 }
 
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t st) {
   if (a.group <= 4)
-    launch_mfma_g<E, HD, BS, 4>(a, st);
+    launch_mfma_g<E, C, HD, BS, 4>(a, st);
   else if (a.group <= 8)
-    launch_mfma_g<E, HD, BS, 8>(a, st);
+    launch_mfma_g<E, C, HD, BS, 8>(a, st);
   else
-    launch_mfma_g<E, HD, BS, 16>(a, st);
+    launch_mfma_g<E, C, HD, BS, 16>(a, st);
   return hipGetLastError();
 }
 
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 static int occupancy_t(int group) {
   int n = 0;
-  const void* f = group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, HD, BS, 4>)
-                  : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, HD, BS, 8>)
-                               : reinterpret_cast<const void*>(&decode_mfma_kernel<E, HD, BS, 16>);
+  const void* f =
+      group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 4>)
+      : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 8>)
+                   : reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 16>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess) return 0;
   return n;
 }
 
-template <typename E>
+template <typename E, typename C>
 static int occupancy_e(int hd, int bs, int group) {
   switch (hd * 100 + bs) {
-    case 6416: return occupancy_t<E, 64, 16>(group);
-    case 6432: return occupancy_t<E, 64, 32>(group);
-    case 12816: return occupancy_t<E, 128, 16>(group);
-    case 12832: return occupancy_t<E, 128, 32>(group);
+    case 6416: return occupancy_t<E, C, 64, 16>(group);
+    case 6432: return occupancy_t<E, C, 64, 32>(group);
+    case 12816: return occupancy_t<E, C, 128, 16>(group);
+    case 12832: return occupancy_t<E, C, 128, 32>(group);
   }
   return 0;
 }
 
-int decode_mfma_occupancy(Elem e, int hd, int bs, int group) {
+int decode_mfma_occupancy(Elem e, bool kv_fp8, int hd, int bs, int group) {
   switch (e) {
-    case Elem::F16: return occupancy_e<F16>(hd, bs, group);
-    case Elem::BF16: return occupancy_e<BF16>(hd, bs, group);
+    case Elem::F16:
+      return kv_fp8 ? occupancy_e<F16, E4M3>(hd, bs, group) : occupancy_e<F16, F16>(hd, bs, group);
+    case Elem::BF16:
+      return kv_fp8 ? occupancy_e<BF16, E4M3>(hd, bs, group)
+                    : occupancy_e<BF16, BF16>(hd, bs, group);
     default: break;
   }
   return 0;
 }
 
-template <typename E, int HD>
+template <typename E, typename C, int HD>
 static hipError_t launch_mfma_hd(int bs, const DecodeArgs& a, hipStream_t st) {
   switch (bs) {
-    case 16: return launch_mfma_t<E, HD, 16>(a, st);
-    case 32: return launch_mfma_t<E, HD, 32>(a, st);
+    case 16: return launch_mfma_t<E, C, HD, 16>(a, st);
+    case 32: return launch_mfma_t<E, C, HD, 32>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename E>
+template <typename E, typename C>
 static hipError_t launch_mfma_e(int hd, int bs, const DecodeArgs& a, hipStream_t st) {
   switch (hd) {
-    case 64: return launch_mfma_hd<E, 64>(bs, a, st);
-    case 128: return launch_mfma_hd<E, 128>(bs, a, st);
+    case 64: return launch_mfma_hd<E, C, 64>(bs, a, st);
+    case 128: return launch_mfma_hd<E, C, 128>(bs, a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -477,10 +542,14 @@ bool decode_mfma_supported(Elem e, int hd, int bs) {
   return (e == Elem::F16 || e == Elem::BF16) && (hd == 64 || hd == 128) && (bs == 16 || bs == 32);
 }
 
-hipError_t launch_decode_mfma(Elem e, int hd, int bs, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_mfma(Elem e, bool kv_fp8, int hd, int bs, const DecodeArgs& a,
+                              hipStream_t st) {
   switch (e) {
-    case Elem::F16: return launch_mfma_e<F16>(hd, bs, a, st);
-    case Elem::BF16: return launch_mfma_e<BF16>(hd, bs, a, st);
+    case Elem::F16:
+      return kv_fp8 ? launch_mfma_e<F16, E4M3>(hd, bs, a, st) : launch_mfma_e<F16, F16>(hd, bs, a, st);
+    case Elem::BF16:
+      return kv_fp8 ? launch_mfma_e<BF16, E4M3>(hd, bs, a, st)
+                    : launch_mfma_e<BF16, BF16>(hd, bs, a, st);
     default: break;
   }
   return hipErrorInvalidValue;

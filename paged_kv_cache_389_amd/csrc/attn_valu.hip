@@ -30,9 +30,9 @@
 
 namespace pkv {
 
-template <typename E, int HD, int BS>
+template <typename C, int HD, int BS>
 struct ValuTiling {
-  static constexpr int VEC = E::kVec;            // elements per 16-byte load
+  static constexpr int VEC = C::kVec;            // cache elements per 16-byte load
   static constexpr int LPR = HD / VEC;           // lanes per token row
   static constexpr int RPI = kWave / LPR;        // token rows per load instruction
   static constexpr int LPB = BS / RPI;           // load instructions per block
@@ -42,8 +42,8 @@ struct ValuTiling {
   static_assert(RPI * LPR == kWave && BS % RPI == 0 && LPB % CH == 0, "unsupported shape");
 };
 
-int valu_unit_tokens(Elem e, int head_dim, int block_size) {
-  const int vec = e == Elem::F32 ? 4 : 8;
+int valu_unit_tokens(Elem e, bool kv_fp8, int head_dim, int block_size) {
+  const int vec = kv_fp8 ? 16 : (e == Elem::F32 ? 4 : 8);
   const int rpi = kWave / (head_dim / vec);
   const int lpb = block_size / rpi;
   return (lpb < 4 ? lpb : 4) * rpi;
@@ -66,23 +66,27 @@ struct ValuState {
   int bad;
 };
 
-// What a wave must read before streaming a piece: its lane's 16 bytes of
-// the query row and the physical blocks of its first 64 units.
+// What a wave must read before streaming a piece: its lane's query
+// elements (QW 16-byte words: the VEC columns it covers) and the physical
+// blocks of its first 64 units.
+template <int QW>
 struct ValuMeta {
-  u32x4 q;
+  u32x4 q[QW];
   int tbl;
 };
 
 // Issue the loads of a piece's ValuMeta (units ta + first + stride*i).
-template <typename E, int HD, int BS>
-__device__ inline ValuMeta valu_meta(const DecodeArgs& a, int s, int h, int ta, int first,
-                                     int stride) {
+template <typename E, typename C, int HD, int BS>
+__device__ inline ValuMeta<KvDot<E, C>::QW> valu_meta(const DecodeArgs& a, int s, int h, int ta,
+                                                      int first, int stride) {
   using T = typename E::storage;
-  using Tl = ValuTiling<E, HD, BS>;
+  using Tl = ValuTiling<C, HD, BS>;
+  constexpr int QW = KvDot<E, C>::QW;
   const int lane = threadIdx.x % kWave, col = lane % Tl::LPR;
   const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + h) * HD;
-  ValuMeta mt;
-  mt.q = ld16(qrow + col * Tl::VEC);
+  ValuMeta<QW> mt;
+#pragma unroll
+  for (int j = 0; j < QW; ++j) mt.q[j] = ld16(qrow + col * Tl::VEC + j * (16 / sizeof(T)));
   const int blk = min((ta + first + stride * lane) / Tl::UPB, a.max_blocks - 1);
   mt.tbl = a.contiguous ? s * a.max_blocks + blk : a.block_tables[(size_t)s * a.max_blocks + blk];
   return mt;
@@ -92,19 +96,19 @@ __device__ inline ValuMeta valu_meta(const DecodeArgs& a, int s, int h, int ta, 
 // sequence s (unit = UT tokens; tokens at or past L > 0 are masked) into the
 // calling wave's state, given the piece's ValuMeta.  Row group `row` of the wave
 // sees every RPI-th token.
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
-                                       int first, int stride, const ValuMeta& meta,
-                                       ValuState<ValuTiling<E, HD, BS>::VEC>& st) {
-  using T = typename E::storage;
-  using Tl = ValuTiling<E, HD, BS>;
+                                       int first, int stride,
+                                       const ValuMeta<KvDot<E, C>::QW>& meta,
+                                       ValuState<ValuTiling<C, HD, BS>::VEC>& st) {
+  using T = typename C::storage;   // cache element
+  using Tl = ValuTiling<C, HD, BS>;
   constexpr int VEC = Tl::VEC, LPR = Tl::LPR, RPI = Tl::RPI, CH = Tl::CH, UT = Tl::UT,
                 UPB = Tl::UPB;
   const int lane = threadIdx.x % kWave;
   const int row = lane / LPR, col = lane % LPR;
   const int g = h / a.group;
   const int tok_end = L;
-  const u32x4 qv = meta.q;
 
   // unit addresses: a buffer descriptor over the unit's tile rows, built in
   // scalar registers, plus a constant 32-bit per-lane byte offset, so no
@@ -154,7 +158,7 @@ __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L,
       float sc[CH];
 #pragma unroll
       for (int c = 0; c < CH; ++c)
-        sc[c] = group_sum<LPR>(E::dot16(kr[c], qv, 0.f)) * a.scale_log2e;
+        sc[c] = group_sum<LPR>(KvDot<E, C>::dot(kr[c], meta.q)) * a.scale_log2e;
       if ((u + 1) * UT <= tok_end) {
         // every token of the unit is inside the context
         float mb = sc[0];
@@ -171,7 +175,7 @@ __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L,
           const float p = fast_exp2(sc[c] - mn);
           l += p;
           float vf[VEC];
-          E::unpack16(vr[c], vf);
+          C::unpack16(vr[c], vf);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
         }
@@ -197,7 +201,7 @@ __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L,
             const float p = fast_exp2(sc[c] - mu);
             l += p;
             float vf[VEC];
-            E::unpack16(vr[c], vf);
+            C::unpack16(vr[c], vf);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(p, vf[e], o[e]);
           }
@@ -253,9 +257,15 @@ __device__ inline void valu_row_merge(ValuState<VEC>& st) {
 
 // Store a merged state's VEC columns at col*VEC: normalised and rounded into
 // out when out is not null, else unnormalised to po and (max, sum) to pml.
-template <typename E, int VEC>
-__device__ inline void valu_emit(float M, float Ls, float* O, bool bad, int col,
+// kScaled: O is in code units of an 8-bit cache and is multiplied by the V
+// scale first (a per-cache constant, so it commutes with every merge).
+template <typename E, int VEC, bool kScaled>
+__device__ inline void valu_emit(float M, float Ls, float* O, bool bad, int col, float v_scale,
                                  typename E::storage* out, float* po, float* pml) {
+  if constexpr (kScaled) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) O[e] *= v_scale;
+  }
   if (bad) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) O[e] = __builtin_nanf("");
@@ -276,11 +286,12 @@ __device__ inline void valu_emit(float M, float Ls, float* O, bool bad, int col,
 // Attention of query head h of sequence s over its units [ta, tb) (tokens
 // at or past L > 0 masked), by the four waves of the workgroup (unit round-robin),
 // merged in LDS.  Result as in valu_emit.
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
-                                  const ValuMeta& meta, typename E::storage* out, float* po,
-                                  float* pml, ValuShared<HD>& sm) {
-  using Tl = ValuTiling<E, HD, BS>;
+                                  const ValuMeta<KvDot<E, C>::QW>& meta,
+                                  typename E::storage* out, float* po, float* pml,
+                                  ValuShared<HD>& sm) {
+  using Tl = ValuTiling<C, HD, BS>;
   constexpr int VEC = Tl::VEC, LPR = Tl::LPR;
   constexpr int NW = 4;
   const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
@@ -291,7 +302,7 @@ __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int 
 #pragma unroll
   for (int e = 0; e < VEC; ++e) st.o[e] = 0.f;
   st.bad = 0;
-  valu_accumulate<E, HD, BS>(a, s, h, L, ta, tb, wave, NW, meta, st);
+  valu_accumulate<E, C, HD, BS>(a, s, h, L, ta, tb, wave, NW, meta, st);
   valu_row_merge<VEC, LPR>(st);
 
   // merge the 4 waves in LDS
@@ -331,17 +342,18 @@ __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int 
       O[e + 2] = acc[2];
       O[e + 3] = acc[3];
     }
-    valu_emit<E, VEC>(M, Ls, O, sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3], col, out, po, pml);
+    valu_emit<E, VEC, !__is_same(E, C)>(M, Ls, O, sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3],
+                                        col, a.v_scale, out, po, pml);
   }
   __syncthreads();   // the LDS states are free for the next piece
 }
 
 // One workgroup per (work item, query head h): the grid is described with
 // DecodeArgs.
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   using T = typename E::storage;
-  constexpr int UT = ValuTiling<E, HD, BS>::UT;
+  constexpr int UT = ValuTiling<C, HD, BS>::UT;
   __shared__ ValuShared<HD> sm;
   __shared__ PlanScratch sm_plan;
   const WorkItem w = work_item(a, a.num_q_heads, sm_plan);
@@ -354,87 +366,108 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
   // the query slice and the blocks of the first units are read together
   const int ta = w.t0 / UT, tb = (w.t1 + UT - 1) / UT;
-  const ValuMeta meta = valu_meta<E, HD, BS>(a, s, h, ta, uniform(threadIdx.x / kWave), 4);
+  const auto meta = valu_meta<E, C, HD, BS>(a, s, h, ta, uniform(threadIdx.x / kWave), 4);
   const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + w.part;
-  valu_piece<E, HD, BS>(a, s, h, w.t1, ta, tb, meta, w.n == 1 ? out : nullptr,
-                        a.part_o + pidx * HD, a.part_ml + 2 * pidx, sm);
+  valu_piece<E, C, HD, BS>(a, s, h, w.t1, ta, tb, meta, w.n == 1 ? out : nullptr,
+                           a.part_o + pidx * HD, a.part_ml + 2 * pidx, sm);
 }
 
 // ------------------------------------------------------------------ dispatch
 
-template <typename E, int HD, int BS>
+// 8-bit caches need RPI = 64 / (HD / 16) rows per load to divide the block.
+template <typename C, int HD, int BS>
+constexpr bool valu_shape_ok() {
+  return kWave % (HD / C::kVec) == 0 && BS % (kWave / (HD / C::kVec)) == 0;
+}
+
+template <typename E, typename C, int HD, int BS>
 static hipError_t launch_valu_t(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid = a.planned ? dim3(a.num_q_heads * a.max_parts * a.num_seqs)
-                              : dim3(a.num_q_heads * a.max_parts, 1, a.num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<E, HD, BS>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  if constexpr (!valu_shape_ok<C, HD, BS>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const dim3 grid = a.planned ? dim3(a.num_q_heads * a.max_parts * a.num_seqs)
+                                : dim3(a.num_q_heads * a.max_parts, 1, a.num_seqs);
+    hipLaunchKernelGGL((decode_valu_kernel<E, C, HD, BS>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
 }
 
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 static int occupancy_t() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_valu_kernel<E, HD, BS>), 256, 0) !=
-      hipSuccess)
+  if constexpr (!valu_shape_ok<C, HD, BS>()) {
     return 0;
-  return n;
+  } else {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&decode_valu_kernel<E, C, HD, BS>), 256, 0) !=
+        hipSuccess)
+      return 0;
+    return n;
+  }
 }
 
-template <typename E, int HD>
+template <typename E, typename C, int HD>
 static hipError_t launch_valu_hd(int bs, const DecodeArgs& a, hipStream_t st) {
   switch (bs) {
-    case 8: return launch_valu_t<E, HD, 8>(a, st);
-    case 16: return launch_valu_t<E, HD, 16>(a, st);
-    case 32: return launch_valu_t<E, HD, 32>(a, st);
+    case 8: return launch_valu_t<E, C, HD, 8>(a, st);
+    case 16: return launch_valu_t<E, C, HD, 16>(a, st);
+    case 32: return launch_valu_t<E, C, HD, 32>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename E>
+template <typename E, typename C>
 static hipError_t launch_valu_e(int hd, int bs, const DecodeArgs& a, hipStream_t st) {
   switch (hd) {
-    case 64: return launch_valu_hd<E, 64>(bs, a, st);
-    case 128: return launch_valu_hd<E, 128>(bs, a, st);
-    case 256: return launch_valu_hd<E, 256>(bs, a, st);
+    case 64: return launch_valu_hd<E, C, 64>(bs, a, st);
+    case 128: return launch_valu_hd<E, C, 128>(bs, a, st);
+    case 256: return launch_valu_hd<E, C, 256>(bs, a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename E>
+template <typename E, typename C>
 static int occupancy_e(int hd, int bs) {
   switch (hd * 100 + bs) {
-    case 6408: return occupancy_t<E, 64, 8>();
-    case 6416: return occupancy_t<E, 64, 16>();
-    case 6432: return occupancy_t<E, 64, 32>();
-    case 12808: return occupancy_t<E, 128, 8>();
-    case 12816: return occupancy_t<E, 128, 16>();
-    case 12832: return occupancy_t<E, 128, 32>();
-    case 25608: return occupancy_t<E, 256, 8>();
-    case 25616: return occupancy_t<E, 256, 16>();
-    case 25632: return occupancy_t<E, 256, 32>();
+    case 6408: return occupancy_t<E, C, 64, 8>();
+    case 6416: return occupancy_t<E, C, 64, 16>();
+    case 6432: return occupancy_t<E, C, 64, 32>();
+    case 12808: return occupancy_t<E, C, 128, 8>();
+    case 12816: return occupancy_t<E, C, 128, 16>();
+    case 12832: return occupancy_t<E, C, 128, 32>();
+    case 25608: return occupancy_t<E, C, 256, 8>();
+    case 25616: return occupancy_t<E, C, 256, 16>();
+    case 25632: return occupancy_t<E, C, 256, 32>();
   }
   return 0;
 }
 
-int decode_valu_occupancy(Elem e, int hd, int bs) {
+int decode_valu_occupancy(Elem e, bool kv_fp8, int hd, int bs) {
   switch (e) {
-    case Elem::F32: return occupancy_e<F32>(hd, bs);
-    case Elem::F16: return occupancy_e<F16>(hd, bs);
-    case Elem::BF16: return occupancy_e<BF16>(hd, bs);
+    case Elem::F32: return kv_fp8 ? occupancy_e<F32, E4M3>(hd, bs) : occupancy_e<F32, F32>(hd, bs);
+    case Elem::F16: return kv_fp8 ? occupancy_e<F16, E4M3>(hd, bs) : occupancy_e<F16, F16>(hd, bs);
+    case Elem::BF16:
+      return kv_fp8 ? occupancy_e<BF16, E4M3>(hd, bs) : occupancy_e<BF16, BF16>(hd, bs);
   }
   return 0;
 }
 
-bool decode_valu_supported(Elem e, int hd, int bs) {
+bool decode_valu_supported(Elem e, bool kv_fp8, int hd, int bs) {
   (void)e;
-  return (hd == 64 || hd == 128 || hd == 256) && (bs == 8 || bs == 16 || bs == 32);
+  if (!(hd == 64 || hd == 128 || hd == 256) || !(bs == 8 || bs == 16 || bs == 32)) return false;
+  return !(kv_fp8 && hd == 64 && bs == 8);   // 16 rows per 8-bit load exceed the block
 }
 
-hipError_t launch_decode_valu(Elem e, int hd, int bs, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_valu(Elem e, bool kv_fp8, int hd, int bs, const DecodeArgs& a,
+                              hipStream_t st) {
   switch (e) {
-    case Elem::F32: return launch_valu_e<F32>(hd, bs, a, st);
-    case Elem::F16: return launch_valu_e<F16>(hd, bs, a, st);
-    case Elem::BF16: return launch_valu_e<BF16>(hd, bs, a, st);
+    case Elem::F32:
+      return kv_fp8 ? launch_valu_e<F32, E4M3>(hd, bs, a, st) : launch_valu_e<F32, F32>(hd, bs, a, st);
+    case Elem::F16:
+      return kv_fp8 ? launch_valu_e<F16, E4M3>(hd, bs, a, st) : launch_valu_e<F16, F16>(hd, bs, a, st);
+    case Elem::BF16:
+      return kv_fp8 ? launch_valu_e<BF16, E4M3>(hd, bs, a, st)
+                    : launch_valu_e<BF16, BF16>(hd, bs, a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -34,6 +34,53 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// The quantising variant for an 8-bit cache: one workgroup per new token;
+// each thread turns 16 source elements (type E) of the token's K or V rows
+// into 16 E4M3 codes of x / scale (E4M3::encode4: float32 quotient,
+// saturated, nearest even) and stores them with one 16-byte store.  Slots
+// are handled as above.  Quantising the cache is named among the memory
+// features of serving libraries ("Memory Optimization ...", section "Broader
+// Context"); the format, the per-cache scales and the rounding are readings.
+template <typename E>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const typename E::storage* __restrict__ k, const typename E::storage* __restrict__ v,
+    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+    const int64_t* __restrict__ slot_mapping, int num_kv_heads, int row_vecs, int block_size,
+    int64_t num_slots, float k_scale, float v_scale) {
+  using T = typename E::storage;
+  const int token = blockIdx.x;
+  const int64_t slot = slot_mapping[token];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot % block_size);
+  const int per_token = num_kv_heads * row_vecs;   // 16-code vectors per token and cache
+  for (int i = threadIdx.x; i < 2 * per_token; i += blockDim.x) {
+    const bool is_v = i >= per_token;
+    const int j = is_v ? i - per_token : i;
+    const int g = j / row_vecs, c = j % row_vecs;
+    const T* src = (is_v ? v : k) + ((size_t)token * per_token + j) * 16;
+    const float scale = is_v ? v_scale : k_scale;
+    float x[16];
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x4 r = ld16(src + 4 * w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * w + e] = __uint_as_float(r[e]);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) E::unpack16(ld16(src + 8 * w), x + 8 * w);
+    }
+    u32x4 codes;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      codes[w] = E4M3::encode4(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3], scale);
+    const size_t dst = (((size_t)blk * num_kv_heads + g) * block_size + off) * row_vecs + c;
+    (is_v ? v_cache : k_cache)[dst] = codes;
+  }
+}
+
 // Grid (chunks, 2, pairs): y selects the K or the V pool; each workgroup
 // copies one chunk of 256 threads x 4 vectors (16 KiB) of one block from
 // block src of the source pools to block dst of the destination pools.
@@ -81,6 +128,40 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slot_mapping,
                      num_kv_heads, row_vecs, block_size, (int64_t)num_blocks * block_size);
   return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t launch_rc_fp8_t(const void* k, const void* v, void* k_cache, void* v_cache,
+                                  const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks, float k_scale,
+                                  float v_scale, hipStream_t st) {
+  using T = typename E::storage;
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<E>, dim3(num_tokens), dim3(256), 0, st,
+                     static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slot_mapping,
+                     num_kv_heads, head_dim / 16, block_size, (int64_t)num_blocks * block_size,
+                     k_scale, v_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(Elem e, const void* k, const void* v, void* k_cache,
+                                        void* v_cache, const int64_t* slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int num_blocks, float k_scale,
+                                        float v_scale, hipStream_t st) {
+  switch (e) {
+    case Elem::F32:
+      return launch_rc_fp8_t<F32>(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                  head_dim, block_size, num_blocks, k_scale, v_scale, st);
+    case Elem::F16:
+      return launch_rc_fp8_t<F16>(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                  head_dim, block_size, num_blocks, k_scale, v_scale, st);
+    case Elem::BF16:
+      return launch_rc_fp8_t<BF16>(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                   num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+                                   v_scale, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,

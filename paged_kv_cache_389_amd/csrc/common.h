@@ -98,6 +98,85 @@ struct BF16 {
   }
 };
 
+// 8-bit cache codes in the OCP E4M3 format (sign, 4-bit exponent with bias
+// 7, 3-bit fraction; largest finite 448, no infinity), which gfx950 converts
+// natively.  Every code is exact in f16, bf16 and f32.  A cache of codes
+// carries one float scale per K or V cache, applied outside the dot products.
+struct E4M3 {
+  using storage = uint8_t;
+  static constexpr int kVec = 16;  // codes per 16 bytes
+  // the 16 codes as floats, byte i of the vector first
+  __device__ static inline void unpack16(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(a[i], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(a[i], true);
+      out[4 * i] = lo[0];
+      out[4 * i + 1] = lo[1];
+      out[4 * i + 2] = hi[0];
+      out[4 * i + 3] = hi[1];
+    }
+  }
+  // the code of x / scale: float32 quotient, saturated to +-448, nearest
+  // even; NaN gives 0x7F
+  __device__ static inline uint32_t encode4(float x0, float x1, float x2, float x3, float scale) {
+    const float xs[4] = {x0 / scale, x1 / scale, x2 / scale, x3 / scale};
+    float c[4];
+    uint32_t nan_mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = fminf(fmaxf(xs[i], -448.f), 448.f);
+      if (xs[i] != xs[i]) nan_mask |= 0xFFu << (8 * i);
+    }
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+    return ((uint32_t)w & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
+  }
+};
+
+// Dot product of one lane's 16 bytes of a cache row (type C) with the
+// matching query elements (type E, QW 16-byte words).
+template <typename E, typename C>
+struct KvDot {
+  static constexpr int QW = C::kVec * (int)sizeof(typename E::storage) / 16;
+  __device__ static inline float dot(u32x4 k, const u32x4* q) {
+    if constexpr (__is_same(E, C)) {
+      return E::dot16(k, q[0], 0.f);
+    } else if constexpr (__is_same(E, F16)) {
+      // codes -> f16 pairs (scale 1: exact), then v_dot2 with the query
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[w], 1.f, false);
+        const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[w], 1.f, true);
+        acc = __builtin_amdgcn_fdot2(lo, lane_as<f16x2>(q[w / 2][2 * (w % 2)]), acc, false);
+        acc = __builtin_amdgcn_fdot2(hi, lane_as<f16x2>(q[w / 2][2 * (w % 2) + 1]), acc, false);
+      }
+      return acc;
+    } else if constexpr (__is_same(E, BF16)) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[w], 1.f, false);
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[w], 1.f, true);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(lo, lane_as<bf16x2>(q[w / 2][2 * (w % 2)]), acc,
+                                              false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(hi, lane_as<bf16x2>(q[w / 2][2 * (w % 2) + 1]),
+                                              acc, false);
+      }
+      return acc;
+    } else {
+      // f32 query: codes -> f32, fused multiply-adds
+      float kf[16];
+      C::unpack16(k, kf);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc = __builtin_fmaf(kf[i], __uint_as_float(q[i / 4][i % 4]), acc);
+      return acc;
+    }
+  }
+};
+
 // Round n floats (n a multiple of 4) to E's storage type and store them at
 // p with the widest aligned vector stores (16 bytes for 8 half-width or 4
 // single-width elements).
@@ -212,6 +291,9 @@ __device__ inline u32x4 bld16(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
 }
 __device__ inline u32x2 bld8(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, const_off, 0));
+}
+__device__ inline uint32_t bld4(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, const_off, 0);
 }
 
 // Value of a wave-uniform lane's register (v_readlane with an SGPR index).

@@ -24,7 +24,7 @@ namespace pkv {
 struct DecodeArgs {
   void* out;                  // [B][Hq][HD] element type
   const void* q;              // [B][Hq][HD]
-  const void* k_cache;        // [NB][Hkv][BS][HD]
+  const void* k_cache;        // [NB][Hkv][BS][HD] element type, or 8-bit codes
   const void* v_cache;
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* context_lens;  // [B]
@@ -34,7 +34,8 @@ struct DecodeArgs {
   // floats per state, ml 2 (max in log2 units, sum)
   float* part_o;
   float* part_ml;
-  float scale_log2e;          // scale * log2(e): scores are kept in log2 units
+  float scale_log2e;          // scale * log2(e) (* K scale for 8-bit codes): scores in log2 units
+  float v_scale;              // 8-bit caches: the V scale (1 otherwise)
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
@@ -100,19 +101,20 @@ __device__ inline WorkItem work_item(const DecodeArgs& a, int units, PlanScratch
 }
 
 // Launchers (one translation unit each).  Return hipSuccess or the launch error.
-hipError_t launch_decode_valu(Elem e, int head_dim, int block_size, const DecodeArgs& a,
-                              hipStream_t stream);
-hipError_t launch_decode_mfma(Elem e, int head_dim, int block_size, const DecodeArgs& a,
-                              hipStream_t stream);
+// kv_fp8: the caches hold E4M3 codes (q and out keep the element type e).
+hipError_t launch_decode_valu(Elem e, bool kv_fp8, int head_dim, int block_size,
+                              const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(Elem e, bool kv_fp8, int head_dim, int block_size,
+                              const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_reduce(Elem e, int head_dim, const DecodeArgs& a, hipStream_t stream);
-bool decode_valu_supported(Elem e, int head_dim, int block_size);
+bool decode_valu_supported(Elem e, bool kv_fp8, int head_dim, int block_size);
 // Tokens per unit of work of the vector-ALU kernel (a wave handles at most
 // 64 units per pass); the MFMA kernel's unit is 16 tokens.
-int valu_unit_tokens(Elem e, int head_dim, int block_size);
+int valu_unit_tokens(Elem e, bool kv_fp8, int head_dim, int block_size);
 bool decode_mfma_supported(Elem e, int head_dim, int block_size);
 // Decode workgroups resident per compute unit (0 if the runtime cannot say).
-int decode_valu_occupancy(Elem e, int head_dim, int block_size);
-int decode_mfma_occupancy(Elem e, int head_dim, int block_size, int group);
+int decode_valu_occupancy(Elem e, bool kv_fp8, int head_dim, int block_size);
+int decode_mfma_occupancy(Elem e, bool kv_fp8, int head_dim, int block_size, int group);
 
 // Writes the work items of a planned grid (see DecodeArgs): items[4k ..
 // 4k+3] = (s, part << 16 | n, t0, t1) for k < *count, largest partition
@@ -126,6 +128,13 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                     int row_bytes, int block_size, int num_blocks,
                                     hipStream_t stream);
+// The quantising write: rows of element type e become E4M3 codes of
+// x / k_scale (K) and x / v_scale (V).
+hipError_t launch_reshape_and_cache_fp8(Elem e, const void* k, const void* v, void* k_cache,
+                                        void* v_cache, const int64_t* slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int num_blocks, float k_scale,
+                                        float v_scale, hipStream_t stream);
 // dst pools[pairs[i][1]] = src pools[pairs[i][0]] for K and V (pools may be
 // the same, for copy-on-write).
 hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,

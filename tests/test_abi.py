@@ -197,3 +197,48 @@ def test_binding_rejects_cpu_tensors(native):
         native.swap_blocks(torch.zeros(4, 1, 2, 8), torch.zeros(4, 1, 2, 8),
                            torch.zeros(4, 1, 2, 8), torch.zeros(4, 1, 2, 8),
                            torch.zeros(1, 2, dtype=torch.int64))
+
+
+def test_fp8_calls_reject_bad_arguments(native):
+    lib = native.lib
+    KV = native.KV_E4M3
+    # supported / plan / workspace take the q type with the 8-bit cache flag
+    assert lib.pkv_supported(1 | KV, 128, 16) == 1
+    assert lib.pkv_supported(1 | KV, 64, 8) == 0      # 16 rows per 8-bit load > block
+    assert lib.pkv_supported(1 | 0x200, 128, 16) == 0
+    assert native.workspace_bytes(8, 8, 8, 128, 16, 64, 1024, 1 | KV) >= 0
+    assert native.plan(64, 32, 8, 128, 16, 256, 4096, 2 | KV)["path"] == native.PATH_MFMA
+    assert native.plan(64, 32, 32, 128, 16, 256, 4096, 2 | KV)["path"] == native.PATH_VALU
+    p = native._Plan()
+    assert lib.pkv_paged_attention_plan(4, 8, 8, 128, 16, 8, 128, 1 | KV, 0, 2, 0,
+                                        ctypes.byref(p)) == -2          # MFMA needs groups
+    assert lib.pkv_paged_attention_plan(4, 8, 2, 128, 16, 8, 128, 1 | KV, 0, 3, 0,
+                                        ctypes.byref(p)) == -2          # no contiguous control
+    # reshape_and_cache_fp8(k, v, kc, vc, slots, n, hkv, hd, bs, nb, dtype, k_scale, v_scale, st)
+    assert lib.pkv_reshape_and_cache_fp8(None, None, None, None, None, 0, 8, 128, 16, 64, 1,
+                                         1.0, 1.0, None) == 0
+    assert lib.pkv_reshape_and_cache_fp8(1, 1, 1, 1, 1, 4, 8, 128, 16, 64, 1, 0.0, 1.0,
+                                         None) == -1
+    assert lib.pkv_reshape_and_cache_fp8(1, 1, 1, 1, 1, 4, 8, 128, 16, 64, 1, 1.0,
+                                         float("nan"), None) == -1
+    assert lib.pkv_reshape_and_cache_fp8(1, 1, 1, 1, 1, 4, 8, 128, 16, 64, 3, 1.0, 1.0,
+                                         None) == -1      # the source may not be codes
+    assert lib.pkv_reshape_and_cache_fp8(1, 1, 1, 1, 1, 4, 8, 72, 16, 64, 1, 1.0, 1.0,
+                                         None) == -2
+    # decode_fp8: scales, path and dtype checked before any launch
+    args = [1, 1, 1, 1, 1, 1, 0.1]
+    tail = [4, 8, 8, 128, 16, 64, 8, 128, 1, None, 0, 0, 0, 0, None, None, None]
+    f = lib.pkv_paged_attention_decode_fp8
+    assert f(*args, float("inf"), 1.0, *tail) == -1
+    assert f(*args, 1.0, 0.0, *tail) == -1
+    bad_path = list(tail)
+    bad_path[12] = 2                  # MFMA with Hq == Hkv
+    assert f(*args, 1.0, 1.0, *bad_path) == -2
+    bad_path[12] = 3
+    assert f(*args, 1.0, 1.0, *bad_path) == -2
+    bad_dtype = list(tail)
+    bad_dtype[8] = 3
+    assert f(*args, 1.0, 1.0, *bad_dtype) == -1
+    # copy and swap move E4M3 blocks as bytes
+    assert lib.pkv_copy_blocks(None, None, None, 0, 8, 128, 16, 64, 3, None) == 0
+    assert lib.pkv_swap_blocks(1, 1, 1, 1, 1, -1, 8, 128, 16, 64, 32, 3, None) == -1
