@@ -157,6 +157,9 @@ def counters_to_traffic(args):
     write, _ = pick(_counter_means(args.write_db), "WRITE_SIZE", is_decode)
     from paged_kv_cache_389_amd import workloads
     wl = workloads.make(args.workload, device="cpu")
+    key, alg = args.workload, wl.decode_bytes()
+    if args.kv_cache == "e4m3":   # one byte per K/V element
+        key, alg = key + "_kv_e4m3", alg - (wl.kv_bytes() - wl.kv_bytes() // wl.esize)
     try:
         with open(args.counters) as fh:
             rec = json.load(fh)
@@ -166,14 +169,14 @@ def counters_to_traffic(args):
         rec = {"sources_sha256": kernel_sources_digest(), "workloads": {}}
     rec["calibration"] = {"copy_mib": args.cal_mib, "fetch_counter_per_byte": round(f_fetch, 4),
                           "write_counter_per_byte": round(f_write, 4)}
-    rec["workloads"][args.workload] = {
+    rec["workloads"][key] = {
         "kernel": kname.split("(")[0], "fetch_kib_per_launch": round(fetch, 1),
         "write_kib_per_launch": round(write, 1),
         "hbm_bytes_per_launch": int(fetch * 1024 / f_fetch + write * 1024 / f_write),
-        "alg_bytes_per_launch": wl.decode_bytes()}
+        "alg_bytes_per_launch": alg}
     with open(args.counters, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)
-    print(json.dumps(rec["workloads"][args.workload]))
+    print(json.dumps(rec["workloads"][key]))
 
 
 def copy_calibration(mib, reps=5):
