@@ -518,7 +518,7 @@ def bench_one(name, args, with_cpu):
                      "kernel": kname},
     }
     if name in ("sharing_fp16", "beam_search_fp16"):
-        line["bytes"]["kv_unique"] = wl.unique_kv_bytes()
+        line["bytes"]["kv_unique"] = wl.unique_kv_bytes() // (wl.esize if dev.get("kv_fp8") else 1)
     if name == "beam_search_fp16":
         from paged_kv_cache_389_amd import workloads
         pairs = [len(h.copy_pairs) for h in wl.history]
