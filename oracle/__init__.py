@@ -17,7 +17,7 @@ Sources (the three web pages on PagedAttention):
   (jackhb1970 blog), section "The KV Cache Bottleneck".
 
 Every function here is pinned by CPU tests (``tests/test_oracle_pins.py``,
-``tests/test_oracle_fp8.py``) to something other than itself: a library
+``tests/test_oracle_fp8.py``, ``tests/test_oracle_prefill.py``) to something other than itself: a library
 attention routine on contiguous data, torch's float8_e4m3fn conversions,
 closed forms, invariants and hand-worked fixtures.
 """
@@ -26,6 +26,7 @@ from .paged_attention import decode, decode_one, kv_head_of
 from .cache_ops import copy_blocks, reshape_and_cache, swap_blocks
 from . import fp8
 from .fp8 import decode_fp8, reshape_and_cache_fp8
+from .prefill import prefill
 
 __all__ = ["decode", "decode_one", "kv_head_of", "copy_blocks", "reshape_and_cache",
-           "swap_blocks", "fp8", "decode_fp8", "reshape_and_cache_fp8"]
+           "swap_blocks", "fp8", "decode_fp8", "reshape_and_cache_fp8", "prefill"]
