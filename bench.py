@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
+PREFILL_WORKLOADS = ("llama3_8b_prefill_bf16",)
 DEFAULT_WORKLOAD = "opt13b_fp16"
 DTYPE_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 WORKLOAD_DESC = {
@@ -63,7 +64,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOAD_DESC))
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                   choices=sorted(WORKLOAD_DESC) + sorted(PREFILL_WORKLOADS))
     p.add_argument("--sweep", action="store_true", help="one line per workload")
     p.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA, 3 contiguous")
@@ -413,6 +415,64 @@ def _pool_worker(path):
                         int(z["hkv"]), [int(x) for x in z["seqs"]], int(z["row"]), float("inf"))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
+
+
+def bench_prefill(name, args):
+    """Causal prefill attention over the paged cache (every prompt token a
+    query).  Throughput in causal attention TFLOP/s (4 * hd flops per query
+    row, head and visible token) over the kernel's time (HIP events the
+    library records around its launch), against the dense 16-bit MFMA peak;
+    the minimum bytes (every K/V row once, q, out) give the HBM side."""
+    from paged_kv_cache_389_amd import _native as pk
+    from paged_kv_cache_389_amd import workloads
+    wl = workloads.make(name, device="cuda")
+    tables = torch.from_numpy(wl.block_tables).cuda()
+    lens = torch.from_numpy(wl.context_lens).cuda()
+    qs = torch.from_numpy(wl.query_start).cuda()
+    out = torch.empty_like(wl.q)
+    kev = [(pk.HipEvent(), pk.HipEvent()) for _ in range(args.steps)]
+
+    def step(i=None):
+        pk.paged_attention_prefill(out, wl.q, wl.k_cache, wl.v_cache, tables, lens, qs, wl.scale,
+                                   wl.max_q_len, int(wl.context_lens.max()),
+                                   kernel_events=None if i is None else kev[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [a.elapsed_ms(b) for a, b in kev]
+    ker = float(np.mean(kms))
+    flops, nbytes = wl.flops(), wl.min_bytes()
+    tflops = flops / (ker / 1e3) / 1e12
+    ms_per_step = wall / args.steps * 1e3
+    return {
+        "metric": "paged prefill attention: causal TFLOP/s (% of MFMA peak) + query tokens/s",
+        "value": round(flops / (ms_per_step / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[wl.dtype],
+        "data": "synthetic (seeded N(0,1) values, random block placement)",
+        "config": {"workload": name, "num_seqs": wl.num_seqs, "heads": f"{wl.num_q_heads}/"
+                   f"{wl.num_kv_heads}", "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "context_lens": "U[512,2048], every token a query", "total_q": wl.total_q,
+                   "seed": wl.seed},
+        "query_tokens_per_s": round(wl.total_q / (ms_per_step / 1e3), 1),
+        "kernel_ms": round(ker, 5), "kernel_ms_median": round(float(np.median(kms)), 5),
+        "kernel_ms_min": round(float(np.min(kms)), 5),
+        "flops": flops, "min_bytes": nbytes,
+        "hbm_gbs_at_min_bytes": round(nbytes / (ker / 1e3) / 1e9, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(name), "kernel": "prefill_mfma_kernel"},
+    }
+
+
 def cpu_baseline(wl, budget_s, pool_workers=0):
     """The float64 oracle over whole sequences (all heads), throughput in the
     metric's unit (algorithmic KV GB/s of the sample).  One thread, in index
@@ -547,6 +607,9 @@ def main():
         return
     if args.swap:
         bench_swap(args)
+        return
+    if args.workload in PREFILL_WORKLOADS:
+        print(json.dumps(bench_prefill(args.workload, args)), flush=True)
         return
     names = sorted(WORKLOAD_DESC) if args.sweep else [args.workload]
     for name in names:

@@ -15,7 +15,9 @@
  *   pkv_swap_blocks             move whole blocks between the device cache and
  *                               a pool in pinned host memory;
  *   pkv_reshape_and_cache_fp8,  the same write and attention over an 8-bit
- *   pkv_paged_attention_decode_fp8  (E4M3) cache.
+ *   pkv_paged_attention_decode_fp8  (E4M3) cache;
+ *   pkv_paged_attention_prefill causal attention of many query tokens per
+ *                               sequence over the same paged cache.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -377,6 +379,50 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache
                                    void* workspace, size_t workspace_bytes, int partition_tokens,
                                    int path, int grid, void* begin_event, void* end_event,
                                    void* stream);
+
+/*
+ * paged_attention_prefill: causal attention of many query tokens per
+ * sequence over the paged cache (prefill, or the recomputation of an
+ * evicted sequence).
+ *
+ * Sequence s has L = context_lens[s] tokens in the cache (its new tokens
+ * included: write them with reshape_and_cache first) and n = query_start[s+1]
+ * - query_start[s] query rows q[query_start[s] .. query_start[s+1]), which
+ * are its last n positions: query i sits at position p = L - n + i and
+ *   out[query_start[s] + i][h][:] = softmax(scale * K_{0..p} q) V_{0..p}
+ * over tokens 0 .. p, each read through block_tables[s] as in decode; a
+ * query with p < 0 gives a zero row.
+ *
+ * Passage: the engine evicts whole sequences when memory runs short and
+ * brings them back by swapping or by recomputation ("vLLM and PagedAttention:
+ * How Ideas from Operating Systems Accelerated LLM Inference", paragraph on
+ * the engine); recomputation attends many tokens at once over the paged
+ * cache.  The causal reading is not printed on the pages.
+ *
+ *   out, q        [total_q][num_q_heads][head_dim]   (q read, out written)
+ *   query_start   int32 [num_seqs + 1], non-decreasing, query_start[0] = 0,
+ *                 query_start[num_seqs] = total_q  (read; values are clamped
+ *                 to [0, total_q])
+ *   max_q_len     host-side bound of every n (sizes the grid; queries past it
+ *                 are not computed)
+ *   k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+ *   max_blocks_per_seq, num_blocks: as in pkv_paged_attention_decode.
+ *   begin_event, end_event: optional hipEvent_t recorded around the kernel.
+ *
+ * dtype PKV_F16 or PKV_BF16; head_dim 64 or 128; block_size 16 or 32;
+ * num_q_heads / num_kv_heads must divide 16 (else PKV_EUNSUPPORTED).  No
+ * workspace.  A table entry outside [0, num_blocks) makes the rows that read
+ * it NaN; nothing is read or written out of bounds.  `out` must not alias
+ * an input.  num_seqs, total_q or max_q_len == 0 is a no-op.
+ */
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                float scale, int num_seqs, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                pkv_dtype dtype, void* begin_event, void* end_event,
+                                void* stream);
 
 #ifdef __cplusplus
 }

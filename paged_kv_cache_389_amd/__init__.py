@@ -11,7 +11,9 @@ Device calls (hand-written gfx950 HIP kernels behind the C ABI in
   pool in pinned host memory (eviction by swapping);
 * :func:`reshape_and_cache_fp8`, :func:`paged_attention_decode_fp8` - the
   same write and attention over an 8-bit (OCP E4M3) cache with per-cache
-  scales.
+  scales;
+* :func:`paged_attention_prefill` - causal attention of many query tokens per
+  sequence over the paged cache (prefill / recomputation).
 
 Host side: :mod:`.block_manager` (block pool, tables, reference counts, fork,
 copy-on-write) and :mod:`.workloads` (seeded synthetic inputs).
@@ -23,6 +25,7 @@ CPU implementation.
 
 _NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "swap_blocks",
            "reshape_and_cache_fp8", "paged_attention_decode_fp8", "KV_E4M3",
+           "paged_attention_prefill",
            "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
            "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")

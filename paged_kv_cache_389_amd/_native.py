@@ -91,6 +91,10 @@ def _load():
     lib.pkv_paged_attention_decode_fp8.argtypes = [
         vp, vp, vp, vp, i32p, i32p, f32, f32, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
         vp, sz, i32, i32, i32, vp, vp, vp]
+    lib.pkv_paged_attention_prefill.restype = i32
+    lib.pkv_paged_attention_prefill.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+        i32, vp, vp, vp]
     return lib
 
 
@@ -103,6 +107,7 @@ EXPORTED = (
     "pkv_paged_attention_decode_ex", "pkv_paged_attention_decode_timed",
     "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
     "pkv_reshape_and_cache_fp8", "pkv_paged_attention_decode_fp8",
+    "pkv_paged_attention_prefill",
 )
 
 
@@ -375,6 +380,50 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, context_l
             int(max_context_len), _DTYPE_CODE[q.dtype], ws_ptr, ws_len, int(partition_tokens),
             int(path), int(grid), ev0, ev1, _stream(q, stream))
     _check("paged_attention_decode_fp8", st)
+    return out
+
+
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                            scale, max_q_len, max_context_len, stream=None, kernel_events=None):
+    """Causal attention of the last ``n_s`` positions of every sequence over
+    its paged KV (``pkv_paged_attention_prefill``).  ``q`` / ``out`` are
+    ``[total_q, Hq, hd]``; sequence s owns rows ``query_start[s] ..
+    query_start[s+1]`` (int32 [B+1] on the device); ``max_q_len`` is a
+    host-side bound of the ``n_s``."""
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start, "query_start")):
+        _dev(t, n)
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("prefill runs on float16 or bfloat16")
+    for t, n in ((out, "out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} dtype {t.dtype} != q dtype {q.dtype}")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must both be [total_q, num_q_heads, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    total_q, hq, hd = q.shape
+    nb, hkv, bs, hd2 = k_cache.shape
+    if hd2 != hd:
+        raise ValueError("head_dim of q and caches differ")
+    num_seqs = context_lens.shape[0]
+    if context_lens.dtype != torch.int32 or context_lens.dim() != 1:
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if query_start.dtype != torch.int32 or query_start.shape != (num_seqs + 1,):
+        raise ValueError("query_start must be int32 [num_seqs + 1]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    with torch.cuda.device(q.device):
+        ev0, ev1 = (kernel_events[0].handle, kernel_events[1].handle) if kernel_events \
+            else (None, None)
+        st = lib.pkv_paged_attention_prefill(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(query_start), ctypes.c_float(scale), num_seqs, total_q,
+            int(max_q_len), hq, hkv, hd, bs, nb, block_tables.shape[1], int(max_context_len),
+            _DTYPE_CODE[q.dtype], ev0, ev1, _stream(q, stream))
+    _check("paged_attention_prefill", st)
     return out
 
 

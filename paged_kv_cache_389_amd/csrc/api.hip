@@ -446,6 +446,57 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   return err == hipSuccess ? PKV_OK : fail_hip(err);
 }
 
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                float scale, int num_seqs, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                pkv_dtype dtype, void* begin_event, void* end_event,
+                                void* stream) {
+  if (!dtype_ok(dtype) || num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
+    return PKV_EINVAL;
+  const int group = num_q_heads / num_kv_heads;
+  if (!prefill_supported(to_elem(dtype), head_dim, block_size, group)) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PKV_EINVAL;
+  if (num_seqs > kMaxGridYZ) return PKV_EUNSUPPORTED;
+  if (max_blocks_per_seq > (1 << 30) / block_size) return PKV_EUNSUPPORTED;
+  const int64_t chunks = ((int64_t)max_q_len * group + 63) / 64;
+  if (chunks * num_kv_heads > INT32_MAX) return PKV_EUNSUPPORTED;
+  const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
+  a.chunks = (int)chunks;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
+    return fail_hip(err);
+  err = launch_prefill(to_elem(dtype), head_dim, block_size, a, st);
+  if (err != hipSuccess) return fail_hip(err);
+  if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
+    return fail_hip(err);
+  return PKV_OK;
+}
+
 int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
                               const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                               int head_dim, int block_size, int num_blocks, pkv_dtype dtype,

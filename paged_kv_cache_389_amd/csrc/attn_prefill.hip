@@ -1,0 +1,255 @@
+// Paged prefill attention: many query tokens per sequence, causal, on the
+// matrix cores.
+//
+// Sequence s has L cached tokens (its new ones included, written by
+// reshape_and_cache beforehand) and n query tokens, its last n positions:
+// query i sits at position L - n + i and attends to positions 0 .. L - n + i,
+// read through the sequence's block table.  This is the attention a
+// recomputation of evicted sequences runs ("vLLM and PagedAttention: How
+// Ideas from Operating Systems Accelerated LLM Inference", paragraph on the
+// engine: eviction by swapping or recomputation); the pages print no
+// formula, and the causal reading above is the plainest one.
+//
+// A wave owns 16 query columns: 16/G query tokens times the G query heads of
+// one KV head.  Against a 16-token tile of keys the columns form the same
+// contraction as grouped decode (S^T = K Q^T, 16x16x32 MFMAs; O^T += V^T P^T,
+// 16x16x16), so the operand layouts are those of the decode MFMA kernel; the
+// only new element is a causal bound per column: column c sees tokens below
+// limit_c, masked by index in the tiles that reach past the wave's smallest
+// bound.  Each wave streams its own tiles 0 .. ceil(max limit / 16) with the
+// table entries of 64 tiles fetched by one vector load and the next tile's
+// loads in flight while the current one is computed; the four waves of a
+// workgroup take consecutive query tokens of one (sequence, KV head), so
+// their tiles overlap and mostly hit in the caches.  No cross-wave merge is
+// needed: a wave owns its columns' whole context.
+#include "common.h"
+#include "decode.h"
+#include "mfma_ops.h"
+
+namespace pkv {
+
+constexpr int kPrefillStages = 2;
+
+template <int HD>
+struct PrefillShared {
+  u32x4 q[4][HD / 32][kWave];   // per wave: Q^T in the B layout
+};
+
+template <typename E, int HD, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(
+    PrefillArgs a) {
+  using T = typename E::storage;
+  using Ops = MfmaOps<E>;
+  constexpr int KSTEPS = HD / 32;
+  constexpr int DPL = HD / 16;
+  constexpr int VW = DPL / 2;
+  constexpr int TPB = BS / 16;
+  constexpr int NS = kPrefillStages;
+  static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
+  __shared__ PrefillShared<HD> sm;
+
+  const int g = blockIdx.x % a.num_kv_heads;
+  // heaviest query chunks (latest positions) first
+  const int chunk = a.chunks - 1 - (int)(blockIdx.x / a.num_kv_heads);
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x % kWave, wave = uniform(threadIdx.x / kWave);
+  const int n = lane & 15, g4 = lane >> 4;
+  const int G = a.group, tpw = 16 / G;
+
+  int q0 = load_uniform(a.query_start + s), q1 = load_uniform(a.query_start + s + 1);
+  q0 = min(max(q0, 0), a.total_q);
+  q1 = min(max(q1, q0), a.total_q);
+  const int nq = q1 - q0;
+  int L = load_uniform(a.context_lens + s);
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int first = (chunk * 4 + wave) * tpw;   // the wave's first query token
+  if (first >= nq) return;                      // no barrier follows: waves leave freely
+
+  // this lane's column: query token i (row q0 + i), head h
+  const int i = first + n / G, h = g * G + n % G;
+  const bool valid = i < nq;
+  const int pos = L - nq + i;
+  const int limit = (valid && pos >= 0) ? pos + 1 : 0;   // tokens [0, limit) are visible
+  int lim_max = limit, lim_min = valid ? limit : INT32_MAX;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    lim_max = max(lim_max, __shfl_xor(lim_max, off, 64));
+    lim_min = min(lim_min, __shfl_xor(lim_min, off, 64));
+  }
+  lim_max = uniform(lim_max);
+  lim_min = uniform(lim_min);
+
+  // Q^T of the wave's columns into its LDS slot (B layout)
+  {
+    const T* qrow = static_cast<const T*>(a.q) + ((size_t)(q0 + (valid ? i : 0)) * a.num_q_heads + h) * HD;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      sm.q[wave][kk][lane] = valid ? ld16(qrow + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
+  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
+  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
+  const uint32_t koff = (uint32_t)((n * HD + g4 * 8) * sizeof(T));
+  const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
+  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
+
+  f32x4 acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  int bad = 0;
+  const int ntiles = (lim_max + 15) / 16;
+
+  for (int pass = 0; pass < ntiles; pass += kWave) {
+    const int mine = min(kWave, ntiles - pass);
+    const int tbl = table[min((pass + lane) / TPB, a.max_blocks - 1)];
+
+    auto load_tile = [&](int t, u32x4* ka, uint32_t (*vv)[VW]) {
+      const bool live = t < mine;
+      const int u = pass + t;
+      int phys = lane_value(tbl, t < kWave ? t : kWave - 1);
+      if (live && (unsigned)phys >= (unsigned)a.num_blocks) bad = 1;
+      if (!live || (unsigned)phys >= (unsigned)a.num_blocks) phys = 0;
+      const size_t toff = (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * HD * sizeof(T);
+      const uint32_t nbytes = live ? (uint32_t)(16 * HD * sizeof(T)) : 0u;
+      const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
+      const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (VW == 2) {
+          const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
+          vv[r][0] = x[0];
+          vv[r][1] = x[1];
+        } else {
+          const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
+          vv[r][0] = x[0];
+          vv[r][1] = x[1];
+          vv[r][2] = x[2];
+          vv[r][3] = x[3];
+        }
+      }
+    };
+
+    auto compute_tile = [&](int t, const u32x4* ka, uint32_t (*vv)[VW]) {
+      const int u = pass + t;
+      __asm__ volatile("" ::: "memory");
+      u32x4 qb[KSTEPS];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm.q[wave][kk][lane];
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
+      if (u * 16 + 16 > lim_min) {
+        // causal bound of each column; value rows past the context are zeroed
+        // so that whatever those slots hold cannot reach the product
+        const int t0 = u * 16 + 4 * g4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (t0 + r >= limit) sc[r] = -INFINITY;
+          if (t0 + r >= L) {
+#pragma unroll
+            for (int w = 0; w < VW; ++w) vv[r][w] = 0u;
+          }
+        }
+      }
+      const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const float mn = fmaxf(m, mb);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float corr = fast_exp2(m - mu);
+      m = mn;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);
+      l = __builtin_fmaf(l, corr, (p[0] + p[1]) + (p[2] + p[3]));
+      if (__any(corr != 1.f)) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] *= corr;
+      }
+      const u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
+      u32x2 pr = {0u, 0u};
+      if constexpr (Ops::kSplit) {
+        pr[0] = Ops::pack2(p[0] - Ops::widen_lo(pb[0]), p[1] - Ops::widen_hi(pb[0]));
+        pr[1] = Ops::pack2(p[2] - Ops::widen_lo(pb[1]), p[3] - Ops::widen_hi(pb[1]));
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const u32x2 va = {pair_of(e, vv[0], vv[1]), pair_of(e, vv[2], vv[3])};
+        acc[e] = Ops::pv(va, pb, acc[e]);
+        if constexpr (Ops::kSplit) acc[e] = Ops::pv(va, pr, acc[e]);
+      }
+    };
+
+    u32x4 kb[NS][KSTEPS];
+    uint32_t vb[NS][4][VW];
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
+    for (int i0 = 0; i0 < mine; i0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        load_tile(i0 + j + NS - 1, kb[(j + NS - 1) % NS], vb[(j + NS - 1) % NS]);
+        if (i0 + j < mine) compute_tile(i0 + j, kb[j], vb[j]);
+      }
+    }
+  }
+
+  // the four token groups of a column hold partial sums of l
+  const float lsum = rows_sum(l);
+  const bool any_bad = __any(bad);
+  if (!valid) return;
+  T* orow = static_cast<T*>(a.out) + ((size_t)(q0 + i) * a.num_q_heads + h) * HD;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;   // no visible token: zero row
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[e][r] * inv;
+    store_rounded<E, DPL>(orow + (4 * g4 + r) * DPL, o);
+  }
+}
+
+template <typename E, int HD, int BS>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_mfma_kernel<E, HD, BS>), dim3(a.num_kv_heads * a.chunks, 1, a.num_seqs),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename E, int HD>
+static hipError_t launch_prefill_hd(int bs, const PrefillArgs& a, hipStream_t st) {
+  switch (bs) {
+    case 16: return launch_prefill_t<E, HD, 16>(a, st);
+    case 32: return launch_prefill_t<E, HD, 32>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t launch_prefill_e(int hd, int bs, const PrefillArgs& a, hipStream_t st) {
+  switch (hd) {
+    case 64: return launch_prefill_hd<E, 64>(bs, a, st);
+    case 128: return launch_prefill_hd<E, 128>(bs, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool prefill_supported(Elem e, int hd, int bs, int group) {
+  return (e == Elem::F16 || e == Elem::BF16) && (hd == 64 || hd == 128) &&
+         (bs == 16 || bs == 32) && group >= 1 && group <= 16 && 16 % group == 0;
+}
+
+hipError_t launch_prefill(Elem e, int hd, int bs, const PrefillArgs& a, hipStream_t st) {
+  switch (e) {
+    case Elem::F16: return launch_prefill_e<F16>(hd, bs, a, st);
+    case Elem::BF16: return launch_prefill_e<BF16>(hd, bs, a, st);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -53,6 +53,30 @@ struct DecodeArgs {
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
 
+// Arguments of the prefill kernel (attn_prefill.hip): causal attention of
+// the last n = query_start[s+1] - query_start[s] positions of each sequence.
+// Grid (num_kv_heads * chunks, 1, num_seqs); a workgroup's 4 waves take 16/G
+// query tokens each.
+struct PrefillArgs {
+  void* out;                    // [total_q][Hq][HD]
+  const void* q;                // [total_q][Hq][HD]
+  const void* k_cache;          // [NB][Hkv][BS][HD]
+  const void* v_cache;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* context_lens;  // [B]
+  const int32_t* query_start;   // [B + 1]
+  float scale_log2e;
+  int num_seqs;
+  int total_q;                  // rows of q / out (query_start is clamped to it)
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                    // Hq / Hkv, a divisor of 16
+  int num_blocks;
+  int max_blocks;
+  int len_cap;                  // lengths are clamped to this (<= max_blocks*BS)
+  int chunks;                   // ceil(max_q_len * group / 64)
+};
+
 // The work of one decode workgroup: tokens [t0, t1) (partition `part` of
 // n) of head unit `unit` of sequence s, or nothing (valid false: an item
 // slot past the list, or a partition past the context).  t1 == 0 only for
@@ -112,6 +136,9 @@ bool decode_valu_supported(Elem e, bool kv_fp8, int head_dim, int block_size);
 // 64 units per pass); the MFMA kernel's unit is 16 tokens.
 int valu_unit_tokens(Elem e, bool kv_fp8, int head_dim, int block_size);
 bool decode_mfma_supported(Elem e, int head_dim, int block_size);
+bool prefill_supported(Elem e, int head_dim, int block_size, int group);
+hipError_t launch_prefill(Elem e, int head_dim, int block_size, const PrefillArgs& a,
+                          hipStream_t stream);
 // Decode workgroups resident per compute unit (0 if the runtime cannot say).
 int decode_valu_occupancy(Elem e, bool kv_fp8, int head_dim, int block_size);
 int decode_mfma_occupancy(Elem e, bool kv_fp8, int head_dim, int block_size, int group);

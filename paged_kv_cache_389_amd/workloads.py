@@ -29,6 +29,10 @@ Five workload shapes (names used throughout the tests and the benchmark):
     through reference counts, then diverge by 0-256 generated tokens; the
     first append into the shared partly filled last block triggers
     copy-on-write.  32 heads (MHA), head_dim 128, block_size 16, pool of 8192.
+``llama3_8b_prefill_bf16``
+    16 prompts of 512-2048 tokens whose every token is a query of the causal
+    prefill attention; 32 query / 8 KV heads, head_dim 128, block_size 16,
+    pool of 4096 blocks.
 ``beam_search_fp16``
     16 requests with prompts of 256-1024 tokens, each decoded with 8 beams
     for 64 steps: every step appends one token to every beam (copy-on-write
@@ -376,6 +380,100 @@ def build_beam_search(name="beam_search_fp16", *, dtype="fp16", num_requests=16,
     return wl
 
 
+@dataclass
+class PrefillWorkload:
+    """Causal multi-token attention inputs: sequence s has ``context_lens[s]``
+    cached tokens, of which the last ``query_start[s+1] - query_start[s]`` are
+    queries (rows of ``q``)."""
+    name: str
+    dtype: torch.dtype
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    seed: int
+    context_lens: np.ndarray        # int32 [B]
+    query_start: np.ndarray         # int32 [B + 1]
+    block_tables: np.ndarray        # int32 [B, W]
+    q: torch.Tensor                 # [total_q, Hq, hd]
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+
+    @property
+    def total_q(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def max_q_len(self) -> int:
+        return int(np.diff(self.query_start).max(initial=0))
+
+    @property
+    def esize(self) -> int:
+        return torch.tensor([], dtype=self.dtype).element_size()
+
+    def flops(self) -> int:
+        """Causal attention flops: 4 * hd per (query row, head, visible token)
+        (QK and PV, one multiply-add = 2 flops each)."""
+        vis = 0
+        for s in range(self.num_seqs):
+            n = int(self.query_start[s + 1] - self.query_start[s])
+            L = int(self.context_lens[s])
+            p = np.arange(L - n, L)
+            vis += int(np.clip(p + 1, 0, None).sum())
+        return 4 * self.head_dim * self.num_q_heads * vis
+
+    def min_bytes(self) -> int:
+        """Bytes the call must move at least: every visible K/V row once, q
+        in, out."""
+        kv = int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * \
+            self.head_dim * self.esize
+        return kv + 2 * self.total_q * self.num_q_heads * self.head_dim * self.esize
+
+
+def build_prefill(name, *, dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                  num_blocks, lens, chunk=None, seed, device="cpu"):
+    """Prefill workload: contexts of ``lens`` (``(lo, hi)`` uniform or an
+    array) in randomly placed blocks; each sequence's queries are its last
+    ``min(L, chunk)`` positions (all of them when ``chunk`` is None)."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    rng = np.random.default_rng(seed)
+    if isinstance(lens, tuple):
+        context_lens = rng.integers(lens[0], lens[1] + 1, size=num_seqs)
+    else:
+        context_lens = np.asarray(lens, dtype=np.int64)
+    bm = BlockManager(num_blocks, block_size, free_order=rng.permutation(num_blocks))
+    seqs = []
+    for L in context_lens.tolist():
+        sq = bm.new_sequence()
+        bm.extend(sq, L)
+        seqs.append(sq)
+    nq = context_lens if chunk is None else np.minimum(context_lens, chunk)
+    query_start = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    g = _gen(device, seed)
+    pool_shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    q = _randn((int(query_start[-1]), num_q_heads, head_dim), dt, g, device)
+    k_cache = _randn(pool_shape, dt, g, device)
+    v_cache = _randn(pool_shape, dt, g, device)
+    return PrefillWorkload(
+        name=name, dtype=dt, num_seqs=num_seqs, num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+        num_blocks=num_blocks, scale=1.0 / math.sqrt(head_dim), seed=seed,
+        context_lens=context_lens.astype(np.int32), query_start=query_start,
+        block_tables=bm.block_table_array(seqs, pad=0), q=q, k_cache=k_cache, v_cache=v_cache)
+
+
+def llama3_8b_prefill_bf16(seed=7, device="cpu", **kw):
+    """Llama-3-8B-shaped prefill: 16 prompts of 512-2048 tokens, every token a
+    query (32 query / 8 KV heads, head_dim 128, block_size 16)."""
+    args = dict(dtype="bf16", num_seqs=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, num_blocks=4096, lens=(512, 2048))
+    args.update(kw)
+    return build_prefill("llama3_8b_prefill_bf16", seed=seed, device=device, **args)
+
+
 def sharing_saving(wl, step=None) -> float:
     """1 - physical / logical blocks of a multi-step workload's step (default:
     the last): the share of block memory that sharing saves against giving
@@ -432,6 +530,7 @@ WORKLOADS = {
     "long_context_gqa_bf16": long_context_gqa_bf16,
     "sharing_fp16": sharing_fp16,
     "beam_search_fp16": beam_search_fp16,
+    "llama3_8b_prefill_bf16": llama3_8b_prefill_bf16,
 }
 
 

@@ -242,3 +242,26 @@ def test_fp8_calls_reject_bad_arguments(native):
     # copy and swap move E4M3 blocks as bytes
     assert lib.pkv_copy_blocks(None, None, None, 0, 8, 128, 16, 64, 3, None) == 0
     assert lib.pkv_swap_blocks(1, 1, 1, 1, 1, -1, 8, 128, 16, 64, 32, 3, None) == -1
+
+
+def test_prefill_rejects_bad_arguments(native):
+    f = native.lib.pkv_paged_attention_prefill
+    # (out, q, kc, vc, tables, lens, qstart, scale, B, total_q, max_q, hq, hkv, hd, bs, nb,
+    #  max_blocks, max_ctx, dtype, ev0, ev1, stream)
+    ok = [1, 1, 1, 1, 1, 1, 1, 0.1, 4, 64, 32, 8, 2, 128, 16, 64, 8, 128, 1, None, None, None]
+
+    def call(**over):
+        args = list(ok)
+        names = ["out", "q", "kc", "vc", "tables", "lens", "qstart", "scale", "B", "total_q",
+                 "max_q", "hq", "hkv", "hd", "bs", "nb", "max_blocks", "max_ctx", "dtype"]
+        for k, v in over.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(B=0) == 0 and call(total_q=0) == 0 and call(max_q=0) == 0
+    assert call(qstart=None) == -1
+    assert call(hkv=3) == -1                 # Hq % Hkv
+    assert call(hq=12, hkv=4) == -2          # group 3 does not divide 16
+    assert call(dtype=0) == -2               # no float32 prefill
+    assert call(hd=256) == -2 and call(bs=8) == -2
+    assert call(max_q=-1) == -1 and call(total_q=-1) == -1
