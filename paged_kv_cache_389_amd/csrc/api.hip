@@ -465,7 +465,8 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
     return PKV_EINVAL;
   if (num_seqs > kMaxGridYZ) return PKV_EUNSUPPORTED;
   if (max_blocks_per_seq > (1 << 30) / block_size) return PKV_EUNSUPPORTED;
-  const int64_t chunks = ((int64_t)max_q_len * group + 63) / 64;
+  const int per_wg = prefill_tokens_per_workgroup(group);
+  const int64_t chunks = ((int64_t)max_q_len + per_wg - 1) / per_wg;
   if (chunks * num_kv_heads > INT32_MAX) return PKV_EUNSUPPORTED;
   const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
   PrefillArgs a;

@@ -10,8 +10,9 @@
 // engine: eviction by swapping or recomputation); the pages print no
 // formula, and the causal reading above is the plainest one.
 //
-// A wave owns 16 query columns: 16/G query tokens times the G query heads of
-// one KV head.  Against a 16-token tile of keys the columns form the same
+// A wave owns kPrefillGroups groups of 16 query columns, each 16/G query
+// tokens times the G query heads of one KV head; every K/V tile it loads
+// serves all its groups.  Against a 16-token tile of keys a group forms the same
 // contraction as grouped decode (S^T = K Q^T, 16x16x32 MFMAs; O^T += V^T P^T,
 // 16x16x16), so the operand layouts are those of the decode MFMA kernel; the
 // only new element is a causal bound per column: column c sees tokens below
@@ -29,14 +30,21 @@
 namespace pkv {
 
 constexpr int kPrefillStages = 2;
+// Probabilities enter the PV product rounded to the input type once (no
+// bf16 head + remainder split as in decode, which doubles the PV work of
+// this compute-heavy kernel).
+constexpr bool kPrefillSplitP = false;
 
-template <int HD>
+// Column groups of 16 per wave: each K/V tile a wave loads serves CG groups.
+constexpr int kPrefillGroups = 4;
+
+template <int HD, int CG>
 struct PrefillShared {
-  u32x4 q[4][HD / 32][kWave];   // per wave: Q^T in the B layout
+  u32x4 q[4][CG][HD / 32][kWave];   // per wave and column group: Q^T in the B layout
 };
 
-template <typename E, int HD, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(
+template <typename E, int HD, int BS, int CG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     PrefillArgs a) {
   using T = typename E::storage;
   using Ops = MfmaOps<E>;
@@ -46,7 +54,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   constexpr int TPB = BS / 16;
   constexpr int NS = kPrefillStages;
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
-  __shared__ PrefillShared<HD> sm;
+  __shared__ PrefillShared<HD, CG> sm;
 
   const int g = blockIdx.x % a.num_kv_heads;
   // heaviest query chunks (latest positions) first
@@ -54,7 +62,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int s = blockIdx.z;
   const int lane = threadIdx.x % kWave, wave = uniform(threadIdx.x / kWave);
   const int n = lane & 15, g4 = lane >> 4;
-  const int G = a.group, tpw = 16 / G;
+  const int G = a.group, tpg = 16 / G, tpw = CG * tpg;   // query tokens per group / wave
 
   int q0 = load_uniform(a.query_start + s), q1 = load_uniform(a.query_start + s + 1);
   q0 = min(max(q0, 0), a.total_q);
@@ -65,12 +73,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int first = (chunk * 4 + wave) * tpw;   // the wave's first query token
   if (first >= nq) return;                      // no barrier follows: waves leave freely
 
-  // this lane's column: query token i (row q0 + i), head h
-  const int i = first + n / G, h = g * G + n % G;
-  const bool valid = i < nq;
-  const int pos = L - nq + i;
-  const int limit = (valid && pos >= 0) ? pos + 1 : 0;   // tokens [0, limit) are visible
-  int lim_max = limit, lim_min = valid ? limit : INT32_MAX;
+  // this lane's column in group c: query token i[c] (row q0 + i[c]), head h
+  const int h = g * G + n % G;
+  int i[CG], limit[CG];
+  bool valid[CG];
+  int lim_max = 0, lim_min = INT32_MAX;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    i[c] = first + c * tpg + n / G;
+    valid[c] = i[c] < nq;
+    const int pos = L - nq + i[c];
+    limit[c] = (valid[c] && pos >= 0) ? pos + 1 : 0;   // tokens [0, limit) are visible
+    lim_max = max(lim_max, limit[c]);
+    if (valid[c]) lim_min = min(lim_min, limit[c]);
+  }
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) {
     lim_max = max(lim_max, __shfl_xor(lim_max, off, 64));
@@ -79,12 +95,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   lim_max = uniform(lim_max);
   lim_min = uniform(lim_min);
 
-  // Q^T of the wave's columns into its LDS slot (B layout)
-  {
-    const T* qrow = static_cast<const T*>(a.q) + ((size_t)(q0 + (valid ? i : 0)) * a.num_q_heads + h) * HD;
+  // Q^T of the wave's columns into its LDS slots (B layout)
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const T* qrow = static_cast<const T*>(a.q) +
+                    ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
-      sm.q[wave][kk][lane] = valid ? ld16(qrow + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+      sm.q[wave][c][kk][lane] = valid[c] ? ld16(qrow + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
   }
 
   const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
@@ -94,10 +112,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
   const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
-  f32x4 acc[DPL];
+  f32x4 acc[CG][DPL];
+  float m[CG], l[CG];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int c = 0; c < CG; ++c) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = -INFINITY;
+    l[c] = 0.f;
+  }
   int bad = 0;
   const int ntiles = (lim_max + 15) / 16;
 
@@ -135,53 +158,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 
     auto compute_tile = [&](int t, const u32x4* ka, uint32_t (*vv)[VW]) {
       const int u = pass + t;
-      __asm__ volatile("" ::: "memory");
-      u32x4 qb[KSTEPS];
+      const bool edge = u * 16 + 16 > lim_min;   // some column's bound or the context ends here
+      const int t0 = u * 16 + 4 * g4;
+      if (edge) {
+        // value rows past the context are zeroed so that whatever those
+        // slots hold cannot reach the product
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm.q[wave][kk][lane];
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
-      float sc[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
-      if (u * 16 + 16 > lim_min) {
-        // causal bound of each column; value rows past the context are zeroed
-        // so that whatever those slots hold cannot reach the product
-        const int t0 = u * 16 + 4 * g4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (t0 + r >= limit) sc[r] = -INFINITY;
+        for (int r = 0; r < 4; ++r)
           if (t0 + r >= L) {
 #pragma unroll
             for (int w = 0; w < VW; ++w) vv[r][w] = 0u;
           }
+      }
+      u32x2 pb[CG], pr[CG];
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        __asm__ volatile("" ::: "memory");
+        u32x4 qb[KSTEPS];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm.q[wave][c][kk][lane];
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (t0 + r >= limit[c]) sc[r] = -INFINITY;   // the column's causal bound
+        }
+        const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        const float mn = fmaxf(m[c], mb);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        const float corr = fast_exp2(m[c] - mu);
+        m[c] = mn;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);
+        l[c] = __builtin_fmaf(l[c], corr, (p[0] + p[1]) + (p[2] + p[3]));
+        if (__any(corr != 1.f)) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
+        }
+        pb[c] = u32x2{Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
+        pr[c] = u32x2{0u, 0u};
+        if constexpr (kPrefillSplitP) {
+          pr[c][0] = Ops::pack2(p[0] - Ops::widen_lo(pb[c][0]), p[1] - Ops::widen_hi(pb[c][0]));
+          pr[c][1] = Ops::pack2(p[2] - Ops::widen_lo(pb[c][1]), p[3] - Ops::widen_hi(pb[c][1]));
         }
       }
-      const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-      const float mn = fmaxf(m, mb);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float corr = fast_exp2(m - mu);
-      m = mn;
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);
-      l = __builtin_fmaf(l, corr, (p[0] + p[1]) + (p[2] + p[3]));
-      if (__any(corr != 1.f)) {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] *= corr;
-      }
-      const u32x2 pb = {Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
-      u32x2 pr = {0u, 0u};
-      if constexpr (Ops::kSplit) {
-        pr[0] = Ops::pack2(p[0] - Ops::widen_lo(pb[0]), p[1] - Ops::widen_hi(pb[0]));
-        pr[1] = Ops::pack2(p[2] - Ops::widen_lo(pb[1]), p[3] - Ops::widen_hi(pb[1]));
-      }
+      // one V^T operand per lane-dim e serves every column group
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         const u32x2 va = {pair_of(e, vv[0], vv[1]), pair_of(e, vv[2], vv[3])};
-        acc[e] = Ops::pv(va, pb, acc[e]);
-        if constexpr (Ops::kSplit) acc[e] = Ops::pv(va, pr, acc[e]);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+          acc[c][e] = Ops::pv(va, pb[c], acc[c][e]);
+          if constexpr (kPrefillSplitP) acc[c][e] = Ops::pv(va, pr[c], acc[c][e]);
+        }
       }
     };
 
@@ -198,27 +233,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
   }
 
-  // the four token groups of a column hold partial sums of l
-  const float lsum = rows_sum(l);
   const bool any_bad = __any(bad);
-  if (!valid) return;
-  T* orow = static_cast<T*>(a.out) + ((size_t)(q0 + i) * a.num_q_heads + h) * HD;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;   // no visible token: zero row
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float o[DPL];
+  for (int c = 0; c < CG; ++c) {
+    // the four token groups of a column hold partial sums of l
+    const float lsum = rows_sum(l[c]);
+    if (!valid[c]) continue;
+    T* orow = static_cast<T*>(a.out) + ((size_t)(q0 + i[c]) * a.num_q_heads + h) * HD;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;   // no visible token: zero row
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[e][r] * inv;
-    store_rounded<E, DPL>(orow + (4 * g4 + r) * DPL, o);
+    for (int r = 0; r < 4; ++r) {
+      float o[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[c][e][r] * inv;
+      store_rounded<E, DPL>(orow + (4 * g4 + r) * DPL, o);
+    }
   }
 }
 
 template <typename E, int HD, int BS>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<E, HD, BS>), dim3(a.num_kv_heads * a.chunks, 1, a.num_seqs),
-                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<E, HD, BS, kPrefillGroups>),
+                     dim3(a.num_kv_heads * a.chunks, 1, a.num_seqs), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+
+int prefill_tokens_per_workgroup(int group) { return 4 * kPrefillGroups * (16 / group); }
 
 template <typename E, int HD>
 static hipError_t launch_prefill_hd(int bs, const PrefillArgs& a, hipStream_t st) {

@@ -55,8 +55,8 @@ enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
 
 // Arguments of the prefill kernel (attn_prefill.hip): causal attention of
 // the last n = query_start[s+1] - query_start[s] positions of each sequence.
-// Grid (num_kv_heads * chunks, 1, num_seqs); a workgroup's 4 waves take 16/G
-// query tokens each.
+// Grid (num_kv_heads * chunks, 1, num_seqs); a workgroup's 4 waves take
+// consecutive query tokens (16/G per column group of 16).
 struct PrefillArgs {
   void* out;                    // [total_q][Hq][HD]
   const void* q;                // [total_q][Hq][HD]
@@ -74,7 +74,7 @@ struct PrefillArgs {
   int num_blocks;
   int max_blocks;
   int len_cap;                  // lengths are clamped to this (<= max_blocks*BS)
-  int chunks;                   // ceil(max_q_len * group / 64)
+  int chunks;                   // ceil(max_q_len / query tokens per workgroup)
 };
 
 // The work of one decode workgroup: tokens [t0, t1) (partition `part` of
@@ -137,6 +137,9 @@ bool decode_valu_supported(Elem e, bool kv_fp8, int head_dim, int block_size);
 int valu_unit_tokens(Elem e, bool kv_fp8, int head_dim, int block_size);
 bool decode_mfma_supported(Elem e, int head_dim, int block_size);
 bool prefill_supported(Elem e, int head_dim, int block_size, int group);
+// Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
+// chunks per KV head and sequence).
+int prefill_tokens_per_workgroup(int group);
 hipError_t launch_prefill(Elem e, int head_dim, int block_size, const PrefillArgs& a,
                           hipStream_t stream);
 // Decode workgroups resident per compute unit (0 if the runtime cannot say).
