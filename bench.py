@@ -150,7 +150,8 @@ def counters_to_traffic(args):
         if not rows:
             raise SystemExit(f"no {counter} rows")
         return max(rows)
-    is_decode = lambda k: "decode_mfma_kernel" in k or "decode_valu_kernel" in k
+    is_decode = lambda k: any(n in k for n in ("decode_mfma_kernel", "decode_valu_kernel",
+                                               "prefill_mfma_kernel"))
     is_other = lambda k: "pkv::" not in k
     cal_bytes = args.cal_mib << 20
     f_fetch = pick(_counter_means(args.cal_fetch_db), "FETCH_SIZE", is_other)[0] * 1024 / cal_bytes
@@ -159,7 +160,8 @@ def counters_to_traffic(args):
     write, _ = pick(_counter_means(args.write_db), "WRITE_SIZE", is_decode)
     from paged_kv_cache_389_amd import workloads
     wl = workloads.make(args.workload, device="cpu")
-    key, alg = args.workload, wl.decode_bytes()
+    key = args.workload
+    alg = wl.min_bytes() if args.workload in PREFILL_WORKLOADS else wl.decode_bytes()
     if args.kv_cache == "e4m3":   # one byte per K/V element
         key, alg = key + "_kv_e4m3", alg - (wl.kv_bytes() - wl.kv_bytes() // wl.esize)
     try:
