@@ -34,6 +34,9 @@ constexpr int kPrefillStages = 2;
 // bf16 head + remainder split as in decode, which doubles the PV work of
 // this compute-heavy kernel).
 constexpr bool kPrefillSplitP = false;
+// How far (log2 units) a tile's maximum may pass the reference maximum
+// before the accumulators are rescaled: probabilities stay below 2^8.
+constexpr float kPrefillSlack = 8.f;
 
 // Column groups of 16 per wave: each K/V tile a wave loads serves CG groups.
 constexpr int kPrefillGroups = 4;
@@ -180,27 +183,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
-        float sc[4];
+        float sr[4];   // scores in log2 units
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2e;
+        for (int r = 0; r < 4; ++r) sr[r] = sacc[r] * a.scale_log2e;
         if (edge) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (t0 + r >= limit[c]) sc[r] = -INFINITY;   // the column's causal bound
+            if (t0 + r >= limit[c]) sr[r] = -INFINITY;   // the column's causal bound
         }
-        const float mb = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-        const float mn = fmaxf(m[c], mb);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float corr = fast_exp2(m[c] - mu);
-        m[c] = mn;
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mu);
-        l[c] = __builtin_fmaf(l[c], corr, (p[0] + p[1]) + (p[2] + p[3]));
-        if (__any(corr != 1.f)) {
+        // Lazy rescaling: m is a reference maximum (log2 units) that moves
+        // only when a tile's maximum passes it by more than kPrefillSlack, so
+        // the probabilities stay below 2^kPrefillSlack and the accumulators
+        // are rescaled a few times per context instead of at most tiles.
+        // The normalised result is the same; only the reference differs.
+        const float mb = rows_max(fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3])));
+        if (__any(mb > m[c] + kPrefillSlack)) {
+          const float mn = fmaxf(m[c], mb);
+          const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m[c] - mn);
+          m[c] = mn;
+          l[c] *= corr;
 #pragma unroll
           for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
         }
+        const float mu = (m[c] == -INFINITY) ? 0.f : m[c];
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sr[r] - mu);   // exp2(-inf) == 0
+        l[c] += (p[0] + p[1]) + (p[2] + p[3]);
         pb[c] = u32x2{Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
         pr[c] = u32x2{0u, 0u};
         if constexpr (kPrefillSplitP) {
