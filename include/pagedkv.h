@@ -403,8 +403,8 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache
  *   query_start   int32 [num_seqs + 1], non-decreasing, query_start[0] = 0,
  *                 query_start[num_seqs] = total_q  (read; values are clamped
  *                 to [0, total_q])
- *   max_q_len     host-side bound of every n (sizes the grid; queries past it
- *                 are not computed)
+ *   max_q_len     host-side bound of every n (sizes the grid; query rows past
+ *                 it may be left unwritten)
  *   k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
  *   max_blocks_per_seq, num_blocks: as in pkv_paged_attention_decode.
  *   begin_event, end_event: optional hipEvent_t recorded around the kernel.
