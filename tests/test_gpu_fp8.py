@@ -323,3 +323,29 @@ def test_full_size_fp8_matches_oracle(name):
         assert np.isfinite(got).all()
         err = float(np.abs(got - want[seqs]).max())
         assert err <= TOL[wl.dtype], f"{name} partition {partition}: max abs err {err}"
+
+
+def test_copy_and_swap_move_code_blocks_bit_exact():
+    """copy_blocks and swap_blocks on uint8 code pools (dtype PKV_E4M3):
+    whole blocks, byte for byte, against the oracle."""
+    say("fp8 copy/swap")
+    g = torch.Generator().manual_seed(401)
+    nb, nh, hkv, bs, hd = 40, 12, 4, 16, 128
+    kc0 = torch.randint(0, 256, (nb, hkv, bs, hd), generator=g, dtype=torch.uint8)
+    vc0 = torch.randint(0, 256, (nb, hkv, bs, hd), generator=g, dtype=torch.uint8)
+    kc, vc = kc0.to(DEV), vc0.to(DEV)
+    pairs = np.array([[3, 30], [7, 31], [39, 0], [5, 99]], np.int64)
+    pk.copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV))
+    want_k, want_v = kc0.numpy().copy(), vc0.numpy().copy()
+    oracle.copy_blocks(want_k, want_v, pairs[:3])
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), want_k) and np.array_equal(vc.cpu().numpy(), want_v)
+    hk = torch.zeros((nh, hkv, bs, hd), dtype=torch.uint8).pin_memory()
+    hv = torch.zeros((nh, hkv, bs, hd), dtype=torch.uint8).pin_memory()
+    out_pairs = np.array([[30, 2], [1, 11], [17, 0]], np.int64)
+    pk.swap_blocks(kc, vc, hk, hv, torch.from_numpy(out_pairs).to(DEV))
+    torch.cuda.synchronize()
+    hk_want = np.zeros((nh, hkv, bs, hd), np.uint8)
+    hv_want = np.zeros_like(hk_want)
+    oracle.swap_blocks(want_k, want_v, hk_want, hv_want, out_pairs)
+    assert np.array_equal(hk.numpy(), hk_want) and np.array_equal(hv.numpy(), hv_want)
