@@ -22,7 +22,8 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every array argument is a DEVICE pointer (memory the caller allocated
- *   on the current HIP device, e.g. a torch tensor's data_ptr()).  The
+ *   on the current HIP device, e.g. a torch tensor's data_ptr()); the pools
+ *   of pkv_swap_blocks may also be pinned host memory.  The
  *   library never allocates device memory, never frees caller memory and
  *   keeps no pointer after the call's work has been enqueued.
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call is
@@ -366,8 +367,10 @@ int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void*
  * layout.  The scales multiply outside the dot products (scores by
  * scale * k_scale, the output by v_scale), which is exact up to rounding
  * order.  The workspace size is pkv_paged_attention_workspace_bytes with
- * dtype | PKV_KV_E4M3.  Runs the vector-ALU kernel (path AUTO or VALU;
- * MFMA and CONTIGUOUS return PKV_EUNSUPPORTED).  Everything else, events
+ * dtype | PKV_KV_E4M3.  Kernels as for 16-bit caches: AUTO takes the MFMA
+ * kernel for 16-bit queries with 2 <= Hq/Hkv <= 16 (head_dim 64 or 128,
+ * block_size 16 or 32) and the vector-ALU kernel otherwise; the
+ * CONTIGUOUS control returns PKV_EUNSUPPORTED.  Everything else, events
  * included, as pkv_paged_attention_decode_timed.
  */
 int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
