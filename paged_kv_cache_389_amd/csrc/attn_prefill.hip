@@ -196,9 +196,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         // the probabilities stay below 2^kPrefillSlack and the accumulators
         // are rescaled a few times per context instead of at most tiles.
         // The normalised result is the same; only the reference differs.
-        const float mb = rows_max(fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3])));
-        if (__any(mb > m[c] + kPrefillSlack)) {
-          const float mn = fmaxf(m[c], mb);
+        // each lane checks its own four scores; the column maximum (a
+        // reduction across the four token groups) is needed only to rescale
+        const float lmax = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
+        if (__any(lmax > m[c] + kPrefillSlack)) {
+          const float mn = fmaxf(m[c], rows_max(lmax));
           const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m[c] - mn);
           m[c] = mn;
           l[c] *= corr;
