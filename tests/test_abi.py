@@ -152,6 +152,7 @@ def _decode(lib, **over):
     (dict(path=2, Hq=2, Hkv=2), -2),   # MFMA needs grouped heads
     (dict(path=2, dtype=0), -2),       # MFMA needs 16-bit types
     (dict(maxL=4096, maxb=256, part=512), -3),   # several partitions and no workspace
+    (dict(B=65536), -2),         # past the largest batch the grid takes (65,535)
     (dict(B=4000, Hq=4, Hkv=4, maxL=64, maxb=4), -3),   # planned grid and no workspace
     (dict(part=-1), -1),
     (dict(grid=3), -1),

@@ -380,3 +380,36 @@ def test_decode_planned_determinism_and_placement(hq, hkv):
                                    0.088, partition=256, grid=2).cpu())
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_decode_largest_batch():
+    """The largest batch the grid takes, 65,535 sequences (short and empty
+    ones, as many single-block contexts): the planning kernel lists 64
+    chunks of 1024; sampled sequences (every 997th, plus the longest) match
+    the oracle and empty sequences give zero rows."""
+    say("decode largest batch")
+    num_seqs, hq, hkv, hd, bs = 65535, 2, 1, 64, 16
+    rng = np.random.default_rng(1500)
+    lens = rng.integers(0, 40, num_seqs)
+    lens[::101] = 0
+    nblk = -(-lens // bs)
+    total = int(nblk.sum()) + 1
+    perm = rng.permutation(total)
+    width = int(nblk.max())
+    tables = np.zeros((num_seqs, width), np.int32)
+    starts = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    for j in range(width):
+        has = nblk > j
+        tables[has, j] = perm[starts[has] + j]
+    q = rng.standard_normal((num_seqs, hq, hd)).astype(np.float16)
+    kp = rng.standard_normal((total, hkv, bs, hd)).astype(np.float16)
+    vp = rng.standard_normal((total, hkv, bs, hd)).astype(np.float16)
+    got = decode_gpu(torch.from_numpy(q).to(DEV), torch.from_numpy(kp).to(DEV),
+                     torch.from_numpy(vp).to(DEV), torch.from_numpy(tables).to(DEV),
+                     torch.from_numpy(lens.astype(np.int32)).to(DEV), 0.125)
+    g = got.cpu().double().numpy()
+    assert np.isfinite(g).all()
+    assert not g[lens == 0].any()
+    seqs = sorted(set(range(0, num_seqs, 997)) | {int(np.argmax(lens))})
+    want = oracle.decode(q, kp, vp, tables, lens, 0.125, hkv, seqs=seqs)
+    assert float(np.abs(g[seqs] - want[seqs]).max()) <= TOL[torch.float16]
