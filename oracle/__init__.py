@@ -25,8 +25,8 @@ closed forms, invariants and hand-worked fixtures.
 from .paged_attention import decode, decode_one, kv_head_of
 from .cache_ops import copy_blocks, reshape_and_cache, swap_blocks
 from . import fp8
-from .fp8 import decode_fp8, reshape_and_cache_fp8
+from .fp8 import decode_fp8, prefill_fp8, reshape_and_cache_fp8
 from .prefill import prefill
 
 __all__ = ["decode", "decode_one", "kv_head_of", "copy_blocks", "reshape_and_cache",
-           "swap_blocks", "fp8", "decode_fp8", "reshape_and_cache_fp8", "prefill"]
+           "swap_blocks", "fp8", "decode_fp8", "reshape_and_cache_fp8", "prefill", "prefill_fp8"]

@@ -23,14 +23,16 @@ therefore a reading, the plainest one that fits the rest of the path:
   even fraction (round to nearest even).  Zero keeps its sign.  The float32
   steps are the precision the device kernel decides the code in, so both
   sides take the same decision.
-* Attention over such a cache is the plain attention of ``decode`` over the
-  dequantised values ``value(code) * scale`` (exact in float64).
+* Attention over such a cache (decode or prefill) is the plain attention of
+  ``decode`` / ``prefill`` over the dequantised values ``value(code) * scale``
+  (exact in float64).
 """
 
 import numpy as np
 
 from .cache_ops import reshape_and_cache as _write_rows
 from .paged_attention import decode as _decode
+from .prefill import prefill as _prefill
 
 NAN_CODE = 0x7F
 MAX_CODE = 0x7E      # +448
@@ -113,3 +115,11 @@ def decode_fp8(q, k_codes, v_codes, block_tables, context_lens, scale, k_scale, 
     K and V (float64)."""
     return _decode(q, dequantize(k_codes, k_scale), dequantize(v_codes, v_scale), block_tables,
                    context_lens, scale, num_kv_heads, seqs=seqs, heads=heads)
+
+
+def prefill_fp8(q, k_codes, v_codes, block_tables, context_lens, query_start, scale, k_scale,
+                v_scale, num_kv_heads, rows=None, heads=None):
+    """Causal paged prefill over E4M3 caches: ``prefill`` on the dequantised K
+    and V (float64)."""
+    return _prefill(q, dequantize(k_codes, k_scale), dequantize(v_codes, v_scale), block_tables,
+                    context_lens, query_start, scale, num_kv_heads, rows=rows, heads=heads)

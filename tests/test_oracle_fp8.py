@@ -142,3 +142,22 @@ def test_decode_fp8_scales_factor_out():
     assert np.array_equal(c, 4.0 * a)
     # one token: the output is that token's dequantised V row
     assert np.array_equal(a[1], np.repeat(fp8.e4m3_value(vc[tables[1, 0], :, 0, :]), 2, axis=0))
+
+
+def test_prefill_fp8_one_query_per_sequence_is_decode_fp8():
+    """Prefill over codes with one query per sequence is decode over codes;
+    with every token queried, the last row of each sequence is too."""
+    rng = np.random.default_rng(9)
+    nb, hkv, bs, hd = 10, 2, 4, 8
+    kc = rng.integers(0, 0x7F, (nb, hkv, bs, hd)).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, (nb, hkv, bs, hd)).astype(np.uint8)
+    tables = rng.permutation(nb)[:8].reshape(2, 4)
+    lens = np.array([13, 6])
+    q = rng.standard_normal((2, 4, hd))
+    one = fp8.prefill_fp8(q, kc, vc, tables, lens, np.arange(3), 0.2, 0.5, 0.25, hkv)
+    assert np.array_equal(one, fp8.decode_fp8(q, kc, vc, tables, lens, 0.2, 0.5, 0.25, hkv))
+    qa = rng.standard_normal((19, 4, hd))
+    qs = np.array([0, 13, 19])
+    full = fp8.prefill_fp8(qa, kc, vc, tables, lens, qs, 0.2, 0.5, 0.25, hkv)
+    last = fp8.decode_fp8(qa[[12, 18]], kc, vc, tables, lens, 0.2, 0.5, 0.25, hkv)
+    assert np.allclose(full[[12, 18]], last, rtol=0, atol=1e-13)
