@@ -163,7 +163,9 @@ def counters_to_traffic(args):
     key = args.workload
     alg = wl.min_bytes() if args.workload in PREFILL_WORKLOADS else wl.decode_bytes()
     if args.kv_cache == "e4m3":   # one byte per K/V element
-        key, alg = key + "_kv_e4m3", alg - (wl.kv_bytes() - wl.kv_bytes() // wl.esize)
+        kv = (int(wl.context_lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim *
+              wl.esize)
+        key, alg = key + "_kv_e4m3", alg - (kv - kv // wl.esize)
     try:
         with open(args.counters) as fh:
             rec = json.load(fh)
@@ -434,11 +436,17 @@ def bench_prefill(name, args):
     qs = torch.from_numpy(wl.query_start).cuda()
     out = torch.empty_like(wl.q)
     kev = [(pk.HipEvent(), pk.HipEvent()) for _ in range(args.steps)]
+    kv_bytes = int(wl.context_lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim
+    dev = {"k": wl.k_cache, "v": wl.v_cache}
+    scales = {}
+    if args.kv_cache == "e4m3":
+        quantise_pools(wl, dev)
+        scales = dict(k_scale=dev["k_scale"], v_scale=dev["v_scale"])
 
     def step(i=None):
-        pk.paged_attention_prefill(out, wl.q, wl.k_cache, wl.v_cache, tables, lens, qs, wl.scale,
+        pk.paged_attention_prefill(out, wl.q, dev["k"], dev["v"], tables, lens, qs, wl.scale,
                                    wl.max_q_len, int(wl.context_lens.max()),
-                                   kernel_events=None if i is None else kev[i])
+                                   kernel_events=None if i is None else kev[i], **scales)
 
     for _ in range(args.warmup):
         step()
@@ -451,6 +459,9 @@ def bench_prefill(name, args):
     kms = [a.elapsed_ms(b) for a, b in kev]
     ker = float(np.mean(kms))
     flops, nbytes = wl.flops(), wl.min_bytes()
+    if dev.get("kv_fp8"):   # one byte per K/V element
+        nbytes -= kv_bytes * (wl.esize - 1)
+    tag = name + ("_kv_e4m3" if dev.get("kv_fp8") else "")
     tflops = flops / (ker / 1e3) / 1e12
     ms_per_step = wall / args.steps * 1e3
     return {
@@ -460,7 +471,8 @@ def bench_prefill(name, args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE_NAME[wl.dtype],
         "data": "synthetic (seeded N(0,1) values, random block placement)",
-        "config": {"workload": name, "num_seqs": wl.num_seqs, "heads": f"{wl.num_q_heads}/"
+        "config": {"workload": tag, "kv_cache": "e4m3" if dev.get("kv_fp8") else
+                   DTYPE_NAME[wl.dtype], "num_seqs": wl.num_seqs, "heads": f"{wl.num_q_heads}/"
                    f"{wl.num_kv_heads}", "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "context_lens": "U[512,2048], every token a query", "total_q": wl.total_q,
                    "seed": wl.seed},
@@ -471,7 +483,7 @@ def bench_prefill(name, args):
         "hbm_gbs_at_min_bytes": round(nbytes / (ker / 1e3) / 1e9, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic(name), "kernel": "prefill_mfma_kernel"},
+                     "traffic": recorded_traffic(tag), "kernel": "prefill_mfma_kernel"},
     }
 
 

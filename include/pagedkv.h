@@ -17,7 +17,8 @@
  *   pkv_reshape_and_cache_fp8,  the same write and attention over an 8-bit
  *   pkv_paged_attention_decode_fp8  (E4M3) cache;
  *   pkv_paged_attention_prefill causal attention of many query tokens per
- *                               sequence over the same paged cache.
+ *                               sequence over the same paged cache (and
+ *                               _prefill_fp8 over the 8-bit cache).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -426,6 +427,22 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
                                 int num_blocks, int max_blocks_per_seq, int max_context_len,
                                 pkv_dtype dtype, void* begin_event, void* end_event,
                                 void* stream);
+
+/* paged_attention_prefill_fp8: pkv_paged_attention_prefill over E4M3 caches
+ * (uint8 codes in the cache layout, written by pkv_reshape_and_cache_fp8):
+ * keys and values are value(code) * k_scale and value(code) * v_scale, the
+ * scales applied outside the products as in pkv_paged_attention_decode_fp8.
+ * Scales must be finite and nonzero (else PKV_EINVAL); everything else as
+ * pkv_paged_attention_prefill. */
+int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_start,
+                                    float scale, float k_scale, float v_scale, int num_seqs,
+                                    int total_q, int max_q_len, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    pkv_dtype dtype, void* begin_event, void* end_event,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -95,6 +95,10 @@ def _load():
     lib.pkv_paged_attention_prefill.argtypes = [
         vp, vp, vp, vp, i32p, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
         i32, vp, vp, vp]
+    lib.pkv_paged_attention_prefill_fp8.restype = i32
+    lib.pkv_paged_attention_prefill_fp8.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, i32p, f32, f32, f32, i32, i32, i32, i32, i32, i32, i32, i32,
+        i32, i32, i32, vp, vp, vp]
     return lib
 
 
@@ -107,7 +111,7 @@ EXPORTED = (
     "pkv_paged_attention_decode_ex", "pkv_paged_attention_decode_timed",
     "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
     "pkv_reshape_and_cache_fp8", "pkv_paged_attention_decode_fp8",
-    "pkv_paged_attention_prefill",
+    "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_fp8",
 )
 
 
@@ -384,21 +388,29 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, context_l
 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
-                            scale, max_q_len, max_context_len, stream=None, kernel_events=None):
+                            scale, max_q_len, max_context_len, stream=None, kernel_events=None,
+                            k_scale=None, v_scale=None):
     """Causal attention of the last ``n_s`` positions of every sequence over
     its paged KV (``pkv_paged_attention_prefill``).  ``q`` / ``out`` are
     ``[total_q, Hq, hd]``; sequence s owns rows ``query_start[s] ..
     query_start[s+1]`` (int32 [B+1] on the device); ``max_q_len`` is a
-    host-side bound of the ``n_s``."""
+    host-side bound of the ``n_s``.  With uint8 caches of E4M3 codes, pass
+    ``k_scale`` and ``v_scale`` (``pkv_paged_attention_prefill_fp8``)."""
     for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (block_tables, "block_tables"), (context_lens, "context_lens"),
                  (query_start, "query_start")):
         _dev(t, n)
     if q.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("prefill runs on float16 or bfloat16")
-    for t, n in ((out, "out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        if t.dtype != q.dtype:
-            raise ValueError(f"{n} dtype {t.dtype} != q dtype {q.dtype}")
+    fp8 = k_scale is not None or v_scale is not None
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("8-bit caches need both k_scale and v_scale")
+    cache_dtype = torch.uint8 if fp8 else q.dtype
+    if out.dtype != q.dtype:
+        raise ValueError(f"out dtype {out.dtype} != q dtype {q.dtype}")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != cache_dtype:
+            raise ValueError(f"{n} dtype {t.dtype}, expected {cache_dtype}")
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must both be [total_q, num_q_heads, head_dim]")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -418,11 +430,16 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     with torch.cuda.device(q.device):
         ev0, ev1 = (kernel_events[0].handle, kernel_events[1].handle) if kernel_events \
             else (None, None)
-        st = lib.pkv_paged_attention_prefill(
-            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-            _ptr(context_lens), _ptr(query_start), ctypes.c_float(scale), num_seqs, total_q,
-            int(max_q_len), hq, hkv, hd, bs, nb, block_tables.shape[1], int(max_context_len),
-            _DTYPE_CODE[q.dtype], ev0, ev1, _stream(q, stream))
+        common = (int(max_q_len), hq, hkv, hd, bs, nb, block_tables.shape[1],
+                  int(max_context_len), _DTYPE_CODE[q.dtype], ev0, ev1, _stream(q, stream))
+        head = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                _ptr(context_lens), _ptr(query_start), ctypes.c_float(scale))
+        if fp8:
+            st = lib.pkv_paged_attention_prefill_fp8(*head, ctypes.c_float(k_scale),
+                                                     ctypes.c_float(v_scale), num_seqs, total_q,
+                                                     *common)
+        else:
+            st = lib.pkv_paged_attention_prefill(*head, num_seqs, total_q, *common)
     _check("paged_attention_prefill", st)
     return out
 

@@ -446,14 +446,20 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   return err == hipSuccess ? PKV_OK : fail_hip(err);
 }
 
-int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
-                                const void* v_cache, const int32_t* block_tables,
-                                const int32_t* context_lens, const int32_t* query_start,
-                                float scale, int num_seqs, int total_q, int max_q_len,
-                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                                int num_blocks, int max_blocks_per_seq, int max_context_len,
-                                pkv_dtype dtype, void* begin_event, void* end_event,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both prefill entry points: kv_fp8 says the caches hold E4M3 codes with the
+// given scales (ignored otherwise).
+int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens,
+                 const int32_t* query_start, float scale, bool kv_fp8, float k_scale,
+                 float v_scale, int num_seqs, int total_q, int max_q_len, int num_q_heads,
+                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                 int max_blocks_per_seq, int max_context_len, int dtype, void* begin_event,
+                 void* end_event, void* stream) {
+  if (kv_fp8 && (!finite_nonzero(k_scale) || !finite_nonzero(v_scale))) return PKV_EINVAL;
   if (!dtype_ok(dtype) || num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
@@ -477,7 +483,8 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start = query_start;
-  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2e = (float)((double)scale * (kv_fp8 ? (double)k_scale : 1.0) * 1.4426950408889634);
+  a.v_scale = kv_fp8 ? v_scale : 1.f;
   a.num_seqs = num_seqs;
   a.total_q = total_q;
   a.num_q_heads = num_q_heads;
@@ -491,11 +498,44 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
   hipError_t err;
   if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
     return fail_hip(err);
-  err = launch_prefill(to_elem(dtype), head_dim, block_size, a, st);
+  err = launch_prefill(to_elem(dtype), kv_fp8, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
   if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
     return fail_hip(err);
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                float scale, int num_seqs, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                pkv_dtype dtype, void* begin_event, void* end_event,
+                                void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      false, 1.f, 1.f, num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                      dtype, begin_event, end_event, stream);
+}
+
+int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_start,
+                                    float scale, float k_scale, float v_scale, int num_seqs,
+                                    int total_q, int max_q_len, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    pkv_dtype dtype, void* begin_event, void* end_event,
+                                    void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      true, k_scale, v_scale, num_seqs, total_q, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                      max_context_len, dtype, begin_event, end_event, stream);
 }
 
 int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,

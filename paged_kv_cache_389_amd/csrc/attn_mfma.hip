@@ -66,18 +66,6 @@ struct MfmaState {
   int bad;
 };
 
-// Head dim of element i < 8 of k-step kk in lane group g4, for the A
-// operand (K) and the B operand (Q^T) alike.  16-bit caches: dims 32*kk +
-// 8*g4 + i.  8-bit caches: a lane reads 16 contiguous codes at 64*(kk/2) +
-// 16*g4 and feeds the first 8 to k-step 2*(kk/2), the next 8 to the step
-// after.  Both orders cover every dim once, and a dot product does not
-// depend on the order of its terms.
-template <typename C>
-__device__ constexpr int mfma_dim0(int kk, int g4) {
-  return sizeof(typename C::storage) == 1 ? 64 * (kk / 2) + 16 * g4 + 8 * (kk % 2)
-                                          : 32 * kk + 8 * g4;
-}
-
 // Write Q^T of the G query heads of KV head g of sequence s into q (B
 // layout: lane (n, g4) holds head n, the dims mfma_dim0 gives; zero past G).
 template <typename E, typename C, int HD>

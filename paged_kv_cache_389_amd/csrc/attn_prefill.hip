@@ -46,14 +46,22 @@ struct PrefillShared {
   u32x4 q[4][CG][HD / 32][kWave];   // per wave and column group: Q^T in the B layout
 };
 
-template <typename E, int HD, int BS, int CG>
+// C is the cache element: E itself, or E4M3 codes, loaded at half the width
+// (16 codes of a K row per load, feeding two k-steps; V rows at half width)
+// and widened to E right before the products, as in the decode MFMA kernel;
+// the K scale is folded into scale_log2e and the V scale multiplies the output.
+template <typename E, typename C, int HD, int BS, int CG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     PrefillArgs a) {
-  using T = typename E::storage;
+  using TQ = typename E::storage;   // query and output
+  using T = typename C::storage;    // cache element
   using Ops = MfmaOps<E>;
+  constexpr bool k8 = sizeof(T) == 1;
   constexpr int KSTEPS = HD / 32;
   constexpr int DPL = HD / 16;
   constexpr int VW = DPL / 2;
+  constexpr int KL = k8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per tile
+  constexpr int VL = k8 ? VW / 2 : VW;           // dwords of V loaded per lane and token
   constexpr int TPB = BS / 16;
   constexpr int NS = kPrefillStages;
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
@@ -101,17 +109,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // Q^T of the wave's columns into its LDS slots (B layout)
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
-    const T* qrow = static_cast<const T*>(a.q) +
-                    ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
+    const TQ* qrow = static_cast<const TQ*>(a.q) +
+                     ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
-      sm.q[wave][c][kk][lane] = valid[c] ? ld16(qrow + kk * 32 + g4 * 8) : u32x4{0, 0, 0, 0};
+      sm.q[wave][c][kk][lane] =
+          valid[c] ? ld16(qrow + mfma_dim0<C>(kk, g4)) : u32x4{0, 0, 0, 0};
   }
 
   const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
-  const uint32_t koff = (uint32_t)((n * HD + g4 * 8) * sizeof(T));
+  const uint32_t koff = (uint32_t)((n * HD + mfma_dim0<C>(0, g4)) * sizeof(T));
   const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
   const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int mine = min(kWave, ntiles - pass);
     const int tbl = table[min((pass + lane) / TPB, a.max_blocks - 1)];
 
-    auto load_tile = [&](int t, u32x4* ka, uint32_t (*vv)[VW]) {
+    auto load_tile = [&](int t, u32x4* ka, uint32_t (*vv)[VL]) {
       const bool live = t < mine;
       const int u = pass + t;
       int phys = lane_value(tbl, t < kWave ? t : kWave - 1);
@@ -142,10 +151,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
       const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
+      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (VW == 2) {
+        if constexpr (VL == 1) {
+          vv[r][0] = bld4(vt, voff, r * HD * sizeof(T));
+        } else if constexpr (VL == 2) {
           const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
@@ -159,8 +170,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     };
 
-    auto compute_tile = [&](int t, const u32x4* ka, uint32_t (*vv)[VW]) {
+    auto compute_tile = [&](int t, const u32x4* kl, uint32_t (*vl)[VL]) {
       const int u = pass + t;
+      // the tile's operands in E's 16-bit values (8-bit codes widened here,
+      // after their loads have landed)
+      u32x4 ka[KSTEPS];
+      uint32_t vv[4][VW];
+      if constexpr (k8) {
+#pragma unroll
+        for (int kk = 0; kk < KL; ++kk) {
+          ka[2 * kk] = u32x4{codes_to_pair<E, false>(kl[kk][0]), codes_to_pair<E, true>(kl[kk][0]),
+                             codes_to_pair<E, false>(kl[kk][1]), codes_to_pair<E, true>(kl[kk][1])};
+          ka[2 * kk + 1] =
+              u32x4{codes_to_pair<E, false>(kl[kk][2]), codes_to_pair<E, true>(kl[kk][2]),
+                    codes_to_pair<E, false>(kl[kk][3]), codes_to_pair<E, true>(kl[kk][3])};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int w = 0; w < VL; ++w) {
+            vv[r][2 * w] = codes_to_pair<E, false>(vl[r][w]);
+            vv[r][2 * w + 1] = codes_to_pair<E, true>(vl[r][w]);
+          }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = kl[kk];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int w = 0; w < VW; ++w) vv[r][w] = vl[r][w];
+      }
       const bool edge = u * 16 + 16 > lim_min;   // some column's bound or the context ends here
       const int t0 = u * 16 + 4 * g4;
       if (edge) {
@@ -231,8 +270,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     };
 
-    u32x4 kb[NS][KSTEPS];
-    uint32_t vb[NS][4][VW];
+    u32x4 kb[NS][KL];
+    uint32_t vb[NS][4][VL];
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
     for (int i0 = 0; i0 < mine; i0 += NS) {
@@ -250,8 +289,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // the four token groups of a column hold partial sums of l
     const float lsum = rows_sum(l[c]);
     if (!valid[c]) continue;
-    T* orow = static_cast<T*>(a.out) + ((size_t)(q0 + i[c]) * a.num_q_heads + h) * HD;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;   // no visible token: zero row
+    TQ* orow = static_cast<TQ*>(a.out) + ((size_t)(q0 + i[c]) * a.num_q_heads + h) * HD;
+    // no visible token: zero row; 8-bit V: code units -> values
+    const float inv = lsum > 0.f ? (k8 ? a.v_scale : 1.f) / lsum : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float o[DPL];
@@ -262,29 +302,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 }
 
-template <typename E, int HD, int BS>
+template <typename E, typename C, int HD, int BS>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<E, HD, BS, kPrefillGroups>),
+  hipLaunchKernelGGL((prefill_mfma_kernel<E, C, HD, BS, kPrefillGroups>),
                      dim3(a.num_kv_heads * a.chunks, 1, a.num_seqs), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 int prefill_tokens_per_workgroup(int group) { return 4 * kPrefillGroups * (16 / group); }
 
-template <typename E, int HD>
+template <typename E, typename C, int HD>
 static hipError_t launch_prefill_hd(int bs, const PrefillArgs& a, hipStream_t st) {
   switch (bs) {
-    case 16: return launch_prefill_t<E, HD, 16>(a, st);
-    case 32: return launch_prefill_t<E, HD, 32>(a, st);
+    case 16: return launch_prefill_t<E, C, HD, 16>(a, st);
+    case 32: return launch_prefill_t<E, C, HD, 32>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename E>
+template <typename E, typename C>
 static hipError_t launch_prefill_e(int hd, int bs, const PrefillArgs& a, hipStream_t st) {
   switch (hd) {
-    case 64: return launch_prefill_hd<E, 64>(bs, a, st);
-    case 128: return launch_prefill_hd<E, 128>(bs, a, st);
+    case 64: return launch_prefill_hd<E, C, 64>(bs, a, st);
+    case 128: return launch_prefill_hd<E, C, 128>(bs, a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -294,10 +334,15 @@ bool prefill_supported(Elem e, int hd, int bs, int group) {
          (bs == 16 || bs == 32) && group >= 1 && group <= 16 && 16 % group == 0;
 }
 
-hipError_t launch_prefill(Elem e, int hd, int bs, const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_prefill(Elem e, bool kv_fp8, int hd, int bs, const PrefillArgs& a,
+                          hipStream_t st) {
   switch (e) {
-    case Elem::F16: return launch_prefill_e<F16>(hd, bs, a, st);
-    case Elem::BF16: return launch_prefill_e<BF16>(hd, bs, a, st);
+    case Elem::F16:
+      return kv_fp8 ? launch_prefill_e<F16, E4M3>(hd, bs, a, st)
+                    : launch_prefill_e<F16, F16>(hd, bs, a, st);
+    case Elem::BF16:
+      return kv_fp8 ? launch_prefill_e<BF16, E4M3>(hd, bs, a, st)
+                    : launch_prefill_e<BF16, BF16>(hd, bs, a, st);
     default: break;
   }
   return hipErrorInvalidValue;

@@ -65,7 +65,8 @@ struct PrefillArgs {
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* context_lens;  // [B]
   const int32_t* query_start;   // [B + 1]
-  float scale_log2e;
+  float scale_log2e;            // scale * log2(e) (* K scale for 8-bit codes)
+  float v_scale;                // 8-bit caches: the V scale (1 otherwise)
   int num_seqs;
   int total_q;                  // rows of q / out (query_start is clamped to it)
   int num_q_heads;
@@ -140,7 +141,9 @@ bool prefill_supported(Elem e, int head_dim, int block_size, int group);
 // Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
 // chunks per KV head and sequence).
 int prefill_tokens_per_workgroup(int group);
-hipError_t launch_prefill(Elem e, int head_dim, int block_size, const PrefillArgs& a,
+// kv_fp8: the caches hold E4M3 codes (v_scale applies; the K scale is in
+// scale_log2e).
+hipError_t launch_prefill(Elem e, bool kv_fp8, int head_dim, int block_size, const PrefillArgs& a,
                           hipStream_t stream);
 // Decode workgroups resident per compute unit (0 if the runtime cannot say).
 int decode_valu_occupancy(Elem e, bool kv_fp8, int head_dim, int block_size);

@@ -69,4 +69,16 @@ __device__ inline uint32_t pair_of(int e, const uint32_t* x, const uint32_t* y) 
   return __builtin_amdgcn_perm(y[e >> 1], x[e >> 1], sel);
 }
 
+// Head dim of element i < 8 of k-step kk in lane group g4, for the A
+// operand (K) and the B operand (Q^T) alike.  16-bit caches: dims 32*kk +
+// 8*g4 + i.  8-bit caches: a lane reads 16 contiguous codes at 64*(kk/2) +
+// 16*g4 and feeds the first 8 to k-step 2*(kk/2), the next 8 to the step
+// after.  Both orders cover every dim once, and a dot product does not
+// depend on the order of its terms.
+template <typename C>
+__device__ constexpr int mfma_dim0(int kk, int g4) {
+  return sizeof(typename C::storage) == 1 ? 64 * (kk / 2) + 16 * g4 + 8 * (kk % 2)
+                                          : 32 * kk + 8 * g4;
+}
+
 }  // namespace pkv

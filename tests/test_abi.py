@@ -266,3 +266,12 @@ def test_prefill_rejects_bad_arguments(native):
     assert call(dtype=0) == -2               # no float32 prefill
     assert call(hd=256) == -2 and call(bs=8) == -2
     assert call(max_q=-1) == -1 and call(total_q=-1) == -1
+
+
+def test_prefill_fp8_rejects_bad_scales(native):
+    f = native.lib.pkv_paged_attention_prefill_fp8
+    head = [1, 1, 1, 1, 1, 1, 1, 0.1]
+    tail = [4, 64, 32, 8, 2, 128, 16, 64, 8, 128, 1, None, None, None]
+    assert f(*head, 0.0, 1.0, *tail) == -1
+    assert f(*head, 1.0, float("inf"), *tail) == -1
+    assert f(*head, 1.0, 1.0, *tail[:-4], 0, None, None, None) == -2   # no float32 prefill
