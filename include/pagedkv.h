@@ -45,6 +45,12 @@
  *   detected on the host before anything is enqueued.  PKV_EHIP reports a
  *   failed launch; pkv_last_error() gives the HIP error text.
  * - Calls are thread-safe for distinct streams and buffers.
+ * - Content preconditions (table entries inside the pool, lengths within the
+ *   table, distinct slots, copy destinations distinct and not sources) are
+ *   not checked on the hot path; the kernels only stay in bounds.  With
+ *   PKV_DEBUG=1 in the environment every call synchronises its stream,
+ *   checks them on the host and returns PKV_EINVAL (first offending index in
+ *   pkv_last_error()) before enqueuing anything.
  *
  * Sources: the three web pages on PagedAttention ("Memory Optimization in
  * LLM Serving with PagedAttention"; "vLLM and PagedAttention: How Ideas

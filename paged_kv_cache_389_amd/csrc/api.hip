@@ -3,7 +3,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "decode.h"
 #include "order.h"
@@ -45,6 +47,122 @@ int fail_hip(hipError_t e) {
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// ------------------------------------------------------------ debug checks
+//
+// With PKV_DEBUG=1 in the environment every call synchronises its stream,
+// copies its index arrays to the host and checks the content preconditions
+// the kernels do not check (they only stay in bounds): lengths within the
+// table, table entries inside the pool, slots in range and distinct,
+// copy destinations distinct and never a source of the same call.  A
+// violation returns PKV_EINVAL before anything is enqueued, with the first
+// offending index in pkv_last_error().
+
+bool debug_checks() {
+  const char* e = getenv("PKV_DEBUG");
+  return e && e[0] == '1';
+}
+
+int debug_fail(const std::string& what) {
+  g_last_error = "PKV_DEBUG: " + what;
+  return PKV_EINVAL;
+}
+
+// Copy n elements of a device (or pinned host) array after the stream's
+// earlier work; false (with the HIP error recorded) on failure.
+template <typename T>
+bool fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  hipError_t err = hipStreamSynchronize(st);
+  if (err == hipSuccess) err = hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDefault);
+  if (err != hipSuccess) {
+    g_last_error = hipGetErrorString(err);
+    return false;
+  }
+  return true;
+}
+
+// lengths in [0, len_cap] and the first ceil(L / bs) table entries in the pool
+int debug_check_tables(const int32_t* context_lens, const int32_t* block_tables, int num_seqs,
+                       int max_blocks, int block_size, int num_blocks, int64_t len_cap,
+                       hipStream_t st) {
+  std::vector<int32_t> lens, tables;
+  if (!fetch(lens, context_lens, num_seqs, st)) return PKV_EHIP;
+  if (block_tables && !fetch(tables, block_tables, (size_t)num_seqs * max_blocks, st))
+    return PKV_EHIP;
+  for (int s = 0; s < num_seqs; ++s) {
+    if (lens[s] < 0 || lens[s] > len_cap)
+      return debug_fail("context_lens[" + std::to_string(s) + "] = " + std::to_string(lens[s]) +
+                        " outside [0, " + std::to_string(len_cap) + "]");
+    if (!block_tables) continue;
+    const int nb = (lens[s] + block_size - 1) / block_size;
+    for (int j = 0; j < nb; ++j) {
+      const int32_t b = tables[(size_t)s * max_blocks + j];
+      if (b < 0 || b >= num_blocks)
+        return debug_fail("block_tables[" + std::to_string(s) + "][" + std::to_string(j) +
+                          "] = " + std::to_string(b) + " outside the pool");
+    }
+  }
+  return PKV_OK;
+}
+
+int debug_check_slots(const int64_t* slot_mapping, int num_tokens, int64_t num_slots,
+                      hipStream_t st) {
+  std::vector<int64_t> slots;
+  if (!fetch(slots, slot_mapping, num_tokens, st)) return PKV_EHIP;
+  std::vector<int64_t> seen;
+  for (int j = 0; j < num_tokens; ++j) {
+    if (slots[j] >= num_slots)
+      return debug_fail("slot_mapping[" + std::to_string(j) + "] = " + std::to_string(slots[j]) +
+                        " outside the pool");
+    if (slots[j] >= 0) seen.push_back(slots[j]);
+  }
+  std::sort(seen.begin(), seen.end());
+  for (size_t i = 1; i < seen.size(); ++i)
+    if (seen[i] == seen[i - 1]) return debug_fail("slot " + std::to_string(seen[i]) + " repeated");
+  return PKV_OK;
+}
+
+// same_pool: destinations must also differ from every source (copy-on-write)
+int debug_check_pairs(const int64_t* pairs, int num_pairs, int num_src, int num_dst,
+                      bool same_pool, hipStream_t st) {
+  std::vector<int64_t> p;
+  if (!fetch(p, pairs, (size_t)num_pairs * 2, st)) return PKV_EHIP;
+  std::vector<int64_t> src, dst;
+  for (int i = 0; i < num_pairs; ++i) {
+    if (p[2 * i] < 0 || p[2 * i] >= num_src || p[2 * i + 1] < 0 || p[2 * i + 1] >= num_dst)
+      return debug_fail("pair " + std::to_string(i) + " = (" + std::to_string(p[2 * i]) + ", " +
+                        std::to_string(p[2 * i + 1]) + ") outside the pools");
+    src.push_back(p[2 * i]);
+    dst.push_back(p[2 * i + 1]);
+  }
+  std::sort(dst.begin(), dst.end());
+  for (size_t i = 1; i < dst.size(); ++i)
+    if (dst[i] == dst[i - 1])
+      return debug_fail("destination block " + std::to_string(dst[i]) + " repeated");
+  if (same_pool) {
+    std::sort(src.begin(), src.end());
+    for (int64_t d : dst)
+      if (std::binary_search(src.begin(), src.end(), d))
+        return debug_fail("block " + std::to_string(d) + " is both a source and a destination");
+  }
+  return PKV_OK;
+}
+
+int debug_check_query_start(const int32_t* query_start, int num_seqs, int total_q, int max_q_len,
+                            hipStream_t st) {
+  std::vector<int32_t> qs;
+  if (!fetch(qs, query_start, (size_t)num_seqs + 1, st)) return PKV_EHIP;
+  if (qs[0] != 0 || qs[num_seqs] != total_q)
+    return debug_fail("query_start must run from 0 to total_q");
+  for (int s = 0; s < num_seqs; ++s)
+    if (qs[s + 1] < qs[s] || qs[s + 1] - qs[s] > max_q_len)
+      return debug_fail("query_start[" + std::to_string(s + 1) + "]: " +
+                        std::to_string(qs[s + 1] - qs[s]) + " queries (max_q_len " +
+                        std::to_string(max_q_len) + ")");
+  return PKV_OK;
+}
 
 // Compute units of the current device (cached per device; 256 if unknown).
 int compute_units() {
@@ -315,6 +433,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const size_t need = lo.total;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
+  if (debug_checks()) {
+    const int rc = debug_check_tables(context_lens, contiguous ? nullptr : block_tables, num_seqs,
+                                      max_blocks_per_seq, block_size, num_blocks, pl.len_cap,
+                                      static_cast<hipStream_t>(stream));
+    if (rc != PKV_OK) return rc;
+  }
   const bool use_mfma = pl.mfma;
 
   DecodeArgs a;
@@ -440,6 +564,11 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_EINVAL;
   const int row_bytes = head_dim * elem_size(dtype);
   if (row_bytes % 16) return PKV_EUNSUPPORTED;
+  if (debug_checks()) {
+    const int rc = debug_check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                     static_cast<hipStream_t>(stream));
+    if (rc != PKV_OK) return rc;
+  }
   hipError_t err = launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                             num_kv_heads, row_bytes, block_size, num_blocks,
                                             static_cast<hipStream_t>(stream));
@@ -475,6 +604,15 @@ int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_ca
   const int64_t chunks = ((int64_t)max_q_len + per_wg - 1) / per_wg;
   if (chunks * num_kv_heads > INT32_MAX) return PKV_EUNSUPPORTED;
   const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+  if (debug_checks()) {
+    hipStream_t dst = static_cast<hipStream_t>(stream);
+    int rc = debug_check_query_start(query_start, num_seqs, total_q, max_q_len, dst);
+    if (rc == PKV_OK)
+      rc = debug_check_tables(context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                              block_size, num_blocks,
+                              table_cap < max_context_len ? table_cap : max_context_len, dst);
+    if (rc != PKV_OK) return rc;
+  }
   PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -548,6 +686,11 @@ int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void*
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_EINVAL;
   if (head_dim % 16) return PKV_EUNSUPPORTED;
+  if (debug_checks()) {
+    const int rc = debug_check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                     static_cast<hipStream_t>(stream));
+    if (rc != PKV_OK) return rc;
+  }
   hipError_t err = launch_reshape_and_cache_fp8(to_elem(dtype), k, v, k_cache, v_cache,
                                                 slot_mapping, num_tokens, num_kv_heads, head_dim,
                                                 block_size, num_blocks, k_scale, v_scale,
@@ -566,6 +709,10 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, 
   const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_size(dtype);
   if (block_bytes % 16) return PKV_EUNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    const int rc = debug_check_pairs(src_dst_pairs, num_pairs, num_blocks, num_blocks, true, st);
+    if (rc != PKV_OK) return rc;
+  }
   for (int first = 0; first < num_pairs; first += kMaxGridYZ) {
     const int n = num_pairs - first < kMaxGridYZ ? num_pairs - first : kMaxGridYZ;
     hipError_t err = launch_copy_blocks(k_cache, v_cache, k_cache, v_cache,
@@ -588,6 +735,11 @@ int pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src
   const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_size(dtype);
   if (block_bytes % 16) return PKV_EUNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    const int rc = debug_check_pairs(src_dst_pairs, num_pairs, num_src_blocks, num_dst_blocks,
+                                     false, st);
+    if (rc != PKV_OK) return rc;
+  }
   for (int first = 0; first < num_pairs; first += kMaxGridYZ) {
     const int n = num_pairs - first < kMaxGridYZ ? num_pairs - first : kMaxGridYZ;
     hipError_t err = launch_copy_blocks(dst_k, dst_v, src_k, src_v,
