@@ -392,9 +392,10 @@ def _oracle_inputs(wl, seqs):
     return host(wl.q.cpu()), host(kc), host(vc), tables
 
 
-def _time_oracle(q, kc, vc, tables, lens, scale, hkv, seqs, row, budget_s):
+def _time_oracle(q, kc, vc, tables, lens, scale, hkv, seqs, row, budget_s, rows_out=None):
     """Single-threaded oracle over ``seqs`` in order until ``budget_s``;
-    returns (sequences done, KV bytes, seconds)."""
+    returns (sequences done, KV bytes, seconds).  ``rows_out`` (a dict), if
+    given, receives each sequence's oracle rows."""
     import oracle
     from threadpoolctl import threadpool_limits
     done, secs, kv = 0, 0.0, 0
@@ -402,8 +403,10 @@ def _time_oracle(q, kc, vc, tables, lens, scale, hkv, seqs, row, budget_s):
         torch.set_num_threads(1)
         for s in seqs:
             t = time.perf_counter()
-            oracle.decode(q, kc, vc, tables, lens, scale, hkv, seqs=[s])
+            o = oracle.decode(q, kc, vc, tables, lens, scale, hkv, seqs=[s])
             secs += time.perf_counter() - t
+            if rows_out is not None:
+                rows_out[s] = o[s]
             done += 1
             kv += int(lens[s]) * row
             if secs >= budget_s:
@@ -487,7 +490,7 @@ def bench_prefill(name, args):
     }
 
 
-def cpu_baseline(wl, budget_s, pool_workers=0):
+def cpu_baseline(wl, budget_s, pool_workers=0, gpu_out=None):
     """The float64 oracle over whole sequences (all heads), throughput in the
     metric's unit (algorithmic KV GB/s of the sample).  One thread, in index
     order until the time budget is used; then, with ``pool_workers`` > 1, a
@@ -498,12 +501,17 @@ def cpu_baseline(wl, budget_s, pool_workers=0):
     row = 2 * wl.num_kv_heads * wl.head_dim * wl.esize
     order = list(range(wl.num_seqs))
     q, kc, vc, tables = _oracle_inputs(wl, order)
+    rows = {}
     done, kv, secs = _time_oracle(q, kc, vc, tables, wl.context_lens, wl.scale,
-                                  wl.num_kv_heads, order, row, budget_s)
+                                  wl.num_kv_heads, order, row, budget_s, rows_out=rows)
     res = {"value": round(kv / secs / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "seconds": round(secs, 3), "queries_per_s": round(done / secs, 3),
            "sample": f"{done} of {wl.num_seqs} sequences x all {wl.num_q_heads} query heads "
                      f"(decode only, float64 numpy, one thread)"}
+    if gpu_out is not None and rows:
+        # the timed run's own output on the sampled sequences, against the oracle
+        g = gpu_out.detach().to("cpu", torch.float64).numpy()
+        res["max_abs_err_vs_gpu"] = float(max(np.abs(g[s] - r).max() for s, r in rows.items()))
     if pool_workers > 1:
         res["pool"] = _cpu_pool(wl, row, order[:min(wl.num_seqs, done * pool_workers)],
                                 pool_workers)
@@ -577,6 +585,8 @@ def bench_one(name, args, with_cpu):
                    "partition_tokens": plan["partition_tokens"], "max_parts": plan["max_parts"],
                    "longest_first": bool(plan["longest_first"])},
         "queries_per_s": round(wl.num_seqs / (ms_per_step / 1e3), 1),
+        "kv_utilisation": round(float(wl.meta["utilisation"]), 4) if "utilisation" in wl.meta
+        else None,
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 5),
         "decode_ms_min": round(float(np.min(decode_ms)), 5),
@@ -600,7 +610,7 @@ def bench_one(name, args, with_cpu):
                         "copy_pairs_per_step_mean": round(float(np.mean(pairs)), 2),
                         "block_saving_vs_unshared": round(workloads.sharing_saving(wl), 4)}
     if with_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s, args.cpu_pool)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s, args.cpu_pool, dev["out"])
     return line
 
 
