@@ -73,6 +73,9 @@ def parse():
     p.add_argument("--kv-cache", default="auto", choices=["auto", "e4m3"],
                    help="e4m3: quantise the pools to 8-bit codes and time the 8-bit path")
     p.add_argument("--placement", default="random", choices=["random", "sequential"])
+    p.add_argument("--grouped", action="store_true",
+                   help="decode with the grouped call: sequences sharing their first block "
+                        "(forks of one prompt) read each shared tile once")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--cpu-pool", type=int, default=min(16, len(os.sched_getaffinity(0))),
@@ -151,7 +154,7 @@ def counters_to_traffic(args):
             raise SystemExit(f"no {counter} rows")
         return max(rows)
     is_decode = lambda k: any(n in k for n in ("decode_mfma_kernel", "decode_valu_kernel",
-                                               "prefill_mfma_kernel"))
+                                               "prefill_mfma_kernel", "decode_grouped_kernel"))
     is_other = lambda k: "pkv::" not in k
     cal_bytes = args.cal_mib << 20
     f_fetch = pick(_counter_means(args.cal_fetch_db), "FETCH_SIZE", is_other)[0] * 1024 / cal_bytes
@@ -166,6 +169,8 @@ def counters_to_traffic(args):
         kv = (int(wl.context_lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim *
               wl.esize)
         key, alg = key + "_kv_e4m3", alg - (kv - kv // wl.esize)
+    if args.grouped:
+        key, alg = key + "_grouped", grouped_decode_bytes(wl, grouped_lists(wl, {}))
     try:
         with open(args.counters) as fh:
             rec = json.load(fh)
@@ -263,6 +268,34 @@ def quantise_pools(wl, dev):
     dev.update(kv_fp8=True, k_scale=k_scale, v_scale=v_scale)
 
 
+def grouped_lists(wl, dev):
+    """Inputs of the grouped decode call (host set-up, not timed): sequences
+    sharing their first block in groups of at most 16 / G, and the groups'
+    tile lists."""
+    from paged_kv_cache_389_amd import block_manager as bmod
+    g = wl.num_q_heads // wl.num_kv_heads
+    t0 = time.perf_counter()
+    groups = bmod.share_groups(wl.block_tables, wl.context_lens, 16 // g)
+    members, tiles, start = bmod.group_tiles(wl.block_tables, wl.context_lens, groups,
+                                             wl.block_size, 16 // g)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    if tiles.shape[0] == 0:
+        tiles = np.zeros((1, 4), np.int32)
+    if dev is not None and torch.cuda.is_available():
+        dev["groups"] = tuple(torch.from_numpy(x).cuda() for x in (members, tiles, start))
+    return {"groups": len(groups), "max_members": 16 // g, "tiles": int(start[-1]),
+            "logical_tiles": int(sum(-(-int(L) // 16) for L in wl.context_lens)),
+            "host_list_ms": round(host_ms, 2)}
+
+
+def grouped_decode_bytes(wl, info):
+    """What the grouped kernel must move: every distinct K/V tile once, q and
+    out, its lists and the lengths."""
+    return (wl.unique_kv_bytes() + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * wl.esize +
+            16 * info["tiles"] + 4 * info["groups"] * info["max_members"] +
+            4 * (info["groups"] + 1) + 4 * wl.num_seqs)
+
+
 def run_gpu(wl, dev, steps, warmup, partition, path, grid):
     from paged_kv_cache_389_amd import _native as pk
     tables = None if path == 3 else dev["tables"]
@@ -291,7 +324,12 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
                                      dev["slots"])
         if i is not None:
             ev[i][0].record()
-        if fp8:
+        if dev.get("groups") is not None:
+            pk.paged_attention_decode_grouped(dev["out"], dev["q"], dev["k"], dev["v"],
+                                              dev["lens"], *dev["groups"], wl.scale,
+                                              wl.max_context_len,
+                                              kernel_events=None if i is None else kev[i])
+        elif fp8:
             pk.paged_attention_decode_fp8(dev["out"], dev["q"], dev["k"], dev["v"], tables,
                                           dev["lens"], wl.scale, dev["k_scale"], dev["v_scale"],
                                           wl.max_context_len, workspace=ws,
@@ -554,14 +592,22 @@ def bench_one(name, args, with_cpu):
     if args.kv_cache == "e4m3":
         with_cpu = False   # the oracle baseline times the 16-bit pools
         quantise_pools(wl, dev)
+    grouped = None
+    if args.grouped:
+        if dev.get("kv_fp8"):
+            raise SystemExit("--grouped runs on 16-bit caches")
+        grouped = grouped_lists(wl, dev)
     alg_decode, alg_writes = step_bytes(wl, dev)
+    if grouped:
+        alg_decode = grouped_decode_bytes(wl, grouped)
     wall, decode_ms, kernel_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition,
                                                args.path, args.grid)
     ms_per_step = wall / args.steps * 1e3
     dec_ms = float(np.mean(decode_ms))
     ker_ms = float(np.mean(kernel_ms))
     achieved = alg_decode / (ker_ms / 1e3) / 1e9
-    kname = ("decode_mfma_kernel" if plan["path"] == 2 else "decode_valu_kernel")
+    kname = ("decode_grouped_kernel" if grouped else
+             "decode_mfma_kernel" if plan["path"] == 2 else "decode_valu_kernel")
     line = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + queries/s",
         "value": round((alg_decode + alg_writes) / (ms_per_step / 1e3) / 1e9, 2),
@@ -575,7 +621,8 @@ def bench_one(name, args, with_cpu):
         "vs_baseline": None,
         "dtype": DTYPE_NAME[wl.dtype],
         "data": "synthetic (seeded N(0,1) values, random block placement)",
-        "config": {"workload": name + ("_kv_e4m3" if dev.get("kv_fp8") else ""),
+        "config": {"workload": name + ("_kv_e4m3" if dev.get("kv_fp8") else "") +
+                               ("_grouped" if grouped else ""),
                    **WORKLOAD_DESC[name], "seed": wl.seed,
                    "kv_cache": "e4m3" if dev.get("kv_fp8") else DTYPE_NAME[wl.dtype],
                    "placement": args.placement,
@@ -598,9 +645,15 @@ def bench_one(name, args, with_cpu):
                   "kv_logical": wl.kv_bytes() // (wl.esize if dev.get("kv_fp8") else 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(name + ("_kv_e4m3" if dev.get("kv_fp8") else "")),
+                     "traffic": recorded_traffic(name + ("_kv_e4m3" if dev.get("kv_fp8") else "") +
+                                                 ("_grouped" if grouped else "")),
                      "kernel": kname},
     }
+    if grouped:
+        line["config"]["kernel"] = "grouped"
+        line["config"]["grid"] = "groups x kv heads"
+        line["grouped"] = grouped
+        line["roofline"]["basis"] = "unique K/V bytes (each distinct tile once)"
     if name in ("sharing_fp16", "beam_search_fp16"):
         line["bytes"]["kv_unique"] = wl.unique_kv_bytes() // (wl.esize if dev.get("kv_fp8") else 1)
     if name == "beam_search_fp16":

@@ -18,7 +18,10 @@
  *   pkv_paged_attention_decode_fp8  (E4M3) cache;
  *   pkv_paged_attention_prefill causal attention of many query tokens per
  *                               sequence over the same paged cache (and
- *                               _prefill_fp8 over the 8-bit cache).
+ *                               _prefill_fp8 over the 8-bit cache);
+ *   pkv_paged_attention_decode_grouped  decode of sequences that share blocks
+ *                               (forks of one prompt), each shared tile read
+ *                               once for all of them.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -449,6 +452,68 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cach
                                     int num_blocks, int max_blocks_per_seq, int max_context_len,
                                     pkv_dtype dtype, void* begin_event, void* end_event,
                                     void* stream);
+
+/*
+ * paged_attention_decode_grouped: decode attention of sequences that share
+ * KV blocks, reading each shared tile once for all of them.
+ *
+ * The output is that of pkv_paged_attention_decode for every sequence named
+ * in a group:
+ *   out[s][h][:] = softmax(scale * K_s q[s][h]) V_s   over the L = context_lens[s]
+ * tokens of s, with fp32 accumulation; only the order in which its tiles
+ * are summed differs.  Rows of sequences in no group are not written.
+ *
+ * Passage: sequences forked from one prompt (parallel sampling, beam search)
+ * map their shared prefix to the same physical blocks through their block
+ * tables, with reference counts and copy-on-write on the last partly filled
+ * block ("Memory Optimization in LLM Serving with PagedAttention", section
+ * "Advanced Capabilities: Memory Sharing with Copy-on-Write"; "vLLM and
+ * PagedAttention: How Ideas from Operating Systems Accelerated LLM
+ * Inference", paragraph on sharing).  Reading a shared block once for all
+ * its sequences is this library's addition.
+ *
+ * Instead of block tables the call takes, per group, the list of distinct
+ * 16-token tiles its members reach (built on the host from the tables, e.g.
+ * by paged_kv_cache_389_amd.block_manager.group_tiles):
+ *   group_members     int32 [num_groups][max_members]: sequence indices, -1 for
+ *                     an empty place; a sequence in at most one group
+ *   group_tile_start  int32 [num_groups + 1]: group j's entries are
+ *                     group_tiles[group_tile_start[j] .. group_tile_start[j+1]),
+ *                     group_tile_start[0] = 0, non-decreasing, at most
+ *                     num_tiles (the kernel clamps the offsets to [0, num_tiles])
+ *   group_tiles       int32 [num_tiles][4], 16-byte aligned: (physical block b,
+ *                     tile index t, member mask, unused).  Entry (b, t, mask)
+ *                     says that for every member m with bit m of mask set,
+ *                     tokens 16t .. 16t+15 of the member live in block b at
+ *                     offsets (16t mod block_size) .. +15, i.e.
+ *                     block_tables[s_m][16t / block_size] == b.  Every member
+ *                     must have exactly one entry for each of its tiles
+ *                     0 .. ceil(L/16) - 1 and none past them.
+ *   out, q            [num_seqs][num_q_heads][head_dim]
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim]
+ *   context_lens      int32 [num_seqs]; clamped to [0, max_context_len]
+ *   begin_event, end_event: optional hipEvent_t recorded around the kernel.
+ * All arrays are device memory, read only except out.
+ *
+ * dtype PKV_F16 or PKV_BF16; head_dim 64 or 128; block_size 16 or 32;
+ * max_members * (num_q_heads / num_kv_heads) <= 16; num_groups and
+ * num_kv_heads <= 65535 (else PKV_EUNSUPPORTED).  group_tiles not 16-byte
+ * aligned, a null pointer or a bad size returns PKV_EINVAL.  No workspace.
+ * A block outside [0, num_blocks) makes the rows of its group NaN; nothing
+ * is read or written out of bounds whatever the list holds.  A missing or
+ * repeated tile gives a wrong row, not a fault; PKV_DEBUG=1 checks the list
+ * (coverage, pool, membership) on the host first.  `out` must not alias an
+ * input.  num_groups or num_seqs == 0 is a no-op.
+ */
+int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* context_lens,
+                                       const int32_t* group_members, const int32_t* group_tiles,
+                                       const int32_t* group_tile_start, int num_tiles,
+                                       float scale, int num_seqs, int num_groups, int max_members,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, int max_context_len,
+                                       pkv_dtype dtype, void* begin_event, void* end_event,
+                                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,9 @@ Device calls (hand-written gfx950 HIP kernels behind the C ABI in
   same write and attention over an 8-bit (OCP E4M3) cache with per-cache
   scales;
 * :func:`paged_attention_prefill` - causal attention of many query tokens per
-  sequence over the paged cache (prefill / recomputation).
+  sequence over the paged cache (prefill / recomputation);
+* :func:`paged_attention_decode_grouped` - decode of sequences that share
+  blocks (forks of one prompt), each shared tile read once per group.
 
 Host side: :mod:`.block_manager` (block pool, tables, reference counts, fork,
 copy-on-write) and :mod:`.workloads` (seeded synthetic inputs).
@@ -25,7 +27,7 @@ CPU implementation.
 
 _NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "swap_blocks",
            "reshape_and_cache_fp8", "paged_attention_decode_fp8", "KV_E4M3",
-           "paged_attention_prefill",
+           "paged_attention_prefill", "paged_attention_decode_grouped",
            "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
            "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")

@@ -270,3 +270,60 @@ class BlockManager:
                 used = min(self.block_size, s.length - j * self.block_size)
                 filled[b] = max(filled.get(b, 0), used)
         return sum(filled.values()) / allocated
+
+
+# ------------------------------------------------------- grouped decode lists
+TILE_TOKENS = 16   # tokens per tile of the grouped decode kernel
+
+
+def share_groups(block_tables, context_lens, max_members: int) -> list[list[int]]:
+    """Sequences grouped by the physical block holding their first tokens
+    (forks of one prompt share it), in batch order, at most ``max_members``
+    per group; a sequence of length zero, or one that shares nothing, forms
+    a group of its own."""
+    by_first: dict[int, list[int]] = {}
+    singles = []
+    for s in range(len(context_lens)):
+        if int(context_lens[s]) <= 0:
+            singles.append([s])
+            continue
+        by_first.setdefault(int(block_tables[s][0]), []).append(s)
+    groups = []
+    for seqs in by_first.values():
+        groups.extend(seqs[i:i + max_members] for i in range(0, len(seqs), max_members))
+    return groups + singles
+
+
+def group_tiles(block_tables, context_lens, groups, block_size: int, max_members: int):
+    """Inputs of the grouped decode call for ``groups`` (lists of sequence
+    indices, each at most ``max_members`` long and no sequence twice).
+
+    Returns ``(members, tiles, tile_start)``: int32 ``[G, max_members]``
+    (-1 pads), int32 ``[T, 4]`` rows ``(block, tile, mask, 0)`` and int32
+    ``[G + 1]``.  Group j's rows ``tile_start[j] .. tile_start[j+1]`` name
+    every distinct (physical block, 16-token tile index) its members reach,
+    with bit m of the mask set for each member m whose table maps that tile
+    to that block; a tile shared by several members appears once."""
+    if block_size % TILE_TOKENS:
+        raise ValueError("block_size must be a multiple of 16")
+    tpb = block_size // TILE_TOKENS
+    members = np.full((len(groups), max_members), -1, dtype=np.int32)
+    rows: list[tuple[int, int, int, int]] = []
+    start = [0]
+    seen = set()
+    for j, grp in enumerate(groups):
+        if len(grp) > max_members:
+            raise ValueError(f"group {j} has {len(grp)} members, more than {max_members}")
+        entries: dict[tuple[int, int], int] = {}
+        for m, s in enumerate(grp):
+            if s in seen:
+                raise ValueError(f"sequence {s} is in two groups")
+            seen.add(s)
+            members[j, m] = s
+            for t in range(-(-int(context_lens[s]) // TILE_TOKENS)):
+                key = (int(block_tables[s][t // tpb]), t)
+                entries[key] = entries.get(key, 0) | (1 << m)
+        rows.extend((b, t, mask, 0) for (b, t), mask in entries.items())
+        start.append(len(rows))
+    tiles = np.array(rows, dtype=np.int32).reshape(-1, 4)
+    return members, tiles, np.array(start, dtype=np.int32)

@@ -150,6 +150,61 @@ int debug_check_pairs(const int64_t* pairs, int num_pairs, int num_src, int num_
   return PKV_OK;
 }
 
+// Grouped decode: members in [0, num_seqs) and in at most one group; tile
+// list offsets non-decreasing from 0; every entry's block in the pool; and
+// for every member exactly one entry with its bit for each of its tiles
+// 0 .. ceil(L / 16) - 1 and none past them.
+int debug_check_groups(const int32_t* context_lens, const int32_t* members, const int32_t* tiles,
+                       const int32_t* tile_start, int num_tiles, int num_seqs, int num_groups,
+                       int max_members, int num_blocks, int64_t len_cap, hipStream_t st) {
+  std::vector<int32_t> lens, mem, start, ent;
+  if (!fetch(lens, context_lens, num_seqs, st) ||
+      !fetch(mem, members, (size_t)num_groups * max_members, st) ||
+      !fetch(start, tile_start, (size_t)num_groups + 1, st))
+    return PKV_EHIP;
+  if (start[0] != 0) return debug_fail("group_tile_start[0] != 0");
+  for (int j = 0; j < num_groups; ++j)
+    if (start[j + 1] < start[j])
+      return debug_fail("group_tile_start decreases at " + std::to_string(j));
+  if (start[num_groups] > num_tiles)
+    return debug_fail("group_tile_start[num_groups] = " + std::to_string(start[num_groups]) +
+                      " past the " + std::to_string(num_tiles) + " rows of group_tiles");
+  if (!fetch(ent, tiles, (size_t)start[num_groups] * 4, st)) return PKV_EHIP;
+  std::vector<char> seen(num_seqs, 0);
+  for (int j = 0; j < num_groups; ++j) {
+    std::vector<std::vector<int>> count(max_members);
+    for (int m = 0; m < max_members; ++m) {
+      const int s = mem[(size_t)j * max_members + m];
+      if (s < 0) continue;
+      if (s >= num_seqs || seen[s])
+        return debug_fail("group_members[" + std::to_string(j) + "][" + std::to_string(m) +
+                          "] = " + std::to_string(s) + " outside the batch or in two groups");
+      seen[s] = 1;
+      if (lens[s] < 0 || lens[s] > len_cap)
+        return debug_fail("context_lens[" + std::to_string(s) + "] outside [0, len_cap]");
+      count[m].assign((lens[s] + 15) / 16, 0);
+    }
+    for (int i = start[j]; i < start[j + 1]; ++i) {
+      const int32_t b = ent[4 * (size_t)i], t = ent[4 * (size_t)i + 1], mask = ent[4 * (size_t)i + 2];
+      if (b < 0 || b >= num_blocks)
+        return debug_fail("group_tiles[" + std::to_string(i) + "] block outside the pool");
+      for (int m = 0; m < max_members; ++m) {
+        if (!((mask >> m) & 1)) continue;
+        if (mem[(size_t)j * max_members + m] < 0 || t < 0 || t >= (int)count[m].size() ||
+            count[m][t]++)
+          return debug_fail("group_tiles[" + std::to_string(i) + "]: tile " + std::to_string(t) +
+                            " of member " + std::to_string(m) + " absent, past its length or twice");
+      }
+    }
+    for (int m = 0; m < max_members; ++m)
+      for (size_t t = 0; t < count[m].size(); ++t)
+        if (!count[m][t])
+          return debug_fail("group " + std::to_string(j) + " member " + std::to_string(m) +
+                            " has no entry for tile " + std::to_string(t));
+  }
+  return PKV_OK;
+}
+
 int debug_check_query_start(const int32_t* query_start, int num_seqs, int total_q, int max_q_len,
                             hipStream_t st) {
   std::vector<int32_t> qs;
@@ -674,6 +729,65 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cach
                       true, k_scale, v_scale, num_seqs, total_q, max_q_len, num_q_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                       max_context_len, dtype, begin_event, end_event, stream);
+}
+
+int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* context_lens,
+                                       const int32_t* group_members, const int32_t* group_tiles,
+                                       const int32_t* group_tile_start, int num_tiles,
+                                       float scale, int num_seqs, int num_groups, int max_members,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, int max_context_len,
+                                       pkv_dtype dtype, void* begin_event, void* end_event,
+                                       void* stream) {
+  if (!dtype_ok(dtype) || num_seqs < 0 || num_groups < 0 || max_members <= 0 || num_tiles < 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
+    return PKV_EINVAL;
+  if (num_groups == 0 || num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || !group_members || !group_tiles ||
+      !group_tile_start)
+    return PKV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(group_tiles) % 16) return PKV_EINVAL;
+  const Elem e = to_elem(dtype);
+  const int group = num_q_heads / num_kv_heads;
+  if (!grouped_supported(e, head_dim, block_size) || max_members * group > 16 ||
+      num_groups > kMaxGridYZ || num_kv_heads > kMaxGridYZ)
+    return PKV_EUNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    const int rc = debug_check_groups(context_lens, group_members, group_tiles, group_tile_start,
+                                      num_tiles, num_seqs, num_groups, max_members, num_blocks,
+                                      max_context_len, st);
+    if (rc != PKV_OK) return rc;
+  }
+  GroupedArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.context_lens = context_lens;
+  a.members = group_members;
+  a.tiles = group_tiles;
+  a.tile_start = group_tile_start;
+  a.num_tiles = num_tiles;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.num_seqs = num_seqs;
+  a.num_groups = num_groups;
+  a.max_members = max_members;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.len_cap = max_context_len;
+  hipError_t err;
+  if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
+    return fail_hip(err);
+  err = launch_decode_grouped(e, head_dim, block_size, a, st);
+  if (err != hipSuccess) return fail_hip(err);
+  if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
+    return fail_hip(err);
+  return PKV_OK;
 }
 
 int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,

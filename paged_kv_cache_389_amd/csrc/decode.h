@@ -53,6 +53,32 @@ struct DecodeArgs {
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
 
+// Arguments of the grouped decode kernel (attn_grouped.hip).  Grid
+// (num_kv_heads, num_groups).  Group j lists its member sequences in
+// members[j][0 .. max_members) (-1: none) and its tiles in
+// tiles[tile_start[j] .. tile_start[j+1]): (physical block, 16-token tile
+// index within the sequences, member bit mask, unused).
+struct GroupedArgs {
+  void* out;                    // [B][Hq][HD]
+  const void* q;                // [B][Hq][HD]
+  const void* k_cache;          // [NB][Hkv][BS][HD]
+  const void* v_cache;
+  const int32_t* context_lens;  // [B]
+  const int32_t* members;       // [num_groups][max_members]
+  const int32_t* tiles;         // [total][4], 16-byte aligned
+  const int32_t* tile_start;    // [num_groups + 1]; clamped to [0, num_tiles]
+  int num_tiles;                // rows of tiles
+  float scale_log2e;
+  int num_seqs;
+  int num_groups;
+  int max_members;              // max_members * group <= 16
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                    // Hq / Hkv
+  int num_blocks;
+  int len_cap;                  // lengths are clamped to this
+};
+
 // Arguments of the prefill kernel (attn_prefill.hip): causal attention of
 // the last n = query_start[s+1] - query_start[s] positions of each sequence.
 // Grid (num_kv_heads * chunks, 1, num_seqs); a workgroup's 4 waves take
@@ -138,6 +164,9 @@ bool decode_valu_supported(Elem e, bool kv_fp8, int head_dim, int block_size);
 int valu_unit_tokens(Elem e, bool kv_fp8, int head_dim, int block_size);
 bool decode_mfma_supported(Elem e, int head_dim, int block_size);
 bool prefill_supported(Elem e, int head_dim, int block_size, int group);
+bool grouped_supported(Elem e, int head_dim, int block_size);
+hipError_t launch_decode_grouped(Elem e, int head_dim, int block_size, const GroupedArgs& a,
+                                 hipStream_t stream);
 // Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
 // chunks per KV head and sequence).
 int prefill_tokens_per_workgroup(int group);
