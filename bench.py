@@ -76,6 +76,8 @@ def parse():
     p.add_argument("--grouped", action="store_true",
                    help="decode with the grouped call: sequences sharing their first block "
                         "(forks of one prompt) read each shared tile once")
+    p.add_argument("--group-part", type=int, default=-1, metavar="TILES",
+                   help="with --grouped: tiles per part (0 = whole groups, -1 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--cpu-pool", type=int, default=min(16, len(os.sched_getaffinity(0))),
@@ -268,10 +270,10 @@ def quantise_pools(wl, dev):
     dev.update(kv_fp8=True, k_scale=k_scale, v_scale=v_scale)
 
 
-def grouped_lists(wl, dev):
+def grouped_lists(wl, dev, part_tiles=-1):
     """Inputs of the grouped decode call (host set-up, not timed): sequences
-    sharing their first block in groups of at most 16 / G, and the groups'
-    tile lists."""
+    sharing their first block in groups of at most 16 / G, the groups' tile
+    lists, and the part size (-1: chosen from the list)."""
     from paged_kv_cache_389_amd import block_manager as bmod
     g = wl.num_q_heads // wl.num_kv_heads
     t0 = time.perf_counter()
@@ -281,9 +283,22 @@ def grouped_lists(wl, dev):
     host_ms = (time.perf_counter() - t0) * 1e3
     if tiles.shape[0] == 0:
         tiles = np.zeros((1, 4), np.int32)
+    max_group_tiles = int(np.diff(start).max(initial=0))
+    if part_tiles < 0:
+        # whole groups (no merge) unless groups x KV heads leave CUs idle; then
+        # parts for about one round of resident workgroups (4 per CU).  Measured on
+        # the beam batch (512 workgroups): parts of 8-48 tiles were 3-4% slower.
+        wgs = len(groups) * wl.num_kv_heads
+        part_tiles = 0 if wgs >= 256 else max(8, -(-int(start[-1]) * wl.num_kv_heads // 1024))
     if dev is not None and torch.cuda.is_available():
+        from paged_kv_cache_389_amd import _native as pk
         dev["groups"] = tuple(torch.from_numpy(x).cuda() for x in (members, tiles, start))
+        dev["group_part"] = (part_tiles, max_group_tiles)
+        need = pk.grouped_workspace_bytes(len(groups), wl.num_kv_heads, wl.head_dim, part_tiles,
+                                          max_group_tiles)
+        dev["group_ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     return {"groups": len(groups), "max_members": 16 // g, "tiles": int(start[-1]),
+            "part_tiles": part_tiles, "max_group_tiles": max_group_tiles,
             "logical_tiles": int(sum(-(-int(L) // 16) for L in wl.context_lens)),
             "host_list_ms": round(host_ms, 2)}
 
@@ -328,6 +343,9 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
             pk.paged_attention_decode_grouped(dev["out"], dev["q"], dev["k"], dev["v"],
                                               dev["lens"], *dev["groups"], wl.scale,
                                               wl.max_context_len,
+                                              part_tiles=dev["group_part"][0],
+                                              max_group_tiles=dev["group_part"][1],
+                                              workspace=dev["group_ws"],
                                               kernel_events=None if i is None else kev[i])
         elif fp8:
             pk.paged_attention_decode_fp8(dev["out"], dev["q"], dev["k"], dev["v"], tables,
@@ -596,7 +614,7 @@ def bench_one(name, args, with_cpu):
     if args.grouped:
         if dev.get("kv_fp8"):
             raise SystemExit("--grouped runs on 16-bit caches")
-        grouped = grouped_lists(wl, dev)
+        grouped = grouped_lists(wl, dev, args.group_part)
     alg_decode, alg_writes = step_bytes(wl, dev)
     if grouped:
         alg_decode = grouped_decode_bytes(wl, grouped)

@@ -492,13 +492,25 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cach
  *   out, q            [num_seqs][num_q_heads][head_dim]
  *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim]
  *   context_lens      int32 [num_seqs]; clamped to [0, max_context_len]
- *   begin_event, end_event: optional hipEvent_t recorded around the kernel.
+ *   part_tiles        0: one workgroup per (group, KV head) walks the whole
+ *                     list; > 0: the list is cut into parts of part_tiles rows,
+ *                     one workgroup each, whose (max, sum, output) states a
+ *                     second kernel merges (more workgroups for few groups)
+ *   max_group_tiles   host-side bound of every group's row count (sizes the
+ *                     grid; rows of a group past it are not read)
+ *   workspace         device memory of at least
+ *                     pkv_paged_attention_grouped_workspace_bytes(...) bytes,
+ *                     16-byte aligned, caller-owned, contents need no
+ *                     initialisation (null when that size is 0)
+ *   begin_event, end_event: optional hipEvent_t recorded around the first
+ *                     kernel (the merge, when there is one, runs after it).
  * All arrays are device memory, read only except out.
  *
  * dtype PKV_F16 or PKV_BF16; head_dim 64 or 128; block_size 16 or 32;
  * max_members * (num_q_heads / num_kv_heads) <= 16; num_groups and
- * num_kv_heads <= 65535 (else PKV_EUNSUPPORTED).  group_tiles not 16-byte
- * aligned, a null pointer or a bad size returns PKV_EINVAL.  No workspace.
+ * num_kv_heads <= 65535, at most 65535 parts per group (else
+ * PKV_EUNSUPPORTED).  group_tiles not 16-byte aligned, a null pointer or a
+ * bad size returns PKV_EINVAL; a missing or short workspace PKV_EWORKSPACE.
  * A block outside [0, num_blocks) makes the rows of its group NaN; nothing
  * is read or written out of bounds whatever the list holds.  A missing or
  * repeated tile gives a wrong row, not a fault; PKV_DEBUG=1 checks the list
@@ -512,8 +524,16 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
                                        float scale, int num_seqs, int num_groups, int max_members,
                                        int num_q_heads, int num_kv_heads, int head_dim,
                                        int block_size, int num_blocks, int max_context_len,
-                                       pkv_dtype dtype, void* begin_event, void* end_event,
-                                       void* stream);
+                                       pkv_dtype dtype, int part_tiles, int max_group_tiles,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* begin_event, void* end_event, void* stream);
+
+/* Bytes of workspace pkv_paged_attention_decode_grouped needs for these
+ * arguments (0 when every group is one part); (size_t)-1 for a negative
+ * argument. */
+size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_heads,
+                                                   int head_dim, int part_tiles,
+                                                   int max_group_tiles);
 
 #ifdef __cplusplus
 }

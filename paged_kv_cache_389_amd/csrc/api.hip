@@ -156,16 +156,20 @@ int debug_check_pairs(const int64_t* pairs, int num_pairs, int num_src, int num_
 // 0 .. ceil(L / 16) - 1 and none past them.
 int debug_check_groups(const int32_t* context_lens, const int32_t* members, const int32_t* tiles,
                        const int32_t* tile_start, int num_tiles, int num_seqs, int num_groups,
-                       int max_members, int num_blocks, int64_t len_cap, hipStream_t st) {
+                       int max_members, int num_blocks, int64_t len_cap, int max_group_tiles,
+                       hipStream_t st) {
   std::vector<int32_t> lens, mem, start, ent;
   if (!fetch(lens, context_lens, num_seqs, st) ||
       !fetch(mem, members, (size_t)num_groups * max_members, st) ||
       !fetch(start, tile_start, (size_t)num_groups + 1, st))
     return PKV_EHIP;
   if (start[0] != 0) return debug_fail("group_tile_start[0] != 0");
-  for (int j = 0; j < num_groups; ++j)
+  for (int j = 0; j < num_groups; ++j) {
     if (start[j + 1] < start[j])
       return debug_fail("group_tile_start decreases at " + std::to_string(j));
+    if (max_group_tiles >= 0 && start[j + 1] - start[j] > max_group_tiles)
+      return debug_fail("group " + std::to_string(j) + " lists more than max_group_tiles rows");
+  }
   if (start[num_groups] > num_tiles)
     return debug_fail("group_tile_start[num_groups] = " + std::to_string(start[num_groups]) +
                       " past the " + std::to_string(num_tiles) + " rows of group_tiles");
@@ -378,6 +382,26 @@ Layout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int hea
   lo.items = lo.scratch + align16((size_t)2 * num_seqs * sizeof(int32_t));
   lo.count = lo.items + (size_t)num_seqs * pl.max_parts * 4 * sizeof(int32_t);
   lo.total = lo.count + 16;
+  return lo;
+}
+
+// Grouped decode with parts: the part states [num_groups][max_parts][Hkv][16]
+// of HD floats (outputs) and 2 floats (max, sum), each part 16-byte aligned;
+// nothing when every group is one part.
+struct GroupedLayout {
+  int max_parts = 1;
+  size_t part_o = 0, part_ml = 0, total = 0;
+};
+
+GroupedLayout grouped_layout(int num_groups, int num_kv_heads, int head_dim, int part_tiles,
+                             int max_group_tiles) {
+  GroupedLayout lo;
+  if (part_tiles > 0 && max_group_tiles > part_tiles)
+    lo.max_parts = (int)(((int64_t)max_group_tiles + part_tiles - 1) / part_tiles);
+  if (lo.max_parts <= 1) return lo;
+  const size_t states = (size_t)num_groups * lo.max_parts * num_kv_heads * 16;
+  lo.part_ml = align16(states * head_dim * sizeof(float));
+  lo.total = lo.part_ml + align16(states * 2 * sizeof(float));
   return lo;
 }
 
@@ -731,6 +755,17 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cach
                       max_context_len, dtype, begin_event, end_event, stream);
 }
 
+size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_heads,
+                                                   int head_dim, int part_tiles,
+                                                   int max_group_tiles) {
+  if (num_groups < 0 || num_kv_heads <= 0 || head_dim <= 0 || part_tiles < 0 ||
+      max_group_tiles < 0)
+    return (size_t)-1;
+  const GroupedLayout lo = grouped_layout(num_groups, num_kv_heads, head_dim, part_tiles,
+                                          max_group_tiles);
+  return lo.total;
+}
+
 int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* context_lens,
                                        const int32_t* group_members, const int32_t* group_tiles,
@@ -738,11 +773,13 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
                                        float scale, int num_seqs, int num_groups, int max_members,
                                        int num_q_heads, int num_kv_heads, int head_dim,
                                        int block_size, int num_blocks, int max_context_len,
-                                       pkv_dtype dtype, void* begin_event, void* end_event,
-                                       void* stream) {
+                                       pkv_dtype dtype, int part_tiles, int max_group_tiles,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* begin_event, void* end_event, void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_groups < 0 || max_members <= 0 || num_tiles < 0 ||
       num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      num_blocks <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
+      num_blocks <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads || part_tiles < 0 ||
+      max_group_tiles < 0)
     return PKV_EINVAL;
   if (num_groups == 0 || num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || !group_members || !group_tiles ||
@@ -754,11 +791,17 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
   if (!grouped_supported(e, head_dim, block_size) || max_members * group > 16 ||
       num_groups > kMaxGridYZ || num_kv_heads > kMaxGridYZ)
     return PKV_EUNSUPPORTED;
+  const GroupedLayout lo = grouped_layout(num_groups, num_kv_heads, head_dim, part_tiles,
+                                          max_group_tiles);
+  if (lo.max_parts > kMaxGridYZ) return PKV_EUNSUPPORTED;
+  if (lo.total > 0 && (!workspace || workspace_bytes < lo.total)) return PKV_EWORKSPACE;
+  if (lo.total > 0 && reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_checks()) {
     const int rc = debug_check_groups(context_lens, group_members, group_tiles, group_tile_start,
                                       num_tiles, num_seqs, num_groups, max_members, num_blocks,
-                                      max_context_len, st);
+                                      max_context_len, part_tiles > 0 ? max_group_tiles : -1,
+                                      st);
     if (rc != PKV_OK) return rc;
   }
   GroupedArgs a;
@@ -780,12 +823,19 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
   a.group = group;
   a.num_blocks = num_blocks;
   a.len_cap = max_context_len;
+  a.part_tiles = lo.max_parts > 1 ? part_tiles : 0;
+  a.max_parts = lo.max_parts;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = lo.total ? reinterpret_cast<float*>(ws + lo.part_o) : nullptr;
+  a.part_ml = lo.total ? reinterpret_cast<float*>(ws + lo.part_ml) : nullptr;
   hipError_t err;
   if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
     return fail_hip(err);
   err = launch_decode_grouped(e, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
   if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
+    return fail_hip(err);
+  if (lo.max_parts > 1 && (err = launch_grouped_merge(e, head_dim, a, st)) != hipSuccess)
     return fail_hip(err);
   return PKV_OK;
 }

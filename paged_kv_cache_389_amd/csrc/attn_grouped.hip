@@ -33,6 +33,24 @@ namespace {
 
 constexpr int kCols = 16;
 
+// Rows [t_begin, t_begin + ntile) of the list that part `part` of group grp
+// covers, offsets clamped to the list; returns the group's part count (at
+// least one: an empty group is one empty part).
+__device__ inline int group_range(const GroupedArgs& a, int grp, int part, int& t_begin,
+                                  int& ntile) {
+  const int t0 = min(max(load_uniform(a.tile_start + grp), 0), a.num_tiles);
+  const int t1 = min(max(load_uniform(a.tile_start + grp + 1), t0), a.num_tiles);
+  if (a.part_tiles <= 0) {
+    t_begin = t0;
+    ntile = t1 - t0;
+    return 1;
+  }
+  const int nparts = max(1, (t1 - t0 + a.part_tiles - 1) / a.part_tiles);
+  t_begin = min(t0 + part * a.part_tiles, t1);
+  ntile = min(a.part_tiles, t1 - t_begin);
+  return nparts;
+}
+
 template <int HD>
 struct GroupShared {
   static constexpr int OS = HD + 4;   // padded row stride of the output tiles
@@ -66,7 +84,12 @@ decode_grouped_kernel(GroupedArgs a) {
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
   __shared__ GroupShared<HD> sm;
 
-  const int g = blockIdx.x, grp = blockIdx.y;
+  const int g = blockIdx.x, grp = blockIdx.y, part = blockIdx.z;
+  // the group's rows of the list, clamped to the list (any offsets stay in
+  // bounds), and this workgroup's part of them
+  int t_begin, ntile;
+  const int nparts = group_range(a, grp, part, t_begin, ntile);
+  if (part >= nparts) return;
   const int tid = threadIdx.x, wave = uniform(tid / kWave), lane = tid % kWave;
   const int n = lane & 15, g4 = lane >> 4;
   const int G = a.group;
@@ -79,9 +102,6 @@ decode_grouped_kernel(GroupedArgs a) {
   int len_n = s_n >= 0 ? a.context_lens[s_n] : 0;
   len_n = len_n < 0 ? 0 : (len_n > a.len_cap ? a.len_cap : len_n);
   const int bit_n = s_n >= 0 ? (1 << mem) : 0;
-  // the group's rows of the list, clamped to the list (any offsets stay in bounds)
-  const int t_begin = min(max(load_uniform(a.tile_start + grp), 0), a.num_tiles);
-  const int ntile = min(max(load_uniform(a.tile_start + grp + 1), t_begin), a.num_tiles) - t_begin;
 
   // the query rows of the columns (B layout), zero for empty columns
   if (wave == 0) {
@@ -225,7 +245,8 @@ decode_grouped_kernel(GroupedArgs a) {
   }
   if (!waited) __syncthreads();   // a wave with no tiles still meets the Q barrier
 
-  // merge the four waves in LDS; every column's row is normalised and stored
+  // merge the four waves in LDS; every column's row is normalised and stored,
+  // or, when the group has several parts, its unnormalised state
   const float lsum = rows_sum(l);
   if (g4 == 0) {
     sm.m[wave][n] = m;
@@ -256,6 +277,13 @@ decode_grouped_kernel(GroupedArgs a) {
       Ls = __builtin_fmaf(wt, sm.l[w][col], Ls);
       O += wt * *reinterpret_cast<const f32x4*>(&sm.o[w][col][d]);
     }
+    if (nparts > 1) {
+      const size_t st = (((size_t)grp * a.max_parts + part) * a.num_kv_heads + g) * kCols + col;
+      if (all_bad) O = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      *reinterpret_cast<f32x4*>(a.part_o + st * HD + d) = O;
+      if (d == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * st) = f32x2{M, Ls};
+      continue;
+    }
     float r[4];
     if (all_bad) {
       r[0] = r[1] = r[2] = r[3] = __builtin_nanf("");
@@ -273,14 +301,63 @@ decode_grouped_kernel(GroupedArgs a) {
   }
 }
 
+// Merge of a group's part states, one workgroup per (KV head, group): for
+// every column with a sequence, the log-sum-exp combination of its parts'
+// (max, sum, output) states, normalised and rounded into its row.
+template <typename E, int HD>
+__global__ __launch_bounds__(256) void grouped_merge_kernel(GroupedArgs a) {
+  using T = typename E::storage;
+  const int g = blockIdx.x, grp = blockIdx.y;
+  int t_begin, ntile;
+  const int nparts = min(group_range(a, grp, 0, t_begin, ntile), a.max_parts);
+  if (nparts <= 1) return;
+  const int G = a.group;
+  for (int idx = threadIdx.x; idx < kCols * (HD / 4); idx += 256) {
+    const int col = idx / (HD / 4), d = (idx % (HD / 4)) * 4;
+    const int mem = col / G;
+    if (mem >= a.max_members) continue;
+    const int s = a.members[(size_t)grp * a.max_members + mem];
+    if (s < 0 || s >= a.num_seqs) continue;
+    const size_t st0 = (((size_t)grp * a.max_parts) * a.num_kv_heads + g) * kCols + col;
+    const size_t pstride = (size_t)a.num_kv_heads * kCols;
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_ml[2 * (st0 + p * pstride)]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float Ls = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < nparts; ++p) {
+      const size_t st = st0 + p * pstride;
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * st);
+      const float wt = fast_exp2(ml[0] - Mu);
+      Ls = __builtin_fmaf(wt, ml[1], Ls);
+      O += wt * *reinterpret_cast<const f32x4*>(a.part_o + st * HD + d);
+    }
+    float r[4];
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;   // no token at all: the zero row
+    r[0] = O[0] * inv;
+    r[1] = O[1] * inv;
+    r[2] = O[2] * inv;
+    r[3] = O[3] * inv;
+    T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G + col % G) * HD;
+    store_rounded<E, 4>(out + d, r);
+  }
+}
+
 template <typename E, int HD>
 hipError_t launch_hd(int bs, const GroupedArgs& a, hipStream_t st) {
-  const dim3 grid(a.num_kv_heads, a.num_groups);
+  const dim3 grid(a.num_kv_heads, a.num_groups, a.max_parts);
   switch (bs) {
     case 16: hipLaunchKernelGGL((decode_grouped_kernel<E, HD, 16>), grid, dim3(256), 0, st, a); break;
     case 32: hipLaunchKernelGGL((decode_grouped_kernel<E, HD, 32>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+template <typename E, int HD>
+hipError_t launch_merge_hd(const GroupedArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((grouped_merge_kernel<E, HD>), dim3(a.num_kv_heads, a.num_groups), dim3(256),
+                     0, st, a);
   return hipGetLastError();
 }
 
@@ -306,6 +383,16 @@ hipError_t launch_decode_grouped(Elem e, int head_dim, int block_size, const Gro
     case Elem::F16: return launch_e<F16>(head_dim, block_size, a, stream);
     case Elem::BF16: return launch_e<BF16>(head_dim, block_size, a, stream);
     default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped_merge(Elem e, int head_dim, const GroupedArgs& a, hipStream_t stream) {
+  const bool f16 = e == Elem::F16;
+  if (e != Elem::F16 && e != Elem::BF16) return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return f16 ? launch_merge_hd<F16, 64>(a, stream) : launch_merge_hd<BF16, 64>(a, stream);
+    case 128: return f16 ? launch_merge_hd<F16, 128>(a, stream) : launch_merge_hd<BF16, 128>(a, stream);
   }
   return hipErrorInvalidValue;
 }

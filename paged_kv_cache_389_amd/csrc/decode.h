@@ -77,6 +77,15 @@ struct GroupedArgs {
   int group;                    // Hq / Hkv
   int num_blocks;
   int len_cap;                  // lengths are clamped to this
+  // Parts: with part_tiles > 0 group j's list is cut into ceil(n_j / part_tiles)
+  // parts of part_tiles rows (grid z, at most max_parts); a group of several
+  // parts leaves one (max, sum, output) state per part and column in
+  // part_ml / part_o, [num_groups][max_parts][Hkv][16] (x2 / x HD floats),
+  // which the merge kernel combines.
+  int part_tiles = 0;
+  int max_parts = 1;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
 };
 
 // Arguments of the prefill kernel (attn_prefill.hip): causal attention of
@@ -167,6 +176,7 @@ bool prefill_supported(Elem e, int head_dim, int block_size, int group);
 bool grouped_supported(Elem e, int head_dim, int block_size);
 hipError_t launch_decode_grouped(Elem e, int head_dim, int block_size, const GroupedArgs& a,
                                  hipStream_t stream);
+hipError_t launch_grouped_merge(Elem e, int head_dim, const GroupedArgs& a, hipStream_t stream);
 // Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
 // chunks per KV head and sequence).
 int prefill_tokens_per_workgroup(int group);

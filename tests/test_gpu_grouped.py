@@ -36,14 +36,20 @@ def _lists(tables, lens, groups, bs, max_members):
     if tiles.shape[0] == 0:
         tiles = np.zeros((1, 4), np.int32)
     return (torch.from_numpy(members).to(DEV), torch.from_numpy(tiles).to(DEV),
-            torch.from_numpy(start).to(DEV))
+            torch.from_numpy(start).to(DEV), int(np.diff(start).max(initial=0)))
 
 
-def _grouped(q, kc, vc, lens_d, lists, scale, max_len):
+def _grouped(q, kc, vc, lens_d, lists, scale, max_len, part_tiles=0):
+    members, tiles, start, max_group_tiles = lists
     out = torch.full_like(q, float("nan"))
-    pk.paged_attention_decode_grouped(out, q, kc, vc, lens_d, *lists, scale, max_len)
+    pk.paged_attention_decode_grouped(out, q, kc, vc, lens_d, members, tiles, start, scale,
+                                      max_len, part_tiles=part_tiles,
+                                      max_group_tiles=max_group_tiles)
     torch.cuda.synchronize()
     return out
+
+
+PARTS = [0, 3, 16]   # whole groups, and parts of 3 / 16 tiles merged by the second kernel
 
 
 def _poison_unowned(kc, vc, tables, lens, bs):
@@ -57,14 +63,14 @@ def _poison_unowned(kc, vc, tables, lens, bs):
     vc.masked_fill_(mask, float("nan"))
 
 
-def _check(wl, max_members, q=None):
+def _check(wl, max_members, part_tiles=0, q=None):
     q = wl.q if q is None else q
     kc, vc = wl.k_cache, wl.v_cache
     _poison_unowned(kc, vc, wl.block_tables, wl.context_lens, wl.block_size)
     groups = bmod.share_groups(wl.block_tables, wl.context_lens, max_members)
     lists = _lists(wl.block_tables, wl.context_lens, groups, wl.block_size, max_members)
     lens_d = torch.from_numpy(wl.context_lens).to(DEV)
-    got = _grouped(q, kc, vc, lens_d, lists, wl.scale, int(wl.context_lens.max()))
+    got = _grouped(q, kc, vc, lens_d, lists, wl.scale, int(wl.context_lens.max()), part_tiles)
     want = oracle.decode(q.cpu(), kc.cpu(), vc.cpu(), wl.block_tables, wl.context_lens,
                          wl.scale, wl.num_kv_heads)
     err = max_err(got, want)
@@ -75,39 +81,42 @@ def _check(wl, max_members, q=None):
     return groups
 
 
+@pytest.mark.parametrize("part_tiles", PARTS)
 @pytest.mark.parametrize("dtype,hd,bs,heads,fanout", [
     (torch.float16, 128, 16, 8, 8),
     (torch.bfloat16, 64, 32, 4, 16),
     (torch.bfloat16, 128, 32, 2, 8),
     (torch.float16, 64, 16, 3, 5),
 ])
-def test_forked_prompts(dtype, hd, bs, heads, fanout):
-    say("grouped forked prompts", dtype, hd, bs, heads, fanout)
+def test_forked_prompts(dtype, hd, bs, heads, fanout, part_tiles):
+    say("grouped forked prompts", dtype, hd, bs, heads, fanout, part_tiles)
     wl = workloads.build_sharing(dtype=dtype, num_prompts=5, fanout=fanout, prompt_len=70,
                                  prompt_extra=(1, 15), max_gen=40, num_heads=heads,
                                  head_dim=hd, block_size=bs, num_blocks=512,
                                  seed=300 + hd + bs + fanout, device=DEV)
-    groups = _check(wl, fanout)
+    groups = _check(wl, fanout, part_tiles)
     assert max(len(g) for g in groups) == fanout   # the forks did share
 
 
+@pytest.mark.parametrize("part_tiles", PARTS)
 @pytest.mark.parametrize("dtype,hq,hkv,hd,bs,width", [
     (torch.bfloat16, 16, 4, 128, 16, 4),    # G = 4: 4 beams x 4 heads = 16 columns
     (torch.float16, 8, 4, 128, 32, 8),      # G = 2
     (torch.float16, 24, 8, 64, 16, 5),      # G = 3: 15 columns used
     (torch.bfloat16, 8, 8, 128, 16, 8),     # multi-head
 ])
-def test_beam_search_batch(dtype, hq, hkv, hd, bs, width):
-    say("grouped beam search", dtype, hq, hkv, hd, bs, width)
+def test_beam_search_batch(dtype, hq, hkv, hd, bs, width, part_tiles):
+    say("grouped beam search", dtype, hq, hkv, hd, bs, width, part_tiles)
     wl = workloads.build_beam_search(dtype=dtype, num_requests=5, beam_width=width,
                                      prompt_lens=(3, 90), steps=30, num_q_heads=hq,
                                      num_kv_heads=hkv, head_dim=hd, block_size=bs,
                                      num_blocks=512, seed=400 + hq + bs, device=DEV)
-    _check(wl, width)
+    _check(wl, width, part_tiles)
 
 
+@pytest.mark.parametrize("part_tiles", [0, 2])
 @pytest.mark.parametrize("max_members", [1, 3, 16])
-def test_unrelated_sequences_any_grouping(max_members):
+def test_unrelated_sequences_any_grouping(max_members, part_tiles):
     """Nothing shared: each tile has one member, and grouping must not change
     any row (empty and one-token contexts included)."""
     say("grouped unrelated", max_members)
@@ -120,7 +129,8 @@ def test_unrelated_sequences_any_grouping(max_members):
     order = rng.permutation(len(lens))
     groups = [list(map(int, order[i:i + max_members])) for i in range(0, len(order), max_members)]
     lists = _lists(tables, L, groups, 16, max_members)
-    got = _grouped(dev["q"], dev["k"], dev["v"], dev["lens"], lists, 0.09, int(L.max()))
+    got = _grouped(dev["q"], dev["k"], dev["v"], dev["lens"], lists, 0.09, int(L.max()),
+                   part_tiles)
     want = oracle.decode(qt, kt, vt, tables, L, 0.09, hkv)
     assert max_err(got, want) <= TOL[torch.float16]
     assert torch.all(got[0] == 0)   # the empty context: zero row
@@ -140,7 +150,8 @@ def test_sequences_outside_groups_are_not_written():
     assert torch.isnan(got[[1, 3]]).all()   # left as the caller filled them
 
 
-def test_out_of_pool_block_gives_nan_rows():
+@pytest.mark.parametrize("part_tiles", [0, 2])
+def test_out_of_pool_block_gives_nan_rows(part_tiles):
     say("grouped bad block")
     wl = workloads.build_sharing(dtype=torch.float16, num_prompts=3, fanout=4, prompt_len=40,
                                  max_gen=20, num_heads=2, head_dim=128, num_blocks=128,
@@ -150,10 +161,10 @@ def test_out_of_pool_block_gives_nan_rows():
                                              wl.block_size, 4)
     tiles[int(start[1]) + 2, 0] = wl.num_blocks + 7   # a tile of group 1 outside the pool
     lists = (torch.from_numpy(members).to(DEV), torch.from_numpy(tiles).to(DEV),
-             torch.from_numpy(start).to(DEV))
+             torch.from_numpy(start).to(DEV), int(np.diff(start).max()))
     lens_d = torch.from_numpy(wl.context_lens).to(DEV)
     got = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, lists, wl.scale,
-                   int(wl.context_lens.max()))
+                   int(wl.context_lens.max()), part_tiles)
     want = oracle.decode(wl.q.cpu(), wl.k_cache.cpu(), wl.v_cache.cpu(), wl.block_tables,
                          wl.context_lens, wl.scale, wl.num_kv_heads)
     bad = [s for s in groups[1]]
@@ -162,15 +173,16 @@ def test_out_of_pool_block_gives_nan_rows():
     assert max_err(got[good], want[good]) <= TOL[torch.float16]
 
 
+@pytest.mark.parametrize("part_tiles", [0, 32])
 @pytest.mark.parametrize("name", ["sharing_fp16", "beam_search_fp16"])
-def test_full_size_workloads_sampled(name):
-    say("grouped full size", name)
+def test_full_size_workloads_sampled(name, part_tiles):
+    say("grouped full size", name, part_tiles)
     wl = workloads.make(name, device=DEV)
     groups = bmod.share_groups(wl.block_tables, wl.context_lens, 8)
     lists = _lists(wl.block_tables, wl.context_lens, groups, wl.block_size, 8)
     lens_d = torch.from_numpy(wl.context_lens).to(DEV)
     got = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, lists, wl.scale,
-                   int(wl.context_lens.max()))
+                   int(wl.context_lens.max()), part_tiles)
     rng = np.random.default_rng(1)
     seqs = sorted(set(int(s) for s in rng.choice(wl.num_seqs, 12, replace=False)) |
                   {int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))})
@@ -196,11 +208,11 @@ def test_debug_rejects_bad_lists(monkeypatch):
     lens_d = torch.from_numpy(wl.context_lens).to(DEV)
     out = torch.empty_like(wl.q)
 
-    def call(mem, til, sta):
+    def call(mem, til, sta, part_tiles=0, max_group_tiles=0):
         pk.paged_attention_decode_grouped(
             out, wl.q, wl.k_cache, wl.v_cache, lens_d, torch.from_numpy(mem).to(DEV),
             torch.from_numpy(til).to(DEV), torch.from_numpy(sta).to(DEV), wl.scale,
-            int(wl.context_lens.max()))
+            int(wl.context_lens.max()), part_tiles=part_tiles, max_group_tiles=max_group_tiles)
 
     call(members, tiles, start)   # valid
     torch.cuda.synchronize()
@@ -218,3 +230,9 @@ def test_debug_rejects_bad_lists(monkeypatch):
         with pytest.raises(pk.PagedKVError) as e:
             call(mem, til, sta)
         assert e.value.status == -1 and match in str(e.value), str(e.value)
+    longest = int(np.diff(start).max())
+    call(members, tiles, start, part_tiles=2, max_group_tiles=longest)   # valid
+    torch.cuda.synchronize()
+    with pytest.raises(pk.PagedKVError) as e:   # a bound below the longest group
+        call(members, tiles, start, part_tiles=2, max_group_tiles=longest - 3)
+    assert e.value.status == -1 and "max_group_tiles" in str(e.value), str(e.value)
