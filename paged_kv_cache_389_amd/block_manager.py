@@ -307,23 +307,39 @@ def group_tiles(block_tables, context_lens, groups, block_size: int, max_members
     if block_size % TILE_TOKENS:
         raise ValueError("block_size must be a multiple of 16")
     tpb = block_size // TILE_TOKENS
-    members = np.full((len(groups), max_members), -1, dtype=np.int32)
-    rows: list[tuple[int, int, int, int]] = []
-    start = [0]
-    seen = set()
+    num_groups = len(groups)
+    members = np.full((num_groups, max_members), -1, dtype=np.int32)
+    seqs, grp_of, mem_of = [], [], []
     for j, grp in enumerate(groups):
         if len(grp) > max_members:
             raise ValueError(f"group {j} has {len(grp)} members, more than {max_members}")
-        entries: dict[tuple[int, int], int] = {}
-        for m, s in enumerate(grp):
-            if s in seen:
-                raise ValueError(f"sequence {s} is in two groups")
-            seen.add(s)
-            members[j, m] = s
-            for t in range(-(-int(context_lens[s]) // TILE_TOKENS)):
-                key = (int(block_tables[s][t // tpb]), t)
-                entries[key] = entries.get(key, 0) | (1 << m)
-        rows.extend((b, t, mask, 0) for (b, t), mask in entries.items())
-        start.append(len(rows))
-    tiles = np.array(rows, dtype=np.int32).reshape(-1, 4)
-    return members, tiles, np.array(start, dtype=np.int32)
+        members[j, :len(grp)] = grp
+        seqs.extend(int(x) for x in grp)
+        grp_of.extend([j] * len(grp))
+        mem_of.extend(range(len(grp)))
+    seqs = np.asarray(seqs, dtype=np.int64)
+    if len(np.unique(seqs)) != len(seqs):
+        raise ValueError("a sequence is in two groups")
+    lens = np.asarray(context_lens, dtype=np.int64)[seqs] if len(seqs) else np.zeros(0, np.int64)
+    ntile = -(-np.maximum(lens, 0) // TILE_TOKENS)
+    # one row per (member, tile index), then one per distinct (group, tile, block)
+    total = int(ntile.sum())
+    first = np.repeat(np.cumsum(ntile) - ntile, ntile)
+    t = np.arange(total, dtype=np.int64) - first
+    seq_rep = np.repeat(seqs, ntile)
+    blk = np.asarray(block_tables)[seq_rep, t // tpb].astype(np.int64)
+    grp = np.repeat(np.asarray(grp_of, dtype=np.int64), ntile)
+    bit = np.left_shift(1, np.repeat(np.asarray(mem_of, dtype=np.int64), ntile))
+    order = np.lexsort((blk, t, grp))
+    blk, t, grp, bit = blk[order], t[order], grp[order], bit[order]
+    new = np.ones(total, dtype=bool)
+    if total:
+        new[1:] = (grp[1:] != grp[:-1]) | (t[1:] != t[:-1]) | (blk[1:] != blk[:-1])
+    heads = np.nonzero(new)[0]
+    tiles = np.zeros((len(heads), 4), dtype=np.int32)
+    if len(heads):
+        tiles[:, 0] = blk[heads]
+        tiles[:, 1] = t[heads]
+        tiles[:, 2] = np.bitwise_or.reduceat(bit, heads)
+    start = np.searchsorted(grp[heads], np.arange(num_groups + 1)).astype(np.int32)
+    return members, tiles, start
