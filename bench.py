@@ -23,6 +23,7 @@ float64 CPU oracle on a bounded sample of the same workload.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -183,7 +184,7 @@ def counters_to_traffic(args):
     rec["calibration"] = {"copy_mib": args.cal_mib, "fetch_counter_per_byte": round(f_fetch, 4),
                           "write_counter_per_byte": round(f_write, 4)}
     rec["workloads"][key] = {
-        "kernel": kname.split("(")[0], "fetch_kib_per_launch": round(fetch, 1),
+        "kernel": re.sub(r"\([^()]*\)$", "", kname), "fetch_kib_per_launch": round(fetch, 1),
         "write_kib_per_launch": round(write, 1),
         "hbm_bytes_per_launch": int(fetch * 1024 / f_fetch + write * 1024 / f_write),
         "alg_bytes_per_launch": alg}
