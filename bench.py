@@ -173,7 +173,8 @@ def counters_to_traffic(args):
               wl.esize)
         key, alg = key + "_kv_e4m3", alg - (kv - kv // wl.esize)
     if args.grouped:
-        key, alg = key + "_grouped", grouped_decode_bytes(wl, grouped_lists(wl, {}))
+        key, alg = key + "_grouped", grouped_decode_bytes(wl, grouped_lists(wl, {}),
+                                                          args.kv_cache == "e4m3")
     try:
         with open(args.counters) as fh:
             rec = json.load(fh)
@@ -304,10 +305,10 @@ def grouped_lists(wl, dev, part_tiles=-1):
             "host_list_ms": round(host_ms, 2)}
 
 
-def grouped_decode_bytes(wl, info):
-    """What the grouped kernel must move: every distinct K/V tile once, q and
-    out, its lists and the lengths."""
-    return (wl.unique_kv_bytes() + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * wl.esize +
+def grouped_decode_bytes(wl, info, kv_fp8=False):
+    """What the grouped kernel must move: every distinct K/V tile once (one
+    byte per element for 8-bit caches), q and out, its lists and the lengths."""
+    return (wl.unique_kv_bytes() // (wl.esize if kv_fp8 else 1) + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * wl.esize +
             16 * info["tiles"] + 4 * info["groups"] * info["max_members"] +
             4 * (info["groups"] + 1) + 4 * wl.num_seqs)
 
@@ -347,7 +348,9 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
                                               part_tiles=dev["group_part"][0],
                                               max_group_tiles=dev["group_part"][1],
                                               workspace=dev["group_ws"],
-                                              kernel_events=None if i is None else kev[i])
+                                              kernel_events=None if i is None else kev[i],
+                                              **({"k_scale": dev["k_scale"],
+                                                  "v_scale": dev["v_scale"]} if fp8 else {}))
         elif fp8:
             pk.paged_attention_decode_fp8(dev["out"], dev["q"], dev["k"], dev["v"], tables,
                                           dev["lens"], wl.scale, dev["k_scale"], dev["v_scale"],
@@ -613,12 +616,10 @@ def bench_one(name, args, with_cpu):
         quantise_pools(wl, dev)
     grouped = None
     if args.grouped:
-        if dev.get("kv_fp8"):
-            raise SystemExit("--grouped runs on 16-bit caches")
         grouped = grouped_lists(wl, dev, args.group_part)
     alg_decode, alg_writes = step_bytes(wl, dev)
     if grouped:
-        alg_decode = grouped_decode_bytes(wl, grouped)
+        alg_decode = grouped_decode_bytes(wl, grouped, bool(dev.get("kv_fp8")))
     wall, decode_ms, kernel_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition,
                                                args.path, args.grid)
     ms_per_step = wall / args.steps * 1e3

@@ -21,7 +21,8 @@
  *                               _prefill_fp8 over the 8-bit cache);
  *   pkv_paged_attention_decode_grouped  decode of sequences that share blocks
  *                               (forks of one prompt), each shared tile read
- *                               once for all of them.
+ *                               once for all of them (and _grouped_fp8 over
+ *                               the 8-bit cache).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -527,6 +528,22 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
                                        pkv_dtype dtype, int part_tiles, int max_group_tiles,
                                        void* workspace, size_t workspace_bytes,
                                        void* begin_event, void* end_event, void* stream);
+
+/* paged_attention_decode_grouped_fp8: pkv_paged_attention_decode_grouped over
+ * E4M3 caches (uint8 codes in the cache layout, written by
+ * pkv_reshape_and_cache_fp8): keys and values are value(code) * k_scale and
+ * value(code) * v_scale, the scales applied outside the products as in
+ * pkv_paged_attention_decode_fp8.  Scales must be finite and nonzero (else
+ * PKV_EINVAL); dtype is the type of q and out; everything else as
+ * pkv_paged_attention_decode_grouped. */
+int pkv_paged_attention_decode_grouped_fp8(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* context_lens, const int32_t* group_members, const int32_t* group_tiles,
+    const int32_t* group_tile_start, int num_tiles, float scale, float k_scale, float v_scale,
+    int num_seqs, int num_groups, int max_members, int num_q_heads, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, int max_context_len, pkv_dtype dtype,
+    int part_tiles, int max_group_tiles, void* workspace, size_t workspace_bytes,
+    void* begin_event, void* end_event, void* stream);
 
 /* Bytes of workspace pkv_paged_attention_decode_grouped needs for these
  * arguments (0 when every group is one part); (size_t)-1 for a negative

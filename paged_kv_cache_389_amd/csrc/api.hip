@@ -766,14 +766,15 @@ size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_he
   return lo.total;
 }
 
-int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,
+static int grouped_impl(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* context_lens,
                                        const int32_t* group_members, const int32_t* group_tiles,
                                        const int32_t* group_tile_start, int num_tiles,
                                        float scale, int num_seqs, int num_groups, int max_members,
                                        int num_q_heads, int num_kv_heads, int head_dim,
                                        int block_size, int num_blocks, int max_context_len,
-                                       pkv_dtype dtype, int part_tiles, int max_group_tiles,
+                                       int dtype, bool kv_fp8, float k_scale, float v_scale,
+                                       int part_tiles, int max_group_tiles,
                                        void* workspace, size_t workspace_bytes,
                                        void* begin_event, void* end_event, void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_groups < 0 || max_members <= 0 || num_tiles < 0 ||
@@ -781,6 +782,7 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
       num_blocks <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads || part_tiles < 0 ||
       max_group_tiles < 0)
     return PKV_EINVAL;
+  if (kv_fp8 && (!finite_nonzero(k_scale) || !finite_nonzero(v_scale))) return PKV_EINVAL;
   if (num_groups == 0 || num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || !group_members || !group_tiles ||
       !group_tile_start)
@@ -814,7 +816,8 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
   a.tiles = group_tiles;
   a.tile_start = group_tile_start;
   a.num_tiles = num_tiles;
-  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2e = (float)((double)scale * (kv_fp8 ? (double)k_scale : 1.0) * 1.4426950408889634);
+  a.v_scale = kv_fp8 ? v_scale : 1.f;
   a.num_seqs = num_seqs;
   a.num_groups = num_groups;
   a.max_members = max_members;
@@ -831,13 +834,46 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
   hipError_t err;
   if (begin_event && (err = hipEventRecord(static_cast<hipEvent_t>(begin_event), st)) != hipSuccess)
     return fail_hip(err);
-  err = launch_decode_grouped(e, head_dim, block_size, a, st);
+  err = launch_decode_grouped(e, kv_fp8, head_dim, block_size, a, st);
   if (err != hipSuccess) return fail_hip(err);
   if (end_event && (err = hipEventRecord(static_cast<hipEvent_t>(end_event), st)) != hipSuccess)
     return fail_hip(err);
   if (lo.max_parts > 1 && (err = launch_grouped_merge(e, head_dim, a, st)) != hipSuccess)
     return fail_hip(err);
   return PKV_OK;
+}
+
+int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* context_lens,
+                                       const int32_t* group_members, const int32_t* group_tiles,
+                                       const int32_t* group_tile_start, int num_tiles,
+                                       float scale, int num_seqs, int num_groups, int max_members,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, int max_context_len,
+                                       pkv_dtype dtype, int part_tiles, int max_group_tiles,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* begin_event, void* end_event, void* stream) {
+  return grouped_impl(out, q, k_cache, v_cache, context_lens, group_members, group_tiles,
+                      group_tile_start, num_tiles, scale, num_seqs, num_groups, max_members,
+                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_context_len, dtype, false, 1.f, 1.f, part_tiles, max_group_tiles,
+                      workspace, workspace_bytes, begin_event, end_event, stream);
+}
+
+int pkv_paged_attention_decode_grouped_fp8(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* context_lens, const int32_t* group_members, const int32_t* group_tiles,
+    const int32_t* group_tile_start, int num_tiles, float scale, float k_scale, float v_scale,
+    int num_seqs, int num_groups, int max_members, int num_q_heads, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, int max_context_len, pkv_dtype dtype,
+    int part_tiles, int max_group_tiles, void* workspace, size_t workspace_bytes,
+    void* begin_event, void* end_event, void* stream) {
+  return grouped_impl(out, q, k_cache, v_cache, context_lens, group_members, group_tiles,
+                      group_tile_start, num_tiles, scale, num_seqs, num_groups, max_members,
+                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_context_len, dtype, true, k_scale, v_scale, part_tiles,
+                      max_group_tiles, workspace, workspace_bytes, begin_event, end_event,
+                      stream);
 }
 
 int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,

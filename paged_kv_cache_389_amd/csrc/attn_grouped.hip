@@ -70,15 +70,23 @@ __device__ inline int row16_max(int v) {
   return v;
 }
 
-template <typename E, int HD, int BS>
+// C is the cache element: E itself, or E4M3 codes (loaded at half width and
+// widened to E's 16-bit values right before the products; the K scale is in
+// scale_log2e, the V scale multiplies the merged output).
+template <typename E, typename C, int HD, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_grouped_kernel(GroupedArgs a) {
-  using T = typename E::storage;
+  using T = typename C::storage;       // cache element
+  using Q = typename E::storage;       // query / output element
   using Ops = MfmaOps<E>;
+  constexpr bool k8 = sizeof(T) == 1;
   constexpr int KSTEPS = HD / 32;      // QK MFMAs per tile
   constexpr int DPL = HD / 16;         // V dims per lane per token == PV MFMAs per tile
-  constexpr int VW = DPL / 2;          // dwords of V per lane per token
+  constexpr int VW = DPL / 2;          // dwords of 16-bit V per lane per token
+  constexpr int KL = k8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per tile
+  constexpr int VL = k8 ? VW / 2 : VW;           // dwords of V loaded per lane per token
   constexpr int TPB = BS / 16;         // tiles per block
+  static_assert(!k8 || KSTEPS % 2 == 0, "8-bit K loads cover two k-steps");
   constexpr int NW = 4;
   constexpr int NS = 2;                // register stages of the tile pipeline
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
@@ -105,18 +113,18 @@ decode_grouped_kernel(GroupedArgs a) {
 
   // the query rows of the columns (B layout), zero for empty columns
   if (wave == 0) {
-    const T* qh = static_cast<const T*>(a.q) +
+    const Q* qh = static_cast<const Q*>(a.q) +
                   ((size_t)(s_n >= 0 ? s_n : 0) * a.num_q_heads + (size_t)g * G + n % G) * HD;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
-      sm.q[kk][lane] = s_n >= 0 ? ld16(qh + mfma_dim0<E>(kk, g4)) : u32x4{0, 0, 0, 0};
+      sm.q[kk][lane] = s_n >= 0 ? ld16(qh + mfma_dim0<C>(kk, g4)) : u32x4{0, 0, 0, 0};
     if (g4 == 0) sm.seq[n] = s_n;
   }
 
   const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
-  const uint32_t koff = (uint32_t)((n * HD + mfma_dim0<E>(0, g4)) * sizeof(T));
+  const uint32_t koff = (uint32_t)((n * HD + mfma_dim0<C>(0, g4)) * sizeof(T));
   const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
 
   f32x4 acc[DPL];
@@ -137,7 +145,7 @@ decode_grouped_kernel(GroupedArgs a) {
 
     // loads of the wave's i-th tile of the pass (an empty descriptor past
     // `mine`: those loads return zeros without a memory access)
-    auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VW]) {
+    auto load_tile = [&](int i, u32x4* ka, uint32_t (*vv)[VL]) {
       const bool live = i < mine;
       const int ii = i < kWave ? i : kWave - 1;
       int phys = lane_value(blk_v, ii);
@@ -151,10 +159,12 @@ decode_grouped_kernel(GroupedArgs a) {
       const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
       const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = bld16(kt, koff, kk * 32 * sizeof(T));
+      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (VW == 2) {
+        if constexpr (VL == 1) {
+          vv[r][0] = bld4(vt, voff, r * HD * sizeof(T));
+        } else if constexpr (VL == 2) {
           const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
@@ -168,14 +178,37 @@ decode_grouped_kernel(GroupedArgs a) {
       }
     };
 
-    auto compute_tile = [&](int i, const u32x4* ka, uint32_t (*vin)[VW]) {
+    auto compute_tile = [&](int i, const u32x4* kl, uint32_t (*vl)[VL]) {
       const int tix = lane_value(tix_v, i);
       const int msk = lane_value(msk_v, i);
+      // the tile's operands in E's 16-bit values (8-bit codes widened here,
+      // after their loads have landed)
+      u32x4 ka[KSTEPS];
       uint32_t vv[4][VW];
+      if constexpr (k8) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int kk = 0; kk < KL; ++kk) {
+          ka[2 * kk] = u32x4{codes_to_pair<E, false>(kl[kk][0]), codes_to_pair<E, true>(kl[kk][0]),
+                             codes_to_pair<E, false>(kl[kk][1]), codes_to_pair<E, true>(kl[kk][1])};
+          ka[2 * kk + 1] =
+              u32x4{codes_to_pair<E, false>(kl[kk][2]), codes_to_pair<E, true>(kl[kk][2]),
+                    codes_to_pair<E, false>(kl[kk][3]), codes_to_pair<E, true>(kl[kk][3])};
+        }
 #pragma unroll
-        for (int w = 0; w < VW; ++w) vv[r][w] = vin[r][w];
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int w = 0; w < VL; ++w) {
+            vv[r][2 * w] = codes_to_pair<E, false>(vl[r][w]);
+            vv[r][2 * w + 1] = codes_to_pair<E, true>(vl[r][w]);
+          }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = kl[kk];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int w = 0; w < VW; ++w) vv[r][w] = vl[r][w];
+      }
       __asm__ volatile("" ::: "memory");   // Q^T is read from LDS per tile
       u32x4 qb[KSTEPS];
 #pragma unroll
@@ -227,8 +260,8 @@ decode_grouped_kernel(GroupedArgs a) {
       }
     };
 
-    u32x4 kb[NS][KSTEPS];
-    uint32_t vb[NS][4][VW];
+    u32x4 kb[NS][KL];
+    uint32_t vb[NS][4][VL];
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
     if (!waited) {   // Q^T is in LDS (the first tile loads overlap its write)
@@ -277,6 +310,7 @@ decode_grouped_kernel(GroupedArgs a) {
       Ls = __builtin_fmaf(wt, sm.l[w][col], Ls);
       O += wt * *reinterpret_cast<const f32x4*>(&sm.o[w][col][d]);
     }
+    if constexpr (k8) O *= a.v_scale;   // 8-bit V: code units -> values (commutes with merges)
     if (nparts > 1) {
       const size_t st = (((size_t)grp * a.max_parts + part) * a.num_kv_heads + g) * kCols + col;
       if (all_bad) O = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
@@ -296,7 +330,7 @@ decode_grouped_kernel(GroupedArgs a) {
     } else {   // an empty context: the zero row
       r[0] = r[1] = r[2] = r[3] = 0.f;
     }
-    T* out = static_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G + col % G) * HD;
+    Q* out = static_cast<Q*>(a.out) + ((size_t)s * a.num_q_heads + (size_t)g * G + col % G) * HD;
     store_rounded<E, 4>(out + d, r);
   }
 }
@@ -343,12 +377,12 @@ __global__ __launch_bounds__(256) void grouped_merge_kernel(GroupedArgs a) {
   }
 }
 
-template <typename E, int HD>
+template <typename E, typename C, int HD>
 hipError_t launch_hd(int bs, const GroupedArgs& a, hipStream_t st) {
   const dim3 grid(a.num_kv_heads, a.num_groups, a.max_parts);
   switch (bs) {
-    case 16: hipLaunchKernelGGL((decode_grouped_kernel<E, HD, 16>), grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((decode_grouped_kernel<E, HD, 32>), grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_grouped_kernel<E, C, HD, 16>), grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((decode_grouped_kernel<E, C, HD, 32>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -361,11 +395,11 @@ hipError_t launch_merge_hd(const GroupedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename E>
+template <typename E, typename C>
 hipError_t launch_e(int hd, int bs, const GroupedArgs& a, hipStream_t st) {
   switch (hd) {
-    case 64: return launch_hd<E, 64>(bs, a, st);
-    case 128: return launch_hd<E, 128>(bs, a, st);
+    case 64: return launch_hd<E, C, 64>(bs, a, st);
+    case 128: return launch_hd<E, C, 128>(bs, a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -377,11 +411,15 @@ bool grouped_supported(Elem e, int head_dim, int block_size) {
          (block_size == 16 || block_size == 32);
 }
 
-hipError_t launch_decode_grouped(Elem e, int head_dim, int block_size, const GroupedArgs& a,
-                                 hipStream_t stream) {
+hipError_t launch_decode_grouped(Elem e, bool kv_fp8, int head_dim, int block_size,
+                                 const GroupedArgs& a, hipStream_t stream) {
   switch (e) {
-    case Elem::F16: return launch_e<F16>(head_dim, block_size, a, stream);
-    case Elem::BF16: return launch_e<BF16>(head_dim, block_size, a, stream);
+    case Elem::F16:
+      return kv_fp8 ? launch_e<F16, E4M3>(head_dim, block_size, a, stream)
+                    : launch_e<F16, F16>(head_dim, block_size, a, stream);
+    case Elem::BF16:
+      return kv_fp8 ? launch_e<BF16, E4M3>(head_dim, block_size, a, stream)
+                    : launch_e<BF16, BF16>(head_dim, block_size, a, stream);
     default: break;
   }
   return hipErrorInvalidValue;

@@ -68,7 +68,8 @@ struct GroupedArgs {
   const int32_t* tiles;         // [total][4], 16-byte aligned
   const int32_t* tile_start;    // [num_groups + 1]; clamped to [0, num_tiles]
   int num_tiles;                // rows of tiles
-  float scale_log2e;
+  float scale_log2e;            // scale * log2(e) (* K scale for 8-bit codes)
+  float v_scale = 1.f;          // 8-bit caches: the V scale
   int num_seqs;
   int num_groups;
   int max_members;              // max_members * group <= 16
@@ -174,8 +175,10 @@ int valu_unit_tokens(Elem e, bool kv_fp8, int head_dim, int block_size);
 bool decode_mfma_supported(Elem e, int head_dim, int block_size);
 bool prefill_supported(Elem e, int head_dim, int block_size, int group);
 bool grouped_supported(Elem e, int head_dim, int block_size);
-hipError_t launch_decode_grouped(Elem e, int head_dim, int block_size, const GroupedArgs& a,
-                                 hipStream_t stream);
+// kv_fp8: the caches hold E4M3 codes (v_scale applies; the K scale is in
+// scale_log2e).
+hipError_t launch_decode_grouped(Elem e, bool kv_fp8, int head_dim, int block_size,
+                                 const GroupedArgs& a, hipStream_t stream);
 hipError_t launch_grouped_merge(Elem e, int head_dim, const GroupedArgs& a, hipStream_t stream);
 // Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
 // chunks per KV head and sequence).

@@ -236,3 +236,57 @@ def test_debug_rejects_bad_lists(monkeypatch):
     with pytest.raises(pk.PagedKVError) as e:   # a bound below the longest group
         call(members, tiles, start, part_tiles=2, max_group_tiles=longest - 3)
     assert e.value.status == -1 and "max_group_tiles" in str(e.value), str(e.value)
+
+
+@pytest.mark.parametrize("part_tiles", [0, 3])
+@pytest.mark.parametrize("dtype,hq,hkv,hd,bs,width,build", [
+    (torch.float16, 8, 8, 128, 16, 8, "sharing"),
+    (torch.bfloat16, 16, 4, 128, 32, 4, "beam"),
+    (torch.bfloat16, 6, 2, 64, 16, 5, "beam"),
+])
+def test_grouped_over_e4m3_codes(dtype, hq, hkv, hd, bs, width, build, part_tiles):
+    """The 8-bit cache: random E4M3 codes in every owned slot, NaN codes in every
+    slot no sequence owns, against the oracle's decode over dequantised codes."""
+    import math
+    from oracle import fp8
+    say("grouped e4m3", dtype, hq, hkv, hd, bs, width, build, part_tiles)
+    if build == "sharing":
+        wl = workloads.build_sharing(num_prompts=4, fanout=width, prompt_len=60, max_gen=40,
+                                     num_heads=hq, head_dim=hd, block_size=bs, num_blocks=512,
+                                     seed=70 + hd, tensors=False)
+    else:
+        wl = workloads.build_beam_search(num_requests=4, beam_width=width, prompt_lens=(5, 90),
+                                         steps=25, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                                         block_size=bs, num_blocks=512, seed=80 + hq,
+                                         tensors=False)
+    rng = np.random.default_rng(hq + hd + bs)
+    nb, h = wl.num_blocks, wl.num_kv_heads
+    kc = rng.integers(0, 256, (nb, h, bs, hd)).astype(np.uint8)
+    vc = rng.integers(0, 256, (nb, h, bs, hd)).astype(np.uint8)
+    for c in (kc, vc):
+        c[(c & 0x7F) == 0x7F] = 0x00
+    used = np.zeros((nb, bs), bool)
+    for s in range(wl.num_seqs):
+        for t in range(int(wl.context_lens[s])):
+            used[wl.block_tables[s][t // bs], t % bs] = True
+    kc[~used[:, None, :, None].repeat(h, 1).repeat(hd, 3)] = 0x7F
+    vc[~used[:, None, :, None].repeat(h, 1).repeat(hd, 3)] = 0xFF
+    q = torch.randn((wl.num_seqs, wl.num_q_heads, hd),
+                    generator=torch.Generator().manual_seed(3)).to(dtype)
+    k_scale, v_scale, scale = 1.0 / 96, 1.0 / 128, 1.0 / math.sqrt(hd)
+    groups = bmod.share_groups(wl.block_tables, wl.context_lens, 16 // (wl.num_q_heads // h))
+    members, tiles, start, longest = _lists(wl.block_tables, wl.context_lens, groups, bs,
+                                            16 // (wl.num_q_heads // h))
+    out = torch.full((wl.num_seqs, wl.num_q_heads, hd), float("nan"), dtype=dtype, device=DEV)
+    pk.paged_attention_decode_grouped(out, q.to(DEV), torch.from_numpy(kc).to(DEV),
+                                      torch.from_numpy(vc).to(DEV),
+                                      torch.from_numpy(wl.context_lens).to(DEV), members, tiles,
+                                      start, scale, int(wl.context_lens.max()),
+                                      part_tiles=part_tiles, max_group_tiles=longest,
+                                      k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    want = fp8.decode_fp8(q, kc, vc, wl.block_tables, wl.context_lens, scale, k_scale, v_scale, h)
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - want).max())
+    assert err <= TOL[dtype], f"max abs err {err}"
