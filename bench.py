@@ -712,6 +712,10 @@ def main():
     for name in names:
         line = bench_one(name, args, with_cpu=not args.no_cpu_baseline and not args.sweep)
         print(json.dumps(line), flush=True)
+        if args.sweep and not args.grouped and name in ("sharing_fp16", "beam_search_fp16"):
+            args.grouped = True    # the same batch through the grouped call
+            print(json.dumps(bench_one(name, args, with_cpu=False)), flush=True)
+            args.grouped = False
 
 
 if __name__ == "__main__":
