@@ -722,51 +722,9 @@ int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_ca
   return PKV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
-                                const void* v_cache, const int32_t* block_tables,
-                                const int32_t* context_lens, const int32_t* query_start,
-                                float scale, int num_seqs, int total_q, int max_q_len,
-                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                                int num_blocks, int max_blocks_per_seq, int max_context_len,
-                                pkv_dtype dtype, void* begin_event, void* end_event,
-                                void* stream) {
-  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
-                      false, 1.f, 1.f, num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads,
-                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                      dtype, begin_event, end_event, stream);
-}
-
-int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cache,
-                                    const void* v_cache, const int32_t* block_tables,
-                                    const int32_t* context_lens, const int32_t* query_start,
-                                    float scale, float k_scale, float v_scale, int num_seqs,
-                                    int total_q, int max_q_len, int num_q_heads,
-                                    int num_kv_heads, int head_dim, int block_size,
-                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
-                                    pkv_dtype dtype, void* begin_event, void* end_event,
-                                    void* stream) {
-  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
-                      true, k_scale, v_scale, num_seqs, total_q, max_q_len, num_q_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                      max_context_len, dtype, begin_event, end_event, stream);
-}
-
-size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_heads,
-                                                   int head_dim, int part_tiles,
-                                                   int max_group_tiles) {
-  if (num_groups < 0 || num_kv_heads <= 0 || head_dim <= 0 || part_tiles < 0 ||
-      max_group_tiles < 0)
-    return (size_t)-1;
-  const GroupedLayout lo = grouped_layout(num_groups, num_kv_heads, head_dim, part_tiles,
-                                          max_group_tiles);
-  return lo.total;
-}
-
-static int grouped_impl(void* out, const void* q, const void* k_cache,
+// Both grouped decode entry points: kv_fp8 says the caches hold E4M3 codes
+// with the given scales (ignored otherwise).
+int grouped_impl(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* context_lens,
                                        const int32_t* group_members, const int32_t* group_tiles,
                                        const int32_t* group_tile_start, int num_tiles,
@@ -841,6 +799,50 @@ static int grouped_impl(void* out, const void* q, const void* k_cache,
   if (lo.max_parts > 1 && (err = launch_grouped_merge(e, head_dim, a, st)) != hipSuccess)
     return fail_hip(err);
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                float scale, int num_seqs, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                pkv_dtype dtype, void* begin_event, void* end_event,
+                                void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      false, 1.f, 1.f, num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                      dtype, begin_event, end_event, stream);
+}
+
+int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_start,
+                                    float scale, float k_scale, float v_scale, int num_seqs,
+                                    int total_q, int max_q_len, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    pkv_dtype dtype, void* begin_event, void* end_event,
+                                    void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      true, k_scale, v_scale, num_seqs, total_q, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                      max_context_len, dtype, begin_event, end_event, stream);
+}
+
+size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_heads,
+                                                   int head_dim, int part_tiles,
+                                                   int max_group_tiles) {
+  if (num_groups < 0 || num_kv_heads <= 0 || head_dim <= 0 || part_tiles < 0 ||
+      max_group_tiles < 0)
+    return (size_t)-1;
+  const GroupedLayout lo = grouped_layout(num_groups, num_kv_heads, head_dim, part_tiles,
+                                          max_group_tiles);
+  return lo.total;
 }
 
 int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,

@@ -22,7 +22,9 @@
 // Per column: tokens at or past the member's length, and tiles outside its
 // mask, get probability zero.  Value rows that no member of the tile reaches
 // are zeroed before the product, so unwritten slots cannot reach a result.
-// The four waves take tiles round-robin and merge in LDS.
+// The four waves take tiles round-robin and merge in LDS.  A group's list
+// may be cut into parts (grid z) whose (max, sum, output) states a second
+// kernel merges; the cache may hold E4M3 codes.
 #include "common.h"
 #include "decode.h"
 #include "mfma_ops.h"
