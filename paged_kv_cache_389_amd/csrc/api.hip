@@ -313,13 +313,15 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
     // unit gets about kWgPerCu workgroups.  Many units: the grid is full
     // anyway, but a context much longer than the others would be one long
     // workgroup that ends last, so contexts longer than half the bound are
-    // cut in two (never below kSplitFloor tokens per partition).
+    // cut in two (never below kSplitFloor tokens per partition; twice that
+    // over 8-bit codes, the same bytes per partition).
     const int64_t units = (int64_t)num_seqs * units_per_seq;
     const int64_t target = (int64_t)kWgPerCu * compute_units();
     const int len = pl.len_cap > 0 ? pl.len_cap : 1;
     if (units >= target) {
+      const int floor_tokens = kv_fp8 ? 2 * kSplitFloor : kSplitFloor;
       p = round_up((len + 1) / 2, pl.part_align);
-      if (p < kSplitFloor) p = kSplitFloor;
+      if (p < floor_tokens) p = floor_tokens;
       if (p >= len) p = round_up(len, pl.part_align);
     } else {
       const int64_t parts = (target + units - 1) / units;
