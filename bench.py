@@ -670,8 +670,11 @@ def bench_one(name, args, with_cpu):
                      "kernel": kname},
     }
     if grouped:
+        for k in ("partition_tokens", "max_parts", "longest_first"):   # the per-sequence plan's
+            line["config"].pop(k, None)
         line["config"]["kernel"] = "grouped"
-        line["config"]["grid"] = "groups x kv heads"
+        line["config"]["grid"] = "groups x kv heads x parts"
+        line["config"]["part_tiles"] = grouped["part_tiles"]
         line["grouped"] = grouped
         line["roofline"]["basis"] = "unique K/V bytes (each distinct tile once)"
     if name in ("sharing_fp16", "beam_search_fp16"):
