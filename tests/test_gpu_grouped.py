@@ -290,3 +290,50 @@ def test_grouped_over_e4m3_codes(dtype, hq, hkv, hd, bs, width, build, part_tile
     assert np.isfinite(got).all()
     err = float(np.abs(got - want).max())
     assert err <= TOL[dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("name", ["sharing_fp16", "beam_search_fp16"])
+def test_full_size_grouped_over_e4m3(name):
+    """The sharing and beam batches at full size with 8-bit pools (every slot
+    quantised by the library's cache write), decoded by the grouped call;
+    sampled sequences (the longest, the shortest, seeded others; all heads)
+    against the oracle's decode over the same codes."""
+    from oracle import fp8
+    from gpu_helpers import compact_pool
+    say("full-size grouped e4m3 build", name)
+    wl = workloads.make(name, device=DEV)
+    nb, hkv, bs, hd = wl.k_cache.shape
+    k_scale = float(wl.k_cache.abs().amax().float()) / 448
+    v_scale = float(wl.v_cache.abs().amax().float()) / 448
+    kc = torch.empty((nb, hkv, bs, hd), dtype=torch.uint8, device=DEV)
+    vc = torch.empty_like(kc)
+    for b0 in range(0, nb, 1024):
+        b1 = min(nb, b0 + 1024)
+        rk = wl.k_cache[b0:b1].permute(0, 2, 1, 3).reshape(-1, hkv, hd).contiguous()
+        rv = wl.v_cache[b0:b1].permute(0, 2, 1, 3).reshape(-1, hkv, hd).contiguous()
+        pk.reshape_and_cache_fp8(rk, rv, kc, vc,
+                                 torch.arange(b0 * bs, b1 * bs, dtype=torch.int64, device=DEV),
+                                 k_scale, v_scale)
+    torch.cuda.synchronize()
+    L = wl.context_lens
+    rng = np.random.default_rng(wl.seed)
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L))} |
+                  {int(s) for s in rng.choice(wl.num_seqs, 6, replace=False)})
+    wl_codes = workloads.Workload(**{**wl.__dict__, "k_cache": kc, "v_cache": vc})
+    kcs, vcs, tables = compact_pool(wl_codes, seqs)
+    want = fp8.decode_fp8(wl.q.cpu(), kcs.numpy(), vcs.numpy(), tables, L, wl.scale, k_scale,
+                          v_scale, wl.num_kv_heads, seqs=seqs)
+    groups = bmod.share_groups(wl.block_tables, L, 16)
+    members, tiles, start, longest = _lists(wl.block_tables, L, groups, bs, 16)
+    for part_tiles in (0, 32):
+        say("full-size grouped e4m3 decode", name, part_tiles)
+        out = torch.empty_like(wl.q)
+        pk.paged_attention_decode_grouped(out, wl.q, kc, vc, torch.from_numpy(L).to(DEV),
+                                          members, tiles, start, wl.scale, wl.max_context_len,
+                                          part_tiles=part_tiles, max_group_tiles=longest,
+                                          k_scale=k_scale, v_scale=v_scale)
+        torch.cuda.synchronize()
+        got = out.cpu().double().numpy()[seqs]
+        assert np.isfinite(got).all()
+        err = float(np.abs(got - want[seqs]).max())
+        assert err <= TOL[wl.dtype], f"{name} parts {part_tiles}: max abs err {err}"
