@@ -22,7 +22,8 @@
 // Per column: tokens at or past the member's length, and tiles outside its
 // mask, get probability zero.  Value rows that no member of the tile reaches
 // are zeroed before the product, so unwritten slots cannot reach a result.
-// The four waves take tiles round-robin and merge in LDS.  A group's list
+// The waves (four, or eight over 8-bit codes) take tiles round-robin and
+// merge in LDS.  A group's list
 // may be cut into parts (grid z) whose (max, sum, output) states a second
 // kernel merges; the cache may hold E4M3 codes.
 #include "common.h"
@@ -53,14 +54,14 @@ __device__ inline int group_range(const GroupedArgs& a, int grp, int part, int& 
   return nparts;
 }
 
-template <int HD>
+template <int HD, int NW>
 struct GroupShared {
   static constexpr int OS = HD + 4;   // padded row stride of the output tiles
   u32x4 q[HD / 32][kWave];
-  float m[4][kCols], l[4][kCols];
-  __attribute__((aligned(16))) float o[4][kCols][OS];
+  float m[NW][kCols], l[NW][kCols];
+  __attribute__((aligned(16))) float o[NW][kCols][OS];
   int seq[kCols];   // sequence of each column, -1 for none
-  int bad[4];
+  int bad[NW];
 };
 
 // Largest value of v over the 16 lanes of each 16-lane row.
@@ -75,8 +76,8 @@ __device__ inline int row16_max(int v) {
 // C is the cache element: E itself, or E4M3 codes (loaded at half width and
 // widened to E's 16-bit values right before the products; the K scale is in
 // scale_log2e, the V scale multiplies the merged output).
-template <typename E, typename C, int HD, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
+template <typename E, typename C, int HD, int BS, int NW = 4>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void
 decode_grouped_kernel(GroupedArgs a) {
   using T = typename C::storage;       // cache element
   using Q = typename E::storage;       // query / output element
@@ -89,10 +90,9 @@ decode_grouped_kernel(GroupedArgs a) {
   constexpr int VL = k8 ? VW / 2 : VW;           // dwords of V loaded per lane per token
   constexpr int TPB = BS / 16;         // tiles per block
   static_assert(!k8 || KSTEPS % 2 == 0, "8-bit K loads cover two k-steps");
-  constexpr int NW = 4;
   constexpr int NS = 2;                // register stages of the tile pipeline
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
-  __shared__ GroupShared<HD> sm;
+  __shared__ GroupShared<HD, NW> sm;
 
   const int g = blockIdx.x, grp = blockIdx.y, part = blockIdx.z;
   // the group's rows of the list, clamped to the list (any offsets stay in
@@ -295,7 +295,9 @@ decode_grouped_kernel(GroupedArgs a) {
   if (lane == 0) sm.bad[wave] = any_bad;
   __syncthreads();
 
-  const int all_bad = sm.bad[0] | sm.bad[1] | sm.bad[2] | sm.bad[3];
+  int all_bad = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) all_bad |= sm.bad[w];
   for (int idx = tid; idx < kCols * (HD / 4); idx += NW * kWave) {
     const int col = idx / (HD / 4), d = (idx % (HD / 4)) * 4;
     const int s = sm.seq[col];
@@ -379,12 +381,15 @@ __global__ __launch_bounds__(256) void grouped_merge_kernel(GroupedArgs a) {
   }
 }
 
+// Eight waves per workgroup over 8-bit codes (half the bytes per tile: twice
+// the waves keep as many bytes in flight per item), four otherwise.
 template <typename E, typename C, int HD>
 hipError_t launch_hd(int bs, const GroupedArgs& a, hipStream_t st) {
+  constexpr int NW = sizeof(typename C::storage) == 1 ? 8 : 4;
   const dim3 grid(a.num_kv_heads, a.num_groups, a.max_parts);
   switch (bs) {
-    case 16: hipLaunchKernelGGL((decode_grouped_kernel<E, C, HD, 16>), grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((decode_grouped_kernel<E, C, HD, 32>), grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_grouped_kernel<E, C, HD, 16, NW>), grid, dim3(NW * 64), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((decode_grouped_kernel<E, C, HD, 32, NW>), grid, dim3(NW * 64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
