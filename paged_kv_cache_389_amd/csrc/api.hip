@@ -726,17 +726,14 @@ int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_ca
 
 // Both grouped decode entry points: kv_fp8 says the caches hold E4M3 codes
 // with the given scales (ignored otherwise).
-int grouped_impl(void* out, const void* q, const void* k_cache,
-                                       const void* v_cache, const int32_t* context_lens,
-                                       const int32_t* group_members, const int32_t* group_tiles,
-                                       const int32_t* group_tile_start, int num_tiles,
-                                       float scale, int num_seqs, int num_groups, int max_members,
-                                       int num_q_heads, int num_kv_heads, int head_dim,
-                                       int block_size, int num_blocks, int max_context_len,
-                                       int dtype, bool kv_fp8, float k_scale, float v_scale,
-                                       int part_tiles, int max_group_tiles,
-                                       void* workspace, size_t workspace_bytes,
-                                       void* begin_event, void* end_event, void* stream) {
+int grouped_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* context_lens, const int32_t* group_members,
+                 const int32_t* group_tiles, const int32_t* group_tile_start, int num_tiles,
+                 float scale, int num_seqs, int num_groups, int max_members, int num_q_heads,
+                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                 int max_context_len, int dtype, bool kv_fp8, float k_scale, float v_scale,
+                 int part_tiles, int max_group_tiles, void* workspace, size_t workspace_bytes,
+                 void* begin_event, void* end_event, void* stream) {
   if (!dtype_ok(dtype) || num_seqs < 0 || num_groups < 0 || max_members <= 0 || num_tiles < 0 ||
       num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads || part_tiles < 0 ||
@@ -750,7 +747,8 @@ int grouped_impl(void* out, const void* q, const void* k_cache,
   if (reinterpret_cast<uintptr_t>(group_tiles) % 16) return PKV_EINVAL;
   const Elem e = to_elem(dtype);
   const int group = num_q_heads / num_kv_heads;
-  if (!grouped_supported(e, head_dim, block_size) || max_members * group > 16 ||
+  if (!grouped_supported(e, head_dim, block_size) || max_members > 16 ||
+      (int64_t)max_members * group > 16 ||
       num_groups > kMaxGridYZ || num_kv_heads > kMaxGridYZ)
     return PKV_EUNSUPPORTED;
   const GroupedLayout lo = grouped_layout(num_groups, num_kv_heads, head_dim, part_tiles,

@@ -275,3 +275,50 @@ def test_prefill_fp8_rejects_bad_scales(native):
     assert f(*head, 0.0, 1.0, *tail) == -1
     assert f(*head, 1.0, float("inf"), *tail) == -1
     assert f(*head, 1.0, 1.0, *tail[:-4], 0, None, None, None) == -2   # no float32 prefill
+
+
+def _grouped(lib, fp8=False, **over):
+    a = dict(out=16, q=16, k=16, v=16, lens=16, members=16, tiles=256, start=16, num_tiles=8,
+             scale=0.1, ks=0.01, vs=0.01, B=8, groups=2, M=4, Hq=8, Hkv=2, hd=128, bs=16,
+             nb=64, maxL=512, dtype=1, part=0, maxg=8, ws=None, wsb=0)
+    a.update(over)
+    head = (a["out"], a["q"], a["k"], a["v"], a["lens"], a["members"], a["tiles"], a["start"],
+            a["num_tiles"], ctypes.c_float(a["scale"]))
+    tail = (a["B"], a["groups"], a["M"], a["Hq"], a["Hkv"], a["hd"], a["bs"], a["nb"], a["maxL"],
+            a["dtype"], a["part"], a["maxg"], a["ws"], a["wsb"], None, None, None)
+    if fp8:
+        return lib.pkv_paged_attention_decode_grouped_fp8(
+            *head, ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]), *tail)
+    return lib.pkv_paged_attention_decode_grouped(*head, *tail)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(M=5), -2),                 # 5 members x 4 heads > 16 columns
+    (dict(M=1 << 30), -2),           # no overflow of members x heads
+    (dict(dtype=0), -2),             # fp32 has no grouped kernel
+    (dict(hd=96), -2),
+    (dict(bs=8), -2),
+    (dict(groups=65536), -2),
+    (dict(tiles=264), -1),           # not 16-byte aligned
+    (dict(num_tiles=-1), -1),
+    (dict(M=0), -1),
+    (dict(Hq=7), -1),
+    (dict(members=None), -1),
+    (dict(part=-2), -1),
+    (dict(part=4, maxg=100), -3),    # parts need a workspace
+])
+def test_grouped_rejects_bad_arguments_before_launch(native, over, status):
+    assert _grouped(native.lib, **over) == status
+
+
+def test_grouped_empty_and_fp8_scales(native):
+    lib = native.lib
+    assert _grouped(lib, groups=0, out=None) == 0
+    assert _grouped(lib, B=0, out=None) == 0
+    assert _grouped(lib, fp8=True, ks=0.0) == -1
+    assert _grouped(lib, fp8=True, vs=float("inf")) == -1
+    ws = lib.pkv_paged_attention_grouped_workspace_bytes
+    assert ws(2, 2, 128, 0, 100) == 0                     # whole groups: no workspace
+    assert ws(2, 2, 128, 8, 8) == 0                       # one part each
+    assert ws(2, 2, 128, 8, 100) == 2 * 13 * 2 * 16 * (128 + 2) * 4
+    assert ws(-1, 2, 128, 8, 100) == ctypes.c_size_t(-1).value
