@@ -28,6 +28,7 @@ CPU implementation.
 _NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "swap_blocks",
            "reshape_and_cache_fp8", "paged_attention_decode_fp8", "KV_E4M3",
            "paged_attention_prefill", "paged_attention_decode_grouped", "grouped_workspace_bytes",
+           "group_tiles",
            "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
            "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")

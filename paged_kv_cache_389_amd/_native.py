@@ -107,6 +107,9 @@ def _load():
     lib.pkv_paged_attention_decode_grouped_fp8.argtypes = [
         vp, vp, vp, vp, i32p, i32p, i32p, i32p, i32, f32, f32, f32, i32, i32, i32, i32, i32, i32,
         i32, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
+    lib.pkv_group_tiles.restype = i32
+    lib.pkv_group_tiles.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32p, i32,
+                                    i32p, vp]
     lib.pkv_paged_attention_grouped_workspace_bytes.restype = sz
     lib.pkv_paged_attention_grouped_workspace_bytes.argtypes = [i32] * 5
     return lib
@@ -123,7 +126,7 @@ EXPORTED = (
     "pkv_reshape_and_cache_fp8", "pkv_paged_attention_decode_fp8",
     "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_fp8",
     "pkv_paged_attention_decode_grouped", "pkv_paged_attention_decode_grouped_fp8",
-    "pkv_paged_attention_grouped_workspace_bytes",
+    "pkv_paged_attention_grouped_workspace_bytes", "pkv_group_tiles",
 )
 
 
@@ -454,6 +457,45 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
             st = lib.pkv_paged_attention_prefill(*head, num_seqs, total_q, *common)
     _check("paged_attention_prefill", st)
     return out
+
+
+def group_tiles(block_tables, context_lens, group_members, block_size, max_context_len,
+                tiles=None, tile_start=None, stream=None):
+    """The grouped decode's tile lists built on the device from the block
+    tables (``pkv_group_tiles``): returns ``(tiles, tile_start)``, int32
+    ``[capacity, 4]`` and ``[G + 1]``; rows from ``tile_start[-1]`` on are
+    unused.  ``tiles`` / ``tile_start`` may be given (reused buffers); by
+    default ``tiles`` holds ``num_seqs * ceil(max_context_len / 16)`` rows,
+    always enough."""
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (group_members, "group_members")):
+        _dev(t, n)
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    if block_tables.dim() != 2 or group_members.dim() != 2:
+        raise ValueError("block_tables and group_members must be 2-D")
+    num_seqs, max_blocks = block_tables.shape
+    if context_lens.shape != (num_seqs,):
+        raise ValueError("context_lens must be [num_seqs]")
+    num_groups, max_members = group_members.shape
+    if tiles is None:
+        rows = max(1, num_seqs * -(-int(max_context_len) // 16))
+        tiles = torch.empty((rows, 4), dtype=torch.int32, device=block_tables.device)
+    if tile_start is None:
+        tile_start = torch.empty(num_groups + 1, dtype=torch.int32, device=block_tables.device)
+    if tiles.dtype != torch.int32 or tiles.dim() != 2 or tiles.shape[1] != 4:
+        raise ValueError("tiles must be int32 [capacity, 4]")
+    if tile_start.dtype != torch.int32 or tile_start.shape != (num_groups + 1,):
+        raise ValueError("tile_start must be int32 [num_groups + 1]")
+    _dev(tiles, "tiles")
+    _dev(tile_start, "tile_start")
+    with torch.cuda.device(block_tables.device):
+        st = lib.pkv_group_tiles(_ptr(block_tables), _ptr(context_lens), _ptr(group_members),
+                                 num_seqs, max_blocks, num_groups, max_members, int(block_size),
+                                 int(max_context_len), _ptr(tiles), tiles.shape[0],
+                                 _ptr(tile_start), _stream(block_tables, stream))
+    _check("group_tiles", st)
+    return tiles, tile_start
 
 
 def grouped_workspace_bytes(num_groups, num_kv_heads, head_dim, part_tiles, max_group_tiles):

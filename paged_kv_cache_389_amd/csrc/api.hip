@@ -834,6 +834,29 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cach
                       max_context_len, dtype, begin_event, end_event, stream);
 }
 
+int pkv_group_tiles(const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* group_members, int num_seqs, int max_blocks_per_seq,
+                    int num_groups, int max_members, int block_size, int max_context_len,
+                    int32_t* group_tiles, int tiles_capacity, int32_t* group_tile_start,
+                    void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_groups < 0 || max_members <= 0 ||
+      block_size <= 0 || max_context_len < 0 || tiles_capacity < 0)
+    return PKV_EINVAL;
+  if (max_members > 16 || block_size % 16 || num_groups > group_tiles_max_groups())
+    return PKV_EUNSUPPORTED;
+  if (!group_tile_start || (num_groups > 0 && (!group_members || !block_tables ||
+                                               !context_lens || !group_tiles)))
+    return PKV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(group_tiles) % 16) return PKV_EINVAL;
+  const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+  const int len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
+  hipError_t err = launch_build_group_tiles(block_tables, context_lens, group_members, num_seqs,
+                                            max_blocks_per_seq, num_groups, max_members,
+                                            block_size, len_cap, group_tiles, tiles_capacity,
+                                            group_tile_start, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : fail_hip(err);
+}
+
 size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_heads,
                                                    int head_dim, int part_tiles,
                                                    int max_group_tiles) {

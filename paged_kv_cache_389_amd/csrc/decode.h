@@ -180,6 +180,15 @@ bool grouped_supported(Elem e, int head_dim, int block_size);
 hipError_t launch_decode_grouped(Elem e, bool kv_fp8, int head_dim, int block_size,
                                  const GroupedArgs& a, hipStream_t stream);
 hipError_t launch_grouped_merge(Elem e, int head_dim, const GroupedArgs& a, hipStream_t stream);
+// The grouped decode's tile lists from the block tables (group_tiles.hip):
+// one workgroup; at most group_tiles_max_groups() groups; rows past `cap`
+// are not written.
+int group_tiles_max_groups();
+hipError_t launch_build_group_tiles(const int32_t* block_tables, const int32_t* context_lens,
+                                    const int32_t* members, int num_seqs, int max_blocks,
+                                    int num_groups, int max_members, int block_size, int len_cap,
+                                    int32_t* tiles, int cap, int32_t* tile_start,
+                                    hipStream_t stream);
 // Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
 // chunks per KV head and sequence).
 int prefill_tokens_per_workgroup(int group);

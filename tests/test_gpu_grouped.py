@@ -337,3 +337,85 @@ def test_full_size_grouped_over_e4m3(name):
         assert np.isfinite(got).all()
         err = float(np.abs(got - want[seqs]).max())
         assert err <= TOL[wl.dtype], f"{name} parts {part_tiles}: max abs err {err}"
+
+
+# ------------------------------------------------ lists built on the device
+
+def _device_lists(tables, lens, groups, bs, max_members, max_len, cap=None):
+    members = np.full((len(groups), max_members), -1, np.int32)
+    for j, g in enumerate(groups):
+        members[j, :len(g)] = g
+    t = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).to(DEV)
+    l = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to(DEV)
+    m = torch.from_numpy(members).to(DEV)
+    tiles = None if cap is None else torch.full((cap, 4), -7, dtype=torch.int32, device=DEV)
+    tiles, start = pk.group_tiles(t, l, m, bs, max_len, tiles=tiles)
+    torch.cuda.synchronize()
+    return members, tiles.cpu().numpy(), start.cpu().numpy()
+
+
+def _same_as_host(tables, lens, groups, bs, max_members, max_len):
+    hm, ht, hs = bmod.group_tiles(tables, lens, groups, bs, max_members)
+    dm, dt, ds = _device_lists(tables, lens, groups, bs, max_members, max_len)
+    assert np.array_equal(hm, dm)
+    assert np.array_equal(hs, ds), (hs[:8], ds[:8])
+    assert np.array_equal(ht, dt[:hs[-1]])
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("build", ["sharing", "beam", "unrelated"])
+def test_device_lists_equal_host_lists(build, bs):
+    say("device lists", build, bs)
+    if build == "sharing":
+        wl = workloads.build_sharing(num_prompts=7, fanout=6, prompt_len=90, max_gen=70,
+                                     block_size=bs, num_blocks=1024, seed=bs, tensors=False)
+    elif build == "beam":
+        wl = workloads.build_beam_search(num_requests=6, beam_width=5, prompt_lens=(3, 120),
+                                         steps=30, block_size=bs, num_blocks=1024, seed=bs + 1,
+                                         tensors=False)
+    else:
+        rng = np.random.default_rng(bs)
+        lens = np.r_[0, 1, 15, 16, 17, rng.integers(0, 400, 35)].astype(np.int32)
+        width = -(-400 // bs) + 1
+        tables = rng.integers(-3, 5000, (len(lens), width)).astype(np.int32)  # any entries
+        order = rng.permutation(len(lens))
+        groups = [list(map(int, order[i:i + 3])) for i in range(0, len(order), 3)]
+        _same_as_host(tables, lens, groups, bs, 3, 400)
+        return
+    for mm in (16, 4):
+        groups = bmod.share_groups(wl.block_tables, wl.context_lens, mm)
+        _same_as_host(wl.block_tables, wl.context_lens, groups, bs, mm,
+                      int(wl.context_lens.max()))
+
+
+def test_device_lists_many_groups_empty_groups_and_capacity():
+    say("device lists: many groups")
+    rng = np.random.default_rng(9)
+    n = 4096
+    lens = rng.integers(0, 70, n).astype(np.int32)
+    lens[::7] = 0                                   # empty groups, some at the ends
+    lens[-1] = 0
+    tables = rng.integers(0, 100000, (n, 5)).astype(np.int32)
+    groups = [[s] for s in range(n)]
+    _same_as_host(tables, lens, groups, 16, 1, 80)
+    # a capacity below the rows: nothing written past it, the offsets still count every row
+    hm, ht, hs = bmod.group_tiles(tables, lens, groups, 16, 1)
+    cap = int(hs[-1]) // 2
+    _, dt, ds = _device_lists(tables, lens, groups, 16, 1, 80, cap=cap)
+    assert np.array_equal(ds, hs)
+    assert np.array_equal(dt, ht[:cap])
+
+
+def test_grouped_decode_from_device_lists():
+    say("grouped decode from device lists")
+    wl = workloads.make("sharing_fp16", device=DEV)
+    groups = bmod.share_groups(wl.block_tables, wl.context_lens, 16)
+    host = _lists(wl.block_tables, wl.context_lens, groups, wl.block_size, 16)
+    members, tiles_d, start_d = host[0], *pk.group_tiles(
+        torch.from_numpy(wl.block_tables).to(DEV), torch.from_numpy(wl.context_lens).to(DEV),
+        host[0], wl.block_size, wl.max_context_len)
+    lens_d = torch.from_numpy(wl.context_lens).to(DEV)
+    a = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, host, wl.scale, wl.max_context_len)
+    b = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, (members, tiles_d, start_d, host[3]),
+                 wl.scale, wl.max_context_len)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
