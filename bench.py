@@ -275,9 +275,11 @@ def quantise_pools(wl, dev):
 
 
 def grouped_lists(wl, dev, part_tiles=-1):
-    """Inputs of the grouped decode call (host set-up, not timed): sequences
-    sharing their first block in groups of at most 16 / G, the groups' tile
-    lists, and the part size (-1: chosen from the list)."""
+    """Inputs of the grouped decode call: sequences sharing their first block
+    in groups of at most 16 / G (host set-up, not timed), the groups' tile
+    lists from the host builder (for sizes; every timed step rebuilds them on
+    the device with pkv_group_tiles), and the part size (-1: chosen from the
+    list)."""
     from paged_kv_cache_389_amd import block_manager as bmod
     g = wl.num_q_heads // wl.num_kv_heads
     t0 = time.perf_counter()
@@ -288,6 +290,9 @@ def grouped_lists(wl, dev, part_tiles=-1):
     if tiles.shape[0] == 0:
         tiles = np.zeros((1, 4), np.int32)
     max_group_tiles = int(np.diff(start).max(initial=0))
+    # room for every list the device builder can make from these tables
+    cap = max(1, wl.num_seqs * -(-wl.max_context_len // 16))
+    tiles = np.concatenate([tiles, np.zeros((cap - tiles.shape[0], 4), np.int32)])
     if part_tiles < 0:
         # whole groups (no merge) unless groups x KV heads leave CUs idle; then
         # parts for about one round of resident workgroups (4 per CU).  Measured on
@@ -341,6 +346,11 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
             else:
                 pk.reshape_and_cache(dev["new_k"], dev["new_v"], dev["k"], dev["v"],
                                      dev["slots"])
+        if dev.get("groups") is not None:
+            # the step's tile lists, built on the device from the block tables
+            pk.group_tiles(dev["tables"], dev["lens"], dev["groups"][0], wl.block_size,
+                           wl.max_context_len, tiles=dev["groups"][1],
+                           tile_start=dev["groups"][2])
         if whole_call:
             ev[i][0].record()
         if dev.get("groups") is not None:
@@ -684,6 +694,7 @@ def bench_one(name, args, with_cpu):
         line["config"]["kernel"] = "grouped"
         line["config"]["grid"] = "groups x kv heads x parts"
         line["config"]["part_tiles"] = grouped["part_tiles"]
+        line["config"]["lists"] = "built on the device every step (group_tiles, timed)"
         line["grouped"] = grouped
         line["roofline"]["basis"] = "unique K/V bytes (each distinct tile once)"
     if name in ("sharing_fp16", "beam_search_fp16"):

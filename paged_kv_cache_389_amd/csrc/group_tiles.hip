@@ -76,14 +76,27 @@ __device__ inline int member_tiles(const BuildArgs& a, int s) {
   return (L + 15) / 16;
 }
 
+constexpr int kCacheSlots = 4096;   // (group, member) places cached in LDS
+
 template <int GMAX>
 __global__ __launch_bounds__(kBuildThreads) void build_group_tiles_kernel(BuildArgs a) {
   __shared__ int item_start[GMAX + 1];   // prefix of the groups' tile counts
   __shared__ int wave_sums[kBuildThreads / kWave];
   __shared__ int total;
+  // when every (group, member) place fits: its sequence and tile count, so
+  // that phase 2 reads only table entries from global memory
+  __shared__ int cache_seq[kCacheSlots], cache_tiles[kCacheSlots];
   const int tid = threadIdx.x;
   const int G = a.num_groups, M = a.max_members;
   const int tpb = a.block_size / 16;
+  const bool cached = (int64_t)G * M <= kCacheSlots;
+  if (cached)
+    for (int k = tid; k < G * M; k += kBuildThreads) {
+      const int s = member_seq(a, k / M, k % M);
+      cache_seq[k] = s;
+      cache_tiles[k] = member_tiles(a, s);
+    }
+  __syncthreads();
 
   // phase 1: T_j, scanned over the groups in chunks of one per thread
   int run = 0;
@@ -91,7 +104,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_group_tiles_kernel(BuildA
     const int j = j0 + tid;
     int T = 0;
     if (j < G)
-      for (int m = 0; m < M; ++m) T = max(T, member_tiles(a, member_seq(a, j, m)));
+      for (int m = 0; m < M; ++m)
+        T = max(T, cached ? cache_tiles[j * M + m] : member_tiles(a, member_seq(a, j, m)));
     const int ex = block_scan(T, wave_sums, &total);
     if (j < G) item_start[j] = run + ex;
     run += total;   // every thread reads the same total
@@ -123,8 +137,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_group_tiles_kernel(BuildA
       blk[m] = 0;
       on[m] = false;
       if (j >= 0 && m < M) {
-        const int s = member_seq(a, j, m);
-        if (t < member_tiles(a, s)) {
+        const int s = cached ? cache_seq[j * M + m] : member_seq(a, j, m);
+        if (t < (cached ? cache_tiles[j * M + m] : member_tiles(a, s))) {
           on[m] = true;
           blk[m] = a.block_tables[(size_t)s * a.max_blocks + min(t / tpb, a.max_blocks - 1)];
         }

@@ -322,3 +322,22 @@ def test_grouped_empty_and_fp8_scales(native):
     assert ws(2, 2, 128, 8, 8) == 0                       # one part each
     assert ws(2, 2, 128, 8, 100) == 2 * 13 * 2 * 16 * (128 + 2) * 4
     assert ws(-1, 2, 128, 8, 100) == ctypes.c_size_t(-1).value
+
+
+def test_group_tiles_rejects_bad_arguments(native):
+    f = native.lib.pkv_group_tiles
+    ok = dict(t=16, l=16, m=16, B=8, W=4, G=2, M=4, bs=16, L=64, tiles=256, cap=32, start=16)
+
+    def call(**over):
+        a = {**ok, **over}
+        return f(a["t"], a["l"], a["m"], a["B"], a["W"], a["G"], a["M"], a["bs"], a["L"],
+                 a["tiles"], a["cap"], a["start"], None)
+
+    assert call(M=17) == -2
+    assert call(bs=24) == -2
+    assert call(G=4097) == -2
+    assert call(tiles=264) == -1      # not 16-byte aligned
+    assert call(start=None) == -1
+    assert call(t=None) == -1
+    assert call(cap=-1) == -1
+    assert call(M=0) == -1

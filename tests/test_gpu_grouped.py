@@ -398,6 +398,9 @@ def test_device_lists_many_groups_empty_groups_and_capacity():
     tables = rng.integers(0, 100000, (n, 5)).astype(np.int32)
     groups = [[s] for s in range(n)]
     _same_as_host(tables, lens, groups, 16, 1, 80)
+    # groups x places past the builder's LDS cache (global reads instead)
+    pairs = [[s, s + 1] for s in range(0, 600, 2)]
+    _same_as_host(tables, lens, pairs, 16, 16, 80)
     # a capacity below the rows: nothing written past it, the offsets still count every row
     hm, ht, hs = bmod.group_tiles(tables, lens, groups, 16, 1)
     cap = int(hs[-1]) // 2
