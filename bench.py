@@ -290,9 +290,6 @@ def grouped_lists(wl, dev, part_tiles=-1):
     if tiles.shape[0] == 0:
         tiles = np.zeros((1, 4), np.int32)
     max_group_tiles = int(np.diff(start).max(initial=0))
-    # room for every list the device builder can make from these tables
-    cap = max(1, wl.num_seqs * -(-wl.max_context_len // 16))
-    tiles = np.concatenate([tiles, np.zeros((cap - tiles.shape[0], 4), np.int32)])
     if part_tiles < 0:
         # whole groups (no merge) unless groups x KV heads leave CUs idle; then
         # parts for about one round of resident workgroups (4 per CU).  Measured on
@@ -301,7 +298,12 @@ def grouped_lists(wl, dev, part_tiles=-1):
         part_tiles = 0 if wgs >= 256 else max(8, -(-int(start[-1]) * wl.num_kv_heads // 1024))
     if dev is not None and torch.cuda.is_available():
         from paged_kv_cache_389_amd import _native as pk
-        dev["groups"] = tuple(torch.from_numpy(x).cuda() for x in (members, tiles, start))
+        # the device builder's buffers: group j's rows from j * stride, start / end per group
+        d_tiles, d_start, d_end = pk.group_tiles(
+            torch.from_numpy(wl.block_tables).cuda(), torch.from_numpy(wl.context_lens).cuda(),
+            torch.from_numpy(members).cuda(), wl.block_size, wl.max_context_len)
+        dev["groups"] = (torch.from_numpy(members).cuda(), d_tiles, d_start)
+        dev["group_end"] = d_end
         dev["group_part"] = (part_tiles, max_group_tiles)
         need = pk.grouped_workspace_bytes(len(groups), wl.num_kv_heads, wl.head_dim, part_tiles,
                                           max_group_tiles)
@@ -350,7 +352,7 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
             # the step's tile lists, built on the device from the block tables
             pk.group_tiles(dev["tables"], dev["lens"], dev["groups"][0], wl.block_size,
                            wl.max_context_len, tiles=dev["groups"][1],
-                           tile_start=dev["groups"][2])
+                           tile_start=dev["groups"][2], tile_end=dev["group_end"])
         if whole_call:
             ev[i][0].record()
         if dev.get("groups") is not None:
@@ -360,6 +362,7 @@ def run_gpu(wl, dev, steps, warmup, partition, path, grid):
                                               part_tiles=dev["group_part"][0],
                                               max_group_tiles=dev["group_part"][1],
                                               workspace=dev["group_ws"],
+                                              group_tile_end=dev["group_end"],
                                               kernel_events=None if i is None or whole_call
                                               else kev[i],
                                               **({"k_scale": dev["k_scale"],

@@ -101,15 +101,17 @@ def _load():
         i32, i32, i32, vp, vp, vp]
     lib.pkv_paged_attention_decode_grouped.restype = i32
     lib.pkv_paged_attention_decode_grouped.argtypes = [
-        vp, vp, vp, vp, i32p, i32p, i32p, i32p, i32, f32, i32, i32, i32, i32, i32, i32, i32, i32,
-        i32, i32, i32, i32, vp, sz, vp, vp, vp]
+        vp, vp, vp, vp, i32p, i32p, i32p, i32p, i32p, i32, f32, i32, i32, i32, i32, i32, i32,
+        i32, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
     lib.pkv_paged_attention_decode_grouped_fp8.restype = i32
     lib.pkv_paged_attention_decode_grouped_fp8.argtypes = [
-        vp, vp, vp, vp, i32p, i32p, i32p, i32p, i32, f32, f32, f32, i32, i32, i32, i32, i32, i32,
-        i32, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
+        vp, vp, vp, vp, i32p, i32p, i32p, i32p, i32p, i32, f32, f32, f32, i32, i32, i32, i32,
+        i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, vp, vp]
     lib.pkv_group_tiles.restype = i32
     lib.pkv_group_tiles.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32p, i32,
-                                    i32p, vp]
+                                    i32p, i32p, vp]
+    lib.pkv_group_tiles_capacity.restype = sz
+    lib.pkv_group_tiles_capacity.argtypes = [i32] * 5
     lib.pkv_paged_attention_grouped_workspace_bytes.restype = sz
     lib.pkv_paged_attention_grouped_workspace_bytes.argtypes = [i32] * 5
     return lib
@@ -126,7 +128,7 @@ EXPORTED = (
     "pkv_reshape_and_cache_fp8", "pkv_paged_attention_decode_fp8",
     "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_fp8",
     "pkv_paged_attention_decode_grouped", "pkv_paged_attention_decode_grouped_fp8",
-    "pkv_paged_attention_grouped_workspace_bytes", "pkv_group_tiles",
+    "pkv_paged_attention_grouped_workspace_bytes", "pkv_group_tiles", "pkv_group_tiles_capacity",
 )
 
 
@@ -460,13 +462,12 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
 
 
 def group_tiles(block_tables, context_lens, group_members, block_size, max_context_len,
-                tiles=None, tile_start=None, stream=None):
+                tiles=None, tile_start=None, tile_end=None, stream=None):
     """The grouped decode's tile lists built on the device from the block
-    tables (``pkv_group_tiles``): returns ``(tiles, tile_start)``, int32
-    ``[capacity, 4]`` and ``[G + 1]``; rows from ``tile_start[-1]`` on are
-    unused.  ``tiles`` / ``tile_start`` may be given (reused buffers); by
-    default ``tiles`` holds ``num_seqs * ceil(max_context_len / 16)`` rows,
-    always enough."""
+    tables (``pkv_group_tiles``): returns ``(tiles, tile_start, tile_end)``,
+    int32 ``[capacity, 4]``, ``[G]`` and ``[G]`` (group j's rows are
+    ``tiles[tile_start[j]:tile_end[j]]``; pass all three to
+    :func:`paged_attention_decode_grouped`).  Buffers may be given for reuse."""
     for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
                  (group_members, "group_members")):
         _dev(t, n)
@@ -478,24 +479,31 @@ def group_tiles(block_tables, context_lens, group_members, block_size, max_conte
     if context_lens.shape != (num_seqs,):
         raise ValueError("context_lens must be [num_seqs]")
     num_groups, max_members = group_members.shape
+    need = lib.pkv_group_tiles_capacity(num_groups, max_members, int(block_size), max_blocks,
+                                        int(max_context_len))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for group_tiles")
+    dev = block_tables.device
     if tiles is None:
-        rows = max(1, num_seqs * -(-int(max_context_len) // 16))
-        tiles = torch.empty((rows, 4), dtype=torch.int32, device=block_tables.device)
+        tiles = torch.empty((max(need, 1), 4), dtype=torch.int32, device=dev)
     if tile_start is None:
-        tile_start = torch.empty(num_groups + 1, dtype=torch.int32, device=block_tables.device)
+        tile_start = torch.empty(max(num_groups, 1), dtype=torch.int32, device=dev)
+    if tile_end is None:
+        tile_end = torch.empty(max(num_groups, 1), dtype=torch.int32, device=dev)
     if tiles.dtype != torch.int32 or tiles.dim() != 2 or tiles.shape[1] != 4:
         raise ValueError("tiles must be int32 [capacity, 4]")
-    if tile_start.dtype != torch.int32 or tile_start.shape != (num_groups + 1,):
-        raise ValueError("tile_start must be int32 [num_groups + 1]")
+    for t, n in ((tile_start, "tile_start"), (tile_end, "tile_end")):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] < num_groups:
+            raise ValueError(f"{n} must be int32 [num_groups]")
+        _dev(t, n)
     _dev(tiles, "tiles")
-    _dev(tile_start, "tile_start")
-    with torch.cuda.device(block_tables.device):
+    with torch.cuda.device(dev):
         st = lib.pkv_group_tiles(_ptr(block_tables), _ptr(context_lens), _ptr(group_members),
                                  num_seqs, max_blocks, num_groups, max_members, int(block_size),
                                  int(max_context_len), _ptr(tiles), tiles.shape[0],
-                                 _ptr(tile_start), _stream(block_tables, stream))
+                                 _ptr(tile_start), _ptr(tile_end), _stream(block_tables, stream))
     _check("group_tiles", st)
-    return tiles, tile_start
+    return tiles, tile_start, tile_end
 
 
 def grouped_workspace_bytes(num_groups, num_kv_heads, head_dim, part_tiles, max_group_tiles):
@@ -509,14 +517,18 @@ def grouped_workspace_bytes(num_groups, num_kv_heads, head_dim, part_tiles, max_
 def paged_attention_decode_grouped(out, q, k_cache, v_cache, context_lens, group_members,
                                    group_tiles, group_tile_start, scale, max_context_len,
                                    part_tiles=0, max_group_tiles=0, workspace=None,
-                                   stream=None, kernel_events=None, k_scale=None, v_scale=None):
+                                   stream=None, kernel_events=None, k_scale=None, v_scale=None,
+                                   group_tile_end=None):
     """Decode attention of sequences that share KV blocks, each shared tile
     read once for its whole group (``pkv_paged_attention_decode_grouped``).
     The rows of every grouped sequence equal :func:`paged_attention_decode`'s.
     ``group_members`` int32 ``[G, M]`` (-1 = empty), ``group_tiles`` int32
     ``[T, 4]`` (block, tile index, member mask, 0), ``group_tile_start`` int32
     ``[G + 1]``, all on the device; build them with
-    :func:`paged_kv_cache_389_amd.block_manager.group_tiles`.  With
+    :func:`paged_kv_cache_389_amd.block_manager.group_tiles` (a prefix
+    ``group_tile_start``), or on the device with :func:`group_tiles` (pass its
+    ``tile_start`` and ``tile_end`` as ``group_tile_start`` /
+    ``group_tile_end``).  With
     ``part_tiles > 0`` each group's list is cut into parts of that many rows
     (``max_group_tiles``: host bound of the groups' row counts) whose states a
     second kernel merges; ``workspace`` (uint8, device) is allocated when None.
@@ -554,8 +566,13 @@ def paged_attention_decode_grouped(out, q, k_cache, v_cache, context_lens, group
     if group_members.dim() != 2:
         raise ValueError("group_members must be [num_groups, max_members]")
     num_groups, max_members = group_members.shape
-    if group_tile_start.shape != (num_groups + 1,):
+    if group_tile_end is None and group_tile_start.shape != (num_groups + 1,):
         raise ValueError("group_tile_start must be [num_groups + 1]")
+    if group_tile_end is not None:
+        _dev(group_tile_end, "group_tile_end")
+        if group_tile_end.dtype != torch.int32 or group_tile_start.shape[0] < num_groups or \
+                group_tile_end.shape[0] < num_groups:
+            raise ValueError("group_tile_start / group_tile_end must be int32 [num_groups]")
     if group_tiles.dim() != 2 or group_tiles.shape[1] != 4:
         raise ValueError("group_tiles must be [total, 4]")
     need = grouped_workspace_bytes(num_groups, hkv, hd, int(part_tiles), int(max_group_tiles))
@@ -568,6 +585,7 @@ def paged_attention_decode_grouped(out, q, k_cache, v_cache, context_lens, group
             else (None, None)
         head = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(context_lens),
                 _ptr(group_members), _ptr(group_tiles), _ptr(group_tile_start),
+                _ptr(group_tile_end) if group_tile_end is not None else None,
                 int(group_tiles.shape[0]), ctypes.c_float(scale))
         tail = (num_seqs, num_groups, max_members, hq, hkv, hd, bs, nb, int(max_context_len),
                 _DTYPE_CODE[q.dtype], int(part_tiles), int(max_group_tiles), ws_ptr, ws_len,

@@ -155,25 +155,29 @@ int debug_check_pairs(const int64_t* pairs, int num_pairs, int num_src, int num_
 // for every member exactly one entry with its bit for each of its tiles
 // 0 .. ceil(L / 16) - 1 and none past them.
 int debug_check_groups(const int32_t* context_lens, const int32_t* members, const int32_t* tiles,
-                       const int32_t* tile_start, int num_tiles, int num_seqs, int num_groups,
-                       int max_members, int num_blocks, int64_t len_cap, int max_group_tiles,
-                       hipStream_t st) {
-  std::vector<int32_t> lens, mem, start, ent;
+                       const int32_t* tile_start, const int32_t* tile_end, int num_tiles,
+                       int num_seqs, int num_groups, int max_members, int num_blocks,
+                       int64_t len_cap, int max_group_tiles, hipStream_t st) {
+  std::vector<int32_t> lens, mem, start, end, ent;
   if (!fetch(lens, context_lens, num_seqs, st) ||
       !fetch(mem, members, (size_t)num_groups * max_members, st) ||
-      !fetch(start, tile_start, (size_t)num_groups + 1, st))
+      !fetch(start, tile_start, (size_t)num_groups + (tile_end ? 0 : 1), st) ||
+      (tile_end && !fetch(end, tile_end, (size_t)num_groups, st)))
     return PKV_EHIP;
-  if (start[0] != 0) return debug_fail("group_tile_start[0] != 0");
+  if (!tile_end) {   // a prefix: group j ends where group j + 1 starts
+    if (start[0] != 0) return debug_fail("group_tile_start[0] != 0");
+    end.assign(start.begin() + 1, start.end());
+    start.pop_back();
+  }
   for (int j = 0; j < num_groups; ++j) {
-    if (start[j + 1] < start[j])
-      return debug_fail("group_tile_start decreases at " + std::to_string(j));
-    if (max_group_tiles >= 0 && start[j + 1] - start[j] > max_group_tiles)
+    if (start[j] < 0 || end[j] < start[j] || end[j] > num_tiles)
+      return debug_fail("group " + std::to_string(j) + " rows [" + std::to_string(start[j]) +
+                        ", " + std::to_string(end[j]) + ") outside the " +
+                        std::to_string(num_tiles) + " rows of group_tiles");
+    if (max_group_tiles >= 0 && end[j] - start[j] > max_group_tiles)
       return debug_fail("group " + std::to_string(j) + " lists more than max_group_tiles rows");
   }
-  if (start[num_groups] > num_tiles)
-    return debug_fail("group_tile_start[num_groups] = " + std::to_string(start[num_groups]) +
-                      " past the " + std::to_string(num_tiles) + " rows of group_tiles");
-  if (!fetch(ent, tiles, (size_t)start[num_groups] * 4, st)) return PKV_EHIP;
+  if (!fetch(ent, tiles, (size_t)num_tiles * 4, st)) return PKV_EHIP;
   std::vector<char> seen(num_seqs, 0);
   for (int j = 0; j < num_groups; ++j) {
     std::vector<std::vector<int>> count(max_members);
@@ -188,7 +192,7 @@ int debug_check_groups(const int32_t* context_lens, const int32_t* members, cons
         return debug_fail("context_lens[" + std::to_string(s) + "] outside [0, len_cap]");
       count[m].assign((lens[s] + 15) / 16, 0);
     }
-    for (int i = start[j]; i < start[j + 1]; ++i) {
+    for (int i = start[j]; i < end[j]; ++i) {
       const int32_t b = ent[4 * (size_t)i], t = ent[4 * (size_t)i + 1], mask = ent[4 * (size_t)i + 2];
       if (b < 0 || b >= num_blocks)
         return debug_fail("group_tiles[" + std::to_string(i) + "] block outside the pool");
@@ -728,7 +732,8 @@ int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_ca
 // with the given scales (ignored otherwise).
 int grouped_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* context_lens, const int32_t* group_members,
-                 const int32_t* group_tiles, const int32_t* group_tile_start, int num_tiles,
+                 const int32_t* group_tiles, const int32_t* group_tile_start,
+                 const int32_t* group_tile_end, int num_tiles,
                  float scale, int num_seqs, int num_groups, int max_members, int num_q_heads,
                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
                  int max_context_len, int dtype, bool kv_fp8, float k_scale, float v_scale,
@@ -759,7 +764,8 @@ int grouped_impl(void* out, const void* q, const void* k_cache, const void* v_ca
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_checks()) {
     const int rc = debug_check_groups(context_lens, group_members, group_tiles, group_tile_start,
-                                      num_tiles, num_seqs, num_groups, max_members, num_blocks,
+                                      group_tile_end, num_tiles, num_seqs, num_groups,
+                                      max_members, num_blocks,
                                       max_context_len, part_tiles > 0 ? max_group_tiles : -1,
                                       st);
     if (rc != PKV_OK) return rc;
@@ -773,6 +779,7 @@ int grouped_impl(void* out, const void* q, const void* k_cache, const void* v_ca
   a.members = group_members;
   a.tiles = group_tiles;
   a.tile_start = group_tile_start;
+  a.tile_end = group_tile_end;
   a.num_tiles = num_tiles;
   a.scale_log2e = (float)((double)scale * (kv_fp8 ? (double)k_scale : 1.0) * 1.4426950408889634);
   a.v_scale = kv_fp8 ? v_scale : 1.f;
@@ -834,26 +841,42 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* q, const void* k_cach
                       max_context_len, dtype, begin_event, end_event, stream);
 }
 
+size_t pkv_group_tiles_capacity(int num_groups, int max_members, int block_size,
+                                int max_blocks_per_seq, int max_context_len) {
+  if (num_groups < 0 || max_members <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return (size_t)-1;
+  const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+  const int64_t len_cap = table_cap < max_context_len ? table_cap : max_context_len;
+  return (size_t)num_groups * (size_t)max_members * (size_t)((len_cap + 15) / 16);
+}
+
 int pkv_group_tiles(const int32_t* block_tables, const int32_t* context_lens,
                     const int32_t* group_members, int num_seqs, int max_blocks_per_seq,
                     int num_groups, int max_members, int block_size, int max_context_len,
                     int32_t* group_tiles, int tiles_capacity, int32_t* group_tile_start,
-                    void* stream) {
+                    int32_t* group_tile_end, void* stream) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_groups < 0 || max_members <= 0 ||
       block_size <= 0 || max_context_len < 0 || tiles_capacity < 0)
     return PKV_EINVAL;
-  if (max_members > 16 || block_size % 16 || num_groups > group_tiles_max_groups())
-    return PKV_EUNSUPPORTED;
-  if (!group_tile_start || (num_groups > 0 && (!group_members || !block_tables ||
-                                               !context_lens || !group_tiles)))
+  if (max_members > 16 || block_size % 16) return PKV_EUNSUPPORTED;
+  if (num_groups == 0) return PKV_OK;
+  if (!group_tile_start || !group_tile_end || !group_members || !block_tables || !context_lens ||
+      !group_tiles)
     return PKV_EINVAL;
   if (reinterpret_cast<uintptr_t>(group_tiles) % 16) return PKV_EINVAL;
+  const size_t need = pkv_group_tiles_capacity(num_groups, max_members, block_size,
+                                               max_blocks_per_seq, max_context_len);
+  if (need > (size_t)INT32_MAX) return PKV_EUNSUPPORTED;   // row offsets are int32
+  if ((size_t)tiles_capacity < need) return PKV_EWORKSPACE;
   const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
   const int len_cap = (int)(table_cap < max_context_len ? table_cap : max_context_len);
+  const int stride = max_members * ((len_cap + 15) / 16);
   hipError_t err = launch_build_group_tiles(block_tables, context_lens, group_members, num_seqs,
                                             max_blocks_per_seq, num_groups, max_members,
-                                            block_size, len_cap, group_tiles, tiles_capacity,
-                                            group_tile_start, static_cast<hipStream_t>(stream));
+                                            block_size, len_cap, group_tiles, stride,
+                                            group_tile_start, group_tile_end,
+                                            static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : fail_hip(err);
 }
 
@@ -871,7 +894,8 @@ size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_he
 int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* context_lens,
                                        const int32_t* group_members, const int32_t* group_tiles,
-                                       const int32_t* group_tile_start, int num_tiles,
+                                       const int32_t* group_tile_start,
+                                       const int32_t* group_tile_end, int num_tiles,
                                        float scale, int num_seqs, int num_groups, int max_members,
                                        int num_q_heads, int num_kv_heads, int head_dim,
                                        int block_size, int num_blocks, int max_context_len,
@@ -879,8 +903,8 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
                                        void* workspace, size_t workspace_bytes,
                                        void* begin_event, void* end_event, void* stream) {
   return grouped_impl(out, q, k_cache, v_cache, context_lens, group_members, group_tiles,
-                      group_tile_start, num_tiles, scale, num_seqs, num_groups, max_members,
-                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      group_tile_start, group_tile_end, num_tiles, scale, num_seqs, num_groups,
+                      max_members, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_context_len, dtype, false, 1.f, 1.f, part_tiles, max_group_tiles,
                       workspace, workspace_bytes, begin_event, end_event, stream);
 }
@@ -888,14 +912,15 @@ int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_c
 int pkv_paged_attention_decode_grouped_fp8(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* context_lens, const int32_t* group_members, const int32_t* group_tiles,
-    const int32_t* group_tile_start, int num_tiles, float scale, float k_scale, float v_scale,
+    const int32_t* group_tile_start, const int32_t* group_tile_end, int num_tiles, float scale,
+    float k_scale, float v_scale,
     int num_seqs, int num_groups, int max_members, int num_q_heads, int num_kv_heads,
     int head_dim, int block_size, int num_blocks, int max_context_len, pkv_dtype dtype,
     int part_tiles, int max_group_tiles, void* workspace, size_t workspace_bytes,
     void* begin_event, void* end_event, void* stream) {
   return grouped_impl(out, q, k_cache, v_cache, context_lens, group_members, group_tiles,
-                      group_tile_start, num_tiles, scale, num_seqs, num_groups, max_members,
-                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      group_tile_start, group_tile_end, num_tiles, scale, num_seqs, num_groups,
+                      max_members, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_context_len, dtype, true, k_scale, v_scale, part_tiles,
                       max_group_tiles, workspace, workspace_bytes, begin_event, end_event,
                       stream);

@@ -42,7 +42,8 @@ constexpr int kCols = 16;
 __device__ inline int group_range(const GroupedArgs& a, int grp, int part, int& t_begin,
                                   int& ntile) {
   const int t0 = min(max(load_uniform(a.tile_start + grp), 0), a.num_tiles);
-  const int t1 = min(max(load_uniform(a.tile_start + grp + 1), t0), a.num_tiles);
+  const int t1 = min(max(load_uniform(a.tile_end ? a.tile_end + grp : a.tile_start + grp + 1), t0),
+                     a.num_tiles);
   if (a.part_tiles <= 0) {
     t_begin = t0;
     ntile = t1 - t0;

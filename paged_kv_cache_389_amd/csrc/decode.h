@@ -67,6 +67,9 @@ struct GroupedArgs {
   const int32_t* members;       // [num_groups][max_members]
   const int32_t* tiles;         // [total][4], 16-byte aligned
   const int32_t* tile_start;    // [num_groups + 1]; clamped to [0, num_tiles]
+  // optional [num_groups]: group j's rows end here (then tile_start needs only
+  // num_groups entries and groups may leave gaps); null: at tile_start[j + 1]
+  const int32_t* tile_end = nullptr;
   int num_tiles;                // rows of tiles
   float scale_log2e;            // scale * log2(e) (* K scale for 8-bit codes)
   float v_scale = 1.f;          // 8-bit caches: the V scale
@@ -180,15 +183,14 @@ bool grouped_supported(Elem e, int head_dim, int block_size);
 hipError_t launch_decode_grouped(Elem e, bool kv_fp8, int head_dim, int block_size,
                                  const GroupedArgs& a, hipStream_t stream);
 hipError_t launch_grouped_merge(Elem e, int head_dim, const GroupedArgs& a, hipStream_t stream);
-// The grouped decode's tile lists from the block tables (group_tiles.hip):
-// one workgroup; at most group_tiles_max_groups() groups; rows past `cap`
-// are not written.
-int group_tiles_max_groups();
+// The grouped decode's tile lists from the block tables (group_tiles.hip).
+// Group j's rows go to tiles[j * stride ..] with tile_start[j] = j * stride
+// and tile_end[j] after its last row; one workgroup per group.
 hipError_t launch_build_group_tiles(const int32_t* block_tables, const int32_t* context_lens,
                                     const int32_t* members, int num_seqs, int max_blocks,
                                     int num_groups, int max_members, int block_size, int len_cap,
-                                    int32_t* tiles, int cap, int32_t* tile_start,
-                                    hipStream_t stream);
+                                    int32_t* tiles, int stride, int32_t* tile_start,
+                                    int32_t* tile_end, hipStream_t stream);
 // Query tokens one prefill workgroup covers (its grid is ceil(max_q_len / this)
 // chunks per KV head and sequence).
 int prefill_tokens_per_workgroup(int group);

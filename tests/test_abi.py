@@ -278,12 +278,13 @@ def test_prefill_fp8_rejects_bad_scales(native):
 
 
 def _grouped(lib, fp8=False, **over):
-    a = dict(out=16, q=16, k=16, v=16, lens=16, members=16, tiles=256, start=16, num_tiles=8,
+    a = dict(out=16, q=16, k=16, v=16, lens=16, members=16, tiles=256, start=16, end=None,
+             num_tiles=8,
              scale=0.1, ks=0.01, vs=0.01, B=8, groups=2, M=4, Hq=8, Hkv=2, hd=128, bs=16,
              nb=64, maxL=512, dtype=1, part=0, maxg=8, ws=None, wsb=0)
     a.update(over)
     head = (a["out"], a["q"], a["k"], a["v"], a["lens"], a["members"], a["tiles"], a["start"],
-            a["num_tiles"], ctypes.c_float(a["scale"]))
+            a["end"], a["num_tiles"], ctypes.c_float(a["scale"]))
     tail = (a["B"], a["groups"], a["M"], a["Hq"], a["Hkv"], a["hd"], a["bs"], a["nb"], a["maxL"],
             a["dtype"], a["part"], a["maxg"], a["ws"], a["wsb"], None, None, None)
     if fp8:
@@ -326,16 +327,23 @@ def test_grouped_empty_and_fp8_scales(native):
 
 def test_group_tiles_rejects_bad_arguments(native):
     f = native.lib.pkv_group_tiles
-    ok = dict(t=16, l=16, m=16, B=8, W=4, G=2, M=4, bs=16, L=64, tiles=256, cap=32, start=16)
+    ok = dict(t=16, l=16, m=16, B=8, W=4, G=2, M=4, bs=16, L=64, tiles=256, cap=32, start=16,
+              end=32)
 
     def call(**over):
         a = {**ok, **over}
         return f(a["t"], a["l"], a["m"], a["B"], a["W"], a["G"], a["M"], a["bs"], a["L"],
-                 a["tiles"], a["cap"], a["start"], None)
+                 a["tiles"], a["cap"], a["start"], a["end"], None)
 
+    cap = native.lib.pkv_group_tiles_capacity
+    assert cap(2, 4, 16, 4, 64) == 2 * 4 * 4
+    assert cap(2, 4, 16, 2, 64) == 2 * 4 * 2          # lengths capped by the table width
+    assert cap(-1, 4, 16, 4, 64) == ctypes.c_size_t(-1).value
+    assert call(G=0, t=None, tiles=None) == 0
     assert call(M=17) == -2
     assert call(bs=24) == -2
-    assert call(G=4097) == -2
+    assert call(cap=31) == -3         # short of one group's rows
+    assert call(end=None) == -1
     assert call(tiles=264) == -1      # not 16-byte aligned
     assert call(start=None) == -1
     assert call(t=None) == -1

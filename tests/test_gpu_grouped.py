@@ -349,17 +349,17 @@ def _device_lists(tables, lens, groups, bs, max_members, max_len, cap=None):
     l = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to(DEV)
     m = torch.from_numpy(members).to(DEV)
     tiles = None if cap is None else torch.full((cap, 4), -7, dtype=torch.int32, device=DEV)
-    tiles, start = pk.group_tiles(t, l, m, bs, max_len, tiles=tiles)
+    tiles, start, end = pk.group_tiles(t, l, m, bs, max_len, tiles=tiles)
     torch.cuda.synchronize()
-    return members, tiles.cpu().numpy(), start.cpu().numpy()
+    return members, tiles.cpu().numpy(), start.cpu().numpy(), end.cpu().numpy()
 
 
 def _same_as_host(tables, lens, groups, bs, max_members, max_len):
     hm, ht, hs = bmod.group_tiles(tables, lens, groups, bs, max_members)
-    dm, dt, ds = _device_lists(tables, lens, groups, bs, max_members, max_len)
+    dm, dt, ds, de = _device_lists(tables, lens, groups, bs, max_members, max_len)
     assert np.array_equal(hm, dm)
-    assert np.array_equal(hs, ds), (hs[:8], ds[:8])
-    assert np.array_equal(ht, dt[:hs[-1]])
+    for j in range(len(groups)):
+        assert np.array_equal(ht[hs[j]:hs[j + 1]], dt[ds[j]:de[j]]), j
 
 
 @pytest.mark.parametrize("bs", [16, 32])
@@ -398,15 +398,11 @@ def test_device_lists_many_groups_empty_groups_and_capacity():
     tables = rng.integers(0, 100000, (n, 5)).astype(np.int32)
     groups = [[s] for s in range(n)]
     _same_as_host(tables, lens, groups, 16, 1, 80)
-    # groups x places past the builder's LDS cache (global reads instead)
-    pairs = [[s, s + 1] for s in range(0, 600, 2)]
+    pairs = [[s, s + 1] for s in range(0, 600, 2)]          # 2 members in 16 places
     _same_as_host(tables, lens, pairs, 16, 16, 80)
-    # a capacity below the rows: nothing written past it, the offsets still count every row
-    hm, ht, hs = bmod.group_tiles(tables, lens, groups, 16, 1)
-    cap = int(hs[-1]) // 2
-    _, dt, ds = _device_lists(tables, lens, groups, 16, 1, 80, cap=cap)
-    assert np.array_equal(ds, hs)
-    assert np.array_equal(dt, ht[:cap])
+    with pytest.raises(pk.PagedKVError) as e:               # a short list buffer
+        _device_lists(tables, lens, groups, 16, 1, 80, cap=n * 5 - 1)
+    assert e.value.status == -3
 
 
 def test_grouped_decode_from_device_lists():
@@ -414,11 +410,19 @@ def test_grouped_decode_from_device_lists():
     wl = workloads.make("sharing_fp16", device=DEV)
     groups = bmod.share_groups(wl.block_tables, wl.context_lens, 16)
     host = _lists(wl.block_tables, wl.context_lens, groups, wl.block_size, 16)
-    members, tiles_d, start_d = host[0], *pk.group_tiles(
+    tiles_d, start_d, end_d = pk.group_tiles(
         torch.from_numpy(wl.block_tables).to(DEV), torch.from_numpy(wl.context_lens).to(DEV),
         host[0], wl.block_size, wl.max_context_len)
     lens_d = torch.from_numpy(wl.context_lens).to(DEV)
     a = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, host, wl.scale, wl.max_context_len)
-    b = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, (members, tiles_d, start_d, host[3]),
-                 wl.scale, wl.max_context_len)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for part_tiles in (0, 32):
+        b = torch.full_like(wl.q, float("nan"))
+        pk.paged_attention_decode_grouped(b, wl.q, wl.k_cache, wl.v_cache, lens_d, host[0],
+                                          tiles_d, start_d, wl.scale, wl.max_context_len,
+                                          part_tiles=part_tiles, max_group_tiles=host[3],
+                                          group_tile_end=end_d)
+        torch.cuda.synchronize()
+        if part_tiles == 0:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        else:
+            assert float((a.float() - b.float()).abs().max()) <= TOL[wl.dtype]
