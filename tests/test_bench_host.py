@@ -1,0 +1,49 @@
+"""Host-side parts of bench.py (no GPU): the one-GPU contract and the grouped
+decode's byte accounting."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_grouped_bytes_count_each_distinct_slot_once():
+    """The grouped roofline's K/V bytes equal the distinct (block, slot) pairs
+    that the tile lists reach, counted by brute force from the lists."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from paged_kv_cache_389_amd import block_manager as bmod, workloads
+    wl = workloads.build_sharing(num_prompts=5, fanout=6, prompt_len=70, max_gen=40,
+                                 num_blocks=512, tensors=False)
+    info = bench.grouped_lists(wl, None, 0)
+    groups = bmod.share_groups(wl.block_tables, wl.context_lens, info["max_members"])
+    members, tiles, start = bmod.group_tiles(wl.block_tables, wl.context_lens, groups,
+                                             wl.block_size, info["max_members"])
+    slots = set()
+    for j in range(len(groups)):
+        for b, t, mask, _ in tiles[start[j]:start[j + 1]]:
+            for m in range(members.shape[1]):
+                if (mask >> m) & 1:
+                    L = int(wl.context_lens[members[j, m]])
+                    for r in range(16):
+                        tok = 16 * int(t) + r
+                        if tok < L:
+                            slots.add((int(b), tok % wl.block_size))
+    row = 2 * wl.num_kv_heads * wl.head_dim * wl.esize
+    assert wl.unique_kv_bytes() == len(slots) * row
+    extra = (2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * wl.esize + 16 * len(tiles) +
+             4 * len(groups) * info["max_members"] + 4 * (len(groups) + 1) + 4 * wl.num_seqs)
+    assert bench.grouped_decode_bytes(wl, info) == len(slots) * row + extra
+    assert bench.grouped_decode_bytes(wl, info, kv_fp8=True) == \
+        len(slots) * row // wl.esize + extra
+    assert info["tiles"] == len(tiles) and np.all(np.diff(start) >= 0)
