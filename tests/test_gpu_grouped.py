@@ -426,3 +426,44 @@ def test_grouped_decode_from_device_lists():
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
         else:
             assert float((a.float() - b.float()).abs().max()) <= TOL[wl.dtype]
+
+
+def test_debug_checks_device_built_lists(monkeypatch):
+    """PKV_DEBUG=1 with per-group start/end offsets (the device builder's form):
+    valid lists pass, an end before its start or a tile missing from a group
+    is rejected before anything runs."""
+    say("grouped debug checks, start/end form")
+    monkeypatch.setenv("PKV_DEBUG", "1")
+    wl = workloads.build_sharing(dtype=torch.float16, num_prompts=3, fanout=4, prompt_len=50,
+                                 max_gen=20, num_heads=2, head_dim=64, num_blocks=128, seed=4,
+                                 device=DEV)
+    groups = bmod.share_groups(wl.block_tables, wl.context_lens, 4)
+    members = np.full((len(groups), 4), -1, np.int32)
+    for j, g in enumerate(groups):
+        members[j, :len(g)] = g
+    m = torch.from_numpy(members).to(DEV)
+    lens = torch.from_numpy(wl.context_lens).to(DEV)
+    tiles, start, end = pk.group_tiles(torch.from_numpy(wl.block_tables).to(DEV), lens, m,
+                                       wl.block_size, wl.max_context_len)
+    out = torch.empty_like(wl.q)
+
+    def call(end_arr):
+        pk.paged_attention_decode_grouped(out, wl.q, wl.k_cache, wl.v_cache, lens, m, tiles,
+                                          start, wl.scale, wl.max_context_len,
+                                          group_tile_end=end_arr)
+
+    call(end)
+    torch.cuda.synchronize()
+    want = oracle.decode(wl.q.cpu(), wl.k_cache.cpu(), wl.v_cache.cpu(), wl.block_tables,
+                         wl.context_lens, wl.scale, wl.num_kv_heads)
+    assert max_err(out, want) <= TOL[torch.float16]
+    bad = end.clone()
+    bad[1] = start[1] - 1                       # end before start
+    with pytest.raises(pk.PagedKVError) as e:
+        call(bad)
+    assert e.value.status == -1 and "outside" in str(e.value), str(e.value)
+    short = end.clone()
+    short[0] -= 1                               # group 0 loses its last row
+    with pytest.raises(pk.PagedKVError) as e:
+        call(short)
+    assert e.value.status == -1 and "no entry" in str(e.value), str(e.value)
