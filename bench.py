@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
 PREFILL_WORKLOADS = ("llama3_8b_prefill_bf16",)
+GROUPABLE = ("sharing_fp16", "beam_search_fp16")
 DEFAULT_WORKLOAD = "opt13b_fp16"
 DTYPE_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 WORKLOAD_DESC = {
@@ -98,6 +99,12 @@ def parse():
     p.add_argument("--cal-mib", type=int, default=1024)
     p.add_argument("--swap", type=int, default=0, metavar="BLOCKS",
                    help="measure swap_blocks of this many K+V block pairs each way instead")
+    p.add_argument("--ceiling", action="store_true",
+                   help="only the reference reads (stream and block gather): the practical "
+                        "bandwidth ceiling")
+    p.add_argument("--quick", action="store_true",
+                   help="the headline line alone (no per-config, paging-control or ceiling "
+                        "objects)")
     return p.parse_args()
 
 
@@ -631,25 +638,102 @@ def _cpu_pool(wl, row, seqs, workers):
                       f"worker processes (rate = sample bytes / slowest worker's oracle time)"}
 
 
-def bench_one(name, args, with_cpu):
-    wl, dev = build_inputs(name, args.placement)
+def roofline_bytes(wl, kv_fp8=False, grouped=None, recorded_hbm=None):
+    """Bytes the decode kernel's roofline fraction is taken on, and their
+    basis.
+
+    Every sequence's own K/V once (the algorithmic bytes) when no two
+    sequences share a block; the grouped call's distinct tiles (each shared
+    tile once) for the grouped kernel.  A per-sequence kernel over sequences
+    that share blocks reads a shared block once per sequence, mostly from
+    L2, so its logical bytes are not HBM bytes: there the basis is the
+    counter-measured HBM bytes per launch when they were recorded for the
+    current kernel sources, else the distinct slots' bytes (every shared
+    slot once; a lower bound of the HBM bytes).  No basis exceeds the bytes
+    the kernel moves from HBM, so the fraction stays at or below 1."""
+    div = wl.esize if kv_fp8 else 1
+    if grouped is not None:
+        return grouped_decode_bytes(wl, grouped, kv_fp8), "unique K/V bytes (each distinct tile once)"
+    logical = wl.decode_bytes() - (wl.kv_bytes() - wl.kv_bytes() // div)
+    unique_kv = wl.unique_kv_bytes() // div
+    if unique_kv >= wl.kv_bytes() // div:
+        return logical, "algorithmic bytes (every sequence's own K/V once)"
+    if recorded_hbm:
+        return int(recorded_hbm), "counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)"
+    return logical - wl.kv_bytes() // div + unique_kv, \
+        "unique K/V bytes (each shared slot once: a lower bound of the HBM bytes)"
+
+
+def _host_blocks(pool, blocks):
+    """Host copies of the given physical blocks of a device pool, in a type
+    that holds the values exactly (bfloat16 widened to float32)."""
+    sel = torch.tensor(blocks, dtype=torch.int64, device=pool.device)
+    t = pool.index_select(0, sel).cpu()
+    return (t.float() if t.dtype == torch.bfloat16 else t).numpy()
+
+
+def oracle_error(wl, dev, seqs, tables=None):
+    """Max abs error of the timed run's output rows of ``seqs`` (all heads)
+    against the float64 oracle over the same device pools (after the timed
+    steps' cache writes).  ``tables`` overrides the block tables (the
+    contiguous control reads block s * W + j)."""
+    import oracle
+    tables = wl.block_tables if tables is None else tables
+    bs = wl.block_size
+    used = sorted({int(b) for s in seqs for b in tables[s, :-(-int(wl.context_lens[s]) // bs)]})
+    index = {b: i for i, b in enumerate(used)}
+    ct = np.zeros(tables.shape, np.int64)
+    for s in seqs:
+        n = -(-int(wl.context_lens[s]) // bs)
+        ct[s, :n] = [index[int(b)] for b in tables[s, :n]]
+    q = dev["q"].cpu()
+    q = (q.float() if q.dtype == torch.bfloat16 else q).numpy()
+    want = oracle.decode(q, _host_blocks(dev["k"], used), _host_blocks(dev["v"], used), ct,
+                         wl.context_lens, wl.scale, wl.num_kv_heads, seqs=list(seqs))
+    got = dev["out"].detach().to("cpu", torch.float64).numpy()
+    return float(max(np.abs(got[s] - want[s]).max() for s in seqs))
+
+
+def oracle_sample(wl, count):
+    """``count`` sequences spread evenly over the batch sorted by length
+    (the longest and the shortest included)."""
+    order = np.argsort(-wl.context_lens.astype(np.int64), kind="stable")
+    if count >= len(order):
+        return sorted(int(s) for s in order)
+    pick = np.unique(np.rint(np.linspace(0, len(order) - 1, count)).astype(int))
+    return sorted(int(order[i]) for i in pick)
+
+
+ERR_SAMPLE = {"tiny_fp32": 4, "opt13b_fp16": 8, "llama3_8b_gqa_bf16": 16,
+              "long_context_gqa_bf16": 2, "sharing_fp16": 8, "beam_search_fp16": 8,
+              "system_prompt_bf16": 8}
+TOL = {torch.float32: 1e-5, torch.float16: 2e-2, torch.bfloat16: 2e-2}
+
+
+def bench_one(name, args, with_cpu, placement=None, path=None, err_sample=None):
+    placement = args.placement if placement is None else placement
+    path = args.path if path is None else path
+    wl, dev = build_inputs(name, placement)
     if args.kv_cache == "e4m3":
         with_cpu = False   # the oracle baseline times the 16-bit pools
         quantise_pools(wl, dev)
+    fp8 = bool(dev.get("kv_fp8"))
     grouped = None
     if args.grouped:
         grouped = grouped_lists(wl, dev, args.group_part)
-    alg_decode, alg_writes = step_bytes(wl, dev)
-    if grouped:
-        alg_decode = grouped_decode_bytes(wl, grouped, bool(dev.get("kv_fp8")))
+    tag = name + ("_kv_e4m3" if fp8 else "") + ("_grouped" if grouped else "")
+    _, alg_writes = step_bytes(wl, dev)
+    recorded = recorded_traffic(tag)
+    alg_decode, basis = roofline_bytes(wl, fp8, grouped, recorded)
     wall, decode_ms, kernel_ms, plan = run_gpu(wl, dev, args.steps, args.warmup, args.partition,
-                                               args.path, args.grid)
+                                               path, args.grid)
     ms_per_step = wall / args.steps * 1e3
     dec_ms = float(np.mean(decode_ms))
     ker_ms = float(np.mean(kernel_ms))
     achieved = alg_decode / (ker_ms / 1e3) / 1e9
     kname = ("decode_grouped_kernel" if grouped else
              "decode_mfma_kernel" if plan["path"] == 2 else "decode_valu_kernel")
+    logical = wl.kv_bytes() // (wl.esize if fp8 else 1)
     line = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + queries/s",
         "value": round((alg_decode + alg_writes) / (ms_per_step / 1e3) / 1e9, 2),
@@ -662,13 +746,13 @@ def bench_one(name, args, with_cpu):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAME[wl.dtype],
-        "data": "synthetic (seeded N(0,1) values, random block placement)",
-        "config": {"workload": name + ("_kv_e4m3" if dev.get("kv_fp8") else "") +
-                               ("_grouped" if grouped else ""),
+        "data": "synthetic (seeded N(0,1) values, "
+                f"{'random' if placement == 'random' else 'sequential'} block placement)",
+        "config": {"workload": tag,
                    **WORKLOAD_DESC[name], "seed": wl.seed,
-                   "kv_cache": "e4m3" if dev.get("kv_fp8") else DTYPE_NAME[wl.dtype],
-                   "placement": args.placement,
-                   "path": ["auto", "valu", "mfma", "contiguous"][args.path],
+                   "kv_cache": "e4m3" if fp8 else DTYPE_NAME[wl.dtype],
+                   "placement": placement,
+                   "path": ["auto", "valu", "mfma", "contiguous"][path],
                    "kernel": ["auto", "valu", "mfma"][plan["path"]],
                    "grid": {1: "direct", 2: "planned"}[plan["grid"]],
                    "partition_tokens": plan["partition_tokens"], "max_parts": plan["max_parts"],
@@ -683,13 +767,11 @@ def bench_one(name, args, with_cpu):
         "kernel_ms_median": round(float(np.median(kernel_ms)), 5),
         "kernel_ms_min": round(float(np.min(kernel_ms)), 5),
         "gbs_at_median": round(alg_decode / (float(np.median(kernel_ms)) / 1e3) / 1e9, 2),
-        "bytes": {"decode_alg": alg_decode, "writes_alg": alg_writes,
-                  "kv_logical": wl.kv_bytes() // (wl.esize if dev.get("kv_fp8") else 1)},
+        "bytes": {"decode_roofline": alg_decode, "writes_alg": alg_writes,
+                  "kv_logical": logical},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(name + ("_kv_e4m3" if dev.get("kv_fp8") else "") +
-                                                 ("_grouped" if grouped else "")),
-                     "kernel": kname},
+                     "traffic": recorded, "kernel": kname, "basis": basis},
     }
     if grouped:
         for k in ("partition_tokens", "max_parts", "longest_first"):   # the per-sequence plan's
@@ -699,18 +781,140 @@ def bench_one(name, args, with_cpu):
         line["config"]["part_tiles"] = grouped["part_tiles"]
         line["config"]["lists"] = "built on the device every step (group_tiles, timed)"
         line["grouped"] = grouped
-        line["roofline"]["basis"] = "unique K/V bytes (each distinct tile once)"
-    if name in ("sharing_fp16", "beam_search_fp16"):
-        line["bytes"]["kv_unique"] = wl.unique_kv_bytes() // (wl.esize if dev.get("kv_fp8") else 1)
+    unique = wl.unique_kv_bytes() // (wl.esize if fp8 else 1)
+    if unique < logical:
+        line["bytes"]["kv_unique"] = unique
+        line["logical_kv_gbs"] = round(logical / (ker_ms / 1e3) / 1e9, 2)
+        line["sharing_saving"] = round(1.0 - unique / logical, 4)
     if name == "beam_search_fp16":
         from paged_kv_cache_389_amd import workloads
         pairs = [len(h.copy_pairs) for h in wl.history]
         line["beam"] = {"copy_pairs_timed_step": pairs[-1],
                         "copy_pairs_per_step_mean": round(float(np.mean(pairs)), 2),
                         "block_saving_vs_unshared": round(workloads.sharing_saving(wl), 4)}
+    if err_sample and not fp8:
+        seqs = oracle_sample(wl, err_sample)
+        tables = None
+        if path == 3:   # the contiguous control reads block s * W + j
+            w = -(-wl.max_context_len // wl.block_size)
+            tables = (np.arange(wl.num_seqs)[:, None] * w + np.arange(w)[None, :]).astype(np.int64)
+        line["max_abs_err"] = oracle_error(wl, dev, seqs, tables)
+        line["tol"] = TOL[wl.dtype]
+        line["err_sample"] = f"{len(seqs)} of {wl.num_seqs} sequences (longest and shortest " \
+                             f"included), all {wl.num_q_heads} heads, vs the float64 oracle"
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s, args.cpu_pool, dev["out"])
+    del wl, dev
     return line
+
+
+def config_entry(line):
+    """The per-configuration summary of one bench line."""
+    r = line["roofline"]
+    e = {"kernel": r["kernel"], "plan": {k: line["config"][k] for k in
+                                         ("grid", "partition_tokens", "max_parts", "part_tiles")
+                                         if k in line["config"]},
+         "kernel_ms": line["kernel_ms"], "decode_ms": line["decode_ms"],
+         "step_ms": line["ms_per_step"], "roofline_bytes": line["bytes"]["decode_roofline"],
+         "basis": r["basis"], "achieved_gbs": r["achieved"], "frac": r["frac"],
+         "traffic": r["traffic"], "queries_per_s": line["queries_per_s"],
+         "max_abs_err": line.get("max_abs_err"), "tol": line.get("tol"),
+         "err_sample": line.get("err_sample")}
+    if line["bytes"]["writes_alg"]:
+        e["step_bytes_writes"] = line["bytes"]["writes_alg"]
+    for k in ("logical_kv_gbs", "sharing_saving"):
+        if k in line:
+            e[k] = line[k]
+    return e
+
+
+# the configurations every default run reports, beside the headline
+PER_CONFIG = (("tiny_fp32", "tiny_fp32", False),
+              ("llama3_8b_gqa_bf16", "llama3_8b_gqa_bf16", False),
+              ("long_context_gqa_bf16", "long_context_gqa_bf16", False),
+              ("sharing_fp16", "sharing_fp16", False),
+              ("sharing_fp16_grouped", "sharing_fp16", True))
+
+
+def per_config(args, headline):
+    """Summaries of every configuration (the headline's included) and the
+    full lines they come from."""
+    out, lines = {"opt13b_fp16": config_entry(headline)}, {}
+    grouped0 = args.grouped
+    for key, name, grouped in PER_CONFIG:
+        args.grouped = grouped
+        lines[key] = bench_one(name, args, False, err_sample=ERR_SAMPLE[name])
+        out[key] = config_entry(lines[key])
+    args.grouped = grouped0
+    return out, lines
+
+
+def paging_control(args, headline=None, long_line=None):
+    """The block-table overhead control: the same kernels with random
+    placement (the workload), sequential placement (blocks in increasing
+    physical order) and no table at all (block j of sequence s at s * W +
+    j), on the OPT-13B-shaped and the long-context batches."""
+    res = {}
+    for name, base in (("opt13b_fp16", headline), ("long_context_gqa_bf16", long_line)):
+        runs = {"random": base or bench_one(name, args, False, err_sample=ERR_SAMPLE[name]),
+                "sequential": bench_one(name, args, False, placement="sequential",
+                                        err_sample=ERR_SAMPLE[name]),
+                "contiguous": bench_one(name, args, False, path=3, err_sample=ERR_SAMPLE[name])}
+        ent = {k: {"kernel_ms": v["kernel_ms"], "kernel_ms_median": v["kernel_ms_median"],
+                   "frac": v["roofline"]["frac"], "max_abs_err": v.get("max_abs_err")}
+               for k, v in runs.items()}
+        r = runs["random"]["kernel_ms_median"]
+        ent["random_over_sequential"] = round(r / runs["sequential"]["kernel_ms_median"], 4)
+        ent["random_over_contiguous"] = round(r / runs["contiguous"]["kernel_ms_median"], 4)
+        res[name] = ent
+    return res
+
+
+def practical_ceiling(reps=10):
+    """Reference reads (``csrc/ceiling.hip``): a contiguous 2 GiB stream and a
+    gather of random distinct 4 KiB and 8 KiB chunks (one 16-token tile of a
+    16-bit hd-128 cache; a 32-token one) from a 2 GiB pool, at a few grid
+    sizes; GB/s of the best, from torch events around each launch."""
+    from paged_kv_cache_389_amd import _native as pk
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(389)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def best(fn, moved, grids):
+        out = {}
+        for wgs in grids:
+            for _ in range(3):
+                fn(wgs)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for a, b in ev:
+                a.record()
+                fn(wgs)
+                b.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            out[wgs] = round(moved / (ms / 1e3) / 1e9, 1)
+        return max(out.values()), out
+
+    res = {"peak_gbs": HBM_PEAK_GBS}
+    s_best, s_all = best(lambda w: pk.ceiling_stream_read(buf, w, sink), nbytes,
+                         [cus * k for k in (2, 4, 8, 16)])
+    res["stream_read_gbs"] = s_best
+    res["stream_read_by_workgroups"] = s_all
+    for cb in (4096, 8192):
+        n = (3 * nbytes // 4) // cb    # three quarters of the pool, random distinct chunks
+        chunks = torch.randperm(nbytes // cb, generator=g)[:n].to(torch.int32).cuda()
+        moved = n * cb
+        g_best, g_all = best(lambda w: pk.ceiling_gather_read(buf, chunks, cb, w, sink), moved,
+                             [cus * k for k in (2, 4, 8)])
+        res[f"gather_{cb // 1024}k_gbs"] = g_best
+        res[f"gather_{cb // 1024}k_by_workgroups"] = g_all
+    res["frac_of_peak"] = {k: round(v / HBM_PEAK_GBS, 4) for k, v in res.items()
+                           if k.endswith("_gbs") and k != "peak_gbs"}
+    del buf
+    return res
 
 
 def main():
@@ -731,17 +935,34 @@ def main():
     if args.swap:
         bench_swap(args)
         return
+    if args.ceiling:
+        print(json.dumps({"practical_ceiling": practical_ceiling()}), flush=True)
+        return
     if args.workload in PREFILL_WORKLOADS:
         print(json.dumps(bench_prefill(args.workload, args)), flush=True)
         return
-    names = sorted(WORKLOAD_DESC) if args.sweep else [args.workload]
-    for name in names:
-        line = bench_one(name, args, with_cpu=not args.no_cpu_baseline and not args.sweep)
-        print(json.dumps(line), flush=True)
-        if args.sweep and not args.grouped and name in ("sharing_fp16", "beam_search_fp16"):
-            args.grouped = True    # the same batch through the grouped call
-            print(json.dumps(bench_one(name, args, with_cpu=False)), flush=True)
-            args.grouped = False
+    if args.sweep:
+        for name in sorted(WORKLOAD_DESC):
+            line = bench_one(name, args, with_cpu=False, err_sample=ERR_SAMPLE.get(name))
+            print(json.dumps(line), flush=True)
+            if not args.grouped and name in GROUPABLE:
+                args.grouped = True    # the same batch through the grouped call
+                print(json.dumps(bench_one(name, args, with_cpu=False,
+                                           err_sample=ERR_SAMPLE.get(name))), flush=True)
+                args.grouped = False
+        return
+    line = bench_one(args.workload, args, with_cpu=not args.no_cpu_baseline,
+                     err_sample=ERR_SAMPLE.get(args.workload))
+    full = (args.workload == DEFAULT_WORKLOAD and not args.quick and not args.grouped and
+            args.kv_cache == "auto" and args.placement == "random" and args.path == 0 and
+            args.partition == 0 and args.grid == 0)
+    if full:
+        t0 = time.perf_counter()
+        line["per_config"], lines = per_config(args, line)
+        line["paging_control"] = paging_control(args, line, lines.get("long_context_gqa_bf16"))
+        line["practical_ceiling"] = practical_ceiling()
+        line["extra_s"] = round(time.perf_counter() - t0, 1)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -606,6 +606,36 @@ size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_he
                                                    int head_dim, int part_tiles,
                                                    int max_group_tiles);
 
+/*
+ * Reference reads (measurement only; not part of the attention path).  They
+ * give the practical ceiling a paged read is judged against beside the HBM3E
+ * peak: the pages locate the cost of serving in memory traffic ("Scaling LLM
+ * Inference: Memory Management with PagedAttention and vLLM", section "The KV
+ * Cache Bottleneck"), so the read rate the memory system sustains bounds
+ * every kernel here.  Each folds what it reads into one XOR per wave,
+ * combined with an atomic XOR into *sink (one uint32 the caller clears); the
+ * value carries no meaning beyond keeping every load live.
+ *
+ * ceiling_stream_read: reads `bytes` contiguous bytes at `src` (16-byte
+ * aligned, bytes a positive multiple of 16) with `workgroups` workgroups of
+ * 256 threads, 16-byte loads, eight in flight per lane.
+ *
+ * ceiling_gather_read: reads chunks[i] (int32 [num_chunks], device) of
+ * `chunk_bytes` (2048, 4096 or 8192) bytes each, chunk c at pool + c *
+ * chunk_bytes; `pool_bytes` bounds the pool, and an index outside it reads
+ * nothing (no fault).  Waves take contiguous runs of the list (64 indices per
+ * vector load) and keep about 16 KiB of chunk loads in flight, the way the
+ * decode kernels read tiles through a block table.
+ *
+ * Both are asynchronous on `stream`; a null pointer or a bad size returns
+ * PKV_EINVAL, a failed launch PKV_EHIP.
+ */
+int pkv_ceiling_stream_read(const void* src, size_t bytes, int workgroups, uint32_t* sink,
+                            void* stream);
+int pkv_ceiling_gather_read(const void* pool, size_t pool_bytes, const int32_t* chunks,
+                            int num_chunks, int chunk_bytes, int workgroups, uint32_t* sink,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -114,6 +114,10 @@ def _load():
     lib.pkv_group_tiles_capacity.argtypes = [i32] * 5
     lib.pkv_paged_attention_grouped_workspace_bytes.restype = sz
     lib.pkv_paged_attention_grouped_workspace_bytes.argtypes = [i32] * 5
+    lib.pkv_ceiling_stream_read.restype = i32
+    lib.pkv_ceiling_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.pkv_ceiling_gather_read.restype = i32
+    lib.pkv_ceiling_gather_read.argtypes = [vp, sz, i32p, i32, i32, i32, vp, vp]
     return lib
 
 
@@ -129,6 +133,7 @@ EXPORTED = (
     "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_fp8",
     "pkv_paged_attention_decode_grouped", "pkv_paged_attention_decode_grouped_fp8",
     "pkv_paged_attention_grouped_workspace_bytes", "pkv_group_tiles", "pkv_group_tiles_capacity",
+    "pkv_ceiling_stream_read", "pkv_ceiling_gather_read",
 )
 
 
@@ -597,6 +602,37 @@ def paged_attention_decode_grouped(out, q, k_cache, v_cache, context_lens, group
             st = lib.pkv_paged_attention_decode_grouped(*head, *tail)
     _check("paged_attention_decode_grouped", st)
     return out
+
+
+def ceiling_stream_read(src, workgroups, sink, stream=None):
+    """Read every byte of the contiguous device tensor ``src`` once
+    (``pkv_ceiling_stream_read``, a reference read for the practical
+    bandwidth ceiling); ``sink`` is a one-element int32 device tensor the
+    kernel XORs into."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    nbytes = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        st = lib.pkv_ceiling_stream_read(_ptr(src), nbytes, int(workgroups), _ptr(sink),
+                                         _stream(src, stream))
+    _check("ceiling_stream_read", st)
+
+
+def ceiling_gather_read(pool, chunks, chunk_bytes, workgroups, sink, stream=None):
+    """Read the ``chunk_bytes`` chunks of the device tensor ``pool`` that the
+    int32 device tensor ``chunks`` names (``pkv_ceiling_gather_read``, a
+    reference read for the practical ceiling of a paged gather)."""
+    _dev(pool, "pool")
+    _dev(chunks, "chunks")
+    _dev(sink, "sink")
+    if chunks.dtype != torch.int32 or chunks.dim() != 1:
+        raise ValueError("chunks must be int32 [n]")
+    nbytes = pool.numel() * pool.element_size()
+    with torch.cuda.device(pool.device):
+        st = lib.pkv_ceiling_gather_read(_ptr(pool), nbytes, _ptr(chunks), chunks.numel(),
+                                         int(chunk_bytes), int(workgroups), _ptr(sink),
+                                         _stream(pool, stream))
+    _check("ceiling_gather_read", st)
 
 
 class HipEvent:

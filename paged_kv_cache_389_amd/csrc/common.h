@@ -286,14 +286,25 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+//
+// POL is the load's cache policy: 0 for ordinary loads, kStream for the
+// nontemporal bit (lines marked for early eviction).  A plain random gather
+// of 4 KiB chunks measured 6.3-6.5 TB/s with it against 5.7-5.9 TB/s
+// without; the decode kernels measured the same with either, and use 0.
+constexpr int kStream = 2;
+template <int POL = 0>
 __device__ inline u32x4 bld16(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, const_off, 0));
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, const_off, POL));
 }
+template <int POL = 0>
 __device__ inline u32x2 bld8(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, const_off, 0));
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, const_off, POL));
 }
+template <int POL = 0>
 __device__ inline uint32_t bld4(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, const_off, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, const_off, POL);
 }
 
 // Value of a wave-uniform lane's register (v_readlane with an SGPR index).

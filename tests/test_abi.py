@@ -349,3 +349,17 @@ def test_group_tiles_rejects_bad_arguments(native):
     assert call(t=None) == -1
     assert call(cap=-1) == -1
     assert call(M=0) == -1
+
+
+def test_ceiling_reads_reject_bad_arguments(native):
+    """The reference reads check their arguments before launching (no GPU)."""
+    lib = native.lib
+    assert lib.pkv_ceiling_stream_read(None, 1024, 8, 1, None) == -1
+    assert lib.pkv_ceiling_stream_read(16, 1000, 8, 1, None) == -1     # not a multiple of 16
+    assert lib.pkv_ceiling_stream_read(8, 1024, 8, 1, None) == -1      # misaligned
+    assert lib.pkv_ceiling_stream_read(16, 1024, 0, 1, None) == -1
+    assert lib.pkv_ceiling_stream_read(16, 1024, 8, None, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, 1 << 20, 16, 4, 3000, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, 1024, 16, 4, 4096, 8, 16, None) == -1   # pool < chunk
+    assert lib.pkv_ceiling_gather_read(16, 1 << 20, None, 4, 4096, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, 1 << 20, 16, 0, 4096, 8, 16, None) == -1
