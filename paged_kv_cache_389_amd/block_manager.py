@@ -34,6 +34,11 @@ Readings where the pages are silent:
 * Slot numbering: slot ``b * block_size + o`` is offset ``o`` of block ``b``.
 * Free blocks are handed out from the end of a free list; its initial order
   may be given (a seeded permutation gives random placement).
+* Copy-on-write pairs wait until the caller takes them (one batch for one
+  copy_blocks call, which copies them in parallel).  Until then a block they
+  name does not return to the free list even when its count drops to zero,
+  and a pending destination cannot be the source of another copy, so the
+  batch never reads a block it writes.
 * A swap moves a group of sequences that holds every reference to its
   blocks (a prompt and its forks): each distinct block moves once, keeps its
   count, and every table of the group is rewritten.
@@ -85,6 +90,11 @@ class BlockManager:
         self._next_id = 0
         # copy-on-write pairs (src, dst) emitted since the last take_copy_pairs()
         self._pending_copies: list[tuple[int, int]] = []
+        # blocks named by a pending pair, and those among them whose count
+        # fell to zero: they stay off the free list until the pairs are taken,
+        # so no block is both a source and a destination of one batch of copies
+        self._pending_blocks: set[int] = set()
+        self._held_for_copy: list[int] = []
         # the host pool that swapped-out blocks live in
         self.num_host_blocks = int(num_host_blocks)
         self._host_free = list(range(self.num_host_blocks - 1, -1, -1))
@@ -110,7 +120,10 @@ class BlockManager:
         if self.refcount[b] < 0:
             raise AssertionError(f"block {b} released more often than held")
         if self.refcount[b] == 0:
-            self._free.append(b)
+            if b in self._pending_blocks:
+                self._held_for_copy.append(b)
+            else:
+                self._free.append(b)
 
     # ------------------------------------------------------------- sequences
     def new_sequence(self) -> Sequence:
@@ -135,10 +148,17 @@ class BlockManager:
         else:
             last = seq.table[-1]
             if self.refcount[last] > 1:
+                if any(last == d for _, d in self._pending_copies):
+                    # its content is still being copied in: one batch of copies
+                    # runs in parallel, so it cannot also be a source
+                    raise ValueError(
+                        f"block {last} is the destination of a pending copy; take the "
+                        "pending pairs (and apply them and the step's writes) first")
                 fresh = self._take()
                 self.refcount[last] -= 1
                 seq.table[-1] = fresh
                 self._pending_copies.append((last, fresh))
+                self._pending_blocks.update((last, fresh))
         slot = seq.table[seq.length // bs] * bs + offset
         seq.length += 1
         return slot
@@ -197,6 +217,9 @@ class BlockManager:
         for b in order:
             if count[b] != refs[b]:
                 raise ValueError(f"block {b} is also held outside the group")
+        if not on_host and any(b in self._pending_blocks for b in order):
+            raise ValueError("the group's blocks are named by pending copy-on-write pairs; "
+                             "take the pairs (and apply them) before swapping")
         return order
 
     def _move(self, seqs, order, to_host: bool) -> np.ndarray:
@@ -238,10 +261,25 @@ class BlockManager:
         return self._move(seqs, order, to_host=False)
 
     def take_copy_pairs(self) -> np.ndarray:
-        """Copy-on-write pairs emitted since the last call, as int64 [n, 2]."""
+        """Copy-on-write pairs emitted since the last call, as int64 [n, 2].
+        Their destinations are distinct and none is a source, as
+        copy_blocks requires; blocks of these pairs that were freed
+        meanwhile return to the free list now."""
         pairs = np.array(self._pending_copies, dtype=np.int64).reshape(-1, 2)
         self._pending_copies = []
+        self._pending_blocks = set()
+        self._free.extend(self._held_for_copy)
+        self._held_for_copy = []
         return pairs
+
+    def held_for_copy(self) -> list[int]:
+        """Unreferenced blocks kept off the free list until the pending
+        copy-on-write pairs that name them are taken."""
+        return list(self._held_for_copy)
+
+    def pending_copy_pairs(self) -> list[tuple[int, int]]:
+        """The pairs take_copy_pairs() would return, without taking them."""
+        return list(self._pending_copies)
 
     # ------------------------------------------------------------ exports
     def block_table_array(self, seqs, width: int | None = None, pad: int = 0):

@@ -22,8 +22,18 @@ def check_invariants(bm, seqs):
         assert len(s.table) == -(-s.length // bm.block_size)
     assert np.array_equal(held, bm.refcount)
     free = bm.free_blocks()
-    assert len(set(free)) == len(free)
-    assert set(free) == set(np.nonzero(bm.refcount == 0)[0].tolist())
+    kept = bm.held_for_copy()
+    assert len(set(free)) == len(free) and len(set(kept)) == len(kept)
+    assert not set(free) & set(kept)
+    assert set(free) | set(kept) == set(np.nonzero(bm.refcount == 0)[0].tolist())
+    # pending copy-on-write pairs: destinations distinct, none a source, and
+    # none of their blocks on the free list
+    pairs = bm.pending_copy_pairs()
+    src = [a for a, _ in pairs]
+    dst = [b for _, b in pairs]
+    assert len(set(dst)) == len(dst)
+    assert not set(dst) & set(src)
+    assert not (set(src) | set(dst)) & set(free)
 
 
 def test_cow_trace_golden(golden_dir):
@@ -105,6 +115,10 @@ def test_free_everything_returns_pool():
     check_invariants(bm, seqs)
     for s in seqs:
         bm.free(s)
+    # blocks of copy-on-write pairs not yet taken are held until they are
+    assert sorted(bm.free_blocks() + bm.held_for_copy()) == list(range(64))
+    pairs = bm.take_copy_pairs()
+    assert len(pairs) == 2
     assert sorted(bm.free_blocks()) == list(range(64))
     assert not bm.refcount.any()
 
@@ -114,6 +128,10 @@ def test_free_everything_returns_pool():
                           st.integers(0, 7), st.integers(0, 9)), max_size=40),
        st.sampled_from([1, 2, 4, 16]))
 def test_random_operation_sequences_keep_invariants(ops, block_size):
+    """Random histories, copy-on-write pairs taken only now and then: the
+    counts, the free list and every batch of pairs stay consistent (a batch
+    never names a block twice as a destination nor as source and
+    destination, even when holders are freed before the batch is taken)."""
     bm = BlockManager(48, block_size)
     seqs = []
     for op, i, n in ops:
@@ -126,11 +144,56 @@ def test_random_operation_sequences_keep_invariants(ops, block_size):
                 seqs.append(bm.fork(seqs[i % len(seqs)]))
             elif op == "free":
                 bm.free(seqs.pop(i % len(seqs)))
+            elif n % 3 == 0:
+                pairs = bm.take_copy_pairs()
+                assert len(set(pairs[:, 1].tolist())) == len(pairs)
+                assert not set(pairs[:, 0].tolist()) & set(pairs[:, 1].tolist())
             else:
                 bm.append_slot(seqs[i % len(seqs)])
-        except OutOfBlocks:
-            pass
+        except (OutOfBlocks, ValueError) as e:
+            if isinstance(e, ValueError):
+                assert "pending copy" in str(e)
         check_invariants(bm, seqs)
+
+
+def test_freed_copy_source_is_not_reused_before_the_pairs_are_taken():
+    """A copy-on-write source whose other holders are freed before the pairs
+    are taken is kept off the free list, so it cannot become the destination
+    of another copy in the same batch (copy_blocks copies a batch in
+    parallel)."""
+    bm = BlockManager(8, 4, free_order=list(range(7, -1, -1)))
+    a = bm.new_sequence()
+    bm.extend(a, 2)                     # block 0, partly filled
+    b = bm.fork(a)
+    bm.append_slot(b)                   # copy (0 -> 1); a keeps block 0
+    bm.free(a)                          # block 0 unreferenced, but a pending source
+    assert 0 not in bm.free_blocks() and bm.held_for_copy() == [0]
+    c = bm.new_sequence()
+    bm.extend(c, 2)
+    d = bm.fork(c)
+    bm.append_slot(d)                   # a second copy: its destination is not block 0
+    pairs = bm.take_copy_pairs()
+    assert pairs[:, 1].tolist()[0] == 1 and 0 not in pairs[:, 1].tolist()
+    assert 0 in bm.free_blocks() and bm.held_for_copy() == []
+    check_invariants(bm, [b, c, d])
+
+
+def test_pending_copy_destination_cannot_be_copied_again():
+    """Forking a sequence whose last block is still a pending copy
+    destination and appending to the fork would chain two copies in one
+    batch; the manager refuses until the pairs are taken."""
+    bm = BlockManager(8, 4)
+    a = bm.new_sequence()
+    bm.extend(a, 2)
+    b = bm.fork(a)
+    bm.append_slot(b)                   # b's last block is a fresh copy destination
+    c = bm.fork(b)
+    with pytest.raises(ValueError, match="pending copy"):
+        bm.append_slot(c)
+    bm.take_copy_pairs()
+    bm.append_slot(c)                   # after the batch, an ordinary copy
+    assert len(bm.take_copy_pairs()) == 1
+    check_invariants(bm, [a, b, c])
 
 
 @pytest.mark.parametrize("extra", [(1, 15), (0, 0)])
@@ -203,6 +266,9 @@ def test_swap_round_trip_keeps_content_sharing_and_counts():
     other = bm.new_sequence()
     bm.extend(other, 5)
     group = [prompt] + kids
+    with pytest.raises(ValueError, match="pending copy-on-write"):
+        bm.swap_out(group)                     # its copies have not been taken yet
+    assert len(bm.take_copy_pairs()) == 3
     dev_k = rng.integers(-900, 900, (nb, hkv, bs, hd)).astype(np.int16)
     dev_v = rng.integers(-900, 900, (nb, hkv, bs, hd)).astype(np.int16)
     host_k = np.zeros((nh, hkv, bs, hd), np.int16)

@@ -32,7 +32,7 @@ CASES = {
     "tiny_fp32": (4, 32),
     "opt13b_fp16": (8, 512),
     "llama3_8b_gqa_bf16": (8, 1024),
-    "long_context_gqa_bf16": (2, 1024),
+    "long_context_gqa_bf16": (8, 1024),
     "sharing_fp16": (8, 512),
     "beam_search_fp16": (8, 512),
 }
@@ -131,3 +131,48 @@ def test_full_size_step_matches_oracle(name):
         err = float(np.abs(g - want[seqs]).max())
         assert np.isfinite(g).all()
         assert err <= TOL[wl.dtype], f"{name} partition {partition} grid {grid}: max abs err {err}"
+
+
+def _identity_tables(wl):
+    """The contiguous control's layout: logical block j of sequence s is
+    physical block s * W + j, W = ceil(max_context_len / block_size)."""
+    w = -(-wl.max_context_len // wl.block_size)
+    return (np.arange(wl.num_seqs)[:, None] * w + np.arange(w)[None, :]).astype(np.int64), w
+
+
+@pytest.mark.parametrize("control", ["sequential", "contiguous"])
+@pytest.mark.parametrize("name", ["opt13b_fp16", "long_context_gqa_bf16"])
+def test_full_size_paging_control_matches_oracle(name, control):
+    """The block-table overhead control at full size, in the launch the
+    benchmark times: sequential placement (same kernel, blocks handed out in
+    increasing order) and the no-table contiguous variant (block j of
+    sequence s read at s * W + j) against the float64 oracle over the same
+    pool, on sampled sequences (every sequence of the long-context batch)."""
+    n_sample = CASES[name][0]
+    say("paging control build", name, control)
+    kw = {"placement": "sequential"} if control == "sequential" else {}
+    wl = workloads.make(name, device=DEV, **kw)
+    lens = torch.from_numpy(wl.context_lens).to(DEV)
+    if control == "sequential":
+        tables = wl.block_tables
+        # blocks in increasing physical order along every sequence
+        for s in range(wl.num_seqs):
+            n = -(-int(wl.context_lens[s]) // wl.block_size)
+            assert np.all(np.diff(tables[s, :n]) > 0)
+        out = _decode(wl, wl.k_cache, wl.v_cache, torch.from_numpy(tables).to(DEV), lens, 0,
+                      pk.GRID_AUTO)
+    else:
+        tables, _ = _identity_tables(wl)
+        assert tables.max() < wl.num_blocks
+        out = torch.empty_like(wl.q)
+        say("paging control contiguous decode", name)
+        pk.paged_attention_decode(out, wl.q, wl.k_cache, wl.v_cache, None, lens, wl.scale,
+                                  wl.max_context_len, path=pk.PATH_CONTIGUOUS)
+        torch.cuda.synchronize()
+    seqs = _sample(wl, n_sample)
+    want = oracle.decode(wl.q.cpu(), wl.k_cache.cpu(), wl.v_cache.cpu(), tables,
+                         wl.context_lens, wl.scale, wl.num_kv_heads, seqs=seqs)
+    g = out.cpu().double().numpy()[seqs]
+    assert np.isfinite(g).all()
+    err = float(np.abs(g - want[seqs]).max())
+    assert err <= TOL[wl.dtype], f"{name} {control}: max abs err {err}"

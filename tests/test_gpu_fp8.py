@@ -265,10 +265,32 @@ FULL = {"opt13b_fp16": (6, 512), "llama3_8b_gqa_bf16": (6, 1024),
         "long_context_gqa_bf16": (2, 1024)}
 
 
+def _oracle_codes_16bit(pool, scale):
+    """The oracle's codes of every element of a 16-bit device pool.  A code
+    depends only on the element's value and the scale, and a 16-bit element
+    has 65,536 bit patterns, so the oracle quantises each pattern once and
+    every element takes its pattern's code (the oracle applied to every
+    element, without encoding the same value twice)."""
+    patterns = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(pool.dtype)
+    table = fp8.quantize(patterns, scale)
+    bits = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    return table[bits]
+
+
+def test_oracle_codes_by_pattern_equal_direct_quantisation():
+    """The per-pattern shortcut of the full-size check equals the oracle
+    applied element by element (NaN, infinities and both zeros included)."""
+    g = torch.Generator().manual_seed(7)
+    x = (torch.randn(4000, generator=g) * 300).to(torch.bfloat16)
+    x[:4] = torch.tensor([float("nan"), float("inf"), -0.0, 0.0], dtype=torch.bfloat16)
+    for sc in (0.37, 1.0, 2.5e-3):
+        assert np.array_equal(_oracle_codes_16bit(x, sc), fp8.quantize(x, sc))
+
+
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_fp8_matches_oracle(name):
     """The workloads at full size with 8-bit pools: the library quantises
-    every slot (compared with the oracle's codes on sampled blocks), then
+    every slot (both whole code buffers compared with the oracle's codes), then
     decode_fp8 runs in the library's own configuration and with a forced
     split on the planned grid; sampled sequences (the longest, the shortest,
     seeded others; all heads) are compared with the oracle."""
@@ -291,12 +313,13 @@ def test_full_size_fp8_matches_oracle(name):
                                  torch.arange(b0 * bs, b1 * bs, dtype=torch.int64, device=DEV),
                                  k_scale, v_scale)
     torch.cuda.synchronize()
+    # the whole K and V code buffers against the oracle's codes of every slot
+    say("full-size fp8 whole-buffer codes", name)
+    for src, codes, sc in ((wl.k_cache, kc, k_scale), (wl.v_cache, vc, v_scale)):
+        want_codes = _oracle_codes_16bit(src, sc)
+        assert np.array_equal(codes.cpu().numpy(), want_codes), "quantised pool differs"
+        del want_codes
     rng = np.random.default_rng(wl.seed)
-    blocks = torch.from_numpy(rng.choice(nb, 16, replace=False)).to(DEV)
-    assert np.array_equal(kc[blocks].cpu().numpy(),
-                          fp8.quantize(wl.k_cache[blocks].cpu(), k_scale))
-    assert np.array_equal(vc[blocks].cpu().numpy(),
-                          fp8.quantize(wl.v_cache[blocks].cpu(), v_scale))
 
     L = wl.context_lens
     seqs = [int(np.argmax(L)), int(np.argmin(L))]

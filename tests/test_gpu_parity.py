@@ -303,10 +303,35 @@ def test_decode_contiguous_control_matches_paged():
             pad = np.zeros((nb * bs, hkv, hd))
             pad[:len(src)] = src
             dst[s * maxb:s * maxb + nb] = pad.reshape(nb, bs, hkv, hd).transpose(0, 2, 1, 3)
-    dev, _ = upload_case(q, kp, vp, tables, np.array(lens), torch.bfloat16)
+    dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, np.array(lens), torch.bfloat16)
     a = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.09)
     b = decode_gpu(dev["q"], dev["k"], dev["v"], None, dev["lens"], 0.09, max_len=256, path=3)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # and both against the oracle, which reads the same layout through the table
+    want = oracle.decode(qt, kt, vt, tables, np.array(lens), 0.09, hkv)
+    assert max_err(b, want) <= 2e-2
+
+
+@pytest.mark.parametrize("hkv", [8, 2], ids=["mha-valu", "gqa-mfma"])
+def test_decode_contiguous_control_against_oracle(hkv):
+    """The no-table control on both kernels (MHA runs on the vector-ALU
+    kernel, grouped heads on the MFMA one) against the float64 oracle given
+    the identity tables s * W + j; fp16, ragged lengths."""
+    say("decode contiguous control vs oracle", hkv)
+    rng = np.random.default_rng(1001)
+    lens = [1, 16, 17, 300, 511]
+    hq, hd, bs = 8, 128, 16
+    w = -(-max(lens) // bs)
+    nb = len(lens) * w
+    q = rng.standard_normal((len(lens), hq, hd))
+    kp = rng.standard_normal((nb, hkv, bs, hd))
+    vp = rng.standard_normal((nb, hkv, bs, hd))
+    tables = (np.arange(len(lens))[:, None] * w + np.arange(w)[None, :]).astype(np.int64)
+    dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, np.array(lens), torch.float16)
+    got = decode_gpu(dev["q"], dev["k"], dev["v"], None, dev["lens"], 0.088, max_len=max(lens),
+                     path=3)
+    want = oracle.decode(qt, kt, vt, tables, np.array(lens), 0.088, hkv)
+    assert max_err(got, want) <= 2e-2
 
 
 @pytest.mark.parametrize("grid", [0, 2], ids=["auto", "planned"])

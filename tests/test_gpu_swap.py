@@ -79,6 +79,7 @@ def test_swap_out_and_in_leaves_decode_unchanged(hq, hkv):
     kids = [bm.fork(prompt) for _ in range(3)]
     for i, k in enumerate(kids):
         bm.extend(k, 5 + 40 * i)
+    bm.take_copy_pairs()       # (the pool holds random rows: the copies need not run)
     other = bm.new_sequence()
     bm.extend(other, 77)
     group = [prompt] + kids
