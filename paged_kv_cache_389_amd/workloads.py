@@ -33,6 +33,12 @@ Five workload shapes (names used throughout the tests and the benchmark):
     16 prompts of 512-2048 tokens whose every token is a query of the causal
     prefill attention; 32 query / 8 KV heads, head_dim 128, block_size 16,
     pool of 4096 blocks.
+``system_prompt_bf16``
+    128 distinct requests sharing 4 cached system prompts of 513-2047 tokens
+    (last block partly filled; the cache entry keeps its own reference), each
+    writing its own prompt of 16-512 tokens (its first token copies the
+    shared partly filled block) and generating 0-64 tokens; 32 query / 8 KV
+    heads, head_dim 128, block_size 16, pool of 8192 blocks.
 ``beam_search_fp16``
     16 requests with prompts of 256-1024 tokens, each decoded with 8 beams
     for 64 steps: every step appends one token to every beam (copy-on-write
@@ -380,6 +386,87 @@ def build_beam_search(name="beam_search_fp16", *, dtype="fp16", num_requests=16,
     return wl
 
 
+def build_system_prompt(name="system_prompt_bf16", *, dtype="bf16", num_prefixes=4,
+                        requests_per_prefix=32, prefix_blocks=(32, 127), prefix_extra=(1, 15),
+                        own_prompt=(16, 512), max_gen=64, num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16, num_blocks=8192, seed=8, device="cpu",
+                        tensors=True):
+    """Distinct requests that share a cached system prompt.
+
+    Each of ``num_prefixes`` system prompts holds ``bs * k + r`` tokens (``k``
+    uniform in ``prefix_blocks``, ``r`` uniform in ``prefix_extra``: with
+    ``r > 0`` its last block is partly filled), written once into a cache
+    entry that keeps its own reference to the prompt's blocks.  Requests
+    arrive round-robin over the prompts (request i uses prompt i mod P):
+    each forks its prompt's entry and writes its own prompt of ``n_i``
+    tokens (uniform in ``own_prompt``), so its first token lands in the
+    shared partly filled block and copies it (the entry still holds it);
+    this admission step's copy-on-write pairs and slots are ``history[0]``.
+    Request i then generates ``d_i`` tokens (uniform in [0, max_gen]); step
+    t appends one token to every request with ``d_i >= t``.  The decode runs
+    over the requests' final state (the cache entries are not in the batch).
+    ``tensors=False`` skips every tensor draw (integer structure only).
+    """
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    rng = np.random.default_rng(seed)
+    bs = block_size
+    plens = bs * rng.integers(prefix_blocks[0], prefix_blocks[1] + 1, size=num_prefixes) + \
+        rng.integers(prefix_extra[0], prefix_extra[1] + 1, size=num_prefixes)
+    num_seqs = num_prefixes * requests_per_prefix
+    own = rng.integers(own_prompt[0], own_prompt[1] + 1, size=num_seqs)
+    gen = rng.integers(0, max_gen + 1, size=num_seqs)
+    bm = BlockManager(num_blocks, bs, free_order=rng.permutation(num_blocks))
+    entries = []
+    for p in range(num_prefixes):
+        e = bm.new_sequence()
+        bm.extend(e, int(plens[p]))
+        entries.append(e)
+    prefix_of = np.arange(num_seqs) % num_prefixes
+    g = _gen(device, seed)
+    pool_shape = (num_blocks, num_kv_heads, bs, head_dim)
+    q = k_cache = v_cache = None
+    if tensors:
+        q = _randn((num_seqs, num_q_heads, head_dim), dt, g, device)
+        k_cache = _randn(pool_shape, dt, g, device)
+        v_cache = _randn(pool_shape, dt, g, device)
+    reqs, slots, seq_index = [], [], []
+    for i in range(num_seqs):
+        x = bm.fork(entries[prefix_of[i]])
+        slots.append(bm.extend(x, int(own[i])))
+        seq_index.append(np.full(int(own[i]), i, np.int64))
+        reqs.append(x)
+    admit = DecodeStepInputs(copy_pairs=bm.take_copy_pairs(),
+                             slot_mapping=np.concatenate(slots).astype(np.int64),
+                             seq_index=np.concatenate(seq_index))
+    history = [admit]
+    for t in range(1, int(gen.max(initial=0)) + 1):
+        active = np.nonzero(gen >= t)[0]
+        st = DecodeStepInputs(copy_pairs=np.zeros((0, 2), np.int64),
+                              slot_mapping=np.array([bm.append_slot(reqs[i]) for i in active],
+                                                    np.int64),
+                              seq_index=active.astype(np.int64))
+        pairs = bm.take_copy_pairs()
+        assert len(pairs) == 0, "generation appends into blocks the request owns"
+        history.append(st)
+    if tensors:
+        for st in history:
+            n = len(st.slot_mapping)
+            st.new_k = _randn((n, num_kv_heads, head_dim), dt, g, device)
+            st.new_v = _randn((n, num_kv_heads, head_dim), dt, g, device)
+    wl = Workload(
+        name=name, dtype=dt, num_seqs=num_seqs, num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=bs, num_blocks=num_blocks,
+        scale=1.0 / math.sqrt(head_dim), seed=seed, context_lens=bm.context_lens(reqs),
+        block_tables=bm.block_table_array(reqs, pad=0), q=q, k_cache=k_cache, v_cache=v_cache,
+        step=history[-1], history=history,
+        meta={"prefix_lens": plens, "prefix_of": prefix_of, "own_prompt": own, "gen": gen,
+              "entry_tables": [list(e.table) for e in entries],
+              "refcount": bm.refcount.copy(), "physical_blocks": bm.num_blocks - bm.num_free,
+              "utilisation": bm.utilisation(reqs + entries)})
+    wl.meta["first_step_pairs"] = admit.copy_pairs
+    return wl
+
+
 @dataclass
 class PrefillWorkload:
     """Causal multi-token attention inputs: sequence s has ``context_lens[s]``
@@ -523,6 +610,10 @@ def beam_search_fp16(seed=6, device="cpu", **kw):
     return build_beam_search("beam_search_fp16", seed=seed, device=device, **kw)
 
 
+def system_prompt_bf16(seed=8, device="cpu", **kw):
+    return build_system_prompt("system_prompt_bf16", seed=seed, device=device, **kw)
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "opt13b_fp16": opt13b_fp16,
@@ -530,6 +621,7 @@ WORKLOADS = {
     "long_context_gqa_bf16": long_context_gqa_bf16,
     "sharing_fp16": sharing_fp16,
     "beam_search_fp16": beam_search_fp16,
+    "system_prompt_bf16": system_prompt_bf16,
     "llama3_8b_prefill_bf16": llama3_8b_prefill_bf16,
 }
 

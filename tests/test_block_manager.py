@@ -390,6 +390,92 @@ def test_beam_search_tokens_follow_the_beams_lineage(seed, width, temp):
     assert 0.0 < workloads.sharing_saving(wl) < 1.0
 
 
+@pytest.mark.parametrize("extra", [(1, 15), (0, 0)])
+def test_system_prompt_closed_forms(extra):
+    """Distinct requests over cached system prompts.  The cache entry keeps
+    its own reference, so every request's first token copies the prompt's
+    partly filled last block: N_p copies per prompt (none when the prompt
+    fills whole blocks).  Full prompt blocks are held by the entry and all
+    N_p requests (count 1 + N_p), the partly filled one by the entry alone;
+    the blocks in use are the prompts' plus each request's own; and the
+    lengths are prompt + own prompt + generated tokens."""
+    bs, P, N = 16, 4, 6
+    wl = workloads.build_system_prompt(num_prefixes=P, requests_per_prefix=N,
+                                       prefix_blocks=(2, 9), prefix_extra=extra,
+                                       own_prompt=(1, 40), max_gen=12, num_blocks=1024,
+                                       tensors=False, seed=8)
+    S = wl.meta["prefix_lens"]
+    pref = wl.meta["prefix_of"]
+    partial = S % bs != 0
+    assert partial.all() if extra == (1, 15) else not partial.any()
+    pairs = wl.history[0].copy_pairs
+    assert len(pairs) == int(N * partial.sum())
+    assert all(len(h.copy_pairs) == 0 for h in wl.history[1:])
+    if len(pairs):
+        assert len(set(pairs[:, 1].tolist())) == len(pairs)
+        assert not set(pairs[:, 1].tolist()) & set(pairs[:, 0].tolist())
+    ref = wl.meta["refcount"]
+    for p, tab in enumerate(wl.meta["entry_tables"]):
+        full = int(S[p]) // bs
+        assert all(ref[b] == 1 + N for b in tab[:full])
+        if partial[p]:
+            assert ref[tab[full]] == 1
+            # each request copied exactly this block, once
+            assert sorted(pairs[:, 0].tolist()).count(tab[full]) == N
+    L = S[pref] + wl.meta["own_prompt"] + wl.meta["gen"]
+    assert np.array_equal(wl.context_lens, L)
+    for i in range(wl.num_seqs):
+        full = int(S[pref[i]]) // bs
+        entry = wl.meta["entry_tables"][pref[i]]
+        assert wl.block_tables[i, :full].tolist() == entry[:full]
+        if partial[pref[i]]:
+            assert wl.block_tables[i, full] != entry[full]
+    ceil = lambda x: -(-x // bs)
+    physical = sum(ceil(int(x)) for x in S) + int(sum(ceil(int(L[i])) - int(S[pref[i]]) // bs
+                                                    for i in range(wl.num_seqs)))
+    assert wl.meta["physical_blocks"] == physical
+    # distinct slots the batch reads: each prompt's full blocks once, and each
+    # request's own blocks (its copy of the prompt's tail, then its tokens)
+    row = 2 * wl.num_kv_heads * wl.head_dim * wl.esize
+    shared = bs * (S // bs)
+    assert wl.unique_kv_bytes() == row * int(shared.sum() + (L - shared[pref]).sum())
+
+
+def test_system_prompt_requests_read_prompt_then_own_tokens():
+    """Replaying the workload's history with the oracle's cache ops on slot
+    ids: each request reads, through its table, its system prompt's tokens
+    followed by exactly its own tokens in order; its copy of the prompt's
+    last block holds the prompt's tail and then its first own token."""
+    import oracle
+    bs = 8
+    wl = workloads.build_system_prompt(num_prefixes=3, requests_per_prefix=4,
+                                       prefix_blocks=(1, 5), prefix_extra=(1, 7),
+                                       own_prompt=(1, 20), max_gen=9, num_kv_heads=1,
+                                       num_q_heads=1, head_dim=4, block_size=bs,
+                                       num_blocks=256, tensors=False, seed=9)
+    nb = wl.num_blocks
+    k = np.arange(nb * bs, dtype=np.int64).reshape(nb, 1, bs, 1).repeat(4, axis=3)
+    v = -k
+    S, pref = wl.meta["prefix_lens"], wl.meta["prefix_of"]
+    entries = wl.meta["entry_tables"]
+    expect = [[entries[pref[i]][p // bs] * bs + p % bs for p in range(int(S[pref[i]]))]
+              for i in range(wl.num_seqs)]
+    for step, st in enumerate(wl.history):
+        oracle.copy_blocks(k, v, st.copy_pairs)
+        ids = 10**7 * (step + 1) + np.arange(len(st.slot_mapping), dtype=np.int64)
+        new = np.repeat(ids[:, None, None], 4, axis=2)
+        oracle.reshape_and_cache(new, -new, k, v, st.slot_mapping)
+        for j, i in enumerate(st.seq_index.tolist()):
+            expect[i].append(int(ids[j]))
+    for i in range(wl.num_seqs):
+        L = int(wl.context_lens[i])
+        assert L == len(expect[i])
+        tab = wl.block_tables[i]
+        got = [int(k[tab[p // bs], 0, p % bs, 0]) for p in range(L)]
+        assert got == expect[i], f"request {i}"
+        assert all(int(v[tab[p // bs], 0, p % bs, 3]) == -e for p, e in enumerate(got))
+
+
 # ------------------------------------------------- grouped decode tile lists
 
 def _expand(members, tiles, start):

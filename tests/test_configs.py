@@ -35,6 +35,7 @@ CASES = {
     "long_context_gqa_bf16": (8, 1024),
     "sharing_fp16": (8, 512),
     "beam_search_fp16": (8, 512),
+    "system_prompt_bf16": (8, 512),
 }
 
 
@@ -97,7 +98,7 @@ def test_full_size_step_matches_oracle(name):
                                  torch.from_numpy(st.slot_mapping).to(DEV))
             n_tok += len(st.slot_mapping)
     torch.cuda.synchronize()
-    if name in ("sharing_fp16", "beam_search_fp16"):
+    if name in ("sharing_fp16", "beam_search_fp16", "system_prompt_bf16"):
         assert n_pairs > 0 and n_tok > 0, "the sharing workloads must copy and write"
     if name == "llama3_8b_gqa_bf16":
         assert n_tok == wl.num_seqs

@@ -174,12 +174,19 @@ def test_out_of_pool_block_gives_nan_rows(part_tiles):
 
 
 @pytest.mark.parametrize("part_tiles", [0, 32])
-@pytest.mark.parametrize("name", ["sharing_fp16", "beam_search_fp16"])
+@pytest.mark.parametrize("name", ["sharing_fp16", "beam_search_fp16", "system_prompt_bf16"])
 def test_full_size_workloads_sampled(name, part_tiles):
+    """The grouped decode at full size: forks of one prompt, beams, and
+    distinct requests sharing cached system prompts (grouped heads: 16 / G
+    members per group), against the oracle on sampled rows and against the
+    per-sequence decode."""
     say("grouped full size", name, part_tiles)
     wl = workloads.make(name, device=DEV)
-    groups = bmod.share_groups(wl.block_tables, wl.context_lens, 8)
-    lists = _lists(wl.block_tables, wl.context_lens, groups, wl.block_size, 8)
+    mm = min(8, 16 // wl.group)
+    groups = bmod.share_groups(wl.block_tables, wl.context_lens, mm)
+    if name == "system_prompt_bf16":
+        assert all(len(g) == mm for g in groups)   # every group shares a prompt
+    lists = _lists(wl.block_tables, wl.context_lens, groups, wl.block_size, mm)
     lens_d = torch.from_numpy(wl.context_lens).to(DEV)
     got = _grouped(wl.q, wl.k_cache, wl.v_cache, lens_d, lists, wl.scale,
                    int(wl.context_lens.max()), part_tiles)
