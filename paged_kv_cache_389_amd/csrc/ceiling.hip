@@ -118,15 +118,15 @@ int pkv_ceiling_gather_read(const void* pool, size_t pool_bytes, const int32_t* 
   const char* p = static_cast<const char*>(pool);
   switch (chunk_bytes) {
     case 2048:
-      hipLaunchKernelGGL(gather_read_kernel<2048, 9>, dim3(workgroups), dim3(256), 0, st, p,
+      hipLaunchKernelGGL((gather_read_kernel<2048, 9>), dim3(workgroups), dim3(256), 0, st, p,
                          pool_chunks, chunks, num_chunks, per_wave, sink);
       break;
     case 4096:
-      hipLaunchKernelGGL(gather_read_kernel<4096, 5>, dim3(workgroups), dim3(256), 0, st, p,
+      hipLaunchKernelGGL((gather_read_kernel<4096, 5>), dim3(workgroups), dim3(256), 0, st, p,
                          pool_chunks, chunks, num_chunks, per_wave, sink);
       break;
     default:
-      hipLaunchKernelGGL(gather_read_kernel<8192, 3>, dim3(workgroups), dim3(256), 0, st, p,
+      hipLaunchKernelGGL((gather_read_kernel<8192, 3>), dim3(workgroups), dim3(256), 0, st, p,
                          pool_chunks, chunks, num_chunks, per_wave, sink);
       break;
   }
