@@ -239,6 +239,37 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                int max_blocks_per_seq, int max_context_len, pkv_dtype dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch pkv_paged_attention_decode_noalloc holds per GPU. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * paged_attention_decode_noalloc: pkv_paged_attention_decode (same
+ * arguments without the workspace, the library's own plan) for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no hipMalloc, hipFree or
+ * other allocating routine; its workspace is a scratch array of
+ * PKV_NOALLOC_SCRATCH_BYTES in device memory that the library holds on every
+ * GPU it runs on until the process ends (looked up on its first call on a
+ * device).  Results are those of pkv_paged_attention_decode with a workspace
+ * of its own (the same kernels and plan).
+ *
+ * A call whose plan needs more workspace than that
+ * (pkv_paged_attention_workspace_bytes(..., 0, PKV_PATH_AUTO, PKV_GRID_AUTO)
+ * above PKV_NOALLOC_SCRATCH_BYTES) returns PKV_EWORKSPACE before touching the
+ * device, with the sizes in pkv_last_error(); argument errors as
+ * pkv_paged_attention_decode.  Every call on one GPU uses that GPU's one
+ * array, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give wrong results; order
+ * them, for example on one stream.
+ */
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int num_seqs,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, int max_blocks_per_seq,
+                                       int max_context_len, pkv_dtype dtype, void* stream);
+
 /* Same as pkv_paged_attention_decode with an explicit partition size
  * (0 = library choice; see pkv_paged_attention_plan for the rules), kernel
  * variant (pkv_decode_path) and grid (pkv_grid).  Used for tuning sweeps,

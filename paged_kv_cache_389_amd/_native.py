@@ -114,6 +114,9 @@ def _load():
     lib.pkv_group_tiles_capacity.argtypes = [i32] * 5
     lib.pkv_paged_attention_grouped_workspace_bytes.restype = sz
     lib.pkv_paged_attention_grouped_workspace_bytes.argtypes = [i32] * 5
+    lib.pkv_paged_attention_decode_noalloc.restype = i32
+    lib.pkv_paged_attention_decode_noalloc.argtypes = [
+        vp, vp, vp, vp, i32p, i32p, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_ceiling_stream_read.restype = i32
     lib.pkv_ceiling_stream_read.argtypes = [vp, sz, i32, vp, vp]
     lib.pkv_ceiling_gather_read.restype = i32
@@ -133,8 +136,9 @@ EXPORTED = (
     "pkv_paged_attention_prefill", "pkv_paged_attention_prefill_fp8",
     "pkv_paged_attention_decode_grouped", "pkv_paged_attention_decode_grouped_fp8",
     "pkv_paged_attention_grouped_workspace_bytes", "pkv_group_tiles", "pkv_group_tiles_capacity",
-    "pkv_ceiling_stream_read", "pkv_ceiling_gather_read",
+    "pkv_ceiling_stream_read", "pkv_ceiling_gather_read", "pkv_paged_attention_decode_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 
 def version() -> str:
@@ -249,6 +253,37 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
             int(max_context_len), _DTYPE_CODE[q.dtype], ws_ptr, ws_len, int(partition_tokens),
             int(path), int(grid), ev0, ev1, _stream(q, stream))
     _check("paged_attention_decode", st)
+    return out
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   max_context_len, stream=None):
+    """:func:`paged_attention_decode` without a workspace argument: the
+    library's own device scratch serves as workspace
+    (``pkv_paged_attention_decode_noalloc``), so nothing is allocated; calls
+    whose plan needs more than ``NOALLOC_SCRATCH_BYTES`` raise.  Calls on one
+    device share that scratch and must be ordered (one stream)."""
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _dev(t, n)
+    if q.dtype not in _DTYPE_CODE or any(t.dtype != q.dtype for t in (out, k_cache, v_cache)):
+        raise ValueError("q, out and both caches must share one supported dtype")
+    if q.dim() != 3 or out.shape != q.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or k_cache.shape[3] != q.shape[2]:
+        raise ValueError("q/out [num_seqs, Hq, hd] and caches [num_blocks, Hkv, bs, hd] expected")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            context_lens.dtype != torch.int32 or context_lens.shape != (q.shape[0],) or \
+            block_tables.shape[0] != q.shape[0]:
+        raise ValueError("block_tables int32 [num_seqs, W] and context_lens int32 [num_seqs]")
+    num_seqs, hq, hd = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    with torch.cuda.device(q.device):
+        st = lib.pkv_paged_attention_decode_noalloc(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), ctypes.c_float(scale), num_seqs, hq, hkv, hd, bs, nb,
+            block_tables.shape[1], int(max_context_len), _DTYPE_CODE[q.dtype],
+            _stream(q, stream))
+    _check("paged_attention_decode_noalloc", st)
     return out
 
 

@@ -416,6 +416,43 @@ size_t workspace_for(int num_seqs, int num_q_heads, int num_kv_heads, int head_d
   return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, pl).total;
 }
 
+// ------------------------------------------------ allocation-free decode
+//
+// The workspace of pkv_paged_attention_decode_noalloc: one array in device
+// memory per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not a device address: the
+// device address is taken once per device with hipGetSymbolAddress (with
+// that device current) and only that address is passed to the kernels.
+// Calls on one GPU share its array; nothing in it needs to start at zero
+// (the decode writes every partial state and list entry it reads).
+constexpr size_t kNoAllocScratchBytes = (size_t)PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, then cached).
+int noalloc_scratch(void** out) {
+  static void* cached[kMaxDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail_hip(err);
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "device index beyond the library's table";
+    return PKV_EUNSUPPORTED;
+  }
+  void* p = __atomic_load_n(&cached[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return fail_hip(err);
+    if (!p) {
+      g_last_error = "hipGetSymbolAddress returned no address for the scratch array";
+      return PKV_EHIP;
+    }
+    __atomic_store_n(&cached[dev], p, __ATOMIC_RELEASE);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 
 }  // namespace
 
@@ -636,6 +673,41 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                        block_size, num_blocks, max_blocks_per_seq,
                                        max_context_len, dtype, workspace, workspace_bytes, 0,
                                        PKV_PATH_AUTO, PKV_GRID_AUTO, stream);
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int num_seqs,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, int max_blocks_per_seq,
+                                       int max_context_len, pkv_dtype dtype, void* stream) {
+  // the workspace this call would need, before anything touches the device
+  const size_t need = pkv_paged_attention_workspace_bytes(
+      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+      max_context_len, dtype, 0, PKV_PATH_AUTO, PKV_GRID_AUTO);
+  if (need == (size_t)-1) {
+    // the argument error pkv_paged_attention_decode reports for these sizes
+    return pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      num_blocks, max_blocks_per_seq, max_context_len, dtype,
+                                      nullptr, 0, stream);
+  }
+  if (need > kNoAllocScratchBytes) {
+    g_last_error = "the call needs " + std::to_string(need) +
+                   " bytes of workspace, more than the " +
+                   std::to_string(kNoAllocScratchBytes) +
+                   " bytes of scratch the allocation-free entry point holds";
+    return PKV_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = noalloc_scratch(&ws);
+    if (rc != PKV_OK) return rc;
+  }
+  return pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    num_blocks, max_blocks_per_seq, max_context_len, dtype, ws,
+                                    ws ? kNoAllocScratchBytes : 0, stream);
 }
 
 int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -1,0 +1,119 @@
+"""The allocation-free decode entry point (GPU), through the C ABI: its
+output equals pkv_paged_attention_decode's (same kernels and plan, own
+workspace) bit for bit and the float64 oracle within tolerance, on two calls
+in a row, the second smaller, with plans that use the scratch (split
+contexts merged by the second kernel); sizes beyond the scratch are refused
+before the device is touched."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+from gpu_helpers import DEV, TOL, max_err, say, upload_case
+from paged_kv_cache_389_amd import _native as pk
+
+pytestmark = pytest.mark.gpu
+
+SCRATCH = pk.NOALLOC_SCRATCH_BYTES
+
+
+def _noalloc(dev, scale, max_len):
+    """pkv_paged_attention_decode_noalloc through ctypes on the current stream."""
+    q, kc = dev["q"], dev["k"]
+    out = torch.full_like(q, float("nan"))
+    nb, hkv, bs, hd = kc.shape
+    st = pk.lib.pkv_paged_attention_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), kc.data_ptr(), dev["v"].data_ptr(),
+        dev["tables"].data_ptr(), dev["lens"].data_ptr(), ctypes.c_float(scale), q.shape[0],
+        q.shape[1], hkv, hd, bs, nb, dev["tables"].shape[1], int(max_len),
+        pk._DTYPE_CODE[q.dtype], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, pk.lib.pkv_last_error().decode()
+    return out
+
+
+def _with_workspace(dev, scale, max_len):
+    out = torch.empty_like(dev["q"])
+    pk.paged_attention_decode(out, dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
+                              scale, max_len)
+    return out
+
+
+def _case(seed, lens, hq, hkv, hd, bs, dtype):
+    rng = np.random.default_rng(seed)
+    q, ks, vs, nblk = pins.random_case(rng, len(lens), hq, hkv, hd, lens, bs)
+    kp, vp, tables, _, _ = pins.page(ks, vs, bs, nblk, rng)
+    dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, np.array(lens), dtype)
+    return dev, (qt, kt, vt, tables)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,first,second", [
+    (torch.bfloat16, 8, 2, [5000, 3000, 17], [2100, 40]),      # grouped heads: MFMA kernel
+    (torch.float16, 4, 4, [4500, 1, 700], [1300, 33]),         # MHA: vector-ALU kernel
+    (torch.float32, 2, 1, [3000, 2999], [600]),                # fp32
+])
+def test_noalloc_equals_the_workspace_call_twice(dtype, hq, hkv, first, second):
+    hd, bs = 128, 16
+    scale = 1.0 / np.sqrt(hd)
+    for call, lens in enumerate((first, second)):
+        say("noalloc decode", dtype, hq, hkv, "call", call, lens)
+        dev, (qt, kt, vt, tables) = _case(700 + call, lens, hq, hkv, hd, bs, dtype)
+        plan = pk.plan(len(lens), hq, hkv, hd, bs, tables.shape[1], max(lens), dtype)
+        assert plan["max_parts"] > 1 and 0 < plan["workspace_bytes"] <= SCRATCH, plan
+        got = _noalloc(dev, scale, max(lens))
+        ref = _with_workspace(dev, scale, max(lens))
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), \
+            "allocation-free call differs from the workspace call"
+        want = oracle.decode(qt, kt, vt, tables, np.array(lens), scale, hkv)
+        assert max_err(got, want) <= TOL[dtype]
+
+
+def test_noalloc_without_split_needs_no_scratch():
+    """A plan with one partition per sequence needs no workspace; the call
+    still runs (the scratch is not looked up) and matches the oracle."""
+    say("noalloc no split")
+    lens = [30, 1, 200, 77] * 64
+    dev, (qt, kt, vt, tables) = _case(720, lens, 8, 2, 128, 16, torch.bfloat16)
+    assert pk.workspace_bytes(len(lens), 8, 2, 128, 16, tables.shape[1], max(lens),
+                              torch.bfloat16) == 0
+    got = _noalloc(dev, 0.1, max(lens))
+    torch.cuda.synchronize()
+    want = oracle.decode(qt, kt, vt, tables, np.array(lens), 0.1, 2)
+    assert max_err(got, want) <= 2e-2
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch():
+    """A plan needing more workspace than the scratch returns PKV_EWORKSPACE
+    before any launch (null pointers: nothing could be read or written)."""
+    n, hq, mb, L = 1024, 32, 6250, 100000
+    need = pk.workspace_bytes(n, hq, hq, 128, 16, mb, L, torch.float16)
+    assert need > SCRATCH
+    st = pk.lib.pkv_paged_attention_decode_noalloc(None, None, None, None, None, None,
+                                                   ctypes.c_float(0.1), n, hq, hq, 128, 16,
+                                                   100000, mb, L, pk.PKV_F16, None)
+    assert st == -3
+    assert b"scratch" in pk.lib.pkv_last_error()
+
+
+def test_noalloc_planned_grid_lists_items_in_scratch():
+    """More than 1024 sequences over more than one round of workgroups: the
+    planning kernel lists the work items in the scratch; two calls in a row,
+    the second smaller, equal the workspace call bit for bit."""
+    rng = np.random.default_rng(730)
+    for call, n in enumerate((1100, 1050)):
+        lens = rng.integers(1, 300, size=n).tolist()
+        say("noalloc planned grid", call, n)
+        dev, (qt, kt, vt, tables) = _case(731 + call, lens, 8, 2, 128, 16, torch.float16)
+        plan = pk.plan(n, 8, 2, 128, 16, tables.shape[1], max(lens), torch.float16)
+        assert plan["grid"] == pk.GRID_PLANNED and 0 < plan["workspace_bytes"] <= SCRATCH, plan
+        got = _noalloc(dev, 0.09, max(lens))
+        ref = _with_workspace(dev, 0.09, max(lens))
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
+        sample = sorted(rng.choice(n, 24, replace=False).tolist())
+        want = oracle.decode(qt, kt, vt, tables, np.array(lens), 0.09, 2, seqs=sample)
+        assert max_err(got[sample], want[sample]) <= 2e-2
