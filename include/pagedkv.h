@@ -102,6 +102,19 @@ typedef enum {
                               block j is physical block s*max_blocks_per_seq + j */
 } pkv_decode_path;
 
+/* OR-ed into the path argument (decode, plan and workspace calls): sequences
+ * of the batch share physical blocks (forks of one prompt, beams, cached
+ * prompts; "Memory Optimization in LLM Serving with PagedAttention", section
+ * "Advanced Capabilities: Memory Sharing with Copy-on-Write").  Without it
+ * the kernels read K/V with streaming (nontemporal) loads, which suit a
+ * batch whose blocks are each read once per call (the lines are not kept for
+ * reuse; a random gather of 4 KiB tiles measured 6.2-6.5 TB/s with them
+ * against 5.6-5.8 TB/s without).  With it the K/V loads keep the cache's
+ * default policy, so a block read by several sequences of the call is served
+ * from the cache after its first read.  The result is the same either way;
+ * only the speed differs. */
+#define PKV_PATH_SHARED_BLOCKS 0x100
+
 /* Library version, e.g. "pagedkv 0.1.0 gfx950". Static string. */
 const char* pkv_version(void);
 

@@ -31,7 +31,7 @@ _NATIVE = ("paged_attention_decode", "reshape_and_cache", "copy_blocks", "swap_b
            "group_tiles",
            "workspace_bytes", "plan",
            "version", "NativeLibraryMissing", "PagedKVError", "PATH_AUTO", "PATH_VALU",
-           "PATH_MFMA", "PATH_CONTIGUOUS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")
+           "PATH_MFMA", "PATH_CONTIGUOUS", "PATH_SHARED_BLOCKS", "GRID_AUTO", "GRID_DIRECT", "GRID_PLANNED", "HipEvent")
 
 __all__ = list(_NATIVE) + ["block_manager", "workloads"]
 

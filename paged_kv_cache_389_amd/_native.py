@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 PKV_F32, PKV_F16, PKV_BF16, PKV_E4M3 = 0, 1, 2, 3
 KV_E4M3 = 0x100   # OR-ed into a q dtype code: the caches hold E4M3 codes
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_CONTIGUOUS = 0, 1, 2, 3
+# OR-ed into a path: the batch's sequences share blocks (cached K/V loads)
+PATH_SHARED_BLOCKS = 0x100
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
 # element types of caches the byte-moving calls accept (uint8: E4M3 codes)
 _CACHE_CODE = {**_DTYPE_CODE, torch.uint8: PKV_E4M3}
@@ -214,7 +216,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (context_lens, "context_lens")):
         _dev(t, n)
-    if path != PATH_CONTIGUOUS or block_tables is not None:
+    if (path & 0xFF) != PATH_CONTIGUOUS or block_tables is not None:
         _dev(block_tables, "block_tables")
         if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
             raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")

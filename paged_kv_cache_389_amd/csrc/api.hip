@@ -48,6 +48,15 @@ int fail_hip(hipError_t e) {
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// The path argument of the decode calls: a pkv_decode_path, optionally
+// OR-ed with PKV_PATH_SHARED_BLOCKS (K/V loads that keep blocks in the cache
+// for the other sequences of the batch that share them).
+bool split_path(int path, int* kernel, bool* shared) {
+  *shared = (path & PKV_PATH_SHARED_BLOCKS) != 0;
+  *kernel = path & ~PKV_PATH_SHARED_BLOCKS;
+  return *kernel >= PKV_PATH_AUTO && *kernel <= PKV_PATH_CONTIGUOUS;
+}
+
 // ------------------------------------------------------------ debug checks
 //
 // With PKV_DEBUG=1 in the environment every call synchronises its stream,
@@ -484,9 +493,10 @@ size_t pkv_paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int nu
                                            int head_dim, int block_size, int max_blocks_per_seq,
                                            int max_context_len, pkv_dtype dtype,
                                            int partition_tokens, int path, int grid) {
+  bool shared = false;
   if (!plan_dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      partition_tokens < 0 || !split_path(path, &path, &shared) ||
       grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED || num_q_heads % num_kv_heads)
     return (size_t)-1;
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -499,9 +509,10 @@ int pkv_paged_attention_plan(int num_seqs, int num_q_heads, int num_kv_heads, in
                              int block_size, int max_blocks_per_seq, int max_context_len,
                              pkv_dtype dtype, int partition_tokens, int path, int grid,
                              pkv_plan* out) {
+  bool shared = false;
   if (!plan_dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      partition_tokens < 0 || path < PKV_PATH_AUTO || path > PKV_PATH_CONTIGUOUS ||
+      partition_tokens < 0 || !split_path(path, &path, &shared) ||
       grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED || num_q_heads % num_kv_heads)
     return PKV_EINVAL;
   const Plan pl = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -531,10 +542,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int max_blocks_per_seq, int max_context_len, int dtype, void* workspace,
                 size_t workspace_bytes, int partition, int path, int grid, void* begin_event,
                 void* end_event, void* stream) {
+  bool shared_blocks = false;
   if (!dtype_ok(dtype) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0 || partition < 0 || path < PKV_PATH_AUTO ||
-      path > PKV_PATH_CONTIGUOUS || grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED)
+      max_context_len < 0 || partition < 0 || !split_path(path, &path, &shared_blocks) ||
+      grid < PKV_GRID_AUTO || grid > PKV_GRID_PLANNED)
     return PKV_EINVAL;
   if (num_q_heads % num_kv_heads) return PKV_EINVAL;
   if (kv_fp8 && (!finite_nonzero(k_scale) || !finite_nonzero(v_scale))) return PKV_EINVAL;
@@ -589,6 +601,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.part_align = pl.part_align;
   a.max_parts = pl.max_parts;
   a.contiguous = contiguous ? 1 : 0;
+  a.cached_kv = shared_blocks ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -640,7 +653,7 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache
                                    void* workspace, size_t workspace_bytes, int partition,
                                    int path, int grid, void* begin_event, void* end_event,
                                    void* stream) {
-  if (path == PKV_PATH_CONTIGUOUS) return PKV_EUNSUPPORTED;
+  if ((path & ~PKV_PATH_SHARED_BLOCKS) == PKV_PATH_CONTIGUOUS) return PKV_EUNSUPPORTED;
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, true, k_scale,
                      v_scale, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, dtype, workspace,

@@ -162,17 +162,17 @@ decode_grouped_kernel(GroupedArgs a) {
       const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
       const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
 #pragma unroll
-      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
+      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16<kStream>(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (VL == 1) {
-          vv[r][0] = bld4(vt, voff, r * HD * sizeof(T));
+          vv[r][0] = bld4<kStream>(vt, voff, r * HD * sizeof(T));
         } else if constexpr (VL == 2) {
-          const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
+          const u32x2 x = bld8<kStream>(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
         } else {
-          const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
+          const u32x4 x = bld16<kStream>(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
           vv[r][2] = x[2];

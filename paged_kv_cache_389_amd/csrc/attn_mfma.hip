@@ -102,7 +102,12 @@ __device__ inline int mfma_first_blocks(const DecodeArgs& a, int s, int ta, int 
 // C is the cache element: E itself, or E4M3 codes, which are loaded at half
 // the width and turned into E's 16-bit values right before the products
 // (the scales are applied outside: K's in scale_log2e, V's on the output).
-template <typename E, typename C, int HD, int BS, bool kWaitQ = false, int NS = kMfmaStages>
+//
+// POL is the cache policy of the K/V loads: kStream (each block is read once
+// per launch) or 0 (blocks shared across the batch, served from the cache
+// after their first read; DecodeArgs::cached_kv).
+template <typename E, typename C, int HD, int BS, bool kWaitQ = false, int NS = kMfmaStages,
+          int POL = kStream>
 __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
                                        int first, int stride, int tbl0, const u32x4 (*q)[kWave],
                                        MfmaState<HD / 16>& st) {
@@ -165,17 +170,17 @@ __device__ inline void mfma_accumulate(const DecodeArgs& a, int s, int g, int L,
       const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
       const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
 #pragma unroll
-      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
+      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16<POL>(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (VL == 1) {
-          vv[r][0] = bld4(vt, voff, r * HD * sizeof(T));
+          vv[r][0] = bld4<POL>(vt, voff, r * HD * sizeof(T));
         } else if constexpr (VL == 2) {
-          const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
+          const u32x2 x = bld8<POL>(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
         } else {
-          const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
+          const u32x4 x = bld16<POL>(vt, voff, r * HD * sizeof(T));
           vv[r][0] = x[0];
           vv[r][1] = x[1];
           vv[r][2] = x[2];
@@ -306,7 +311,7 @@ __device__ inline void mfma_state_init(MfmaState<DPL>& st) {
 // normalised and rounded into `out` (the group's first head) when `out` is
 // not null, else stored unnormalised to the partial states
 // state0 + hh * hh_stride (hh < G).
-template <typename E, typename C, int HD, int BS, int GMAX>
+template <typename E, typename C, int HD, int BS, int GMAX, int POL>
 __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int ta, int tb,
                                   int tbl0, typename E::storage* out, size_t state0,
                                   size_t hh_stride, MfmaShared<HD, GMAX>& sm) {
@@ -318,7 +323,8 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
 
   MfmaState<DPL> st;
   mfma_state_init(st);
-  mfma_accumulate<E, C, HD, BS, true>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q, st);
+  mfma_accumulate<E, C, HD, BS, true, kMfmaStages, POL>(a, s, g, L, ta, tb, wave, NW, tbl0, sm.q,
+                                                        st);
 
   // the four token groups of a head column hold partial sums of l
   const float l = rows_sum(st.l);
@@ -370,7 +376,7 @@ __device__ inline void mfma_piece(const DecodeArgs& a, int s, int g, int L, int 
 
 // One workgroup per (work item, KV head g): the grid is described with
 // DecodeArgs.
-template <typename E, typename C, int HD, int BS, int GMAX>
+template <typename E, typename C, int HD, int BS, int GMAX, int POL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
     DecodeArgs a) {
   using T = typename E::storage;
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   const int tbl0 = mfma_first_blocks<BS>(a, s, ta, wave, 4);
   if (wave == 0) mfma_load_q<E, C, HD>(a, s, g, sm.q);
   const size_t state0 = ((size_t)s * a.num_q_heads + (size_t)g * G) * a.max_parts + w.part;
-  mfma_piece<E, C, HD, BS, GMAX>(a, s, g, w.t1, ta, tb, tbl0, w.n == 1 ? out : nullptr, state0,
+  mfma_piece<E, C, HD, BS, GMAX, POL>(a, s, g, w.t1, ta, tb, tbl0, w.n == 1 ? out : nullptr, state0,
                                  a.max_parts, sm);
 }
 
@@ -398,7 +404,10 @@ template <typename E, typename C, int HD, int BS, int GMAX>
 static void launch_mfma_g(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid = a.planned ? dim3(a.num_kv_heads * a.max_parts * a.num_seqs)
                               : dim3(a.num_kv_heads * a.max_parts, 1, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<E, C, HD, BS, GMAX>), grid, dim3(256), 0, st, a);
+  if (a.cached_kv)
+    hipLaunchKernelGGL((decode_mfma_kernel<E, C, HD, BS, GMAX, 0>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<E, C, HD, BS, GMAX, kStream>), grid, dim3(256), 0, st, a);
 }
 
 template <typename E, typename C, int HD, int BS>
@@ -416,9 +425,9 @@ template <typename E, typename C, int HD, int BS>
 static int occupancy_t(int group) {
   int n = 0;
   const void* f =
-      group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 4>)
-      : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 8>)
-                   : reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 16>);
+      group <= 4 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 4, kStream>)
+      : group <= 8 ? reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 8, kStream>)
+                   : reinterpret_cast<const void*>(&decode_mfma_kernel<E, C, HD, BS, 16, kStream>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess) return 0;
   return n;
 }

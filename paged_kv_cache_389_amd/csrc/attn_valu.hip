@@ -96,7 +96,7 @@ __device__ inline ValuMeta<KvDot<E, C>::QW> valu_meta(const DecodeArgs& a, int s
 // sequence s (unit = UT tokens; tokens at or past L > 0 are masked) into the
 // calling wave's state, given the piece's ValuMeta.  Row group `row` of the wave
 // sees every RPI-th token.
-template <typename E, typename C, int HD, int BS>
+template <typename E, typename C, int HD, int BS, int POL>
 __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
                                        int first, int stride,
                                        const ValuMeta<KvDot<E, C>::QW>& meta,
@@ -147,9 +147,9 @@ __device__ inline void valu_accumulate(const DecodeArgs& a, int s, int h, int L,
       const rsrc_t kt = make_rsrc(kbase + off, kUnitBytes);
       const rsrc_t vt = make_rsrc(vbase + off, kUnitBytes);
 #pragma unroll
-      for (int c = 0; c < CH; ++c) kr[c] = bld16(kt, loff, c * RPI * HD * sizeof(T));
+      for (int c = 0; c < CH; ++c) kr[c] = bld16<POL>(kt, loff, c * RPI * HD * sizeof(T));
 #pragma unroll
-      for (int c = 0; c < CH; ++c) vr[c] = bld16(vt, loff, c * RPI * HD * sizeof(T));
+      for (int c = 0; c < CH; ++c) vr[c] = bld16<POL>(vt, loff, c * RPI * HD * sizeof(T));
     };
 
     // fold the wave's i-th unit into the online state
@@ -286,7 +286,7 @@ __device__ inline void valu_emit(float M, float Ls, float* O, bool bad, int col,
 // Attention of query head h of sequence s over its units [ta, tb) (tokens
 // at or past L > 0 masked), by the four waves of the workgroup (unit round-robin),
 // merged in LDS.  Result as in valu_emit.
-template <typename E, typename C, int HD, int BS>
+template <typename E, typename C, int HD, int BS, int POL>
 __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int ta, int tb,
                                   const ValuMeta<KvDot<E, C>::QW>& meta,
                                   typename E::storage* out, float* po, float* pml,
@@ -302,7 +302,7 @@ __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int 
 #pragma unroll
   for (int e = 0; e < VEC; ++e) st.o[e] = 0.f;
   st.bad = 0;
-  valu_accumulate<E, C, HD, BS>(a, s, h, L, ta, tb, wave, NW, meta, st);
+  valu_accumulate<E, C, HD, BS, POL>(a, s, h, L, ta, tb, wave, NW, meta, st);
   valu_row_merge<VEC, LPR>(st);
 
   // merge the 4 waves in LDS
@@ -350,7 +350,9 @@ __device__ inline void valu_piece(const DecodeArgs& a, int s, int h, int L, int 
 
 // One workgroup per (work item, query head h): the grid is described with
 // DecodeArgs.
-template <typename E, typename C, int HD, int BS>
+// POL: cache policy of the K/V loads (kStream, or 0 when blocks are shared
+// across the batch; DecodeArgs::cached_kv).
+template <typename E, typename C, int HD, int BS, int POL>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   using T = typename E::storage;
   constexpr int UT = ValuTiling<C, HD, BS>::UT;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int ta = w.t0 / UT, tb = (w.t1 + UT - 1) / UT;
   const auto meta = valu_meta<E, C, HD, BS>(a, s, h, ta, uniform(threadIdx.x / kWave), 4);
   const size_t pidx = ((size_t)s * a.num_q_heads + h) * a.max_parts + w.part;
-  valu_piece<E, C, HD, BS>(a, s, h, w.t1, ta, tb, meta, w.n == 1 ? out : nullptr,
+  valu_piece<E, C, HD, BS, POL>(a, s, h, w.t1, ta, tb, meta, w.n == 1 ? out : nullptr,
                            a.part_o + pidx * HD, a.part_ml + 2 * pidx, sm);
 }
 
@@ -387,7 +389,10 @@ static hipError_t launch_valu_t(const DecodeArgs& a, hipStream_t st) {
   } else {
     const dim3 grid = a.planned ? dim3(a.num_q_heads * a.max_parts * a.num_seqs)
                                 : dim3(a.num_q_heads * a.max_parts, 1, a.num_seqs);
-    hipLaunchKernelGGL((decode_valu_kernel<E, C, HD, BS>), grid, dim3(256), 0, st, a);
+    if (a.cached_kv)
+      hipLaunchKernelGGL((decode_valu_kernel<E, C, HD, BS, 0>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<E, C, HD, BS, kStream>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
 }
@@ -399,7 +404,7 @@ static int occupancy_t() {
   } else {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&decode_valu_kernel<E, C, HD, BS>), 256, 0) !=
+            &n, reinterpret_cast<const void*>(&decode_valu_kernel<E, C, HD, BS, kStream>), 256, 0) !=
         hipSuccess)
       return 0;
     return n;

@@ -49,6 +49,9 @@ struct DecodeArgs {
   int contiguous;             // 1: ignore tables; block j of seq s is s*max_blocks + j
   int planned;                // 0: direct grid; 1: planned, each workgroup finds its item
                               // (B <= 1024); 2: planned, items listed by the planning kernel
+  int cached_kv;              // 1: K/V loads keep the cache's default policy (blocks shared
+                              // across the batch are served from the cache after their first
+                              // read); 0: streaming (nontemporal) loads, each block read once
 };
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };

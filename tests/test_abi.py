@@ -156,6 +156,8 @@ def _decode(lib, **over):
     (dict(B=4000, Hq=4, Hkv=4, maxL=64, maxb=4), -3),   # planned grid and no workspace
     (dict(part=-1), -1),
     (dict(grid=3), -1),
+    (dict(path=0x200), -1),            # an unknown flag bit
+    (dict(path=0x104), -1),            # the shared-blocks flag on an unknown path
     (dict(path=7), -1),
 ])
 def test_decode_rejects_bad_arguments_before_launch(native, over, status):
@@ -363,3 +365,21 @@ def test_ceiling_reads_reject_bad_arguments(native):
     assert lib.pkv_ceiling_gather_read(16, 1024, 16, 4, 4096, 8, 16, None) == -1   # pool < chunk
     assert lib.pkv_ceiling_gather_read(16, 1 << 20, None, 4, 4096, 8, 16, None) == -1
     assert lib.pkv_ceiling_gather_read(16, 1 << 20, 16, 0, 4096, 8, 16, None) == -1
+
+
+def test_shared_blocks_flag_is_accepted_and_changes_no_plan(native):
+    """PKV_PATH_SHARED_BLOCKS only changes the K/V load policy: plan and
+    workspace are those of the path without it, for every kernel path."""
+    f16 = 1
+    for path in (0, 1, 2, 3):
+        for sizes in ((4, 8, 2, 128, 16, 64, 1000), (300, 32, 8, 128, 16, 256, 4000),
+                      (8, 40, 40, 128, 16, 128, 2048)):
+            b, hq, hkv, hd, bs, mb, ml = sizes
+            if path == 2 and hq == hkv:
+                continue
+            a = native.plan(b, hq, hkv, hd, bs, mb, ml, f16, 0, path)
+            c = native.plan(b, hq, hkv, hd, bs, mb, ml, f16, 0, path | native.PATH_SHARED_BLOCKS)
+            assert a == c
+            assert native.workspace_bytes(b, hq, hkv, hd, bs, mb, ml, f16, 0, path) == \
+                native.workspace_bytes(b, hq, hkv, hd, bs, mb, ml, f16, 0,
+                                       path | native.PATH_SHARED_BLOCKS)
