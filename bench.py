@@ -179,16 +179,25 @@ def counters_to_traffic(args):
     fetch, kname = pick(_counter_means(args.fetch_db), "FETCH_SIZE", is_decode)
     write, _ = pick(_counter_means(args.write_db), "WRITE_SIZE", is_decode)
     from paged_kv_cache_389_amd import workloads
-    wl = workloads.make(args.workload, device="cpu")
+    kw = {"tensors": False} if args.workload in GROUPABLE else {}
+    wl = workloads.make(args.workload, device="cpu", **kw)
     key = args.workload
-    alg = wl.min_bytes() if args.workload in PREFILL_WORKLOADS else wl.decode_bytes()
-    if args.kv_cache == "e4m3":   # one byte per K/V element
-        kv = (int(wl.context_lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim *
-              wl.esize)
-        key, alg = key + "_kv_e4m3", alg - (kv - kv // wl.esize)
+    fp8 = args.kv_cache == "e4m3"
+    logical = None
+    if args.workload in PREFILL_WORKLOADS:
+        alg = wl.min_bytes()
+        if fp8:   # one byte per K/V element
+            kv = (int(wl.context_lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads *
+                  wl.head_dim * wl.esize)
+            alg -= kv - kv // wl.esize
+    else:
+        # the bytes the bench line's roofline is taken on (each shared slot once)
+        alg, _ = roofline_bytes(wl, fp8, grouped_lists(wl, None) if args.grouped else None)
+        logical = wl.decode_bytes() - ((wl.kv_bytes() - wl.kv_bytes() // wl.esize) if fp8 else 0)
+    if fp8:
+        key += "_kv_e4m3"
     if args.grouped:
-        key, alg = key + "_grouped", grouped_decode_bytes(wl, grouped_lists(wl, {}),
-                                                          args.kv_cache == "e4m3")
+        key += "_grouped"
     try:
         with open(args.counters) as fh:
             rec = json.load(fh)
@@ -203,6 +212,8 @@ def counters_to_traffic(args):
         "write_kib_per_launch": round(write, 1),
         "hbm_bytes_per_launch": int(fetch * 1024 / f_fetch + write * 1024 / f_write),
         "alg_bytes_per_launch": alg}
+    if logical is not None and logical != alg:
+        rec["workloads"][key]["logical_bytes_per_launch"] = logical
     with open(args.counters, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)
     print(json.dumps(rec["workloads"][key]))
