@@ -929,10 +929,12 @@ def paging_control(args, headline=None, long_line=None, rounds=3):
 
 
 def practical_ceiling(reps=10):
-    """Reference reads (``csrc/ceiling.hip``): a contiguous 2 GiB stream and a
+    """Reference reads (``csrc/ceiling.hip``): a contiguous 2 GiB stream, and a
     gather of random distinct 4 KiB and 8 KiB chunks (one 16-token tile of a
-    16-bit hd-128 cache; a 32-token one) from a 2 GiB pool, at a few grid
-    sizes; GB/s of the best, from torch events around each launch."""
+    16-bit hd-128 cache; a 32-token one) from a 2 GiB pool with streaming
+    loads; then 4 KiB chunks with cached loads, and the K and V chunks of one
+    index from two 1 GiB pools (streaming and cached); each at a few grid
+    sizes, GB/s of the best, from torch events around each launch."""
     from paged_kv_cache_389_amd import _native as pk
     nbytes = 2 << 30
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
@@ -969,6 +971,24 @@ def practical_ceiling(reps=10):
                              [cus * k for k in (2, 4, 8)])
         res[f"gather_{cb // 1024}k_gbs"] = g_best
         res[f"gather_{cb // 1024}k_by_workgroups"] = g_all
+    # 4 KiB chunks with the cache's default policy, and the K and V tiles of one
+    # index from two pools (the decode's pattern), streaming and cached
+    half = buf.numel() // 2
+    k_pool, v_pool = buf[:half], buf[half:]
+    n = (3 * (nbytes // 2) // 4) // 4096
+    chunks = torch.randperm((nbytes // 2) // 4096, generator=g)[:n].to(torch.int32).cuda()
+    variants = (("gather_4k_cached", buf, None, True, (3 * nbytes // 4) // 4096),
+                ("gather_4k_two_pools", k_pool, v_pool, False, n),
+                ("gather_4k_two_pools_cached", k_pool, v_pool, True, n))
+    for name, p1, p2, cached, cnt in variants:
+        ch = chunks if p2 is not None else torch.randperm(nbytes // 4096, generator=g)[:cnt].to(
+            torch.int32).cuda()
+        moved = cnt * 4096 * (2 if p2 is not None else 1)
+        g_best, g_all = best(lambda w: pk.ceiling_gather_read(p1, ch, 4096, w, sink, pool2=p2,
+                                                              cached=cached), moved,
+                             [cus * k for k in (2, 4)])
+        res[name + "_gbs"] = g_best
+        res[name + "_by_workgroups"] = g_all
     res["frac_of_peak"] = {k: round(v / HBM_PEAK_GBS, 4) for k, v in res.items()
                            if k.endswith("_gbs") and k != "peak_gbs"}
     del buf

@@ -666,19 +666,22 @@ size_t pkv_paged_attention_grouped_workspace_bytes(int num_groups, int num_kv_he
  *
  * ceiling_gather_read: reads chunks[i] (int32 [num_chunks], device) of
  * `chunk_bytes` (2048, 4096 or 8192) bytes each, chunk c at pool + c *
- * chunk_bytes; `pool_bytes` bounds the pool, and an index outside it reads
- * nothing (no fault).  Waves take contiguous runs of the list (64 indices per
- * vector load) and keep about 16 KiB of chunk loads in flight, the way the
- * decode kernels read tiles through a block table.
+ * chunk_bytes, and at pool2 + c * chunk_bytes as well when pool2 is not NULL
+ * (the K and V tiles of one block); `pool_bytes` bounds each pool, and an
+ * index outside it reads nothing (no fault).  Waves take contiguous runs of
+ * the list (64 indices per vector load) and keep about 16 KiB of chunk loads
+ * in flight, the way the decode kernels read tiles through a block table.
+ * cached = 0: streaming (nontemporal) loads, as the decode kernels' K/V
+ * loads; 1: loads with the cache's default policy (other values PKV_EINVAL).
  *
  * Both are asynchronous on `stream`; a null pointer or a bad size returns
  * PKV_EINVAL, a failed launch PKV_EHIP.
  */
 int pkv_ceiling_stream_read(const void* src, size_t bytes, int workgroups, uint32_t* sink,
                             void* stream);
-int pkv_ceiling_gather_read(const void* pool, size_t pool_bytes, const int32_t* chunks,
-                            int num_chunks, int chunk_bytes, int workgroups, uint32_t* sink,
-                            void* stream);
+int pkv_ceiling_gather_read(const void* pool, const void* pool2, size_t pool_bytes,
+                            const int32_t* chunks, int num_chunks, int chunk_bytes, int cached,
+                            int workgroups, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

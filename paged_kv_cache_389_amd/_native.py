@@ -122,7 +122,7 @@ def _load():
     lib.pkv_ceiling_stream_read.restype = i32
     lib.pkv_ceiling_stream_read.argtypes = [vp, sz, i32, vp, vp]
     lib.pkv_ceiling_gather_read.restype = i32
-    lib.pkv_ceiling_gather_read.argtypes = [vp, sz, i32p, i32, i32, i32, vp, vp]
+    lib.pkv_ceiling_gather_read.argtypes = [vp, vp, sz, i32p, i32, i32, i32, i32, vp, vp]
     return lib
 
 
@@ -655,19 +655,26 @@ def ceiling_stream_read(src, workgroups, sink, stream=None):
     _check("ceiling_stream_read", st)
 
 
-def ceiling_gather_read(pool, chunks, chunk_bytes, workgroups, sink, stream=None):
-    """Read the ``chunk_bytes`` chunks of the device tensor ``pool`` that the
-    int32 device tensor ``chunks`` names (``pkv_ceiling_gather_read``, a
-    reference read for the practical ceiling of a paged gather)."""
+def ceiling_gather_read(pool, chunks, chunk_bytes, workgroups, sink, pool2=None, cached=False,
+                        stream=None):
+    """Read the ``chunk_bytes`` chunks of the device tensor ``pool`` (and of
+    ``pool2``, same size, when given) that the int32 device tensor ``chunks``
+    names (``pkv_ceiling_gather_read``, a reference read for the practical
+    ceiling of a paged gather); streaming loads unless ``cached``."""
     _dev(pool, "pool")
     _dev(chunks, "chunks")
     _dev(sink, "sink")
     if chunks.dtype != torch.int32 or chunks.dim() != 1:
         raise ValueError("chunks must be int32 [n]")
     nbytes = pool.numel() * pool.element_size()
+    if pool2 is not None:
+        _dev(pool2, "pool2")
+        if pool2.numel() * pool2.element_size() != nbytes:
+            raise ValueError("pool2 must have the size of pool")
     with torch.cuda.device(pool.device):
-        st = lib.pkv_ceiling_gather_read(_ptr(pool), nbytes, _ptr(chunks), chunks.numel(),
-                                         int(chunk_bytes), int(workgroups), _ptr(sink),
+        st = lib.pkv_ceiling_gather_read(_ptr(pool), _ptr(pool2) if pool2 is not None else None,
+                                         nbytes, _ptr(chunks), chunks.numel(), int(chunk_bytes),
+                                         1 if cached else 0, int(workgroups), _ptr(sink),
                                          _stream(pool, stream))
     _check("ceiling_gather_read", st)
 

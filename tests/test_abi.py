@@ -361,10 +361,11 @@ def test_ceiling_reads_reject_bad_arguments(native):
     assert lib.pkv_ceiling_stream_read(8, 1024, 8, 1, None) == -1      # misaligned
     assert lib.pkv_ceiling_stream_read(16, 1024, 0, 1, None) == -1
     assert lib.pkv_ceiling_stream_read(16, 1024, 8, None, None) == -1
-    assert lib.pkv_ceiling_gather_read(16, 1 << 20, 16, 4, 3000, 8, 16, None) == -1
-    assert lib.pkv_ceiling_gather_read(16, 1024, 16, 4, 4096, 8, 16, None) == -1   # pool < chunk
-    assert lib.pkv_ceiling_gather_read(16, 1 << 20, None, 4, 4096, 8, 16, None) == -1
-    assert lib.pkv_ceiling_gather_read(16, 1 << 20, 16, 0, 4096, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, None, 1 << 20, 16, 4, 3000, 0, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, None, 1024, 16, 4, 4096, 0, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, 16, 1 << 20, None, 4, 4096, 0, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, None, 1 << 20, 16, 0, 4096, 0, 8, 16, None) == -1
+    assert lib.pkv_ceiling_gather_read(16, None, 1 << 20, 16, 4, 4096, 2, 8, 16, None) == -1
 
 
 def test_shared_blocks_flag_is_accepted_and_changes_no_plan(native):
