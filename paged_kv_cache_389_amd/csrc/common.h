@@ -290,7 +290,9 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // POL is the load's cache policy: 0 for ordinary loads, kStream for the
 // nontemporal bit (lines marked for early eviction).  A plain random gather
 // of 4 KiB chunks measured 6.3-6.5 TB/s with it against 5.7-5.9 TB/s
-// without; the decode kernels measured the same with either, and use 0.
+// without, and the decode kernels gain as much: they stream their K/V loads
+// unless a batch's sequences share blocks, where a block read by several
+// workgroups in one call should stay in the cache.
 constexpr int kStream = 2;
 template <int POL = 0>
 __device__ inline u32x4 bld16(rsrc_t r, uint32_t lane_off, uint32_t const_off) {
