@@ -10,62 +10,105 @@
 // engine: eviction by swapping or recomputation); the pages print no
 // formula, and the causal reading above is the plainest one.
 //
-// A wave owns kPrefillGroups groups of 16 query columns, each 16/G query
-// tokens times the G query heads of one KV head; every K/V tile it loads
-// serves all its groups.  Against a 16-token tile of keys a group forms the same
-// contraction as grouped decode (S^T = K Q^T, 16x16x32 MFMAs; O^T += V^T P^T,
-// 16x16x16), so the operand layouts are those of the decode MFMA kernel; the
-// only new element is a causal bound per column: column c sees tokens below
-// limit_c, masked by index in the tiles that reach past the wave's smallest
-// bound.  Each wave streams its own tiles 0 .. ceil(max limit / 16) with the
-// table entries of 64 tiles fetched by one vector load and the next tile's
-// loads in flight while the current one is computed; the four waves of a
-// workgroup take consecutive query tokens of one (sequence, KV head), so
-// their tiles overlap and mostly hit in the caches.  No cross-wave merge is
-// needed: a wave owns its columns' whole context.
+// A workgroup of four waves takes consecutive query tokens of one
+// (sequence, KV head); a wave owns kPrefillGroups groups of 16 query
+// columns, each 16/G query tokens times the G query heads of the KV head.
+// The context is walked in tiles of 32 tokens (two 16-token units, each in
+// its own block or half block), and each tile's K and V rows are loaded
+// once for the workgroup, straight into LDS (16-byte buffer loads that
+// write LDS): wave w loads unit w & 1 of K (w < 2) or of V (w >= 2).  Tiles
+// are double-buffered with one barrier per tile: the loads of tile j + 1 are
+// issued right after the barrier that opens tile j, so they have a whole
+// tile of work to land.  The rows of a tile sit in LDS with their 16-byte
+// chunks swizzled (chunk c of row r at c ^ (r mod chunks per row)), so that
+// the operand reads below touch distinct banks.  Per tile and group:
+//
+//   S^T = K Q^T       per unit, 16x16x32 MFMAs over the head dim (K rows as
+//                     the A operand, read from LDS; Q^T, the B operand, from
+//                     the wave's LDS slots);
+//   P = exp2(S^T c - m)   one FMA and one exp2 per score, c the positive
+//                     softmax factor in log2 units (a negative scale is
+//                     moved into Q, whose sign flip is exact), m a per-column
+//                     reference maximum that moves only when a tile passes
+//                     it by more than kPrefillSlack (the normalised result
+//                     does not depend on the reference);
+//   O^T += V^T P^T    one 16x16x32 MFMA per 16 output dims and group, whose
+//                     32-deep contraction runs over both units of the tile:
+//                     a lane's score registers hold tokens 4*g4 .. 4*g4 + 3
+//                     of each unit, which is exactly its B operand, and the
+//                     same eight tokens' V rows at DPL consecutive dims,
+//                     regrouped into token pairs per dim by v_perm, form its
+//                     A operand (output row i of product e is dim DPL*i + e).
+//
+// The row sums take the probabilities as rounded for the product (a dot2
+// against ones), so numerator and denominator use the same values.  Loads
+// go through buffer descriptors whose range ends with the context, so rows
+// past it read as zeros (and their scores are masked); the causal bound of
+// each column masks by index only in the tiles that reach past the wave's
+// smallest bound.  No cross-wave merge is needed: a wave owns its columns'
+// whole context; a wave whose columns end before the workgroup's last tile
+// keeps loading its share and skips the arithmetic.
 #include "common.h"
 #include "decode.h"
 #include "mfma_ops.h"
 
 namespace pkv {
 
-constexpr int kPrefillStages = 2;
-// Probabilities enter the PV product rounded to the input type once (no
-// bf16 head + remainder split as in decode, which doubles the PV work of
-// this compute-heavy kernel).
-constexpr bool kPrefillSplitP = false;
 // How far (log2 units) a tile's maximum may pass the reference maximum
 // before the accumulators are rescaled: probabilities stay below 2^8.
 constexpr float kPrefillSlack = 8.f;
 
-// Column groups of 16 per wave: each K/V tile a wave loads serves CG groups.
-constexpr int kPrefillGroups = 4;
+// Column groups of 16 per wave: each K/V tile serves 4 * CG groups.
+constexpr int kPrefillGroups = 3;
 
-template <int HD, int CG>
+template <typename C, int HD, int CG>
 struct PrefillShared {
+  static constexpr int kTile = 32 * HD * (int)sizeof(typename C::storage);   // bytes of 32 rows
   u32x4 q[4][CG][HD / 32][kWave];   // per wave and column group: Q^T in the B layout
+  __attribute__((aligned(16))) unsigned char kv[2][2][kTile];   // [buffer][K, V][32 swizzled rows]
 };
 
-// C is the cache element: E itself, or E4M3 codes, loaded at half the width
-// (16 codes of a K row per load, feeding two k-steps; V rows at half width)
-// and widened to E right before the products, as in the decode MFMA kernel;
-// the K scale is folded into scale_log2e and the V scale multiplies the output.
+__device__ inline float max3f(float x, float y, float z) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte buffer load that writes LDS: lane l's 16 bytes (at lane_off in
+// the buffer) land at dst + 16 * l; dst must be wave-uniform.  Its wait is
+// the vector-memory counter.  (A plain device function: the builtin has no
+// host form, and a lambda body is also compiled for the host.)
+__device__ inline void buffer_load_lds16(rsrc_t r, unsigned char* dst, uint32_t lane_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, lane_off, 0, 0, 0);
+}
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+// C is the cache element: E itself, or E4M3 codes (16 codes of a K row per
+// read, feeding two k-steps; V rows at half width), widened to E right
+// before the products, as in the decode MFMA kernel; the K scale is folded
+// into scale_log2e and the V scale multiplies the output.
 template <typename E, typename C, int HD, int BS, int CG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     PrefillArgs a) {
   using TQ = typename E::storage;   // query and output
   using T = typename C::storage;    // cache element
   using Ops = MfmaOps<E>;
+  using SM = PrefillShared<C, HD, CG>;
   constexpr bool k8 = sizeof(T) == 1;
   constexpr int KSTEPS = HD / 32;
-  constexpr int DPL = HD / 16;
-  constexpr int VW = DPL / 2;
-  constexpr int KL = k8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per tile
-  constexpr int VL = k8 ? VW / 2 : VW;           // dwords of V loaded per lane and token
-  constexpr int TPB = BS / 16;
-  constexpr int NS = kPrefillStages;
-  static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4), "unsupported shape");
-  __shared__ PrefillShared<HD, CG> sm;
+  constexpr int DPL = HD / 16;                   // output dims per lane and column
+  constexpr int VW = DPL / 2;                    // dwords of one V row's DPL dims (16-bit)
+  constexpr int KL = k8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K reads per unit
+  constexpr int VL = k8 ? VW / 2 : VW;           // dwords of V read per row
+  constexpr int TPB = BS / 16;                   // 16-token units per block
+  constexpr int kRow = HD * (int)sizeof(T);      // bytes of one token row of one head
+  constexpr int NCH = kRow / 16;                 // 16-byte chunks per row
+  constexpr int LPU = 16 * kRow / 1024;          // 1 KiB loads per unit
+  static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4) && LPU >= 1,
+                "unsupported shape");
+  __shared__ SM sm;
 
   const int g = blockIdx.x % a.num_kv_heads;
   // heaviest query chunks (latest positions) first
@@ -81,8 +124,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int nq = q1 - q0;
   int L = load_uniform(a.context_lens + s);
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int first = (chunk * 4 + wave) * tpw;   // the wave's first query token
-  if (first >= nq) return;                      // no barrier follows: waves leave freely
+  const int wg_first = chunk * 4 * tpw;
+  if (wg_first >= nq) return;   // the whole workgroup: no barrier has been reached
+  // tokens the workgroup reads: up to the bound of its last query token
+  const int wg_lim = max(0, L - nq + min(nq, wg_first + 4 * tpw));
+  const int wg_units = (wg_lim + 15) / 16;
+  const int wg_tiles = (wg_units + 1) / 2;
+  const int first = wg_first + wave * tpw;   // the wave's first query token
 
   // this lane's column in group c: query token i[c] (row q0 + i[c]), head h
   const int h = g * G + n % G;
@@ -105,185 +153,248 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
   lim_max = uniform(lim_max);
   lim_min = uniform(lim_min);
+  const int my_tiles = (lim_max + 31) / 32;   // tiles this wave computes (<= wg_tiles)
 
-  // Q^T of the wave's columns into its LDS slots (B layout)
+  // Q^T of the wave's columns into its LDS slots (B layout), every load
+  // issued before the first store (columns past the queries read row 0 and
+  // store zeros); a negative factor is moved into Q (sign flip of both
+  // halves of every word)
+  const float cs = fabsf(a.scale_log2e);
+  const float inv_cs = 1.f / cs;
+  const uint32_t flip = a.scale_log2e < 0.f ? 0x80008000u : 0u;
+  {
+    u32x4 qv[CG][KSTEPS];
 #pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    const TQ* qrow = static_cast<const TQ*>(a.q) +
-                     ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
+    for (int c = 0; c < CG; ++c) {
+      const TQ* qrow = static_cast<const TQ*>(a.q) +
+                       ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      sm.q[wave][c][kk][lane] =
-          valid[c] ? ld16(qrow + mfma_dim0<C>(kk, g4)) : u32x4{0, 0, 0, 0};
+      for (int kk = 0; kk < KSTEPS; ++kk) qv[c][kk] = ld16(qrow + mfma_dim0<C>(kk, g4));
+    }
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        sm.q[wave][c][kk][lane] = valid[c] ? (qv[c][kk] ^ flip) : u32x4{0, 0, 0, 0};
   }
+  int my_bad = INT32_MAX;   // first tile whose share this wave loaded named a block outside the pool
 
-  const size_t block_bytes = (size_t)a.num_kv_heads * BS * HD * sizeof(T);
-  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * BS * HD * sizeof(T);
-  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * BS * HD * sizeof(T);
-  const uint32_t koff = (uint32_t)((n * HD + mfma_dim0<C>(0, g4)) * sizeof(T));
-  const uint32_t voff = (uint32_t)(((4 * g4) * HD + n * DPL) * sizeof(T));
+  // ---- this wave's share of every tile: unit `mu` of K (waves 0, 1) or V
+  const int mu = wave & 1;
+  const char* src = static_cast<const char*>(wave < 2 ? a.k_cache : a.v_cache) +
+                    (size_t)g * BS * kRow;
+  const size_t block_bytes = (size_t)a.num_kv_heads * BS * kRow;
   const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
+  // lane l of load q writes LDS bytes q * 1024 + 16 * l of the unit, which
+  // hold chunk (slot ^ swizzle) of row (q * 1024 + 16 * l) / kRow
+  uint32_t src_off[LPU];
+#pragma unroll
+  for (int q = 0; q < LPU; ++q) {
+    const int slot = q * 1024 + 16 * lane;
+    const int row = slot / kRow, ch = (slot % kRow) / 16;
+    src_off[q] = (uint32_t)(row * kRow + ((ch ^ ((16 * mu + row) & (NCH - 1))) * 16));
+  }
+  // table entries of 64 units per window, one vector load each
+  int wbase = 0;
+  int tbl = table[min(lane / TPB, a.max_blocks - 1)];
+  auto load_tile = [&](int j) {
+    const int u = 2 * j + mu;
+    if (u >= wbase + 64) {
+      wbase += 64;
+      tbl = table[min((wbase + lane) / TPB, a.max_blocks - 1)];
+    }
+    const bool live = u < wg_units;
+    int phys = live ? lane_value(tbl, u - wbase) : 0;
+    if (live && (unsigned)phys >= (unsigned)a.num_blocks) {
+      my_bad = min(my_bad, j);
+      phys = 0;
+    }
+    const uint32_t bytes = live ? (uint32_t)min(L - 16 * u, 16) * kRow : 0u;
+    const rsrc_t r = make_rsrc(src + (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * kRow,
+                               bytes);
+    unsigned char* dst = &sm.kv[j & 1][wave >> 1][mu * 16 * kRow];
+#pragma unroll
+    for (int q = 0; q < LPU; ++q)
+      buffer_load_lds16(r, dst + q * 1024, src_off[q]);
+  };
+
+  // ---- per-lane LDS offsets of the operands inside a 32-row tile
+  // K (A operand of S^T): row 16 * hh + n, chunk 4 * kk + g4
+  uint32_t k_at[2][KL];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int kk = 0; kk < KL; ++kk) {
+      const int row = 16 * hh + n;
+      k_at[hh][kk] = (uint32_t)(row * kRow + (((4 * kk + g4) ^ (row & (NCH - 1))) * 16));
+    }
+  // V (A operand of O^T after regrouping): row 16 * hh + 4 * g4 + rr, the
+  // lane's DPL dims at byte DPL * n * sizeof(T) of the row
+  uint32_t v_at[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 16 * hh + 4 * g4 + rr;
+      const int byte = n * DPL * (int)sizeof(T);
+      v_at[hh][rr] = (uint32_t)(row * kRow + (((byte / 16) ^ (row & (NCH - 1))) * 16) + byte % 16);
+    }
 
   f32x4 acc[CG][DPL];
-  float m[CG], l[CG];
+  float nmu[CG], thr[CG], l[CG];
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[c] = -INFINITY;
+    nmu[c] = 0.f;         // minus the reference maximum (log2 units), 0 while there is none
+    thr[c] = -INFINITY;   // raw score above which the reference must move
     l[c] = 0.f;
   }
-  int bad = 0;
-  const int ntiles = (lim_max + 15) / 16;
 
-  for (int pass = 0; pass < ntiles; pass += kWave) {
-    const int mine = min(kWave, ntiles - pass);
-    const int tbl = table[min((pass + lane) / TPB, a.max_blocks - 1)];
+  // S^T of both units of the current tile for group c
+  auto scores = [&](const u32x4 (*ka)[KSTEPS], int c, float* sv) {
+    u32x4 qb[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm.q[wave][c][kk][lane];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) x = Ops::qk(ka[hh][kk], qb[kk], x);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sv[4 * hh + rr] = x[rr];
+    }
+  };
 
-    auto load_tile = [&](int t, u32x4* ka, uint32_t (*vv)[VL]) {
-      const bool live = t < mine;
-      const int u = pass + t;
-      int phys = lane_value(tbl, t < kWave ? t : kWave - 1);
-      if (live && (unsigned)phys >= (unsigned)a.num_blocks) bad = 1;
-      if (!live || (unsigned)phys >= (unsigned)a.num_blocks) phys = 0;
-      const size_t toff = (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * HD * sizeof(T);
-      const uint32_t nbytes = live ? (uint32_t)(16 * HD * sizeof(T)) : 0u;
-      const rsrc_t kt = make_rsrc(kbase + toff, nbytes);
-      const rsrc_t vt = make_rsrc(vbase + toff, nbytes);
+  // (cached loads: the later chunks of the sequence read the same tiles)
+  if (wg_tiles > 0) load_tile(0);
+  for (int j = 0; j < wg_tiles; ++j) {
+    // this wave's share of tile j has landed; the barrier makes every
+    // share visible and tells that every wave is done with tile j - 1,
+    // whose buffer the loads of tile j + 1 then overwrite
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (j + 1 < wg_tiles) load_tile(j + 1);
+    if (j >= my_tiles) continue;   // this wave's columns end before the tile
+    const unsigned char* kt = sm.kv[j & 1][0];
+    const unsigned char* vt = sm.kv[j & 1][1];
+
+    // ---- the tile's K rows as E values (8-bit codes widened here)
+    u32x4 ka[2][KSTEPS];
 #pragma unroll
-      for (int kk = 0; kk < KL; ++kk) ka[kk] = bld16(kt, koff, kk * (k8 ? 64 : 32) * sizeof(T));
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (VL == 1) {
-          vv[r][0] = bld4(vt, voff, r * HD * sizeof(T));
-        } else if constexpr (VL == 2) {
-          const u32x2 x = bld8(vt, voff, r * HD * sizeof(T));
-          vv[r][0] = x[0];
-          vv[r][1] = x[1];
+      for (int kk = 0; kk < KL; ++kk) {
+        const u32x4 x = *(lds_u32x4*)(kt + k_at[hh][kk]);
+        if constexpr (k8) {
+          ka[hh][2 * kk] = u32x4{codes_to_pair<E, false>(x[0]), codes_to_pair<E, true>(x[0]),
+                                 codes_to_pair<E, false>(x[1]), codes_to_pair<E, true>(x[1])};
+          ka[hh][2 * kk + 1] = u32x4{codes_to_pair<E, false>(x[2]), codes_to_pair<E, true>(x[2]),
+                                     codes_to_pair<E, false>(x[3]), codes_to_pair<E, true>(x[3])};
         } else {
-          const u32x4 x = bld16(vt, voff, r * HD * sizeof(T));
-          vv[r][0] = x[0];
-          vv[r][1] = x[1];
-          vv[r][2] = x[2];
-          vv[r][3] = x[3];
+          ka[hh][kk] = x;
         }
-      }
-    };
-
-    auto compute_tile = [&](int t, const u32x4* kl, uint32_t (*vl)[VL]) {
-      const int u = pass + t;
-      // the tile's operands in E's 16-bit values (8-bit codes widened here,
-      // after their loads have landed)
-      u32x4 ka[KSTEPS];
-      uint32_t vv[4][VW];
-      if constexpr (k8) {
-#pragma unroll
-        for (int kk = 0; kk < KL; ++kk) {
-          ka[2 * kk] = u32x4{codes_to_pair<E, false>(kl[kk][0]), codes_to_pair<E, true>(kl[kk][0]),
-                             codes_to_pair<E, false>(kl[kk][1]), codes_to_pair<E, true>(kl[kk][1])};
-          ka[2 * kk + 1] =
-              u32x4{codes_to_pair<E, false>(kl[kk][2]), codes_to_pair<E, true>(kl[kk][2]),
-                    codes_to_pair<E, false>(kl[kk][3]), codes_to_pair<E, true>(kl[kk][3])};
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int w = 0; w < VL; ++w) {
-            vv[r][2 * w] = codes_to_pair<E, false>(vl[r][w]);
-            vv[r][2 * w + 1] = codes_to_pair<E, true>(vl[r][w]);
-          }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = kl[kk];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int w = 0; w < VW; ++w) vv[r][w] = vl[r][w];
-      }
-      const bool edge = u * 16 + 16 > lim_min;   // some column's bound or the context ends here
-      const int t0 = u * 16 + 4 * g4;
-      if (edge) {
-        // value rows past the context are zeroed so that whatever those
-        // slots hold cannot reach the product
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t0 + r >= L) {
-#pragma unroll
-            for (int w = 0; w < VW; ++w) vv[r][w] = 0u;
-          }
-      }
-      u32x2 pb[CG], pr[CG];
-#pragma unroll
-      for (int c = 0; c < CG; ++c) {
-        __asm__ volatile("" ::: "memory");
-        u32x4 qb[KSTEPS];
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm.q[wave][c][kk][lane];
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) sacc = Ops::qk(ka[kk], qb[kk], sacc);
-        float sr[4];   // scores in log2 units
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sr[r] = sacc[r] * a.scale_log2e;
-        if (edge) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (t0 + r >= limit[c]) sr[r] = -INFINITY;   // the column's causal bound
-        }
-        // Lazy rescaling: m is a reference maximum (log2 units) that moves
-        // only when a tile's maximum passes it by more than kPrefillSlack, so
-        // the probabilities stay below 2^kPrefillSlack and the accumulators
-        // are rescaled a few times per context instead of at most tiles.
-        // The normalised result is the same; only the reference differs.
-        // each lane checks its own four scores; the column maximum (a
-        // reduction across the four token groups) is needed only to rescale
-        const float lmax = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-        if (__any(lmax > m[c] + kPrefillSlack)) {
-          const float mn = fmaxf(m[c], rows_max(lmax));
-          const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m[c] - mn);
-          m[c] = mn;
-          l[c] *= corr;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
-        }
-        const float mu = (m[c] == -INFINITY) ? 0.f : m[c];
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sr[r] - mu);   // exp2(-inf) == 0
-        l[c] += (p[0] + p[1]) + (p[2] + p[3]);
-        pb[c] = u32x2{Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3])};
-        pr[c] = u32x2{0u, 0u};
-        if constexpr (kPrefillSplitP) {
-          pr[c][0] = Ops::pack2(p[0] - Ops::widen_lo(pb[c][0]), p[1] - Ops::widen_hi(pb[c][0]));
-          pr[c][1] = Ops::pack2(p[2] - Ops::widen_lo(pb[c][1]), p[3] - Ops::widen_hi(pb[c][1]));
-        }
-      }
-      // one V^T operand per lane-dim e serves every column group
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const u32x2 va = {pair_of(e, vv[0], vv[1]), pair_of(e, vv[2], vv[3])};
-#pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          acc[c][e] = Ops::pv(va, pb[c], acc[c][e]);
-          if constexpr (kPrefillSplitP) acc[c][e] = Ops::pv(va, pr[c], acc[c][e]);
-        }
-      }
-    };
-
-    u32x4 kb[NS][KL];
-    uint32_t vb[NS][4][VL];
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) load_tile(j, kb[j], vb[j]);
-    for (int i0 = 0; i0 < mine; i0 += NS) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        load_tile(i0 + j + NS - 1, kb[(j + NS - 1) % NS], vb[(j + NS - 1) % NS]);
-        if (i0 + j < mine) compute_tile(i0 + j, kb[j], vb[j]);
       }
     }
-  }
 
-  const bool any_bad = __any(bad);
+    // ---- scores and probabilities: group c + 1's products are issued in
+    // the same stretch of code as group c's exponentials, interleaved one
+    // product to three vector instructions
+    const bool edge = 32 * j + 32 > lim_min;   // some column's bound or the context ends here
+    const int t0 = 32 * j + 4 * g4;            // token of score row 0 of unit 0
+    u32x4 pb[CG];
+    float sn[8];
+    scores(ka, 0, sn);
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      float sv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] = sn[k];
+      if (edge) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (t0 + 16 * (k / 4) + (k % 4) >= limit[c]) sv[k] = -INFINITY;
+      }
+      const float lm = max3f(max3f(sv[0], sv[1], sv[2]), max3f(sv[3], sv[4], sv[5]),
+                             __builtin_elementwise_maximum(sv[6], sv[7]));
+      if (__any(lm > thr[c])) {
+        // move the reference to the column maximum (across the four token
+        // groups of the column) and rescale what has been accumulated
+        const float mo = thr[c] == -INFINITY ? -INFINITY : -nmu[c];   // none yet: -inf
+        const float mn = fmaxf(mo, rows_max(lm) * cs);
+        const float corr = mo == -INFINITY ? 1.f : fast_exp2(mo - mn);
+        if (mn != -INFINITY) {
+          nmu[c] = -mn;
+          thr[c] = (mn + kPrefillSlack) * inv_cs;
+        }
+        l[c] *= corr;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
+      }
+      if (c + 1 < CG) scores(ka, c + 1, sn);
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = fast_exp2(__builtin_fmaf(sv[k], cs, nmu[c]));   // exp2(-inf) == 0
+      pb[c] = u32x4{Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3]), Ops::pack2(p[4], p[5]),
+                    Ops::pack2(p[6], p[7])};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) l[c] = Ops::sum2(pb[c][w], l[c]);
+      if (c + 1 < CG) {
+        __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS, 0);   // the next group's Q reads
+#pragma unroll
+        for (int k = 0; k < 2 * KSTEPS; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three vector instructions
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- values: one A operand per output dim e serves every group
+    uint32_t vv[2][4][VW];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        uint32_t x[VL];
+        if constexpr (VL == 1) {
+          x[0] = *(lds_u32*)(vt + v_at[hh][rr]);
+        } else if constexpr (VL == 2) {
+          const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
+          x[0] = y[0];
+          x[1] = y[1];
+        } else {
+          const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) x[w] = y[w];
+        }
+        if constexpr (k8) {
+#pragma unroll
+          for (int w = 0; w < VL; ++w) {
+            vv[hh][rr][2 * w] = codes_to_pair<E, false>(x[w]);
+            vv[hh][rr][2 * w + 1] = codes_to_pair<E, true>(x[w]);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < VW; ++w) vv[hh][rr][w] = x[w];
+        }
+      }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const u32x4 va = {pair_of(e, vv[0][0], vv[0][1]), pair_of(e, vv[0][2], vv[0][3]),
+                        pair_of(e, vv[1][0], vv[1][1]), pair_of(e, vv[1][2], vv[1][3])};
+#pragma unroll
+      for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(va, pb[c], acc[c][e]);
+    }
+  }
+  // the first tile any wave found naming a block outside the pool, through
+  // the K/V buffers once every wave is done with them
+  __syncthreads();
+  int* bad = reinterpret_cast<int*>(&sm.kv[0][0][0]);
+  if (lane == 0) bad[wave] = my_bad;
+  __syncthreads();
+  const int bad_tile = min(min(bad[0], bad[1]), min(bad[2], bad[3]));
+  const bool any_bad = bad_tile < my_tiles;   // a tile this wave read is among them
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     // the four token groups of a column hold partial sums of l
@@ -293,11 +404,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // no visible token: zero row; 8-bit V: code units -> values
     const float inv = lsum > 0.f ? (k8 ? a.v_scale : 1.f) / lsum : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int rr = 0; rr < 4; ++rr) {
       float o[DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[c][e][r] * inv;
-      store_rounded<E, DPL>(orow + (4 * g4 + r) * DPL, o);
+      for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[c][e][rr] * inv;
+      store_rounded<E, DPL>(orow + (4 * g4 + rr) * DPL, o);
     }
   }
 }

@@ -30,6 +30,10 @@ struct MfmaOps<F16> {
   __device__ static inline float widen_hi(uint32_t v) {
     return (float)__builtin_bit_cast(f16x2, v)[1];
   }
+  // acc + both halves of a packed pair (a dot2 against ones)
+  __device__ static inline float sum2(uint32_t v, float acc) {
+    return __builtin_amdgcn_fdot2(lane_as<f16x2>(v), lane_as<f16x2>(0x3C003C00u), acc, false);
+  }
 };
 
 template <>
@@ -49,6 +53,10 @@ struct MfmaOps<BF16> {
   }
   __device__ static inline float widen_lo(uint32_t v) { return __uint_as_float(v << 16); }
   __device__ static inline float widen_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+  __device__ static inline float sum2(uint32_t v, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(lane_as<bf16x2>(v), lane_as<bf16x2>(0x3F803F80u), acc,
+                                          false);
+  }
 };
 
 // Two E4M3 codes (bytes 2*kHi, 2*kHi + 1 of w) as a pair of E's 16-bit
