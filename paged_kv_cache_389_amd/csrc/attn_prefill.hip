@@ -13,6 +13,9 @@
 // A workgroup of four waves takes consecutive query tokens of one
 // (sequence, KV head); a wave owns kPrefillGroups groups of 16 query
 // columns, each 16/G query tokens times the G query heads of the KV head.
+// Workgroups go out sequence by sequence, longest context first (batches of
+// up to 64 sequences; larger ones in index order), and each sequence's
+// chunks latest-first, so that the heaviest work starts early.
 // The context is walked in tiles of 32 tokens (two 16-token units, each in
 // its own block or half block), and each tile's K and V rows are loaded
 // once for the workgroup, straight into LDS (16-byte buffer loads that
@@ -24,8 +27,8 @@
 // the operand reads below touch distinct banks.  Per tile and group:
 //
 //   S^T = K Q^T       per unit, 16x16x32 MFMAs over the head dim (K rows as
-//                     the A operand, read from LDS; Q^T, the B operand, from
-//                     the wave's LDS slots);
+//                     the A operand, read from LDS; Q^T, the B operand, held
+//                     in the wave's registers for the whole kernel);
 //   P = exp2(S^T c - m)   one FMA and one exp2 per score, c the positive
 //                     softmax factor in log2 units (a negative scale is
 //                     moved into Q, whose sign flip is exact), m a per-column
@@ -64,7 +67,6 @@ constexpr int kPrefillGroups = 3;
 template <typename C, int HD, int CG>
 struct PrefillShared {
   static constexpr int kTile = 32 * HD * (int)sizeof(typename C::storage);   // bytes of 32 rows
-  u32x4 q[4][CG][HD / 32][kWave];   // per wave and column group: Q^T in the B layout
   __attribute__((aligned(16))) unsigned char kv[2][2][kTile];   // [buffer][K, V][32 swizzled rows]
 };
 
@@ -113,7 +115,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int g = blockIdx.x % a.num_kv_heads;
   // heaviest query chunks (latest positions) first
   const int chunk = a.chunks - 1 - (int)(blockIdx.x / a.num_kv_heads);
-  const int s = blockIdx.z;
+  // sequences longest first (batches of up to 64 sequences): blockIdx.z
+  // is the rank of the sequence's context length (ties by index)
+  int s = blockIdx.z;
+  if (a.num_seqs <= kWave) {
+    const int li = threadIdx.x % kWave;
+    const int Li = li < a.num_seqs ? a.context_lens[li] : INT32_MIN;
+    int r = 0;
+    for (int t = 0; t < a.num_seqs; ++t) {
+      const int Lt = __builtin_amdgcn_readlane(Li, t);
+      r += (Lt > Li || (Lt == Li && t < li)) ? 1 : 0;
+    }
+    const unsigned long long m = __ballot(li < a.num_seqs && r == (int)blockIdx.z);
+    s = __builtin_ctzll(m);
+  }
   const int lane = threadIdx.x % kWave, wave = uniform(threadIdx.x / kWave);
   const int n = lane & 15, g4 = lane >> 4;
   const int G = a.group, tpg = 16 / G, tpw = CG * tpg;   // query tokens per group / wave
@@ -155,30 +170,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   lim_min = uniform(lim_min);
   const int my_tiles = (lim_max + 31) / 32;   // tiles this wave computes (<= wg_tiles)
 
-  // Q^T of the wave's columns into its LDS slots (B layout), every load
-  // issued before the first store (columns past the queries read row 0 and
-  // store zeros); a negative factor is moved into Q (sign flip of both
-  // halves of every word)
-  const float cs = fabsf(a.scale_log2e);
-  const float inv_cs = 1.f / cs;
-  const uint32_t flip = a.scale_log2e < 0.f ? 0x80008000u : 0u;
-  {
-    u32x4 qv[CG][KSTEPS];
-#pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      const TQ* qrow = static_cast<const TQ*>(a.q) +
-                       ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qv[c][kk] = ld16(qrow + mfma_dim0<C>(kk, g4));
-    }
-#pragma unroll
-    for (int c = 0; c < CG; ++c)
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        sm.q[wave][c][kk][lane] = valid[c] ? (qv[c][kk] ^ flip) : u32x4{0, 0, 0, 0};
-  }
   int my_bad = INT32_MAX;   // first tile whose share this wave loaded named a block outside the pool
-
   // ---- this wave's share of every tile: unit `mu` of K (waves 0, 1) or V
   const int mu = wave & 1;
   const char* src = static_cast<const char*>(wave < 2 ? a.k_cache : a.v_cache) +
@@ -218,6 +210,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       buffer_load_lds16(r, dst + q * 1024, src_off[q]);
   };
 
+  if (wg_tiles > 0) load_tile(0);   // in flight while Q is staged
+
+  // Q^T of the wave's columns into its LDS slots (B layout), every load
+  // issued before the first store (columns past the queries read row 0 and
+  // store zeros); a negative factor is moved into Q (sign flip of both
+  // halves of every word)
+  const float cs = fabsf(a.scale_log2e);
+  const float inv_cs = 1.f / cs;
+  const uint32_t flip = a.scale_log2e < 0.f ? 0x80008000u : 0u;
+  u32x4 qv[CG][KSTEPS];   // Q^T of the wave's columns in the B layout, for the whole kernel
+  {
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const TQ* qrow = static_cast<const TQ*>(a.q) +
+                       ((size_t)(q0 + (valid[c] ? i[c] : 0)) * a.num_q_heads + h) * HD;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qv[c][kk] = ld16(qrow + mfma_dim0<C>(kk, g4));
+    }
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        qv[c][kk] = valid[c] ? (qv[c][kk] ^ flip) : u32x4{0, 0, 0, 0};
+  }
+
   // ---- per-lane LDS offsets of the operands inside a 32-row tile
   // K (A operand of S^T): row 16 * hh + n, chunk 4 * kk + g4
   uint32_t k_at[2][KL];
@@ -252,10 +269,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 
   // S^T of both units of the current tile for group c
-  auto scores = [&](const u32x4 (*ka)[KSTEPS], int c, float* sv) {
-    u32x4 qb[KSTEPS];
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qb[kk] = sm.q[wave][c][kk][lane];
+  auto scores = [&](const u32x4 (*ka)[KSTEPS], const u32x4* qb, float* sv) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -266,8 +280,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  // (cached loads: the later chunks of the sequence read the same tiles)
-  if (wg_tiles > 0) load_tile(0);
   for (int j = 0; j < wg_tiles; ++j) {
     // this wave's share of tile j has landed; the barrier makes every
     // share visible and tells that every wave is done with tile j - 1,
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int t0 = 32 * j + 4 * g4;            // token of score row 0 of unit 0
     u32x4 pb[CG];
     float sn[8];
-    scores(ka, 0, sn);
+    scores(ka, qv[0], sn);
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
       float sv[8];
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
       }
-      if (c + 1 < CG) scores(ka, c + 1, sn);
+      if (c + 1 < CG) scores(ka, qv[c + 1], sn);
       float p[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) p[k] = fast_exp2(__builtin_fmaf(sv[k], cs, nmu[c]));   // exp2(-inf) == 0
@@ -340,7 +352,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int w = 0; w < 4; ++w) l[c] = Ops::sum2(pb[c][w], l[c]);
       if (c + 1 < CG) {
-        __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS, 0);   // the next group's Q reads
 #pragma unroll
         for (int k = 0; k < 2 * KSTEPS; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product

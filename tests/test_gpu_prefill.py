@@ -72,6 +72,29 @@ def test_prefill_matches_oracle(dtype, hq, hkv, hd, bs):
     assert np.array_equal(got[qs[3]:qs[3] + 3], np.zeros((3, hq, hd)))
 
 
+@pytest.mark.parametrize("num_seqs", [64, 65])
+def test_prefill_sequence_order_covers_every_sequence(num_seqs):
+    """Workgroups go out longest context first (ranked on the device for up
+    to 64 sequences, index order beyond): with many tied lengths every
+    sequence is still computed exactly once, on both sides of the bound."""
+    say("prefill order", num_seqs)
+    rng = np.random.default_rng(900 + num_seqs)
+    hq, hkv, hd, bs = 4, 2, 64, 16
+    lens = rng.choice([3, 17, 40, 40, 64], size=num_seqs).tolist()   # many ties
+    ks = [rng.standard_normal((L, hkv, hd)) for L in lens]
+    vs = [rng.standard_normal((L, hkv, hd)) for L in lens]
+    nblk = sum(-(-L // bs) for L in lens) + 2
+    kp, vp, tables, cl, _ = pins.page(ks, vs, bs, nblk, rng)
+    nq = [min(L, int(rng.integers(1, 20))) for L in lens]
+    qs = np.concatenate([[0], np.cumsum(nq)])
+    q = torch.from_numpy(rng.standard_normal((int(qs[-1]), hq, hd))).to(torch.bfloat16)
+    kt, vt = torch.from_numpy(kp).to(torch.bfloat16), torch.from_numpy(vp).to(torch.bfloat16)
+    got = _run(q, kt, vt, tables, cl, qs, 0.125, torch.bfloat16).cpu().double().numpy()
+    want = oracle.prefill(q, kt, vt, tables, cl, qs, 0.125, hkv)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - want).max()) <= TOL[torch.bfloat16]
+
+
 def test_one_query_per_sequence_matches_decode_kernel():
     """n = 1 everywhere is decode: prefill and the decode kernel agree within
     the tolerance with the oracle and with each other."""
