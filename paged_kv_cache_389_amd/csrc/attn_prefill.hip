@@ -38,10 +38,14 @@
 //   O^T += V^T P^T    one 16x16x32 MFMA per 16 output dims and group, whose
 //                     32-deep contraction runs over both units of the tile:
 //                     a lane's score registers hold tokens 4*g4 .. 4*g4 + 3
-//                     of each unit, which is exactly its B operand, and the
-//                     same eight tokens' V rows at DPL consecutive dims,
-//                     regrouped into token pairs per dim by v_perm, form its
-//                     A operand (output row i of product e is dim DPL*i + e).
+//                     of each unit, which is exactly its B operand; the same
+//                     eight tokens' V values at one dim form its A operand,
+//                     read by two transposing LDS reads (ds_read_b64_tr_b16)
+//                     for 16-bit caches (output row n of product e is dim
+//                     16*e + n), and for 8-bit codes widened from the lane's
+//                     V rows at DPL consecutive dims and regrouped into token
+//                     pairs per dim by v_perm (row n of product e: dim
+//                     DPL*n + e).
 //
 // The row sums take the probabilities as rounded for the product (a dot2
 // against ones), so numerator and denominator use the same values.  Loads
@@ -75,6 +79,17 @@ __device__ inline float max3f(float x, float y, float z) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Position of the 16-byte chunks of tile row r in LDS: chunk c sits at
+// c ^ swz(r).  With 16 chunks per row the rows of a 16-row unit get 16
+// distinct values, so the K operand reads (16 rows, one chunk) and the V
+// transposing reads (4 rows, 8 of their chunks) each touch distinct banks.
+template <int NCH>
+__device__ constexpr int swz(int r) {
+  if constexpr (NCH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return r & (NCH - 1);
+}
 
 // 16-byte buffer load that writes LDS: lane l's 16 bytes (at lane_off in
 // the buffer) land at dst + 16 * l; dst must be wave-uniform.  Its wait is
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   for (int q = 0; q < LPU; ++q) {
     const int slot = q * 1024 + 16 * lane;
     const int row = slot / kRow, ch = (slot % kRow) / 16;
-    src_off[q] = (uint32_t)(row * kRow + ((ch ^ ((16 * mu + row) & (NCH - 1))) * 16));
+    src_off[q] = (uint32_t)(row * kRow + ((ch ^ swz<NCH>(16 * mu + row)) * 16));
   }
   // table entries of 64 units per window, one vector load each
   int wbase = 0;
@@ -243,7 +258,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int kk = 0; kk < KL; ++kk) {
       const int row = 16 * hh + n;
-      k_at[hh][kk] = (uint32_t)(row * kRow + (((4 * kk + g4) ^ (row & (NCH - 1))) * 16));
+      k_at[hh][kk] = (uint32_t)(row * kRow + (((4 * kk + g4) ^ swz<NCH>(row)) * 16));
     }
   // V (A operand of O^T after regrouping): row 16 * hh + 4 * g4 + rr, the
   // lane's DPL dims at byte DPL * n * sizeof(T) of the row
@@ -254,8 +269,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int rr = 0; rr < 4; ++rr) {
       const int row = 16 * hh + 4 * g4 + rr;
       const int byte = n * DPL * (int)sizeof(T);
-      v_at[hh][rr] = (uint32_t)(row * kRow + (((byte / 16) ^ (row & (NCH - 1))) * 16) + byte % 16);
+      v_at[hh][rr] = (uint32_t)(row * kRow + (((byte / 16) ^ swz<NCH>(row)) * 16) + byte % 16);
     }
+  // 16-bit caches: V^T operands by transposing reads.  Lane 4 * k + q of a
+  // 16-lane group names row 16 * hh + 4 * g4 + k at dims 16 * e + 4 * q .. + 3;
+  // lane n of the group then holds those rows' values at dim 16 * e + n,
+  // tokens in the order of its score registers (output row n of product e
+  // is dim 16 * e + n).
+  const int tr_q = n & 3;
+  int tr_row[2], tr_swz[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    tr_row[hh] = 16 * hh + 4 * g4 + (n >> 2);
+    tr_swz[hh] = swz<NCH>(tr_row[hh]);
+  }
 
   f32x4 acc[CG][DPL];
   float nmu[CG], thr[CG], l[CG];
@@ -361,7 +388,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- values: one A operand per output dim e serves every group
+    if constexpr (!k8) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        uint32_t w[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int ch = (2 * e + (tr_q >> 1)) ^ tr_swz[hh];
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vt + tr_row[hh] * kRow + ch * 16 + (tr_q & 1) * 8));
+          const u32x2 y = __builtin_bit_cast(u32x2, x);
+          w[2 * hh] = y[0];
+          w[2 * hh + 1] = y[1];
+        }
+        const u32x4 va = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(va, pb[c], acc[c][e]);
+      }
+      continue;
+    }
+    // ---- 8-bit caches: one A operand per output dim e serves every group
     uint32_t vv[2][4][VW];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -414,12 +460,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     TQ* orow = static_cast<TQ*>(a.out) + ((size_t)(q0 + i[c]) * a.num_q_heads + h) * HD;
     // no visible token: zero row; 8-bit V: code units -> values
     const float inv = lsum > 0.f ? (k8 ? a.v_scale : 1.f) / lsum : 0.f;
+    if constexpr (!k8) {
+      // element rr of product e: dim 16 * e + 4 * g4 + rr
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float o[DPL];
+      for (int e = 0; e < DPL; ++e) {
+        float o[4];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[c][e][rr] * inv;
-      store_rounded<E, DPL>(orow + (4 * g4 + rr) * DPL, o);
+        for (int rr = 0; rr < 4; ++rr) o[rr] = any_bad ? __builtin_nanf("") : acc[c][e][rr] * inv;
+        store_rounded<E, 4>(orow + 16 * e + 4 * g4, o);
+      }
+    } else {
+      // element rr of product e: dim DPL * (4 * g4 + rr) + e
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float o[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = any_bad ? __builtin_nanf("") : acc[c][e][rr] * inv;
+        store_rounded<E, DPL>(orow + (4 * g4 + rr) * DPL, o);
+      }
     }
   }
 }
