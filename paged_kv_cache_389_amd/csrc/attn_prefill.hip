@@ -231,7 +231,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // issued before the first store (columns past the queries read row 0 and
   // store zeros); a negative factor is moved into Q (sign flip of both
   // halves of every word)
-  const float cs = fabsf(a.scale_log2e);
+  // (a zero scale becomes the smallest normal float: every visible score
+  // then weighs exp2(0) = 1 exactly, and a masked one, -inf times it, 0)
+  const float cs = fmaxf(fabsf(a.scale_log2e), __FLT_MIN__);
   const float inv_cs = 1.f / cs;
   const uint32_t flip = a.scale_log2e < 0.f ? 0x80008000u : 0u;
   u32x4 qv[CG][KSTEPS];   // Q^T of the wave's columns in the B layout, for the whole kernel

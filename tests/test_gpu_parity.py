@@ -223,6 +223,26 @@ def test_decode_single_token_is_the_value_row(dtype, hq, hkv):
             assert torch.equal(got[s, h], vt[b, h // (hq // hkv), 0]), (s, h)
 
 
+@pytest.mark.parametrize("path", [pk.PATH_VALU, pk.PATH_MFMA], ids=["valu", "mfma"])
+def test_decode_zero_scale_is_the_mean_of_the_values(path):
+    """scale = 0 weighs every token alike: the output is the mean of the
+    sequence's V rows (split partitions included), with no NaN from the
+    masked slots past the context."""
+    say("decode scale 0", path)
+    lens = [1, 19, 300, 700]
+    q, kp, vp, tables, L = _case(501, lens, 8, 2, 128, 16)
+    dev, (qt, kt, vt) = upload_case(q, kp, vp, tables, L, torch.bfloat16)
+    got = decode_gpu(dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"], 0.0,
+                     partition=256, path=path).cpu().double().numpy()
+    assert np.isfinite(got).all()
+    v = vt.double().numpy()
+    for s, n in enumerate(lens):
+        nb = -(-n // 16)
+        rows = v[tables[s, :nb]].transpose(0, 2, 1, 3).reshape(nb * 16, 2, 128)[:n]
+        mean = np.repeat(rows.mean(axis=0), 4, axis=0)
+        assert np.abs(got[s] - mean).max() <= TOL[torch.bfloat16], s
+
+
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=DT_ID.get)
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2)])
 def test_decode_placement_invariance_and_determinism(dtype, hq, hkv):

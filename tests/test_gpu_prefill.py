@@ -95,6 +95,64 @@ def test_prefill_sequence_order_covers_every_sequence(num_seqs):
     assert float(np.abs(got - want).max()) <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0], ids=["negative", "zero"])
+def test_prefill_negative_and_zero_scale(scale):
+    """A negative factor is moved into Q (an exact sign flip) and must give
+    the oracle's result; a zero one gives the plain mean of the visible V
+    rows."""
+    say("prefill scale", scale)
+    rng = np.random.default_rng(71)
+    hq, hkv, hd, bs = 8, 2, 128, 16
+    lens = [70, 33, 130]
+    ks = [rng.standard_normal((L, hkv, hd)) for L in lens]
+    vs = [rng.standard_normal((L, hkv, hd)) for L in lens]
+    kp, vp, tables, cl, _ = pins.page(ks, vs, bs, 20, rng)
+    qs = np.array([0, 70, 80, 140])
+    q = torch.from_numpy(rng.standard_normal((140, hq, hd))).to(torch.bfloat16)
+    kt, vt = torch.from_numpy(kp).to(torch.bfloat16), torch.from_numpy(vp).to(torch.bfloat16)
+    got = _run(q, kt, vt, tables, cl, qs, scale, torch.bfloat16).cpu().double().numpy()
+    want = oracle.prefill(q, kt, vt, tables, cl, qs, scale, hkv)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - want).max()) <= TOL[torch.bfloat16]
+    if scale == 0.0:   # row i of sequence 0 (all its tokens are queries): mean of V rows 0..i
+        v0 = vt.double().numpy()[tables[0, :5]].transpose(0, 2, 1, 3).reshape(-1, hkv, hd)[:70]
+        mean = np.cumsum(v0, axis=0) / np.arange(1, 71)[:, None, None]
+        assert np.abs(got[:70] - np.repeat(mean, hq // hkv, axis=1)).max() <= TOL[torch.bfloat16]
+
+
+def test_prefill_table_entry_outside_the_pool_and_long_bs32_context():
+    """A table entry past the pool makes the rows that read its block NaN,
+    and no other sequence's rows; a 1,500-token context at block size 32
+    walks past the first 64-unit window of table entries."""
+    say("prefill out-of-pool + long bs32")
+    rng = np.random.default_rng(72)
+    hq, hkv, hd, bs = 8, 2, 128, 32
+    lens = [1500, 200, 90]
+    ks = [rng.standard_normal((L, hkv, hd)) for L in lens]
+    vs = [rng.standard_normal((L, hkv, hd)) for L in lens]
+    nblk = sum(-(-L // bs) for L in lens) + 2
+    kp, vp, tables, cl, _ = pins.page(ks, vs, bs, nblk, rng)
+    nq = [60, 200, 90]
+    qs = np.concatenate([[0], np.cumsum(nq)])
+    q = torch.from_numpy(rng.standard_normal((int(qs[-1]), hq, hd))).to(torch.bfloat16)
+    kt, vt = torch.from_numpy(kp).to(torch.bfloat16), torch.from_numpy(vp).to(torch.bfloat16)
+    want = oracle.prefill(q, kt, vt, tables, cl, qs, 1 / math.sqrt(hd), hkv)
+    got = _run(q, kt, vt, tables, cl, qs, 1 / math.sqrt(hd), torch.bfloat16).cpu().double().numpy()
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - want).max()) <= TOL[torch.bfloat16]
+    # sequence 1 (200 tokens, every one a query): block 3 (tokens 96..127)
+    # named outside the pool; queries at positions >= 96 read it
+    bad = tables.copy()
+    bad[1, 3] = nblk + 5
+    got = _run(q, kt, vt, bad, cl, qs, 1 / math.sqrt(hd), torch.bfloat16).cpu().double().numpy()
+    s1 = got[qs[1]:qs[2]]
+    assert np.isnan(s1[96:]).all()
+    for s in (0, 2):   # other sequences are untouched
+        assert float(np.abs(got[qs[s]:qs[s + 1]] - want[qs[s]:qs[s + 1]]).max()) <= TOL[torch.bfloat16]
+    ok = ~np.isnan(s1).any(axis=(1, 2))   # rows computed without the block are right
+    assert float(np.abs(s1[ok] - want[qs[1]:qs[2]][ok]).max()) <= TOL[torch.bfloat16]
+
+
 def test_one_query_per_sequence_matches_decode_kernel():
     """n = 1 everywhere is decode: prefill and the decode kernel agree within
     the tolerance with the oracle and with each other."""
