@@ -23,8 +23,8 @@
 // are double-buffered with one barrier per tile: the loads of tile j + 1 are
 // issued right after the barrier that opens tile j, so they have a whole
 // tile of work to land.  The rows of a tile sit in LDS with their 16-byte
-// chunks swizzled (chunk c of row r at c ^ (r mod chunks per row)), so that
-// the operand reads below touch distinct banks.  Per tile and group:
+// chunks swizzled (chunk c of row r at c ^ swz(r)), so that the operand
+// reads below touch distinct banks.  Per tile and group:
 //
 //   S^T = K Q^T       per unit, 16x16x32 MFMAs over the head dim (K rows as
 //                     the A operand, read from LDS; Q^T, the B operand, held
@@ -68,7 +68,7 @@ constexpr float kPrefillSlack = 8.f;
 // Column groups of 16 per wave: each K/V tile serves 4 * CG groups.
 constexpr int kPrefillGroups = 3;
 
-template <typename C, int HD, int CG>
+template <typename C, int HD>
 struct PrefillShared {
   static constexpr int kTile = 32 * HD * (int)sizeof(typename C::storage);   // bytes of 32 rows
   __attribute__((aligned(16))) unsigned char kv[2][2][kTile];   // [buffer][K, V][32 swizzled rows]
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   using TQ = typename E::storage;   // query and output
   using T = typename C::storage;    // cache element
   using Ops = MfmaOps<E>;
-  using SM = PrefillShared<C, HD, CG>;
+  using SM = PrefillShared<C, HD>;
   constexpr bool k8 = sizeof(T) == 1;
   constexpr int KSTEPS = HD / 32;
   constexpr int DPL = HD / 16;                   // output dims per lane and column
