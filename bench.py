@@ -542,12 +542,17 @@ def _pool_worker(path):
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
 
 
-def bench_prefill(name, args):
+PREFILL_WARMUP = 100   # untimed prefill steps at least (see bench_prefill)
+
+
+def bench_prefill(name, args, err_sample=None):
     """Causal prefill attention over the paged cache (every prompt token a
     query).  Throughput in causal attention TFLOP/s (4 * hd flops per query
     row, head and visible token) over the kernel's time (HIP events the
     library records around its launch), against the dense 16-bit MFMA peak;
-    the minimum bytes (every K/V row once, q, out) give the HBM side."""
+    the minimum bytes (every K/V row once, q, out) give the HBM side.  With
+    ``err_sample`` (16-bit pools), the first and last query rows of that many
+    sequences (spread over the lengths) against the float64 oracle."""
     from paged_kv_cache_389_amd import _native as pk
     from paged_kv_cache_389_amd import workloads
     wl = workloads.make(name, device="cuda")
@@ -568,7 +573,12 @@ def bench_prefill(name, args):
                                    wl.max_q_len, int(wl.context_lens.max()),
                                    kernel_events=None if i is None else kev[i], **scales)
 
-    for _ in range(args.warmup):
+    # A compute-bound kernel reaches the part's sustained clocks only after
+    # some tens of milliseconds of work: with 3 warmup steps the timed ones
+    # ran 0.417-0.421 ms, with 100 or 400 0.342-0.345 ms (the memory-bound
+    # decode kernels move by 1% at most), so at least PREFILL_WARMUP steps.
+    warmup = max(args.warmup, PREFILL_WARMUP)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -584,10 +594,14 @@ def bench_prefill(name, args):
     tag = name + ("_kv_e4m3" if dev.get("kv_fp8") else "")
     tflops = flops / (ker / 1e3) / 1e12
     ms_per_step = wall / args.steps * 1e3
+    err = {}
+    if err_sample and not dev.get("kv_fp8"):
+        err = prefill_oracle_error(wl, dev, out, err_sample)
     return {
+        **err,
         "metric": "paged prefill attention: causal TFLOP/s (% of MFMA peak) + query tokens/s",
         "value": round(flops / (ms_per_step / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE_NAME[wl.dtype],
         "data": "synthetic (seeded N(0,1) values, random block placement)",
@@ -720,6 +734,45 @@ def oracle_error(wl, dev, seqs, tables=None):
                          wl.context_lens, wl.scale, wl.num_kv_heads, seqs=list(seqs))
     got = dev["out"].detach().to("cpu", torch.float64).numpy()
     return float(max(np.abs(got[s] - want[s]).max() for s in seqs))
+
+
+def prefill_oracle_error(wl, dev, out, count):
+    """Max abs error of the timed prefill's first and last query rows of
+    ``count`` sequences (all heads) against the float64 oracle, which reads
+    only those sequences' blocks of the device pools."""
+    import oracle
+    seqs = oracle_sample(wl, count)
+    bs = wl.block_size
+    used = sorted({int(b) for s in seqs for b in wl.block_tables[s, :-(-int(wl.context_lens[s]) // bs)]})
+    index = {b: i for i, b in enumerate(used)}
+    ct = np.zeros(wl.block_tables.shape, np.int64)
+    rows = []
+    for s in seqs:
+        n = -(-int(wl.context_lens[s]) // bs)
+        ct[s, :n] = [index[int(b)] for b in wl.block_tables[s, :n]]
+        q0, q1 = int(wl.query_start[s]), int(wl.query_start[s + 1])
+        rows += sorted({q0, q1 - 1}) if q1 > q0 else []
+    q = wl.q.cpu()
+    q = (q.float() if q.dtype == torch.bfloat16 else q).numpy()
+    want = oracle.prefill(q, _host_blocks(dev["k"], used), _host_blocks(dev["v"], used), ct,
+                          wl.context_lens, wl.query_start, wl.scale, wl.num_kv_heads, rows=rows)
+    got = out.detach().to("cpu", torch.float64).numpy()
+    return {"max_abs_err": float(max(np.abs(got[r] - want[r]).max() for r in rows)),
+            "tol": TOL[wl.dtype],
+            "err_sample": f"first and last query rows of {len(seqs)} of {wl.num_seqs} sequences "
+                          f"(all {wl.num_q_heads} heads) against the float64 oracle"}
+
+
+def prefill_entry(line):
+    """The prefill summary the default run reports beside the decode configs."""
+    r = line["roofline"]
+    return {"kernel": r["kernel"], "workload": line["config"]["workload"],
+            "kernel_ms": line["kernel_ms"], "kernel_ms_median": line["kernel_ms_median"],
+            "flops": line["flops"], "achieved_tflops": r["achieved"], "peak_tflops": r["peak"],
+            "frac": r["frac"], "traffic": r["traffic"], "min_bytes": line["min_bytes"],
+            "query_tokens_per_s": line["query_tokens_per_s"], "warmup": line["warmup"],
+            "max_abs_err": line.get("max_abs_err"), "tol": line.get("tol"),
+            "err_sample": line.get("err_sample")}
 
 
 def oracle_sample(wl, count):
@@ -1038,6 +1091,8 @@ def main():
     if full:
         t0 = time.perf_counter()
         line["per_config"], lines = per_config(args, line)
+        # the next row's causal prefill, on the matrix-core roofline
+        line["prefill"] = prefill_entry(bench_prefill("llama3_8b_prefill_bf16", args, err_sample=4))
         line["paging_control"] = paging_control(args, line, lines.get("long_context_gqa_bf16"))
         line["practical_ceiling"] = practical_ceiling()
         line["extra_s"] = round(time.perf_counter() - t0, 1)
