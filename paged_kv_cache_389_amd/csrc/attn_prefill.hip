@@ -391,8 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 
     if constexpr (!k8) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
+      auto read_va = [&](int e) {
         uint32_t w[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -403,9 +402,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           w[2 * hh] = y[0];
           w[2 * hh + 1] = y[1];
         }
-        const u32x4 va = {w[0], w[1], w[2], w[3]};
+        return u32x4{w[0], w[1], w[2], w[3]};
+      };
+      // the operands of the next products are read while those of e are
+      // used (the compiler keeps one pair of reads ahead)
+      u32x4 vq[3];
+      vq[0] = read_va(0);
+      if (DPL > 1) vq[1] = read_va(1);
 #pragma unroll
-        for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(va, pb[c], acc[c][e]);
+      for (int e = 0; e < DPL; ++e) {
+        if (e + 2 < DPL) vq[(e + 2) % 3] = read_va(e + 2);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(vq[e % 3], pb[c], acc[c][e]);
       }
       continue;
     }
