@@ -177,8 +177,10 @@ def counters_to_traffic(args):
     cal_bytes = args.cal_mib << 20
     f_fetch = pick(_counter_means(args.cal_fetch_db), "FETCH_SIZE", is_other)[0] * 1024 / cal_bytes
     f_write = pick(_counter_means(args.cal_write_db), "WRITE_SIZE", is_other)[0] * 1024 / cal_bytes
+    # the attention kernel of the run: the one with the most fetched bytes;
+    # its own WRITE_SIZE (another kernel of the run may write more)
     fetch, kname = pick(_counter_means(args.fetch_db), "FETCH_SIZE", is_decode)
-    write, _ = pick(_counter_means(args.write_db), "WRITE_SIZE", is_decode)
+    write, _ = pick(_counter_means(args.write_db), "WRITE_SIZE", lambda k: k == kname)
     from paged_kv_cache_389_amd import workloads
     kw = {"tensors": False} if args.workload in GROUPABLE else {}
     wl = workloads.make(args.workload, device="cpu", **kw)

@@ -118,3 +118,28 @@ def test_prefill_error_sample_reads_the_sampled_rows():
     s = bench.oracle_sample(wl, 3)[0]
     out[int(wl.query_start[s + 1]) - 1, 1, 5] += 0.25
     assert abs(bench.prefill_oracle_error(wl, dev, out, 3)["max_abs_err"] - 0.25) < 1e-9
+
+
+def test_counter_record_takes_both_counters_from_one_kernel(tmp_path, monkeypatch):
+    """The attention kernel of a profiled run is the one that fetched the
+    most; its WRITE_SIZE is its own, even when another kernel of the same run
+    (a prefill writing 180 MiB, say) wrote more."""
+    import argparse
+    import json
+    sys.path.insert(0, ROOT)
+    import bench
+    dec = "void pkv::decode_valu_kernel<pkv::F32, pkv::F32, 64, 16, 2>(pkv::DecodeArgs)"
+    pre = "void pkv::prefill_mfma_kernel<pkv::BF16, pkv::BF16, 128, 16, 3>(pkv::PrefillArgs)"
+    means = {"fetch": {(dec, "FETCH_SIZE"): 300.0, (pre, "FETCH_SIZE"): 100.0},
+             "write": {(dec, "WRITE_SIZE"): 4.0, (pre, "WRITE_SIZE"): 180000.0},
+             "cf": {("copy", "FETCH_SIZE"): 512.0 * 1024},
+             "cw": {("copy", "WRITE_SIZE"): 1024.0 * 1024}}
+    monkeypatch.setattr(bench, "_counter_means", lambda db: means[db])
+    out = tmp_path / "rec.json"
+    args = argparse.Namespace(cal_mib=1024, cal_fetch_db="cf", cal_write_db="cw", fetch_db="fetch",
+                              write_db="write", workload="tiny_fp32", kv_cache="auto",
+                              grouped=False, counters=str(out))
+    bench.counters_to_traffic(args)
+    rec = json.loads(out.read_text())["workloads"]["tiny_fp32"]
+    assert rec["kernel"].startswith("void pkv::decode_valu_kernel")
+    assert rec["fetch_kib_per_launch"] == 300.0 and rec["write_kib_per_launch"] == 4.0
