@@ -406,6 +406,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       };
       // the operands of the next products are read while those of e are
       // used (the compiler keeps one pair of reads ahead)
+      // the value products at raised wave priority: the other wave of the
+      // SIMD then fills the gaps with its own (vector) work rather than
+      // holding the matrix core's issue back (0.5-1% faster, measured)
+      __builtin_amdgcn_s_setprio(1);
       u32x4 vq[3];
       vq[0] = read_va(0);
       if (DPL > 1) vq[1] = read_va(1);
@@ -415,6 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(vq[e % 3], pb[c], acc[c][e]);
       }
+      __builtin_amdgcn_s_setprio(0);
       continue;
     }
     // ---- 8-bit caches: one A operand per output dim e serves every group
