@@ -227,12 +227,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   if (wg_tiles > 0) load_tile(0);   // in flight while Q is staged
 
-  // Q^T of the wave's columns into its LDS slots (B layout), every load
-  // issued before the first store (columns past the queries read row 0 and
-  // store zeros); a negative factor is moved into Q (sign flip of both
-  // halves of every word)
-  // (a zero scale becomes the smallest normal float: every visible score
-  // then weighs exp2(0) = 1 exactly, and a masked one, -inf times it, 0)
+  // Q^T of the wave's columns (B layout) in registers for the whole kernel,
+  // every load issued before the first use (columns past the queries read
+  // row 0 and hold zeros); a negative factor is moved into Q (sign flip of
+  // both halves of every word), and a zero one becomes the smallest normal
+  // float: every visible score then weighs exp2(0) = 1 exactly, and a
+  // masked one, -inf times it, 0
   const float cs = fmaxf(fabsf(a.scale_log2e), __FLT_MIN__);
   const float inv_cs = 1.f / cs;
   const uint32_t flip = a.scale_log2e < 0.f ? 0x80008000u : 0u;
@@ -262,8 +262,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int row = 16 * hh + n;
       k_at[hh][kk] = (uint32_t)(row * kRow + (((4 * kk + g4) ^ swz<NCH>(row)) * 16));
     }
-  // V (A operand of O^T after regrouping): row 16 * hh + 4 * g4 + rr, the
-  // lane's DPL dims at byte DPL * n * sizeof(T) of the row
+  // 8-bit caches: the V codes of row 16 * hh + 4 * g4 + rr at the lane's DPL
+  // dims (byte DPL * n of the row), widened and regrouped at the products
   uint32_t v_at[2][4];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
