@@ -22,7 +22,10 @@
 // write LDS): wave w loads unit w & 1 of K (w < 2) or of V (w >= 2).  Tiles
 // are double-buffered with one barrier per tile: the loads of tile j + 1 are
 // issued right after the barrier that opens tile j, so they have a whole
-// tile of work to land.  The rows of a tile sit in LDS with their 16-byte
+// tile of work to land.  The two buffers are separate LDS objects and the
+// tile loop is unrolled by two, so that each read names its buffer at
+// compile time and the compiler does not make it wait for the loads in
+// flight into the other one.  The rows of a tile sit in LDS with their 16-byte
 // chunks swizzled (chunk c of row r at c ^ swz(r)), so that the operand
 // reads below touch distinct banks.  Per tile and group:
 //
@@ -42,7 +45,8 @@
 //                     eight tokens' V values at one dim form its A operand,
 //                     read by two transposing LDS reads (ds_read_b64_tr_b16)
 //                     for 16-bit caches (output row n of product e is dim
-//                     16*e + n), and for 8-bit codes widened from the lane's
+//                     16*e + n; all of a tile's are issued once its score
+//                     products are, into the K operands' registers), and for 8-bit codes widened from the lane's
 //                     V rows at DPL consecutive dims and regrouped into token
 //                     pairs per dim by v_perm (row n of product e: dim
 //                     DPL*n + e).
@@ -71,7 +75,7 @@ constexpr int kPrefillGroups = 3;
 template <typename C, int HD>
 struct PrefillShared {
   static constexpr int kTile = 32 * HD * (int)sizeof(typename C::storage);   // bytes of 32 rows
-  __attribute__((aligned(16))) unsigned char kv[2][2][kTile];   // [buffer][K, V][32 swizzled rows]
+  __attribute__((aligned(16))) unsigned char kv[2][kTile];   // [K, V][32 swizzled rows]
 };
 
 __device__ inline float max3f(float x, float y, float z) {
@@ -125,7 +129,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int LPU = 16 * kRow / 1024;          // 1 KiB loads per unit
   static_assert(HD % 32 == 0 && BS % 16 == 0 && (VW == 2 || VW == 4) && LPU >= 1,
                 "unsupported shape");
-  __shared__ SM sm;
+  __shared__ SM sm0;
+  __shared__ SM sm1;
 
   const int g = blockIdx.x % a.num_kv_heads;
   // heaviest query chunks (latest positions) first
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // table entries of 64 units per window, one vector load each
   int wbase = 0;
   int tbl = table[min(lane / TPB, a.max_blocks - 1)];
-  auto load_tile = [&](int j) {
+  auto load_tile = [&](int j, SM& buf) {
     const int u = 2 * j + mu;
     if (u >= wbase + 64) {
       wbase += 64;
@@ -219,13 +224,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const uint32_t bytes = live ? (uint32_t)min(L - 16 * u, 16) * kRow : 0u;
     const rsrc_t r = make_rsrc(src + (size_t)phys * block_bytes + (size_t)(u % TPB) * 16 * kRow,
                                bytes);
-    unsigned char* dst = &sm.kv[j & 1][wave >> 1][mu * 16 * kRow];
+    unsigned char* dst = &buf.kv[wave >> 1][mu * 16 * kRow];
 #pragma unroll
     for (int q = 0; q < LPU; ++q)
       buffer_load_lds16(r, dst + q * 1024, src_off[q]);
   };
 
-  if (wg_tiles > 0) load_tile(0);   // in flight while Q is staged
+  if (wg_tiles > 0) load_tile(0, sm0);   // in flight while Q is staged
 
   // Q^T of the wave's columns (B layout) in registers for the whole kernel,
   // every load issued before the first use (columns past the queries read
@@ -278,13 +283,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // lane n of the group then holds those rows' values at dim 16 * e + n,
   // tokens in the order of its score registers (output row n of product e
   // is dim 16 * e + n).
-  const int tr_q = n & 3;
-  int tr_row[2], tr_swz[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    tr_row[hh] = 16 * hh + 4 * g4 + (n >> 2);
-    tr_swz[hh] = swz<NCH>(tr_row[hh]);
-  }
+  // Chunk 2 * e + (q >> 1) of a row stored at chunk (2 * e) ^ (q >> 1) ^ swz:
+  // with rows a power of two of chunks, the byte offset is tr_at ^ (32 * e);
+  // rows 16 .. 31 take the same swizzle as rows 0 .. 15, 16 rows further on.
+  const int tr_q = n & 3, tr_row = 4 * g4 + (n >> 2);
+  const uint32_t tr_at =
+      (uint32_t)(tr_row * kRow + (((tr_q >> 1) ^ swz<NCH>(tr_row)) * 16) + (tr_q & 1) * 8);
 
   f32x4 acc[CG][DPL];
   float nmu[CG], thr[CG], l[CG];
@@ -309,16 +313,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  for (int j = 0; j < wg_tiles; ++j) {
+  auto tile = [&](int j, SM& cur, SM& nxt) {
     // this wave's share of tile j has landed; the barrier makes every
     // share visible and tells that every wave is done with tile j - 1,
     // whose buffer the loads of tile j + 1 then overwrite
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (j + 1 < wg_tiles) load_tile(j + 1);
-    if (j >= my_tiles) continue;   // this wave's columns end before the tile
-    const unsigned char* kt = sm.kv[j & 1][0];
-    const unsigned char* vt = sm.kv[j & 1][1];
+    if (j + 1 < wg_tiles) load_tile(j + 1, nxt);
+    if (j >= my_tiles) return;   // this wave's columns end before the tile
+    const unsigned char* kt = cur.kv[0];
+    const unsigned char* vt = cur.kv[1];
 
     // ---- the tile's K rows as E values (8-bit codes widened here)
     u32x4 ka[2][KSTEPS];
@@ -338,9 +342,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     }
 
+    auto read_va = [&](int e) {
+      uint32_t w[4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vt + (tr_at ^ (32u * e)) + hh * 16 * kRow));
+        const u32x2 y = __builtin_bit_cast(u32x2, x);
+        w[2 * hh] = y[0];
+        w[2 * hh + 1] = y[1];
+      }
+      return u32x4{w[0], w[1], w[2], w[3]};
+    };
+    u32x4 vall[DPL];
     // ---- scores and probabilities: group c + 1's products are issued in
-    // the same stretch of code as group c's exponentials, interleaved one
-    // product to three vector instructions
+    // the same stretch of code as group c's vector work, with a hint to
+    // interleave one product to three vector instructions
     const bool edge = 32 * j + 32 > lim_min;   // some column's bound or the context ends here
     const int t0 = 32 * j + 4 * g4;            // token of score row 0 of unit 0
     u32x4 pb[CG];
@@ -373,6 +390,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
       }
       if (c + 1 < CG) scores(ka, qv[c + 1], sn);
+      if constexpr (!k8) {
+        // every V^T operand of the tile, in the K operands' registers, while
+        // the exponentials run
+        if (c + 2 == CG) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) vall[e] = read_va(e);
+        }
+      }
       float p[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) p[k] = fast_exp2(__builtin_fmaf(sv[k], cs, nmu[c]));   // exp2(-inf) == 0
@@ -391,35 +416,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 
     if constexpr (!k8) {
-      auto read_va = [&](int e) {
-        uint32_t w[4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int ch = (2 * e + (tr_q >> 1)) ^ tr_swz[hh];
-          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vt + tr_row[hh] * kRow + ch * 16 + (tr_q & 1) * 8));
-          const u32x2 y = __builtin_bit_cast(u32x2, x);
-          w[2 * hh] = y[0];
-          w[2 * hh + 1] = y[1];
-        }
-        return u32x4{w[0], w[1], w[2], w[3]};
-      };
       // the operands of the next products are read while those of e are
       // used (the compiler keeps one pair of reads ahead)
       // the value products at raised wave priority (when both waves of the
       // SIMD are ready to issue, these go first; measured 0.5-1% faster)
       __builtin_amdgcn_s_setprio(1);
-      u32x4 vq[3];
-      vq[0] = read_va(0);
-      if (DPL > 1) vq[1] = read_va(1);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        if (e + 2 < DPL) vq[(e + 2) % 3] = read_va(e + 2);
+      for (int e = 0; e < DPL; ++e)
 #pragma unroll
-        for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(vq[e % 3], pb[c], acc[c][e]);
-      }
+        for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(vall[e], pb[c], acc[c][e]);
       __builtin_amdgcn_s_setprio(0);
-      continue;
+      return;
     }
     // ---- 8-bit caches: one A operand per output dim e serves every group
     uint32_t vv[2][4][VW];
@@ -457,11 +464,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int c = 0; c < CG; ++c) acc[c][e] = Ops::qk(va, pb[c], acc[c][e]);
     }
+  };
+  // two buffers, each its own LDS object named at compile time, so that
+  // the reads of one tile need not wait for the loads into the other
+  for (int j = 0; j < wg_tiles; j += 2) {
+    tile(j, sm0, sm1);
+    if (j + 1 < wg_tiles) tile(j + 1, sm1, sm0);
   }
   // the first tile any wave found naming a block outside the pool, through
   // the K/V buffers once every wave is done with them
   __syncthreads();
-  int* bad = reinterpret_cast<int*>(&sm.kv[0][0][0]);
+  int* bad = reinterpret_cast<int*>(&sm0.kv[0][0]);
   if (lane == 0) bad[wave] = my_bad;
   __syncthreads();
   const int bad_tile = min(min(bad[0], bad[1]), min(bad[2], bad[3]));
