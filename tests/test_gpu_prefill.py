@@ -1,8 +1,10 @@
 """Paged prefill (causal multi-token) attention on the GPU against the
 oracle: ragged query counts (whole prompts, chunks of a longer context, one
 query, more queries than tokens, none), MHA and grouped heads, head_dim 64
-and 128, block sizes 16 and 32, NaN in every slot no query may see, and the
-Llama-3-8B-shaped prefill batch at full size on sampled rows."""
+and 128, block sizes 16 and 32, NaN in every slot no query may see, the
+Llama-3-8B-shaped prefill batch at full size on sampled rows, and a seeded
+random sweep over head layouts, dtypes, head dims, block sizes, cache types
+and length mixes of up to 1600 tokens."""
 
 import math
 
@@ -314,3 +316,81 @@ def test_prefill_fp8_after_quantising_write():
     fp8.reshape_and_cache_fp8(k, v, kw, vw, slots, ks, vs)
     want = fp8.prefill_fp8(q, kw, vw, tables, cl, qs, 1 / math.sqrt(hd), ks, vs, hkv)
     assert float(np.abs(out.cpu().double().numpy() - want).max()) <= TOL[torch.bfloat16]
+
+
+def _sweep_case(i):
+    """Seeded random prefill batch i: head layout, dtype, head dim, block
+    size, cache type, 1-6 sequences of 1-1600 tokens (log-uniform), each
+    with a whole prompt, a chunk, no query or more queries than tokens."""
+    rng = np.random.default_rng(7000 + i)
+    dtype = (torch.float16, torch.bfloat16)[i % 2]
+    fp8 = i % 4 >= 2
+    hd = (64, 128)[(i // 4) % 2]
+    bs = (16, 32)[(i // 3) % 2]
+    g = (1, 2, 4, 8, 16)[i % 5]
+    hkv = (1, 2)[(i // 5) % 2]
+    n_seq = int(rng.integers(1, 7))
+    lens = [int(np.exp(rng.uniform(0, np.log(1600)))) for _ in range(n_seq)]
+    nq = []
+    for L in lens:
+        kind = rng.integers(0, 4)
+        nq.append(L if kind == 0 else int(rng.integers(1, min(L, 200) + 1)) if kind == 1 else
+                  0 if kind == 2 else L + int(rng.integers(1, 9)))
+    if max(nq) == 0:
+        nq[0] = lens[0]
+    return rng, dtype, fp8, hd, bs, g * hkv, hkv, lens, nq
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_prefill_random_sweep(i):
+    """Random batches over the supported space against the oracle, on every
+    row of short sequences and on the first, last and eight random rows of
+    long ones (the rest finite)."""
+    from oracle import fp8 as ofp8
+    rng, dtype, fp8, hd, bs, hq, hkv, lens, nq = _sweep_case(i)
+    say("prefill sweep", i, dtype, "fp8" if fp8 else "16-bit", hq, hkv, hd, bs, lens, nq)
+    nblk = sum(-(-L // bs) for L in lens) + 3
+    if fp8:
+        # codes as floats (no NaN code among the owned ones), paged, then NaN codes
+        # in every slot no sequence owns
+        ks = [rng.integers(0, 256, (L, hkv, hd)).astype(np.float64) for L in lens]
+        vs = [rng.integers(0, 256, (L, hkv, hd)).astype(np.float64) for L in lens]
+        for x in ks + vs:
+            x[(x.astype(np.int64) & 0x7F) == 0x7F] = 0
+        kp, vp, tables, cl, _ = pins.page(ks, vs, bs, nblk, rng)
+        kc = np.where(np.isnan(kp), 0x7F, kp).astype(np.uint8)
+        vc = np.where(np.isnan(vp), 0xFF, vp).astype(np.uint8)
+        kt, vt = torch.from_numpy(kc), torch.from_numpy(vc)
+    else:
+        ks = [rng.standard_normal((L, hkv, hd)) for L in lens]
+        vs = [rng.standard_normal((L, hkv, hd)) for L in lens]
+        kp, vp, tables, cl, _ = pins.page(ks, vs, bs, nblk, rng)
+        kt, vt = torch.from_numpy(kp).to(dtype), torch.from_numpy(vp).to(dtype)
+    qs = np.concatenate([[0], np.cumsum(nq)])
+    q = torch.from_numpy(rng.standard_normal((int(qs[-1]), hq, hd))).to(dtype)
+    scale = float(rng.uniform(0.5, 1.5)) / math.sqrt(hd)
+    k_scale, v_scale = 1.0 / 96, 1.0 / 128
+    out = torch.full(q.shape, float("nan"), dtype=dtype, device=DEV)
+    extra = dict(k_scale=k_scale, v_scale=v_scale) if fp8 else {}
+    pk.paged_attention_prefill(out, q.to(DEV), kt.to(DEV), vt.to(DEV),
+                               torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(DEV),
+                               torch.from_numpy(np.ascontiguousarray(cl, np.int32)).to(DEV),
+                               torch.from_numpy(qs.astype(np.int32)).to(DEV), scale,
+                               int(max(nq)), int(max(lens)), **extra)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    rows = []
+    for s, n in enumerate(nq):
+        r0 = int(qs[s])
+        if n <= 40:
+            rows += range(r0, r0 + n)
+        else:
+            rows += list(range(r0, r0 + 8)) + list(range(r0 + n - 8, r0 + n))
+            rows += [int(x) for x in rng.choice(np.arange(r0 + 8, r0 + n - 8), 8, replace=False)]
+    if fp8:
+        want = ofp8.prefill_fp8(q, kc, vc, tables, cl, qs, scale, k_scale, v_scale, hkv, rows=rows)
+    else:
+        want = oracle.prefill(q, kt, vt, tables, cl, qs, scale, hkv, rows=rows)
+    err = float(np.abs(got[rows] - want[rows]).max())
+    assert err <= TOL[dtype], f"max abs err {err}"
