@@ -45,11 +45,12 @@
 //                     eight tokens' V values at one dim form its A operand,
 //                     read by two transposing LDS reads (ds_read_b64_tr_b16)
 //                     for 16-bit caches (output row n of product e is dim
-//                     16*e + n; all of a tile's are issued once its score
-//                     products are, into the K operands' registers), and for 8-bit codes widened from the lane's
+//                     16*e + n), and for 8-bit codes widened from the lane's
 //                     V rows at DPL consecutive dims and regrouped into token
 //                     pairs per dim by v_perm (row n of product e: dim
-//                     DPL*n + e).
+//                     DPL*n + e); either way all of a tile's V reads are
+//                     issued once its score products are, into the K
+//                     operands' registers.
 //
 // The row sums take the probabilities as rounded for the product (a dot2
 // against ones), so numerator and denominator use the same values.  Loads
@@ -355,6 +356,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       return u32x4{w[0], w[1], w[2], w[3]};
     };
     u32x4 vall[DPL];
+    uint32_t vraw[2][4][VL];
     // ---- scores and probabilities: group c + 1's products are issued in
     // the same stretch of code as group c's vector work, with a hint to
     // interleave one product to three vector instructions
@@ -390,12 +392,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
       }
       if (c + 1 < CG) scores(ka, qv[c + 1], sn);
-      if constexpr (!k8) {
-        // every V^T operand of the tile, in the K operands' registers, while
-        // the exponentials run
-        if (c + 2 == CG) {
+      // every V operand of the tile, in the K operands' registers, while the
+      // exponentials run (8-bit: the codes, widened at the products)
+      if (c + 2 == CG) {
+        if constexpr (!k8) {
 #pragma unroll
           for (int e = 0; e < DPL; ++e) vall[e] = read_va(e);
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              if constexpr (VL == 1) {
+                vraw[hh][rr][0] = *(lds_u32*)(vt + v_at[hh][rr]);
+              } else if constexpr (VL == 2) {
+                const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
+                vraw[hh][rr][0] = y[0];
+                vraw[hh][rr][1] = y[1];
+              } else {
+                const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vraw[hh][rr][w] = y[w];
+              }
+            }
         }
       }
       float p[8];
@@ -433,30 +452,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        uint32_t x[VL];
-        if constexpr (VL == 1) {
-          x[0] = *(lds_u32*)(vt + v_at[hh][rr]);
-        } else if constexpr (VL == 2) {
-          const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
-          x[0] = y[0];
-          x[1] = y[1];
-        } else {
-          const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
+      for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) x[w] = y[w];
+        for (int w = 0; w < VL; ++w) {
+          vv[hh][rr][2 * w] = codes_to_pair<E, false>(vraw[hh][rr][w]);
+          vv[hh][rr][2 * w + 1] = codes_to_pair<E, true>(vraw[hh][rr][w]);
         }
-        if constexpr (k8) {
-#pragma unroll
-          for (int w = 0; w < VL; ++w) {
-            vv[hh][rr][2 * w] = codes_to_pair<E, false>(x[w]);
-            vv[hh][rr][2 * w + 1] = codes_to_pair<E, true>(x[w]);
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < VW; ++w) vv[hh][rr][w] = x[w];
-        }
-      }
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
       const u32x4 va = {pair_of(e, vv[0][0], vv[0][1]), pair_of(e, vv[0][2], vv[0][3]),
