@@ -143,3 +143,20 @@ def test_counter_record_takes_both_counters_from_one_kernel(tmp_path, monkeypatc
     rec = json.loads(out.read_text())["workloads"]["tiny_fp32"]
     assert rec["kernel"].startswith("void pkv::decode_valu_kernel")
     assert rec["fetch_kib_per_launch"] == 300.0 and rec["write_kib_per_launch"] == 4.0
+
+
+def test_counter_record_matches_the_kernel_sources_and_every_workload_has_its_trace():
+    """The committed HBM-counter record was taken on the kernels in the tree
+    (the bench reports its traffic only then), and each workload in it has
+    its kernel-trace summary under profiles/ naming the same workload."""
+    sys.path.insert(0, ROOT)
+    import glob
+    import json
+    import bench
+    rec = json.load(open(os.path.join(ROOT, "profiles", "decode_traffic.json")))
+    assert rec["sources_sha256"] == bench.kernel_sources_digest(), \
+        "kernels changed since the counters were taken: profile again"
+    for key, r in rec["workloads"].items():
+        hits = glob.glob(os.path.join(ROOT, "profiles", f"*__{key}.md"))
+        assert len(hits) == 1, key
+        assert r["hbm_bytes_per_launch"] > 0 and r["alg_bytes_per_launch"] > 0, key
