@@ -383,8 +383,7 @@ struct Layout {
 
 size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
-Layout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                        const Plan& pl) {
+Layout workspace_layout(int num_seqs, int num_q_heads, int head_dim, const Plan& pl) {
   Layout lo;
   const size_t states = pl.max_parts > 1 ? (size_t)num_seqs * num_q_heads * pl.max_parts : 0;
   lo.part_o = 0;
@@ -422,7 +421,7 @@ GroupedLayout grouped_layout(int num_groups, int num_kv_heads, int head_dim, int
 
 size_t workspace_for(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                      const Plan& pl) {
-  return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, pl).total;
+  return workspace_layout(num_seqs, num_q_heads, head_dim, pl).total;
 }
 
 // ------------------------------------------------ allocation-free decode
@@ -563,7 +562,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                             max_blocks_per_seq, max_context_len,
                             kv_fp8 ? (dtype | PKV_KV_E4M3) : dtype, partition, path, grid);
   if (pl.status != PKV_OK) return pl.status;
-  const Layout lo = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, pl);
+  const Layout lo = workspace_layout(num_seqs, num_q_heads, head_dim, pl);
   const size_t need = lo.total;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
