@@ -4,7 +4,6 @@ entries, lengths past the table, repeated or out-of-pool slots, copy
 destinations repeated or also sources, malformed query offsets) with
 PKV_EINVAL before anything is enqueued.  Valid calls behave as without it."""
 
-import numpy as np
 import pytest
 import torch
 

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import pins
-from gpu_helpers import DEV, TOL, max_err, say, upload_case
+from gpu_helpers import TOL, max_err, say, upload_case
 from paged_kv_cache_389_amd import _native as pk
 
 pytestmark = pytest.mark.gpu
