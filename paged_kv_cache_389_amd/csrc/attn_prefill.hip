@@ -27,7 +27,11 @@
 // compile time and the compiler does not make it wait for the loads in
 // flight into the other one.  The rows of a tile sit in LDS with their 16-byte
 // chunks swizzled (chunk c of row r at c ^ swz(r)), so that the operand
-// reads below touch distinct banks.  Per tile and group:
+// reads below touch distinct banks.  Per tile, the score products of every
+// group are issued back to back and the column maxima follow in the same
+// stretch of code, so that one group's maximum is taken while the next
+// group's products run; whether any reference must move is decided once for
+// the tile.  Per tile and group:
 //
 //   S^T = K Q^T       per unit, 16x16x32 MFMAs over the head dim (K rows as
 //                     the A operand, read from LDS; Q^T, the B operand, held
@@ -357,81 +361,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     };
     u32x4 vall[DPL];
     uint32_t vraw[2][4][VL];
-    // ---- scores and probabilities: group c + 1's products are issued in
-    // the same stretch of code as group c's vector work, with a hint to
-    // interleave one product to three vector instructions
+    // ---- scores of every group, issued back to back; the maxima follow in
+    // the same stretch (no branch between), then one decision per tile
     const bool edge = 32 * j + 32 > lim_min;   // some column's bound or the context ends here
     const int t0 = 32 * j + 4 * g4;            // token of score row 0 of unit 0
     u32x4 pb[CG];
-    float sn[8];
-    scores(ka, qv[0], sn);
+    float sv[CG][8];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) scores(ka, qv[c], sv[c]);
+    // every V operand of the tile, in the K operands' registers, while the
+    // exponentials run (8-bit: the codes, widened at the products)
+      if constexpr (!k8) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vall[e] = read_va(e);
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            if constexpr (VL == 1) {
+              vraw[hh][rr][0] = *(lds_u32*)(vt + v_at[hh][rr]);
+            } else if constexpr (VL == 2) {
+              const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
+              vraw[hh][rr][0] = y[0];
+              vraw[hh][rr][1] = y[1];
+            } else {
+              const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) vraw[hh][rr][w] = y[w];
+            }
+          }
+      }
+    float lm[CG];
+    bool up = false;
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
-      float sv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) sv[k] = sn[k];
       if (edge) {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (t0 + 16 * (k / 4) + (k % 4) >= limit[c]) sv[k] = -INFINITY;
+          if (t0 + 16 * (k / 4) + (k % 4) >= limit[c]) sv[c][k] = -INFINITY;
       }
-      const float lm = max3f(max3f(sv[0], sv[1], sv[2]), max3f(sv[3], sv[4], sv[5]),
-                             __builtin_elementwise_maximum(sv[6], sv[7]));
-      if (__any(lm > thr[c])) {
-        // move the reference to the column maximum (across the four token
-        // groups of the column) and rescale what has been accumulated
-        const float mo = thr[c] == -INFINITY ? -INFINITY : -nmu[c];   // none yet: -inf
-        const float mn = fmaxf(mo, rows_max(lm) * cs);
-        const float corr = mo == -INFINITY ? 1.f : fast_exp2(mo - mn);
-        if (mn != -INFINITY) {
-          nmu[c] = -mn;
-          thr[c] = (mn + kPrefillSlack) * inv_cs;
-        }
-        l[c] *= corr;
+      lm[c] = max3f(max3f(sv[c][0], sv[c][1], sv[c][2]), max3f(sv[c][3], sv[c][4], sv[c][5]),
+                    __builtin_elementwise_maximum(sv[c][6], sv[c][7]));
+      up = up || lm[c] > thr[c];
+    }
+    if (__any(up)) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
-      }
-      if (c + 1 < CG) scores(ka, qv[c + 1], sn);
-      // every V operand of the tile, in the K operands' registers, while the
-      // exponentials run (8-bit: the codes, widened at the products)
-      if (c + 2 == CG) {
-        if constexpr (!k8) {
+      for (int c = 0; c < CG; ++c) {
+        if (__any(lm[c] > thr[c])) {
+          // move the reference to the column maximum (across the four token
+          // groups of the column) and rescale what has been accumulated
+          const float mo = thr[c] == -INFINITY ? -INFINITY : -nmu[c];   // none yet: -inf
+          const float mn = fmaxf(mo, rows_max(lm[c]) * cs);
+          const float corr = mo == -INFINITY ? 1.f : fast_exp2(mo - mn);
+          if (mn != -INFINITY) {
+            nmu[c] = -mn;
+            thr[c] = (mn + kPrefillSlack) * inv_cs;
+          }
+          l[c] *= corr;
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) vall[e] = read_va(e);
-        } else {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              if constexpr (VL == 1) {
-                vraw[hh][rr][0] = *(lds_u32*)(vt + v_at[hh][rr]);
-              } else if constexpr (VL == 2) {
-                const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
-                vraw[hh][rr][0] = y[0];
-                vraw[hh][rr][1] = y[1];
-              } else {
-                const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) vraw[hh][rr][w] = y[w];
-              }
-            }
+          for (int e = 0; e < DPL; ++e) acc[c][e] *= corr;
         }
       }
+    }
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
       float p[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) p[k] = fast_exp2(__builtin_fmaf(sv[k], cs, nmu[c]));   // exp2(-inf) == 0
+      for (int k = 0; k < 8; ++k) p[k] = fast_exp2(__builtin_fmaf(sv[c][k], cs, nmu[c]));   // exp2(-inf) == 0
       pb[c] = u32x4{Ops::pack2(p[0], p[1]), Ops::pack2(p[2], p[3]), Ops::pack2(p[4], p[5]),
                     Ops::pack2(p[6], p[7])};
 #pragma unroll
       for (int w = 0; w < 4; ++w) l[c] = Ops::sum2(pb[c][w], l[c]);
-      if (c + 1 < CG) {
-#pragma unroll
-        for (int k = 0; k < 2 * KSTEPS; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three vector instructions
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     if constexpr (!k8) {
