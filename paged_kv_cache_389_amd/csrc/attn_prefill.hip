@@ -28,10 +28,9 @@
 // flight into the other one.  The rows of a tile sit in LDS with their 16-byte
 // chunks swizzled (chunk c of row r at c ^ swz(r)), so that the operand
 // reads below touch distinct banks.  Per tile, the score products of every
-// group are issued back to back and the column maxima follow in the same
-// stretch of code, so that one group's maximum is taken while the next
-// group's products run; whether any reference must move is decided once for
-// the tile.  Per tile and group:
+// group are issued back to back (the tile's V reads go out among them), the
+// column maxima follow, and whether any reference must move is decided once
+// for the tile.  Per tile and group:
 //
 //   S^T = K Q^T       per unit, 16x16x32 MFMAs over the head dim (K rows as
 //                     the A operand, read from LDS; Q^T, the B operand, held
@@ -361,8 +360,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     };
     u32x4 vall[DPL];
     uint32_t vraw[2][4][VL];
-    // ---- scores of every group, issued back to back; the maxima follow in
-    // the same stretch (no branch between), then one decision per tile
+    // ---- scores of every group, issued back to back; then the maxima and
+    // one decision per tile on moving references
     const bool edge = 32 * j + 32 > lim_min;   // some column's bound or the context ends here
     const int t0 = 32 * j + 4 * g4;            // token of score row 0 of unit 0
     u32x4 pb[CG];
@@ -371,27 +370,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int c = 0; c < CG; ++c) scores(ka, qv[c], sv[c]);
     // every V operand of the tile, in the K operands' registers, while the
     // exponentials run (8-bit: the codes, widened at the products)
-      if constexpr (!k8) {
+    if constexpr (!k8) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) vall[e] = read_va(e);
-      } else {
+      for (int e = 0; e < DPL; ++e) vall[e] = read_va(e);
+    } else {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            if constexpr (VL == 1) {
-              vraw[hh][rr][0] = *(lds_u32*)(vt + v_at[hh][rr]);
-            } else if constexpr (VL == 2) {
-              const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
-              vraw[hh][rr][0] = y[0];
-              vraw[hh][rr][1] = y[1];
-            } else {
-              const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (VL == 1) {
+            vraw[hh][rr][0] = *(lds_u32*)(vt + v_at[hh][rr]);
+          } else if constexpr (VL == 2) {
+            const u32x2 y = *(lds_u32x2*)(vt + v_at[hh][rr]);
+            vraw[hh][rr][0] = y[0];
+            vraw[hh][rr][1] = y[1];
+          } else {
+            const u32x4 y = *(lds_u32x4*)(vt + v_at[hh][rr]);
 #pragma unroll
-              for (int w = 0; w < 4; ++w) vraw[hh][rr][w] = y[w];
-            }
+            for (int w = 0; w < 4; ++w) vraw[hh][rr][w] = y[w];
           }
-      }
+        }
+    }
     float lm[CG];
     bool up = false;
 #pragma unroll
